@@ -1,0 +1,109 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case compiles a copy of one oracle module with one planted mistake (a
+dropped term, a wrong sign, a transposed operand, an off-by-one), swaps it
+in, and checks that at least one pin test then fails.  CPU only; the real
+oracle is restored after every case.
+"""
+import importlib.util
+import inspect
+import os
+import sys
+
+import pytest
+
+import oracle
+import oracle.ckpt
+import oracle.plan
+import oracle.refresh
+import test_oracle_ckpt as T_ckpt
+import test_oracle_plan as T_plan
+import test_oracle_refresh as T_ref
+
+ORACLE_DIR = os.path.dirname(inspect.getfile(oracle))
+
+
+def _mutant(modname, old, new):
+    path = os.path.join(ORACLE_DIR, modname + ".py")
+    src = open(path).read()
+    assert src.count(old) >= 1, (modname, old)
+    src = src.replace(old, new, 1)
+    spec = importlib.util.spec_from_loader("oracle._mutant_" + modname, loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    mod.__package__ = "oracle"
+    sys.modules[spec.name] = mod          # dataclasses look their module up
+    exec(compile(src, path + " (mutant)", "exec"), mod.__dict__)
+    return mod
+
+
+def _swap(monkeypatch, modname, mod):
+    """Point the oracle package, its submodules and the pin modules at the
+    mutant's functions."""
+    real = getattr(oracle, modname)
+    for name, obj in vars(mod).items():
+        if callable(obj) and getattr(real, name, None) is not None and not name.startswith("__"):
+            for holder in (oracle, oracle.plan, oracle.ckpt, oracle.refresh):
+                if getattr(holder, name, None) is getattr(real, name):
+                    monkeypatch.setattr(holder, name, obj)
+
+
+def _some_pin_fails(pins):
+    for pin in pins:
+        try:
+            pin()
+        except Exception:
+            return True
+    return False
+
+
+PLAN_PINS = [T_plan.test_half_decay_gives_log2_1000, T_plan.test_exact_tie_is_omitted,
+             T_plan.test_eq7_windows_worked_by_hand, T_plan.test_gate_inverts_to_chosen_decay,
+             T_plan.test_horizon_is_where_decay_reaches_eps,
+             T_plan.test_static_logit_lengthens_horizons,
+             T_plan.test_ragged_offsets_order_and_bytes,
+             T_plan.test_c1_budget_decomposition_and_eq8,
+             T_plan.test_eq6_reproduces_kda_2p63_and_eq8_2p64,
+             T_plan.test_refreshed_heads_rule, T_plan.test_mask_equals_decay_threshold_rule]
+CKPT_PINS = [T_ckpt.test_round_trip_equals_masked_state, T_ckpt.test_pack_is_bijection_onto_payload,
+             T_ckpt.test_raw_bits_survive, T_ckpt.test_unpack_overwrites_every_byte_and_zero_is_positive,
+             T_ckpt.test_conv_bytes_follow_payload]
+REFRESH_PINS = [T_ref.test_rank1_matches_printed_matrix_form, T_ref.test_beta_one_recalls_last_value_exactly,
+                T_ref.test_beta_zero_is_pure_column_decay, T_ref.test_one_hot_write_then_decay_closed_form,
+                T_ref.test_contraction_bound, lambda: T_ref.test_refresh_expected_wiring_gate_and_rows(8, 8),
+                lambda: T_ref.test_refresh_expected_wiring_gate_and_rows(8, 4),
+                T_ref.test_refresh_expected_respects_windows, T_ref.test_gdn_scalar_decay_equals_broadcast]
+
+MUTATIONS = [
+    # plan
+    ("plan", "np.exp(A_log) * softplus(a + dt_bias)", "np.exp(A_log) * softplus(a - dt_bias)", PLAN_PINS),
+    ("plan", "return -np.exp(A_log) * softplus", "return -np.exp(-A_log) * softplus", PLAN_PINS),
+    ("plan", "return np.float64(math.log(eps)) / g", "return np.float64(math.log(eps)) * g", PLAN_PINS),
+    ("plan", "retained = H > w_max", "retained = H >= w_max", PLAN_PINS),
+    ("plan", "while p < x:", "while p <= x:", PLAN_PINS),
+    ("plan", "min(max(next_pow2(H_s), 4), w_max)", "max(min(next_pow2(H_s), w_max), 4)", PLAN_PINS),
+    ("plan", "p_off += lay.r * lay.unit_bytes", "p_off += lay.n * lay.unit_bytes", PLAN_PINS),
+    ("plan", "return np.flatnonzero(~per_head.all(axis=1))", "return np.flatnonzero(~per_head.any(axis=1))", PLAN_PINS),
+    ("plan", "c_dense += lay.conv_bytes", "c_dense += 0", PLAN_PINS + CKPT_PINS),
+    # pack / unpack
+    ("ckpt", "P[j] = S[h, :, k]", "P[j] = S[h, :, (k + 1) % S.shape[2]]", CKPT_PINS),
+    ("ckpt", "S[...] = 0", "pass", CKPT_PINS),
+    ("ckpt", "S[h, :, k] = P[j]", "S[h, :, (k + 1) % S.shape[2]] = P[j]", CKPT_PINS),
+    ("ckpt", "dst[b:b + lay.conv_bytes] = src[a:a + lay.conv_bytes]", "pass", CKPT_PINS),
+    # refresh
+    ("refresh", 'Ak = np.einsum("...ij,...j->...i", A, k)', 'Ak = np.einsum("...ij,...j->...i", S, k)', REFRESH_PINS),
+    ("refresh", "c = beta[..., None] * (v - Ak)", "c = beta[..., None] * (Ak - v)", REFRESH_PINS),
+    ("refresh", "c = beta[..., None] * (v - Ak)", "c = (v - Ak)", REFRESH_PINS),
+    ("refresh", "A = S * alpha[..., None, :]", "A = S * alpha[..., :, None]", REFRESH_PINS),
+    ("refresh", "return A + c[..., :, None] * k[..., None, :]", "return A + k[..., :, None] * c[..., None, :]", REFRESH_PINS),
+    ("refresh", "al = np.exp(gate_log_decay(Al, Db, a))", "al = np.exp(-gate_log_decay(Al, Db, a))", REFRESH_PINS),
+    ("refresh", "g += lay.n_heads * lay.d_k if lay.kind != GDN else lay.n_heads", "g += lay.n_heads * lay.d_k", REFRESH_PINS),
+    ("refresh", "vs = bf16_bits_to_f64(v_bits[t0:t1, vo[li]", "vs = bf16_bits_to_f64(v_bits[t0:t1, ko[li]", REFRESH_PINS),
+]
+
+
+@pytest.mark.parametrize("modname,old,new,pins", MUTATIONS,
+                         ids=[f"{m[0]}:{i}" for i, m in enumerate(MUTATIONS)])
+def test_planted_mistake_is_caught(monkeypatch, modname, old, new, pins):
+    mod = _mutant(modname, old, new)
+    _swap(monkeypatch, modname, mod)
+    assert _some_pin_fails(pins), f"no pin caught: {old!r} -> {new!r}"
