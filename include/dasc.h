@@ -1,0 +1,237 @@
+/*
+ * dasc.h — C ABI of the MI355X (gfx950) state-checkpoint hot path of
+ * decay-aware state compression (dasc).
+ *
+ * Page citations name the page by title and the section / equation there:
+ *   [dasc]     "dasc: Decay-Aware State Compression for Hybrid
+ *              Linear-Attention Serving" (arXiv HTML version);
+ *   [dasc-pp]  the same paper's paperpeel version (Appendix B.2);
+ *   [dasc-sum] the picx.dev summary of dasc, "Methodology" (Eq. 6, Eq. 7).
+ *
+ * Conventions for every call:
+ *   - Return value: DASC_OK (0) or a negative DASC_E* code.  A failing call
+ *     leaves a message for dasc_last_error() (thread-local) and has not
+ *     launched anything.  No C++ exception crosses this boundary.
+ *   - Validation is done on the host from host-known sizes only; the host
+ *     never reads device memory.  Index arrays that live on the device are
+ *     bounds-checked by the kernels themselves: an out-of-range entry is
+ *     skipped (no memory outside the given ranges is touched) and sets a
+ *     bit in the plan's device status word (dasc_plan_status).
+ *   - Data calls (pack, unpack, refresh) are asynchronous on `stream` (a
+ *     hipStream_t; NULL is the default stream) and allocate nothing.  The
+ *     caller owns every device buffer and keeps it valid until the stream
+ *     work completes — in particular a checkpoint being packed stays valid
+ *     (and unchanged) until the pack has completed on its stream, which is
+ *     the pages' transactional-demotion rule ([dasc-pp] Appendix B.2).
+ *   - Device pointers must be 16-byte aligned; strides must be multiples of
+ *     16 bytes.  Pool and dense ranges must not overlap.
+ *
+ * Data layouts (all little-endian, row-major):
+ *   dense checkpoint: for each layer l in order, the temporal state
+ *     [H_l, d_v, d_k] fp32 with k fastest ([dasc] Appendix E.1 indexes the
+ *     state S_{l,h,v,k}); then for each layer in order its conv bytes (bf16,
+ *     copied raw).  dense_bytes = sum_l H_l d_v d_k 4 + sum_l conv_bytes_l.
+ *   pool slot (ragged Scheme 2, [dasc] Appendix B): for each layer in order,
+ *     its r_l retained units in ascending unit order, starting at unit offset
+ *     o_l (o_0 = 0, o_{l+1} = o_l + r_l); a GDN unit is one head [d_v, d_k]
+ *     fp32, a KDA unit (h, k) is the column S[h, :, k] stored as d_v
+ *     contiguous fp32; then every layer's conv bytes (uncompressed,
+ *     [dasc-pp] §4.4).  slot_bytes = sum_l r_l unit_bytes_l + sum conv.
+ *   units: a GDN unit is a head (index h); a KDA unit is a key channel
+ *     (h, k) with index h*d_k + k ([dasc] §4.1).
+ */
+#ifndef DASC_H
+#define DASC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DASC_OK 0
+#define DASC_EINVAL (-1)        /* bad argument (null, size, alignment, overlap) */
+#define DASC_ENOTUPLOADED (-2)  /* data call on a plan whose tables are not on the device */
+#define DASC_EHIP (-3)          /* a HIP runtime call failed */
+#define DASC_ENOMEM (-4)        /* host allocation failed */
+#define DASC_EUNSUPPORTED (-5)  /* shape outside what the kernels implement */
+
+#define DASC_GDN 0  /* head-wise decay: one unit per head */
+#define DASC_KDA 1  /* channel-wise decay: one unit per key channel (h, k) */
+
+/* Bits of the device status word. */
+#define DASC_STATUS_BAD_INDEX 1u   /* a checkpoint / slot index was out of range */
+#define DASC_STATUS_BAD_TOKENS 2u  /* a request's token range was invalid */
+
+typedef struct dasc_plan* dasc_plan_t; /* opaque, library-owned host object */
+
+typedef struct {
+  int32_t kind;          /* DASC_GDN or DASC_KDA */
+  int32_t n_heads;       /* H_l */
+  int32_t d_k;           /* key width (columns of S) */
+  int32_t d_v;           /* value width (rows of S) */
+  const float* A_log;    /* host; one per unit: [H] (GDN) or [H*d_k] (KDA) */
+  const float* dt_bias;  /* host; same shape as A_log */
+  int64_t conv_bytes;    /* bf16 conv-state bytes this layer adds (multiple of 16) */
+} dasc_layer_desc;
+
+typedef struct {
+  int32_t n_layers;
+  int32_t w_replay;             /* Eq. 7 window over all local units; 0 if none */
+  int64_t n_units;              /* sum_l n_l */
+  int64_t n_retained;           /* sum_l r_l */
+  int64_t temporal_dense_bytes; /* B_temp^dense */
+  int64_t temporal_rag_bytes;   /* B_temp^rag */
+  int64_t conv_bytes;           /* B_conv */
+  int64_t dense_bytes;          /* bytes of one dense checkpoint */
+  int64_t slot_bytes;           /* bytes of one pool slot */
+  int64_t r_max;                /* R_max = max_l r_l */
+  double r_bar;                 /* mean_l r_l */
+  double c_temp;                /* [dasc-sum] Eq. 6: sum n_l / sum r_l (inf if none kept) */
+  double c_ckpt;                /* Eq. 6: (B_temp^dense + B_conv) / (B_temp^rag + B_conv) */
+  double c_temp_pad;            /* [dasc] App. B Scheme 1: sum n_l / (L R_max) */
+  double layout_gain;           /* R_max / r_bar */
+  int64_t n_refresh_heads;      /* (layer, head) pairs a refresh replays */
+  int64_t device_bytes;         /* size of the device tables (dasc_plan_upload) */
+  int64_t k_row, v_row;         /* refresh row widths (elements): sum H d_k, sum H d_v */
+  int64_t gate_row, beta_row;   /* sum (H d_k for KDA, H for GDN), sum H */
+} dasc_plan_info;
+
+typedef struct {
+  int32_t kind, n_heads, d_k, d_v;
+  int64_t n_units;       /* n_l */
+  int64_t n_retained;    /* r_l */
+  int64_t unit_offset;   /* o_l (units) */
+  int64_t unit_bytes;    /* d_v d_k 4 (GDN) or d_v 4 (KDA) */
+  int64_t dense_offset;  /* byte offset of the layer's state in a dense checkpoint */
+  int64_t conv_dense_offset;
+  int64_t pool_offset;   /* byte offset of the layer's units in a pool slot */
+  int64_t conv_pool_offset;
+  int64_t conv_bytes;
+  int32_t w_layer;       /* max Eq. 7 window over the layer's local units (0 if none) */
+  int32_t n_refresh_heads;
+  int64_t k_row_offset, v_row_offset, gate_row_offset, beta_row_offset; /* refresh rows */
+} dasc_layer_info;
+
+/*
+ * Build the static selection plan ([dasc] §4.1).  For every unit u:
+ *   g_u   = -exp(A_log_u) * softplus(a_s + dt_bias_u)      ([dasc] §3.3 Eq. 2)
+ *   H_s,u = ln(eps) / g_u                                   ([dasc] §3.3 Eq. 3)
+ *   u is retained (global) iff H_s,u > w_max, else local (omitted).
+ * Local units get the window W_u = clamp(next_pow2(H_s,u), 4, w_max)
+ * ([dasc-sum] Eq. 7).  Computed in double precision on the host.  A gate
+ * that underflows to -0 gives H_s = +inf (retained).
+ * layers: host array of n_layers descriptors (read during the call only).
+ * Requirements: n_heads, d_k, d_v >= 1; d_v*d_k a multiple of 4 (GDN);
+ * d_k and d_v multiples of 4 and at most 128 (KDA); conv_bytes >= 0 and a
+ * multiple of 16; A_log and dt_bias finite; 0 < eps < 1; w_max >= 0.  The
+ * refresh needs d_k == d_v in {16, 32, 64, 128} for every layer it replays
+ * (otherwise dasc_ckpt_refresh_suffix returns DASC_EUNSUPPORTED).
+ * On success *out owns host memory released by dasc_plan_destroy.
+ */
+int dasc_plan_build(const dasc_layer_desc* layers, int32_t n_layers, double a_s,
+                    double eps, int32_t w_max, dasc_plan_t* out);
+
+/* Totals and ratios of a plan (host only). */
+int dasc_plan_query(dasc_plan_t plan, dasc_plan_info* out);
+
+/* One layer's counts and offsets (host only). */
+int dasc_plan_layer(dasc_plan_t plan, int32_t layer, dasc_layer_info* out);
+
+/* Per-unit results for one layer, into caller host arrays of n_l entries
+ * (any pointer may be NULL): retained flag (1/0), H_s (double), and the
+ * Eq. 7 window W_u for local units (0 for retained units). */
+int dasc_plan_units(dasc_plan_t plan, int32_t layer, uint8_t* retained,
+                    double* horizon, int32_t* window);
+
+/* [dasc] Appendix C.1 Eq. 8 on one rank: floor(budget / slot_bytes) - 1 slots
+ * (slot 0 reserved).  dense != 0 prices a dense slot instead of a pool slot.
+ * Returns the count (-1 when the budget holds no slot at all), or INT64_MIN
+ * for a null plan or a negative budget. */
+int64_t dasc_plan_slots(dasc_plan_t plan, int64_t budget_bytes, int32_t dense);
+
+/* Copy the plan's device tables (task lists, channel maps, gate parameters,
+ * status word) into a caller-allocated device buffer of at least
+ * info.device_bytes bytes, 256-byte aligned, on `stream`; the copy is
+ * complete when this call returns.  Later data calls use that buffer, which
+ * must stay valid until the plan is destroyed or uploaded elsewhere.  The
+ * status word is cleared. */
+int dasc_plan_upload(dasc_plan_t plan, void* device_buffer, int64_t bytes, void* stream);
+
+/* Read (and with clear != 0, then clear) the device status word: an OR of
+ * DASC_STATUS_* bits set by kernels since the last clear.  Synchronises
+ * `stream`. */
+int dasc_plan_status(dasc_plan_t plan, uint32_t* status, int32_t clear, void* stream);
+
+int dasc_plan_destroy(dasc_plan_t plan);
+
+/*
+ * Ragged flat-pack, the store path ([dasc] §4.1, Appendix B Scheme 2;
+ * [dasc-pp] Appendix B.2 "Insertion and reuse"): for i in [0, n):
+ *   pool[dst_slot[i]] <- retained units and conv bytes of dense[src_idx[i]],
+ * where dense[j] = dense_base + j*dense_stride (j < n_dense) and pool[s] =
+ * pool_base + s*pool_stride (s < n_slots).  Raw bit copies: bit-exact, NaN
+ * payloads, -0.0 and denormals preserved.  src_idx / dst_slot: device int32
+ * arrays of n entries, in any order; two entries must not name the same
+ * destination slot.  Source checkpoints are read only.
+ */
+int dasc_ckpt_pack(dasc_plan_t plan, const void* dense_base, int64_t dense_stride,
+                   int64_t n_dense, const int32_t* src_idx, void* pool_base,
+                   int64_t pool_stride, int64_t n_slots, const int32_t* dst_slot,
+                   int32_t n, void* stream);
+
+/*
+ * Unpack with zero-fill, dasc-nr ([dasc] §4.2): for i in [0, n):
+ *   dense[dst_idx[i]] <- the retained units of pool[src_slot[i]] exactly,
+ *   +0.0 (all-zero bits) in every local unit, and the stored conv bytes.
+ * Every byte of each destination checkpoint is written; the pool is read
+ * only (the stored checkpoint is unchanged).  Two entries must not name the
+ * same destination checkpoint.
+ */
+int dasc_ckpt_unpack_zero_fill(dasc_plan_t plan, const void* pool_base,
+                               int64_t pool_stride, int64_t n_slots,
+                               const int32_t* src_slot, void* dense_base,
+                               int64_t dense_stride, int64_t n_dense,
+                               const int32_t* dst_idx, int32_t n, void* stream);
+
+/*
+ * Bounded-suffix refresh, dasc-wr ([dasc] §4.2): for each request r in
+ * [0, n), each layer l and each head h the plan replays (GDN: local heads;
+ * KDA: heads with at least one local channel), start from a zero fp32
+ * scratch state S [d_v, d_k] and apply, for every token t of the request,
+ *   S <- S Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ * ([dasc] §3.1 Eq. 1), where alpha_t = exp(g_t) and g_t = -exp(A_log)
+ * softplus(a_t + dt_bias) is the model's gate ([dasc] §3.3 Eq. 2) with the
+ * token's own logit a_t (one per head for GDN, per channel for KDA; A_log
+ * and dt_bias are the plan's).  Then write only the local units of S into
+ * dense[dst_idx[r]]: retained units, the conv bytes and the pool are left
+ * untouched.  A request with zero tokens writes zeros into its local units.
+ * Arithmetic: fp32 state and gate, bf16 inputs widened exactly.
+ * Inputs, token-major over the concatenated tokens of all requests
+ * (T = tok_offsets[n] tokens; layer blocks back to back in layer order,
+ * heads in order inside a block; per-layer starts in dasc_layer_info):
+ *   k     [T, sum_l H_l d_k]  bf16 bits      v    [T, sum_l H_l d_v] bf16 bits
+ *   a     [T, sum_l (H_l d_k for KDA, H_l for GDN)] bf16 bits
+ *   beta  [T, sum_l H_l]      fp32
+ *   tok_offsets [n+1] int64, device: request r owns tokens
+ *     [tok_offsets[r], tok_offsets[r+1]); must be non-decreasing within
+ *     [0, n_tokens] (a request that breaks this is skipped and flagged).
+ *   dst_idx [n] int32, device; two entries must not name the same checkpoint.
+ */
+int dasc_ckpt_refresh_suffix(dasc_plan_t plan, const uint16_t* k, const uint16_t* v,
+                             const uint16_t* a, const float* beta,
+                             const int64_t* tok_offsets, int64_t n_tokens,
+                             void* dense_base, int64_t dense_stride, int64_t n_dense,
+                             const int32_t* dst_idx, int32_t n, void* stream);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* dasc_last_error(void);
+
+/* Library version string. */
+const char* dasc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DASC_H */

@@ -1,0 +1,673 @@
+// Host side of the dasc checkpoint library: the static selection plan, the
+// device task tables, argument validation and the extern "C" entry points.
+//
+// Pages cited by title:
+//   [dasc]     "dasc: Decay-Aware State Compression for Hybrid Linear-Attention
+//              Serving" (arXiv HTML version)
+//   [dasc-sum] the picx.dev summary of dasc, "Methodology" (Eq. 6, Eq. 7)
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <limits>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/dasc.h"
+#include "dasc_internal.h"
+
+using namespace dasc;
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const std::string& msg) {
+  g_error = msg;
+  return code;
+}
+
+// softplus(x) = ln(1 + e^x), without overflow for large x.
+double softplus(double x) {
+  return x > 0.0 ? x + std::log1p(std::exp(-x)) : std::log1p(std::exp(x));
+}
+
+// Smallest power of two >= x for x > 1; 1 otherwise (NaN included).
+double next_pow2(double x) {
+  if (!(x > 1.0)) return 1.0;
+  double p = 1.0;
+  while (p < x) p *= 2.0;
+  return p;
+}
+
+struct LayerPlan {
+  int32_t kind, n_heads, d_k, d_v;
+  int64_t n, r;
+  int64_t conv_bytes;
+  int64_t unit_bytes;
+  int64_t unit_off, dense_off, conv_dense_off, pool_off, conv_pool_off;
+  int64_t k_row_off, v_row_off, g_row_off, b_row_off;
+  int64_t unit_base;  // first unit of the layer in the plan-wide unit order
+  int32_t w_layer;
+  int32_t n_refresh;
+  std::vector<uint8_t> retained;
+  std::vector<double> horizon;
+  std::vector<int32_t> window;
+  std::vector<float> A_log, dt_bias;
+};
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+struct dasc_plan {
+  std::vector<LayerPlan> layers;
+  double a_s = 0, eps = 0;
+  int32_t w_max = 0;
+  dasc_plan_info info{};
+  int64_t k_row = 0, v_row = 0, g_row = 0, b_row = 0;
+
+  // host image of the device tables
+  std::vector<CopyTask> pack_copy, unpack_copy;
+  std::vector<KdaTask> kda;
+  std::vector<uint8_t> maps;
+  std::vector<RefreshTask> refresh;
+  std::vector<float> gate_expA, gate_dt;
+  std::vector<Group> kda_groups, refresh_groups;
+  int64_t off_pack = 0, off_unpack = 0, off_kda = 0, off_maps = 0, off_refresh = 0,
+          off_expA = 0, off_dt = 0, off_status = 0, table_bytes = 0;
+
+  uint8_t* device = nullptr;  // caller-owned upload target
+  DeviceTables dev{};
+};
+
+namespace {
+
+void push_range(std::vector<CopyTask>& out, uint64_t dense_off, uint64_t pool_off, uint64_t bytes,
+                uint32_t type) {
+  while (bytes > 0) {
+    uint32_t b = static_cast<uint32_t>(std::min<uint64_t>(bytes, kCopyChunk));
+    CopyTask t{};
+    t.dense_off = dense_off;
+    t.pool_off = pool_off;
+    t.bytes = b;
+    t.type = type;
+    out.push_back(t);
+    dense_off += b;
+    pool_off += b;
+    bytes -= b;
+  }
+}
+
+// Turn the mask into task lists and lay out the device tables.
+void build_tables(dasc_plan* p) {
+  // KDA heads are grouped by shape so that each group uses one kernel.
+  std::vector<std::pair<int, int>> shapes;
+  for (const auto& L : p->layers) {
+    if (L.kind != kKDA) continue;
+    auto s = std::make_pair(L.d_k, L.d_v);
+    if (std::find(shapes.begin(), shapes.end(), s) == shapes.end()) shapes.push_back(s);
+  }
+  for (const auto& L : p->layers) {
+    if (L.kind == kGDN) {
+      int64_t j = 0;
+      for (int h = 0; h < L.n_heads; ++h) {
+        uint64_t d_off = L.dense_off + h * L.unit_bytes;
+        if (L.retained[h]) {
+          uint64_t p_off = L.pool_off + j * L.unit_bytes;
+          push_range(p->pack_copy, d_off, p_off, L.unit_bytes, kTaskCopy);
+          push_range(p->unpack_copy, d_off, p_off, L.unit_bytes, kTaskCopy);
+          ++j;
+        } else {
+          push_range(p->unpack_copy, d_off, 0, L.unit_bytes, kTaskZero);
+        }
+      }
+    } else {
+      // Fully omitted KDA heads have no task of their own: unpack clears them.
+      const int64_t head_bytes = int64_t(L.d_v) * L.d_k * 4;
+      for (int h = 0; h < L.n_heads; ++h) {
+        int r = 0;
+        for (int k = 0; k < L.d_k; ++k) r += L.retained[h * L.d_k + k];
+        if (r == 0) push_range(p->unpack_copy, L.dense_off + h * head_bytes, 0, head_bytes, kTaskZero);
+      }
+    }
+  }
+  // KDA tasks, shape group by shape group.
+  for (const auto& s : shapes) {
+    Group g{s.first, s.second, static_cast<uint32_t>(p->kda.size()), 0};
+    for (const auto& L : p->layers) {
+      if (L.kind != kKDA || L.d_k != s.first || L.d_v != s.second) continue;
+      const int64_t head_bytes = int64_t(L.d_v) * L.d_k * 4;
+      int64_t j = 0;  // retained units of the layer seen so far
+      for (int h = 0; h < L.n_heads; ++h) {
+        uint8_t map[kMapBytes];
+        std::memset(map, 0, 128);
+        std::memset(map + 128, kLocal, 128);
+        uint32_t r = 0;
+        for (int k = 0; k < L.d_k; ++k) {
+          if (L.retained[h * L.d_k + k]) {
+            map[r] = static_cast<uint8_t>(k);
+            map[128 + k] = static_cast<uint8_t>(r);
+            ++r;
+          }
+        }
+        if (r > 0) {
+          KdaTask t{};
+          t.dense_off = L.dense_off + h * head_bytes;
+          t.pool_off = L.pool_off + j * L.unit_bytes;
+          t.r = r;
+          t.map_idx = static_cast<uint32_t>(p->maps.size() / kMapBytes);
+          p->maps.insert(p->maps.end(), map, map + kMapBytes);
+          p->kda.push_back(t);
+        }
+        j += r;
+      }
+    }
+    g.count = static_cast<uint32_t>(p->kda.size()) - g.first;
+    if (g.count) p->kda_groups.push_back(g);
+  }
+  // Conv state: one contiguous block after the temporal payload on both sides.
+  const dasc_plan_info& I = p->info;
+  push_range(p->pack_copy, I.temporal_dense_bytes, I.temporal_rag_bytes, I.conv_bytes, kTaskCopy);
+  push_range(p->unpack_copy, I.temporal_dense_bytes, I.temporal_rag_bytes, I.conv_bytes, kTaskCopy);
+
+  // Refresh tasks, grouped by head width.
+  std::vector<std::pair<int, int>> rshapes;
+  for (const auto& L : p->layers) {
+    auto s = std::make_pair(L.d_k, L.d_v);
+    if (L.n_refresh && std::find(rshapes.begin(), rshapes.end(), s) == rshapes.end())
+      rshapes.push_back(s);
+  }
+  for (const auto& s : rshapes) {
+    Group g{s.first, s.second, static_cast<uint32_t>(p->refresh.size()), 0};
+    for (const auto& L : p->layers) {
+      if (L.d_k != s.first || L.d_v != s.second) continue;
+      const int64_t head_bytes = int64_t(L.d_v) * L.d_k * 4;
+      for (int h = 0; h < L.n_heads; ++h) {
+        RefreshTask t{};
+        bool any_local = false;
+        for (int k = 0; k < L.d_k && k < 128; ++k) {
+          bool local = L.kind == kGDN ? !L.retained[h] : !L.retained[h * L.d_k + k];
+          if (local) {
+            t.local[k >> 5] |= 1u << (k & 31);
+            any_local = true;
+          }
+        }
+        if (!any_local) continue;
+        t.dense_off = L.dense_off + h * head_bytes;
+        t.k_off = static_cast<uint32_t>(L.k_row_off + int64_t(h) * L.d_k);
+        t.v_off = static_cast<uint32_t>(L.v_row_off + int64_t(h) * L.d_v);
+        t.g_off = static_cast<uint32_t>(L.g_row_off + (L.kind == kKDA ? int64_t(h) * L.d_k : h));
+        t.b_off = static_cast<uint32_t>(L.b_row_off + h);
+        t.param_off = static_cast<uint32_t>(L.unit_base + (L.kind == kKDA ? int64_t(h) * L.d_k : h));
+        t.kind = static_cast<uint32_t>(L.kind);
+        p->refresh.push_back(t);
+      }
+    }
+    g.count = static_cast<uint32_t>(p->refresh.size()) - g.first;
+    if (g.count) p->refresh_groups.push_back(g);
+  }
+
+  // Gate parameters, per unit in plan order: exp(A_log) rounded once from
+  // double, and dt_bias as given.
+  for (const auto& L : p->layers) {
+    for (int64_t u = 0; u < L.n; ++u) {
+      p->gate_expA.push_back(static_cast<float>(std::exp(static_cast<double>(L.A_log[u]))));
+      p->gate_dt.push_back(L.dt_bias[u]);
+    }
+  }
+
+  int64_t o = 0;
+  auto section = [&](int64_t bytes) {
+    int64_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  p->off_pack = section(p->pack_copy.size() * sizeof(CopyTask));
+  p->off_unpack = section(p->unpack_copy.size() * sizeof(CopyTask));
+  p->off_kda = section(p->kda.size() * sizeof(KdaTask));
+  p->off_maps = section(p->maps.size());
+  p->off_refresh = section(p->refresh.size() * sizeof(RefreshTask));
+  p->off_expA = section(p->gate_expA.size() * sizeof(float));
+  p->off_dt = section(p->gate_dt.size() * sizeof(float));
+  p->off_status = section(16);
+  p->table_bytes = o;
+  p->info.device_bytes = o;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dasc_last_error(void) { return g_error.c_str(); }
+
+const char* dasc_version(void) { return "dasc-hip 0.1 (gfx950)"; }
+
+int dasc_plan_build(const dasc_layer_desc* layers, int32_t n_layers, double a_s, double eps,
+                    int32_t w_max, dasc_plan_t* out) {
+  if (!out) return fail(DASC_EINVAL, "plan_build: out is null");
+  *out = nullptr;
+  if (!layers || n_layers <= 0) return fail(DASC_EINVAL, "plan_build: no layers");
+  if (!(eps > 0.0 && eps < 1.0)) return fail(DASC_EINVAL, "plan_build: eps must be in (0, 1)");
+  if (w_max < 0) return fail(DASC_EINVAL, "plan_build: w_max must be >= 0");
+  if (!std::isfinite(a_s)) return fail(DASC_EINVAL, "plan_build: a_s must be finite");
+
+  dasc_plan* p = new (std::nothrow) dasc_plan();
+  if (!p) return fail(DASC_ENOMEM, "plan_build: out of host memory");
+  try {
+    p->a_s = a_s;
+    p->eps = eps;
+    p->w_max = w_max;
+    const double log_eps = std::log(eps);
+    int64_t unit_off = 0, dense_off = 0, pool_off = 0, unit_base = 0;
+    int64_t k_row = 0, v_row = 0, g_row = 0, b_row = 0;
+    for (int32_t l = 0; l < n_layers; ++l) {
+      const dasc_layer_desc& d = layers[l];
+      const std::string at = "plan_build: layer " + std::to_string(l) + ": ";
+      if (d.kind != kGDN && d.kind != kKDA) {
+        delete p;
+        return fail(DASC_EINVAL, at + "kind must be DASC_GDN or DASC_KDA");
+      }
+      if (d.n_heads < 1 || d.d_k < 1 || d.d_v < 1) {
+        delete p;
+        return fail(DASC_EINVAL, at + "n_heads, d_k and d_v must be >= 1");
+      }
+      if (d.kind == kGDN && (int64_t(d.d_v) * d.d_k) % 4 != 0) {
+        delete p;
+        return fail(DASC_EINVAL, at + "GDN head state must be a multiple of 16 bytes");
+      }
+      if (d.kind == kKDA && !kda_shape_supported(d.d_k, d.d_v)) {
+        delete p;
+        return fail(DASC_EINVAL, at + "KDA needs d_k and d_v multiples of 4, at most 128");
+      }
+      if (d.conv_bytes < 0 || d.conv_bytes % 16 != 0) {
+        delete p;
+        return fail(DASC_EINVAL, at + "conv_bytes must be >= 0 and a multiple of 16");
+      }
+      if (!d.A_log || !d.dt_bias) {
+        delete p;
+        return fail(DASC_EINVAL, at + "A_log and dt_bias are required");
+      }
+      LayerPlan L{};
+      L.kind = d.kind;
+      L.n_heads = d.n_heads;
+      L.d_k = d.d_k;
+      L.d_v = d.d_v;
+      L.n = d.kind == kGDN ? d.n_heads : int64_t(d.n_heads) * d.d_k;
+      L.unit_bytes = d.kind == kGDN ? int64_t(d.d_v) * d.d_k * 4 : int64_t(d.d_v) * 4;
+      L.conv_bytes = d.conv_bytes;
+      L.A_log.assign(d.A_log, d.A_log + L.n);
+      L.dt_bias.assign(d.dt_bias, d.dt_bias + L.n);
+      L.retained.resize(L.n);
+      L.horizon.resize(L.n);
+      L.window.assign(L.n, 0);
+      int64_t r = 0;
+      int32_t w_layer = 0;
+      for (int64_t u = 0; u < L.n; ++u) {
+        if (!std::isfinite(L.A_log[u]) || !std::isfinite(L.dt_bias[u])) {
+          delete p;
+          return fail(DASC_EINVAL, at + "A_log and dt_bias must be finite");
+        }
+        // [dasc] §3.3 Eq. 2 at the static logit, then Eq. 3.
+        const double g = -std::exp(static_cast<double>(L.A_log[u])) *
+                         softplus(a_s + static_cast<double>(L.dt_bias[u]));
+        const double H = log_eps / g;
+        L.horizon[u] = H;
+        // [dasc] §4.1: global (retained) iff H_s > W_max.
+        const bool keep = H > static_cast<double>(w_max);
+        L.retained[u] = keep ? 1 : 0;
+        if (keep) {
+          ++r;
+        } else {
+          // [dasc-sum] Eq. 7: clamp(next_pow2(H_s), 4, W_max).
+          const double w = std::min(std::max(next_pow2(H), 4.0), static_cast<double>(w_max));
+          L.window[u] = static_cast<int32_t>(w);
+          w_layer = std::max(w_layer, L.window[u]);
+        }
+      }
+      L.r = r;
+      L.w_layer = w_layer;
+      L.unit_off = unit_off;
+      L.dense_off = dense_off;
+      L.pool_off = pool_off;
+      L.unit_base = unit_base;
+      L.k_row_off = k_row;
+      L.v_row_off = v_row;
+      L.g_row_off = g_row;
+      L.b_row_off = b_row;
+      int32_t nref = 0;
+      for (int h = 0; h < L.n_heads; ++h) {
+        bool any_local = false;
+        if (L.kind == kGDN) {
+          any_local = !L.retained[h];
+        } else {
+          for (int k = 0; k < L.d_k; ++k) any_local |= !L.retained[h * L.d_k + k];
+        }
+        nref += any_local;
+      }
+      L.n_refresh = nref;
+      unit_off += r;
+      dense_off += int64_t(L.n_heads) * L.d_v * L.d_k * 4;
+      pool_off += r * L.unit_bytes;
+      unit_base += L.n;
+      k_row += int64_t(L.n_heads) * L.d_k;
+      v_row += int64_t(L.n_heads) * L.d_v;
+      g_row += L.kind == kKDA ? int64_t(L.n_heads) * L.d_k : L.n_heads;
+      b_row += L.n_heads;
+      p->layers.push_back(std::move(L));
+    }
+    if (k_row > std::numeric_limits<uint32_t>::max() || unit_base > std::numeric_limits<uint32_t>::max()) {
+      delete p;
+      return fail(DASC_EINVAL, "plan_build: model too wide for 32-bit row offsets");
+    }
+    p->k_row = k_row;
+    p->v_row = v_row;
+    p->g_row = g_row;
+    p->b_row = b_row;
+    p->info.k_row = k_row;
+    p->info.v_row = v_row;
+    p->info.gate_row = g_row;
+    p->info.beta_row = b_row;
+
+    dasc_plan_info& I = p->info;
+    I.n_layers = n_layers;
+    int64_t n_units = 0, n_ret = 0, conv = 0, r_max = 0, nref = 0;
+    int32_t w_replay = 0;
+    for (auto& L : p->layers) {
+      n_units += L.n;
+      n_ret += L.r;
+      conv += L.conv_bytes;
+      r_max = std::max(r_max, L.r);
+      w_replay = std::max(w_replay, L.w_layer);
+      nref += L.n_refresh;
+    }
+    I.n_units = n_units;
+    I.n_retained = n_ret;
+    I.temporal_dense_bytes = dense_off;
+    I.temporal_rag_bytes = pool_off;
+    I.conv_bytes = conv;
+    I.dense_bytes = dense_off + conv;
+    I.slot_bytes = pool_off + conv;
+    I.r_max = r_max;
+    I.w_replay = w_replay;
+    I.n_refresh_heads = nref;
+    const double inf = std::numeric_limits<double>::infinity();
+    I.r_bar = static_cast<double>(n_ret) / n_layers;
+    I.c_temp = n_ret ? static_cast<double>(n_units) / static_cast<double>(n_ret) : inf;
+    I.c_ckpt = I.slot_bytes ? static_cast<double>(I.dense_bytes) / static_cast<double>(I.slot_bytes) : inf;
+    I.c_temp_pad = r_max ? static_cast<double>(n_units) / (static_cast<double>(n_layers) * r_max) : inf;
+    I.layout_gain = n_ret ? static_cast<double>(r_max) / I.r_bar : inf;
+    int64_t c_dense = dense_off, c_pool = pool_off;
+    for (auto& L : p->layers) {
+      L.conv_dense_off = c_dense;
+      L.conv_pool_off = c_pool;
+      c_dense += L.conv_bytes;
+      c_pool += L.conv_bytes;
+    }
+    build_tables(p);
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return fail(DASC_ENOMEM, "plan_build: out of host memory");
+  }
+  *out = p;
+  return DASC_OK;
+}
+
+int dasc_plan_query(dasc_plan_t p, dasc_plan_info* out) {
+  if (!p || !out) return fail(DASC_EINVAL, "plan_query: null argument");
+  *out = p->info;
+  return DASC_OK;
+}
+
+int dasc_plan_layer(dasc_plan_t p, int32_t layer, dasc_layer_info* out) {
+  if (!p || !out) return fail(DASC_EINVAL, "plan_layer: null argument");
+  if (layer < 0 || layer >= static_cast<int32_t>(p->layers.size()))
+    return fail(DASC_EINVAL, "plan_layer: layer out of range");
+  const LayerPlan& L = p->layers[layer];
+  dasc_layer_info I{};
+  I.kind = L.kind;
+  I.n_heads = L.n_heads;
+  I.d_k = L.d_k;
+  I.d_v = L.d_v;
+  I.n_units = L.n;
+  I.n_retained = L.r;
+  I.unit_offset = L.unit_off;
+  I.unit_bytes = L.unit_bytes;
+  I.dense_offset = L.dense_off;
+  I.conv_dense_offset = L.conv_dense_off;
+  I.pool_offset = L.pool_off;
+  I.conv_pool_offset = L.conv_pool_off;
+  I.conv_bytes = L.conv_bytes;
+  I.w_layer = L.w_layer;
+  I.n_refresh_heads = L.n_refresh;
+  I.k_row_offset = L.k_row_off;
+  I.v_row_offset = L.v_row_off;
+  I.gate_row_offset = L.g_row_off;
+  I.beta_row_offset = L.b_row_off;
+  *out = I;
+  return DASC_OK;
+}
+
+int dasc_plan_units(dasc_plan_t p, int32_t layer, uint8_t* retained, double* horizon,
+                    int32_t* window) {
+  if (!p) return fail(DASC_EINVAL, "plan_units: null plan");
+  if (layer < 0 || layer >= static_cast<int32_t>(p->layers.size()))
+    return fail(DASC_EINVAL, "plan_units: layer out of range");
+  const LayerPlan& L = p->layers[layer];
+  if (retained) std::memcpy(retained, L.retained.data(), L.n);
+  if (horizon) std::memcpy(horizon, L.horizon.data(), L.n * sizeof(double));
+  if (window) std::memcpy(window, L.window.data(), L.n * sizeof(int32_t));
+  return DASC_OK;
+}
+
+int64_t dasc_plan_slots(dasc_plan_t p, int64_t budget_bytes, int32_t dense) {
+  if (!p || budget_bytes < 0) {
+    fail(DASC_EINVAL, "plan_slots: null plan or negative budget");
+    return std::numeric_limits<int64_t>::min();
+  }
+  const int64_t b = dense ? p->info.dense_bytes : p->info.slot_bytes;
+  if (b <= 0) {
+    fail(DASC_EINVAL, "plan_slots: empty slot");
+    return std::numeric_limits<int64_t>::min();
+  }
+  // [dasc] Appendix C.1 Eq. 8, one rank: slot 0 is reserved.
+  return budget_bytes / b - 1;
+}
+
+int dasc_plan_upload(dasc_plan_t p, void* device_buffer, int64_t bytes, void* stream) {
+  if (!p || !device_buffer) return fail(DASC_EINVAL, "plan_upload: null argument");
+  if (bytes < p->table_bytes) return fail(DASC_EINVAL, "plan_upload: buffer smaller than device_bytes");
+  if (reinterpret_cast<uintptr_t>(device_buffer) % 256 != 0)
+    return fail(DASC_EINVAL, "plan_upload: buffer must be 256-byte aligned");
+  std::vector<uint8_t> img;
+  try {
+    img.assign(p->table_bytes, 0);
+  } catch (const std::bad_alloc&) {
+    return fail(DASC_ENOMEM, "plan_upload: out of host memory");
+  }
+  auto put = [&](int64_t off, const void* src, size_t n) {
+    if (n) std::memcpy(img.data() + off, src, n);
+  };
+  put(p->off_pack, p->pack_copy.data(), p->pack_copy.size() * sizeof(CopyTask));
+  put(p->off_unpack, p->unpack_copy.data(), p->unpack_copy.size() * sizeof(CopyTask));
+  put(p->off_kda, p->kda.data(), p->kda.size() * sizeof(KdaTask));
+  put(p->off_maps, p->maps.data(), p->maps.size());
+  put(p->off_refresh, p->refresh.data(), p->refresh.size() * sizeof(RefreshTask));
+  put(p->off_expA, p->gate_expA.data(), p->gate_expA.size() * sizeof(float));
+  put(p->off_dt, p->gate_dt.data(), p->gate_dt.size() * sizeof(float));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(device_buffer, img.data(), p->table_bytes, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(DASC_EHIP, std::string("plan_upload: ") + hipGetErrorString(e));
+  uint8_t* d = static_cast<uint8_t*>(device_buffer);
+  p->device = d;
+  p->dev.pack_copy = reinterpret_cast<const CopyTask*>(d + p->off_pack);
+  p->dev.unpack_copy = reinterpret_cast<const CopyTask*>(d + p->off_unpack);
+  p->dev.kda = reinterpret_cast<const KdaTask*>(d + p->off_kda);
+  p->dev.maps = d + p->off_maps;
+  p->dev.refresh = reinterpret_cast<const RefreshTask*>(d + p->off_refresh);
+  p->dev.gate_expA = reinterpret_cast<const float*>(d + p->off_expA);
+  p->dev.gate_dt = reinterpret_cast<const float*>(d + p->off_dt);
+  p->dev.status = reinterpret_cast<uint32_t*>(d + p->off_status);
+  return DASC_OK;
+}
+
+int dasc_plan_status(dasc_plan_t p, uint32_t* status, int32_t clear, void* stream) {
+  if (!p || !status) return fail(DASC_EINVAL, "plan_status: null argument");
+  if (!p->device) return fail(DASC_ENOTUPLOADED, "plan_status: plan not uploaded");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t word[4] = {0, 0, 0, 0};
+  hipError_t e = hipMemcpyAsync(word, p->dev.status, sizeof(word), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e == hipSuccess && clear) {
+    const uint32_t zero[4] = {0, 0, 0, 0};
+    e = hipMemcpyAsync(p->dev.status, zero, sizeof(zero), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+  }
+  if (e != hipSuccess) return fail(DASC_EHIP, std::string("plan_status: ") + hipGetErrorString(e));
+  *status = word[0];
+  return DASC_OK;
+}
+
+int dasc_plan_destroy(dasc_plan_t p) {
+  delete p;
+  return DASC_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+bool aligned16(const void* ptr) { return reinterpret_cast<uintptr_t>(ptr) % 16 == 0; }
+
+bool overlap(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
+  auto x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + static_cast<uintptr_t>(b_bytes) && y < x + static_cast<uintptr_t>(a_bytes);
+}
+
+// Common checks of pack and unpack; `what` names the call in messages.
+int check_move(const dasc_plan* p, const char* what, const void* dense, int64_t dense_stride,
+               int64_t n_dense, const void* pool, int64_t pool_stride, int64_t n_slots,
+               const void* idx_a, const void* idx_b, int32_t n) {
+  const std::string w(what);
+  if (!p) return fail(DASC_EINVAL, w + ": null plan");
+  if (!p->device) return fail(DASC_ENOTUPLOADED, w + ": plan tables not uploaded");
+  if (n < 0 || n > 65535) return fail(DASC_EINVAL, w + ": n must be in [0, 65535]");
+  if (n == 0) return DASC_OK;
+  if (!dense || !pool || !idx_a || !idx_b) return fail(DASC_EINVAL, w + ": null pointer");
+  if (!aligned16(dense) || !aligned16(pool)) return fail(DASC_EINVAL, w + ": bases must be 16-byte aligned");
+  if (dense_stride < p->info.dense_bytes || dense_stride % 16)
+    return fail(DASC_EINVAL, w + ": dense_stride must be >= dense_bytes and a multiple of 16");
+  if (pool_stride < p->info.slot_bytes || pool_stride % 16)
+    return fail(DASC_EINVAL, w + ": pool_stride must be >= slot_bytes and a multiple of 16");
+  if (n_dense <= 0 || n_slots <= 0) return fail(DASC_EINVAL, w + ": n_dense and n_slots must be > 0");
+  if (overlap(dense, dense_stride * n_dense, pool, pool_stride * n_slots))
+    return fail(DASC_EINVAL, w + ": pool and dense ranges overlap");
+  return DASC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dasc_ckpt_pack(dasc_plan_t p, const void* dense_base, int64_t dense_stride, int64_t n_dense,
+                   const int32_t* src_idx, void* pool_base, int64_t pool_stride, int64_t n_slots,
+                   const int32_t* dst_slot, int32_t n, void* stream) {
+  int rc = check_move(p, "ckpt_pack", dense_base, dense_stride, n_dense, pool_base, pool_stride,
+                      n_slots, src_idx, dst_slot, n);
+  if (rc != DASC_OK || n == 0) return rc;
+  const uint8_t* src = static_cast<const uint8_t*>(dense_base);
+  uint8_t* dst = static_cast<uint8_t*>(pool_base);
+  int e = 0;
+  for (const Group& g : p->kda_groups) {
+    e = launch_kda(true, g.d_k, g.d_v, p->dev.kda + g.first, g.count, p->dev.maps, src_idx,
+                   dst_slot, src, dense_stride, n_dense, dst, pool_stride, n_slots, n,
+                   p->dev.status, stream);
+    if (e) break;
+  }
+  if (!e && !p->pack_copy.empty())
+    e = launch_copy(true, p->dev.pack_copy, static_cast<uint32_t>(p->pack_copy.size()), src_idx,
+                    dst_slot, src, dense_stride, n_dense, dst, pool_stride, n_slots, n,
+                    p->dev.status, stream);
+  if (e) return fail(DASC_EHIP, std::string("ckpt_pack: launch failed: ") +
+                                    hipGetErrorString(static_cast<hipError_t>(e)));
+  return DASC_OK;
+}
+
+int dasc_ckpt_unpack_zero_fill(dasc_plan_t p, const void* pool_base, int64_t pool_stride,
+                               int64_t n_slots, const int32_t* src_slot, void* dense_base,
+                               int64_t dense_stride, int64_t n_dense, const int32_t* dst_idx,
+                               int32_t n, void* stream) {
+  int rc = check_move(p, "ckpt_unpack_zero_fill", dense_base, dense_stride, n_dense, pool_base,
+                      pool_stride, n_slots, src_slot, dst_idx, n);
+  if (rc != DASC_OK || n == 0) return rc;
+  const uint8_t* src = static_cast<const uint8_t*>(pool_base);
+  uint8_t* dst = static_cast<uint8_t*>(dense_base);
+  int e = 0;
+  for (const Group& g : p->kda_groups) {
+    e = launch_kda(false, g.d_k, g.d_v, p->dev.kda + g.first, g.count, p->dev.maps, src_slot,
+                   dst_idx, src, pool_stride, n_slots, dst, dense_stride, n_dense, n,
+                   p->dev.status, stream);
+    if (e) break;
+  }
+  if (!e && !p->unpack_copy.empty())
+    e = launch_copy(false, p->dev.unpack_copy, static_cast<uint32_t>(p->unpack_copy.size()),
+                    src_slot, dst_idx, src, pool_stride, n_slots, dst, dense_stride, n_dense, n,
+                    p->dev.status, stream);
+  if (e) return fail(DASC_EHIP, std::string("ckpt_unpack_zero_fill: launch failed: ") +
+                                    hipGetErrorString(static_cast<hipError_t>(e)));
+  return DASC_OK;
+}
+
+int dasc_ckpt_refresh_suffix(dasc_plan_t p, const uint16_t* k, const uint16_t* v,
+                             const uint16_t* a, const float* beta, const int64_t* tok_offsets,
+                             int64_t n_tokens, void* dense_base, int64_t dense_stride,
+                             int64_t n_dense, const int32_t* dst_idx, int32_t n, void* stream) {
+  const char* w = "ckpt_refresh_suffix";
+  if (!p) return fail(DASC_EINVAL, std::string(w) + ": null plan");
+  if (!p->device) return fail(DASC_ENOTUPLOADED, std::string(w) + ": plan tables not uploaded");
+  if (n < 0 || n > 65535) return fail(DASC_EINVAL, std::string(w) + ": n must be in [0, 65535]");
+  for (const Group& g : p->refresh_groups)
+    if (!refresh_shape_supported(g.d_k, g.d_v))
+      return fail(DASC_EUNSUPPORTED, std::string(w) + ": refresh needs d_k == d_v in {16, 32, 64, 128}");
+  if (n == 0 || p->refresh.empty()) return DASC_OK;
+  if (!tok_offsets || !dense_base || !dst_idx) return fail(DASC_EINVAL, std::string(w) + ": null pointer");
+  if (n_tokens < 0) return fail(DASC_EINVAL, std::string(w) + ": n_tokens must be >= 0");
+  if (n_tokens > 0 && (!k || !v || !a || !beta))
+    return fail(DASC_EINVAL, std::string(w) + ": null input pointer");
+  if (!aligned16(dense_base) || dense_stride < p->info.dense_bytes || dense_stride % 16)
+    return fail(DASC_EINVAL, std::string(w) + ": dense base/stride misaligned or too small");
+  if (n_dense <= 0) return fail(DASC_EINVAL, std::string(w) + ": n_dense must be > 0");
+  RefreshArgs args{};
+  args.gate_expA = p->dev.gate_expA;
+  args.gate_dt = p->dev.gate_dt;
+  args.k = k;
+  args.v = v;
+  args.a = a;
+  args.beta = beta;
+  args.k_row = p->k_row;
+  args.v_row = p->v_row;
+  args.g_row = p->g_row;
+  args.b_row = p->b_row;
+  args.tok_off = tok_offsets;
+  args.n_tokens = n_tokens;
+  args.dense = static_cast<uint8_t*>(dense_base);
+  args.dense_stride = dense_stride;
+  args.n_dense = n_dense;
+  args.dst_idx = dst_idx;
+  args.n = n;
+  args.status = p->dev.status;
+  for (const Group& g : p->refresh_groups) {
+    args.tasks = p->dev.refresh + g.first;
+    args.n_tasks = g.count;
+    int e = launch_refresh(g.d_k, args, stream);
+    if (e) return fail(DASC_EHIP, std::string(w) + ": launch failed: " +
+                                      hipGetErrorString(static_cast<hipError_t>(e)));
+  }
+  return DASC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,168 @@
+"""The C ABI without a GPU: every declared symbol is exported, the host
+planner matches the oracle bit-exactly, and host-side validation rejects bad
+arguments before anything reaches a device."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import recurrent_state_cache_amd as R
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "dasc.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dasc_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) == 13
+    out = subprocess.run(["nm", "-D", "--defined-only", R.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\b[TW]\s+(dasc_[a-z0-9_]+)\b", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(R.lib, n)
+
+
+def _compare(cfg_layers, a_s, eps, w_max):
+    P = R.Plan(cfg_layers, a_s, eps, w_max)
+    O = oracle.build_plan(cfg_layers, a_s, eps, w_max)
+    info = P.info()
+    for l, L in enumerate(O.layers):
+        r, H, w = P.units(l)
+        li = P.layer(l)
+        assert np.array_equal(r.astype(bool), L.retained), l
+        np.testing.assert_allclose(H, L.H_s, rtol=1e-14, atol=0)
+        expect_w = np.zeros(L.n, np.int64)
+        expect_w[L.local_idx] = L.W_u
+        assert np.array_equal(w, expect_w), l
+        assert li["n_retained"] == L.r and li["n_units"] == L.n
+        assert li["unit_offset"] == O.unit_off[l]
+        assert li["dense_offset"] == O.temporal_off[l]
+        assert li["pool_offset"] == O.pool_off[l]
+        assert li["conv_dense_offset"] == O.conv_off[l]
+        assert li["conv_pool_offset"] == O.pool_conv_off[l]
+        assert li["unit_bytes"] == L.unit_bytes
+        assert li["w_layer"] == O.W_layer[l]
+        assert li["n_refresh_heads"] == len(O.refreshed_heads(l))
+    assert info["n_retained"] == sum(L.r for L in O.layers)
+    assert info["temporal_dense_bytes"] == O.B_temp_dense
+    assert info["temporal_rag_bytes"] == O.B_temp_rag
+    assert info["conv_bytes"] == O.B_conv
+    assert info["dense_bytes"] == O.dense_bytes and info["slot_bytes"] == O.slot_bytes
+    assert info["w_replay"] == O.W_replay and info["r_max"] == O.R_max
+    for key, val in (("c_temp", O.C_temp), ("c_ckpt", O.C_ckpt), ("c_temp_pad", O.C_temp_pad)):
+        assert info[key] == val or (math.isinf(val) and math.isinf(info[key])), key
+    return P, O
+
+
+@pytest.mark.parametrize("name", ["tiny_kda", "gdn", "kda", "mixed"])
+def test_plan_matches_oracle_on_configs(name):
+    cfg = W.CONFIGS[name]()
+    _compare(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max)
+
+
+@pytest.mark.parametrize("w_max", [0, 1, 4, 9, 16, 64, 1 << 30])
+def test_plan_matches_oracle_across_thresholds(w_max):
+    rng = np.random.default_rng(w_max % 97)
+    layers = [
+        W.Layer(W.GDN, 6, 8, 8, rng.uniform(-1, 2, 6).astype(np.float32),
+                rng.normal(0, 1, 6).astype(np.float32), 32),
+        W.Layer(W.KDA, 3, 8, 4, rng.normal(0, 1.5, 24).astype(np.float32),
+                rng.normal(0, 1, 24).astype(np.float32), 48),
+        W.Layer(W.KDA, 2, 16, 16, rng.normal(0, 1.5, 32).astype(np.float32),
+                rng.normal(0, 1, 32).astype(np.float32), 0),
+    ]
+    _compare(layers, -0.3, 1e-3, w_max)
+
+
+def test_exact_tie_decided_like_oracle():
+    lay = W.Layer(W.GDN, 1, 4, 4, np.zeros(1, np.float32), np.full(1, 0.25, np.float32))
+    P4, _ = _compare([lay], -0.25, 0.0625, 4)
+    assert P4.units(0)[0][0] == 0 and P4.units(0)[1][0] == 4.0
+    P3, _ = _compare([lay], -0.25, 0.0625, 3)
+    assert P3.units(0)[0][0] == 1
+
+
+def test_eq8_slots_from_c1_budget():
+    layers = [W.Layer(W.KDA, 4, 128, 128, np.full(512, 3.0, np.float32),
+                      np.zeros(512, np.float32), 3 * 1536 * 2) for _ in range(20)]
+    P = R.Plan(layers, -0.3, 1e-3, 0)
+    assert P.slots(694_681_600) == 127 and P.slots(694_681_600, dense=True) == 127
+    assert P.slots(1000) == -1
+    assert R.lib.dasc_plan_slots(None, 10, 0) == -(1 << 63)
+
+
+def _desc(kind=0, H=2, dk=8, dv=8, A=None, D=None, conv=0):
+    n = H if kind == 0 else H * dk
+    A = np.zeros(n, np.float32) if A is None else A
+    D = np.zeros(n, np.float32) if D is None else D
+    return W.Layer(kind, H, dk, dv, A, D, conv)
+
+
+@pytest.mark.parametrize("layer,kw", [
+    (dict(kind=2), {}),
+    (dict(H=0), {}),
+    (dict(kind=1, dk=6), {}),
+    (dict(kind=1, dk=256), {}),
+    (dict(kind=1, dv=6), {}),
+    (dict(conv=8), {}),
+    (dict(conv=-16), {}),
+    (dict(A=np.array([np.nan, 0], np.float32)), {}),
+    (dict(D=np.array([0, np.inf], np.float32)), {}),
+    ({}, dict(eps=0.0)),
+    ({}, dict(eps=1.0)),
+    ({}, dict(w_max=-1)),
+    ({}, dict(a_s=float("nan"))),
+])
+def test_plan_build_rejects(layer, kw):
+    args = dict(a_s=-0.3, eps=1e-3, w_max=16)
+    args.update(kw)
+    with pytest.raises(R.DascError) as e:
+        R.Plan([_desc(**layer)], **args)
+    assert e.value.code == -1
+    assert R.lib.dasc_last_error().decode()
+
+
+def test_null_and_empty_plan_arguments():
+    h = ctypes.c_void_p()
+    assert R.lib.dasc_plan_build(None, 1, -0.3, 1e-3, 16, ctypes.byref(h)) == -1
+    assert R.lib.dasc_plan_build(None, 0, -0.3, 1e-3, 16, None) == -1
+    assert R.lib.dasc_plan_query(None, None) == -1
+    assert R.lib.dasc_plan_layer(None, 0, None) == -1
+    P = R.Plan([_desc()], w_max=16)
+    assert R.lib.dasc_plan_units(P._h, 5, None, None, None) == -1
+    assert R.lib.dasc_plan_upload(P._h, None, 0, None) == -1
+    assert R.lib.dasc_plan_destroy(None) == 0
+
+
+def test_data_calls_need_uploaded_tables():
+    # Nothing is launched: the host rejects the call first.
+    P = R.Plan([_desc()], w_max=16)
+    fake = ctypes.c_void_p(16)
+    assert R.lib.dasc_ckpt_pack(P._h, fake, 4096, 1, fake, fake, 4096, 1, fake, 1, None) == -2
+    assert R.lib.dasc_ckpt_unpack_zero_fill(P._h, fake, 4096, 1, fake, fake, 4096, 1, fake, 1,
+                                            None) == -2
+    assert R.lib.dasc_ckpt_refresh_suffix(P._h, fake, fake, fake, fake, fake, 1, fake, 4096, 1,
+                                          fake, 1, None) == -2
+    assert R.lib.dasc_ckpt_pack(None, fake, 4096, 1, fake, fake, 4096, 1, fake, 1, None) == -1
+    s = ctypes.c_uint32()
+    assert R.lib.dasc_plan_status(P._h, ctypes.byref(s), 0, None) == -2
+
+
+def test_refresh_rows_reported():
+    cfg = W.mixed()
+    info = R.Plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max).info()
+    assert info["k_row"] == 27 * 32 * 128 and info["v_row"] == 27 * 32 * 128
+    assert info["gate_row"] == 14 * 32 + 13 * 32 * 128 and info["beta_row"] == 27 * 32

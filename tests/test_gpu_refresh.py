@@ -1,0 +1,181 @@
+"""GPU parity of the bounded-suffix refresh against the fp64 oracle, through
+the C ABI: max error over the written (local) entries, relative to the
+Frobenius norm of the fp64 scratch state, must stay within 1e-4; everything
+the refresh must not touch (retained units, conv bytes, other checkpoints)
+must be bit-identical afterwards."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from helpers import head_state, local_mask_of_head, log, mask_words, refresh_error
+
+pytestmark = pytest.mark.gpu
+
+R = pytest.importorskip("recurrent_state_cache_amd")
+
+TOL = 1e-4
+
+
+def _plans(cfg):
+    return (R.Plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max).upload(),
+            oracle.build_plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max))
+
+
+def _host_rows(x, rows):
+    return x[rows[0]:rows[1]].cpu()
+
+
+def _bits16(t):
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _check_requests(P, O, inp, before, after, dst, reqs, layers=None, label=""):
+    """Compare the refreshed heads of the given requests (and layers) with
+    the oracle; check untouched bytes of those destinations bit-exactly."""
+    tok = inp.tok_off.cpu().numpy()
+    mask = mask_words(O)
+    worst = 0.0
+    for r in reqs:
+        t0, t1 = int(tok[r]), int(tok[r + 1])
+        k = _bits16(_host_rows(inp.k, (t0, t1)))
+        v = _bits16(_host_rows(inp.v, (t0, t1)))
+        a = _bits16(_host_rows(inp.a, (t0, t1)))
+        b = _host_rows(inp.beta, (t0, t1)).numpy()
+        ref = oracle.refresh_expected(O, k, v, a, b, np.array([0, t1 - t0]), layers=layers)
+        d = int(dst[r])
+        got = after[d].cpu().numpy()
+        old = before[d].cpu().numpy()
+        # retained units and conv bytes untouched
+        assert np.array_equal(got.view(np.uint32) & mask, old.view(np.uint32) & mask), f"req {r}"
+        for (_, li, h), S64 in ref.items():
+            local = local_mask_of_head(O, li, h)
+            g = head_state(got, O, li, h)
+            assert np.all(np.isfinite(g[local]))
+            err = refresh_error(g, S64, local)
+            worst = max(worst, err)
+            assert err <= TOL, f"{label} req {r} layer {li} head {h}: {err:.3e}"
+    log(f"[refresh] {label}: worst error {worst:.3e} over requests {list(reqs)}")
+    return worst
+
+
+def test_refresh_tiny_kda_all_heads():
+    cfg = W.tiny_kda()
+    P, O = _plans(cfg)
+    Wn = W.windows(cfg)
+    inp = W.refresh_inputs(cfg, Wn, device="cpu")
+    inp = W.RefreshInputs(*(x.cuda() for x in (inp.k, inp.v, inp.a, inp.beta, inp.tok_off)))
+    dense = W.dense_states(cfg, 3, device="cuda", seed=99)
+    before = dense.clone()
+    dst = torch.tensor([2, 0], dtype=torch.int32, device="cuda")
+    R.ckpt_refresh_suffix(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, dense, dst)
+    torch.cuda.synchronize()
+    assert P.status() == 0
+    assert torch.equal(dense[1], before[1])                 # not a destination
+    _check_requests(P, O, inp, before, dense, dst.cpu().numpy(), [0, 1], label="tiny")
+
+
+def test_refresh_kda_full_size_sampled():
+    cfg = W.kda_refresh()
+    log(f"[refresh] kda: {cfg.n_req} requests x {cfg.window[0]} tokens, "
+        f"{len(cfg.layers)} layers x 32 heads")
+    P, O = _plans(cfg)
+    Wn = W.windows(cfg)
+    inp = W.refresh_inputs(cfg, Wn, device="cuda")
+    dense = W.dense_states(cfg, cfg.n_req, device="cuda", seed=5)
+    before = dense.clone()
+    dst = torch.from_numpy(np.random.default_rng(1).permutation(cfg.n_req).astype(np.int32)).cuda()
+    R.ckpt_refresh_suffix(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, dense, dst)
+    torch.cuda.synchronize()
+    assert P.status() == 0
+    _check_requests(P, O, inp, before, dense, dst.cpu().numpy(), [0, 37], layers=[0, 19],
+                    label="kda")
+    _check_requests(P, O, inp, before, dense, dst.cpu().numpy(), [63], layers=[9], label="kda")
+
+
+def test_refresh_mixed_sampled():
+    cfg = W.mixed(n_ckpt=64)
+    P, O = _plans(cfg)
+    Wn = W.windows(cfg)
+    log(f"[refresh] mixed: windows {Wn.min()}..{Wn.max()}, {int(Wn.sum())} tokens")
+    inp = W.refresh_inputs(cfg, Wn, device="cuda")
+    dense = W.dense_states(cfg, cfg.n_req, device="cuda", seed=6)
+    before = dense.clone()
+    dst = torch.arange(cfg.n_req, dtype=torch.int32, device="cuda")
+    R.ckpt_refresh_suffix(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, dense, dst)
+    torch.cuda.synchronize()
+    assert P.status() == 0
+    reqs = [int(np.argmax(Wn)), int(np.argmin(Wn))]
+    _check_requests(P, O, inp, before, dense, dst.cpu().numpy(), reqs, layers=[0, 1, 26],
+                    label="mixed")
+
+
+def test_zero_window_writes_zero_locals_and_bad_ranges_are_flagged():
+    cfg = W.tiny_kda()
+    P, O = _plans(cfg)
+    inp = W.refresh_inputs(cfg, np.array([8, 8]), device="cpu")
+    k, v, a, beta = (x.cuda() for x in (inp.k, inp.v, inp.a, inp.beta))
+    dense = W.dense_states(cfg, 2, device="cuda", seed=3)
+    before = dense.clone()
+    tok = torch.tensor([0, 0, 8], dtype=torch.int64, device="cuda")   # request 0 is empty
+    dst = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    R.ckpt_refresh_suffix(P, k, v, a, beta, tok, dense, dst)
+    torch.cuda.synchronize()
+    assert P.status() == 0
+    m = torch.from_numpy(mask_words(O).view(np.int32)).cuda()
+    assert torch.equal(dense[0].view(torch.int32), before[0].view(torch.int32) & m)
+    # a request whose range runs past the tokens is skipped and flagged
+    dense2 = before.clone()
+    bad = torch.tensor([0, 8, 17], dtype=torch.int64, device="cuda")   # 17 > 16 rows
+    R.ckpt_refresh_suffix(P, k, v, a, beta, bad, dense2, dst)
+    torch.cuda.synchronize()
+    assert P.status() & R.STATUS_BAD_TOKENS
+    assert torch.equal(dense2[1], before[1])
+
+
+def test_recall_invariant_on_gpu():
+    # GDN heads that are all local; beta = 1 and keys of exactly unit norm in
+    # bf16 (+-1/4 on 16 coordinates): the final state recalls the last value,
+    # S_W k_W = v_W, independently of the oracle.
+    d, H, T = 128, 4, 40
+    lay = W.Layer(W.GDN, H, d, d, np.full(H, 2.0, np.float32), np.zeros(H, np.float32), 0)
+    cfg = W.Config("recall", [lay], w_max=64)
+    P, O = _plans(cfg)
+    assert len(O.refreshed_heads(0)) == H
+    rng = np.random.default_rng(8)
+    k = np.zeros((T, H, d), np.float32)
+    for t in range(T):
+        for h in range(H):
+            idx = rng.choice(d, 16, replace=False)
+            k[t, h, idx] = rng.choice([-0.25, 0.25], 16)
+    kt = torch.from_numpy(k.reshape(T, H * d)).to(torch.bfloat16).cuda()
+    vt = torch.randn(T, H * d).to(torch.bfloat16).cuda()
+    at = torch.randn(T, H).to(torch.bfloat16).cuda()
+    bt = torch.ones(T, H, dtype=torch.float32, device="cuda")
+    dense = torch.zeros((1, O.dense_bytes), dtype=torch.uint8, device="cuda")
+    R.ckpt_refresh_suffix(P, kt, vt, at, bt, torch.tensor([0, T], device="cuda"), dense,
+                          torch.zeros(1, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    row = dense[0].cpu().numpy()
+    for h in range(H):
+        S = head_state(row, O, 0, h).astype(np.float64)
+        vlast = vt[-1, h * d:(h + 1) * d].float().cpu().numpy()
+        recall = S @ k[-1, h].astype(np.float64)
+        assert np.max(np.abs(recall - vlast)) <= 1e-5 * max(1.0, np.linalg.norm(vlast))
+
+
+def test_unsupported_refresh_shape_is_rejected():
+    lay = W.Layer(W.GDN, 2, 128, 160, np.full(2, 2.0, np.float32), np.zeros(2, np.float32), 0)
+    cfg = W.Config("wide", [lay], w_max=64)
+    P, _ = _plans(cfg)
+    T = 2
+    z = torch.zeros(T, 256, dtype=torch.bfloat16, device="cuda")
+    dense = torch.zeros((1, P.info()["dense_bytes"]), dtype=torch.uint8, device="cuda")
+    with pytest.raises(R.DascError) as e:
+        R.ckpt_refresh_suffix(P, z, torch.zeros(T, 320, dtype=torch.bfloat16, device="cuda"),
+                              torch.zeros(T, 2, dtype=torch.bfloat16, device="cuda"),
+                              torch.zeros(T, 2, device="cuda"),
+                              torch.tensor([0, T], device="cuda"), dense,
+                              torch.zeros(1, dtype=torch.int32, device="cuda"))
+    assert e.value.code == -5
