@@ -1,0 +1,250 @@
+"""Benchmark of the dasc checkpoint hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+pack n checkpoints into pool slots, unpack them with zero-fill, and refresh
+n_req requests over their suffix windows (the static plan is built once,
+before timing, as the pages build it offline; its host time is reported).
+
+Default workload "kda": Kimi-Linear-shaped KDA layers (20 x 32 heads,
+d = 128, fp32 state, bf16 conv 4 x (3*32*128) per layer), 64 checkpoints
+packed and unpacked, 64 requests x 256 tokens refreshed.  Other workloads:
+"gdn" (36 x 32 GDN heads, 64 checkpoints; refresh 64 x 256 tokens over the
+omitted heads) and "mixed" (27 alternating layers, 512 checkpoints, 64
+requests with windows U{64..1024}).
+
+Prints ONE JSON line.  value = pack+unpack GB/s (algorithmic bytes / time);
+refresh request-tokens/s and the per-kernel rooflines ride along.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP32_VECTOR_PEAK_TF = 157.3    # MI355X fp32 vector (packed FMA), TFLOP/s
+FP32_UNPACKED_PEAK_TF = 78.6   # 256 CU x 64 lanes x 2 flop x 2.4 GHz without packed FMA
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", choices=["kda", "gdn", "mixed"], default="kda")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def _workload(name):
+    import workloads as W
+    if name == "kda":
+        cfg = W.kda(n_ckpt=64, n_req=64, window=256)
+        desc = "KDA 20x32 heads d=128: pack+unpack 64 ckpts, refresh 64 req x 256 tok"
+    elif name == "gdn":
+        cfg = W.gdn(n_ckpt=64)
+        cfg.n_req, cfg.window = 64, (256, 256)
+        desc = "GDN 36x32 heads d=128: pack+unpack 64 ckpts, refresh 64 req x 256 tok"
+    else:
+        cfg = W.mixed(n_ckpt=512, n_req=64)
+        desc = "mixed 27 layers GDN/KDA d=128: pack+unpack 512 ckpts, refresh 64 req x U{64..1024}"
+    return cfg, desc
+
+
+def _algorithmic_bytes(P):
+    """Bytes pack and unpack must move, from the plan: pack reads each GDN
+    retained head and every KDA head with a retained channel in full (a
+    strided column forces whole rows), writes the ragged payload, and copies
+    the conv bytes; unpack reads the payload and the conv bytes and writes
+    the whole dense checkpoint."""
+    info = P.info()
+    read_pack = 0
+    for l in range(info["n_layers"]):
+        L = P.layer(l)
+        ret = P.units(l)[0]
+        if L["kind"] == 0:
+            read_pack += int(ret.sum()) * L["unit_bytes"]
+        else:
+            per_head = ret.reshape(L["n_heads"], L["d_k"]).any(axis=1)
+            read_pack += int(per_head.sum()) * L["d_v"] * L["d_k"] * 4
+    pack = read_pack + info["temporal_rag_bytes"] + 2 * info["conv_bytes"]
+    unpack = info["temporal_rag_bytes"] + info["temporal_dense_bytes"] + 2 * info["conv_bytes"]
+    return pack, unpack
+
+
+def _calibrate_copy(steps):
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_per_dispatch_read": n,
+                      "bytes_per_dispatch_write": n, "dispatches": steps}), flush=True)
+
+
+def _cpu_baseline(cfg, P, dense_cpu, pack_bytes_per_ckpt, unpack_bytes_per_ckpt, inp_rows,
+                  tokens_per_req):
+    """The fp64 NumPy oracle, single-threaded, on a bounded sample: pack and
+    unpack of a few checkpoints, refresh of one request over 8 layers."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    with threadpool_limits(limits=1):
+        O = oracle.build_plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max)
+        n = dense_cpu.shape[0]
+        pool = np.zeros((n, O.slot_bytes), np.uint8)
+        out = np.zeros((n, O.dense_bytes), np.uint8)
+        t = time.perf_counter()
+        oracle.pack(O, dense_cpu, list(range(n)), pool, list(range(n)))
+        oracle.unpack_zero_fill(O, pool, list(range(n)), out, list(range(n)))
+        t_move = time.perf_counter() - t
+        k, v, a, b = inp_rows
+        layers = [l for l in range(len(O.layers)) if len(O.refreshed_heads(l))][:8]
+        t = time.perf_counter()
+        oracle.refresh_expected(O, k, v, a, b, np.array([0, tokens_per_req]), layers=layers)
+        t_ref = time.perf_counter() - t
+    heads_sampled = sum(len(O.refreshed_heads(l)) for l in layers)
+    heads_all = sum(len(O.refreshed_heads(l)) for l in range(len(O.layers)))
+    # one request-token = one token through every refreshed head of every layer
+    sec_per_req_token = t_ref / tokens_per_req * heads_all / heads_sampled
+    gbs = n * (pack_bytes_per_ckpt + unpack_bytes_per_ckpt) / t_move / 1e9
+    return {
+        "value": round(gbs, 4), "unit": "GB/s pack+unpack",
+        "refresh_request_tokens_per_s": round(1.0 / sec_per_req_token, 3),
+        "cores": 1, "kind": "oracle",
+        "sample": (f"pack+unpack of {n} checkpoints ({t_move:.2f} s); refresh of 1 request x "
+                   f"{tokens_per_req} tokens over {len(layers)} layers / {heads_sampled} heads "
+                   f"({t_ref:.2f} s), scaled to all {heads_all} refreshed heads"),
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the library has no "
+              f"multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    if args.calibrate_copy:
+        _calibrate_copy(args.steps)
+        return
+
+    import recurrent_state_cache_amd as R
+    import workloads as W
+
+    cfg, desc = _workload(args.workload)
+    t = time.perf_counter()
+    P = R.Plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max)
+    plan_ms = (time.perf_counter() - t) * 1e3
+    P.upload()
+    info = P.info()
+    n = cfg.n_ckpt
+    dense = W.dense_states(cfg, n, device="cuda")
+    pool = torch.empty((n, info["slot_bytes"]), dtype=torch.uint8, device="cuda")
+    out = torch.empty((n, info["dense_bytes"]), dtype=torch.uint8, device="cuda")
+    perm = np.random.default_rng(cfg.seed).permutation(n).astype(np.int32)
+    src = torch.arange(n, dtype=torch.int32, device="cuda")
+    slot = torch.from_numpy(perm).cuda()
+    Wn = W.windows(cfg)
+    inp = W.refresh_inputs(cfg, Wn, device="cuda")
+    dst = torch.arange(cfg.n_req, dtype=torch.int32, device="cuda") % n
+    total_tokens = int(Wn.sum())
+    pack_b, unpack_b = _algorithmic_bytes(P)
+    # Eq. 1 per token and replayed head: decay (1), readout (2), rank-1 write (2) flops per element
+    flops = total_tokens * sum(5 * P.layer(l)["d_v"] * P.layer(l)["d_k"] * P.layer(l)["n_refresh_heads"]
+                               for l in range(info["n_layers"]))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(e=None):
+        if e: e[0].record(stream)
+        R.ckpt_pack(P, dense, src, pool, slot, stream)
+        if e: e[1].record(stream)
+        R.ckpt_unpack_zero_fill(P, pool, slot, out, src, stream)
+        if e: e[2].record(stream)
+        R.ckpt_refresh_suffix(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, out, dst, stream)
+        if e: e[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert P.status() == 0, "kernels flagged bad arguments"
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert P.status() == 0
+
+    t_pack = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
+    t_unpack = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
+    t_ref = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
+    pack_total = n * pack_b
+    unpack_total = n * unpack_b
+    mover_gbs = (pack_total + unpack_total) * args.steps / (t_pack.sum() + t_unpack.sum()) / 1e9
+    ref_tf = flops / t_ref.mean() / 1e12
+
+    def hbm(bytes_, secs):
+        a = bytes_ / secs / 1e9
+        return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None,
+                "ms": round(secs * 1e3, 4), "bytes": int(bytes_)}
+
+    roof_ref = {"bound": "alu", "achieved": round(ref_tf, 3), "peak": FP32_VECTOR_PEAK_TF,
+                "unit": "TFLOP/s", "frac": round(ref_tf / FP32_VECTOR_PEAK_TF, 4),
+                "traffic": None, "kernel": "refresh_kernel<128>",
+                "frac_of_unpacked_fp32": round(ref_tf / FP32_UNPACKED_PEAK_TF, 4),
+                "ms": round(t_ref.mean() * 1e3, 4), "flops": int(flops)}
+    line = {
+        "metric": "checkpoint pack+unpack GB/s (% HBM peak); suffix-refresh tokens/s, 1 MI355X",
+        "value": round(mover_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32 copy (pack/unpack), f32 (refresh)",
+        "data": "synthetic",
+        "config": {"workload": desc, "checkpoints": n, "requests": cfg.n_req,
+                   "refresh_tokens": total_tokens, "w_max": cfg.w_max,
+                   "dense_bytes": info["dense_bytes"], "slot_bytes": info["slot_bytes"],
+                   "c_ckpt": round(info["c_ckpt"], 4)},
+        "pack_unpack_frac_of_hbm_peak": round(mover_gbs / HBM_PEAK_GBS, 4),
+        "refresh_request_tokens_per_s": round(total_tokens / t_ref.mean(), 1),
+        "plan_build_ms": round(plan_ms, 3),
+        "roofline": roof_ref,
+        "roofline_pack": hbm(pack_total, t_pack.mean()),
+        "roofline_unpack": hbm(unpack_total, t_unpack.mean()),
+    }
+    if not args.no_cpu_baseline:
+        m = min(8, n)
+        dense_cpu = dense[:m].cpu().numpy()
+        T0, T1 = int(inp.tok_off[0]), int(inp.tok_off[1])
+        bits = lambda x: x[T0:T1].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+        rows = (bits(inp.k), bits(inp.v), bits(inp.a), inp.beta[T0:T1].cpu().numpy())
+        line["cpu_baseline"] = _cpu_baseline(cfg, P, dense_cpu, pack_b, unpack_b, rows, T1 - T0)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -206,9 +206,10 @@ class Plan:
         return int(s.value)
 
     def close(self):
-        if getattr(self, "_h", None):
-            lib.dasc_plan_destroy(self._h)
-            self._h = None
+        h = getattr(self, "_h", None)
+        self._h = None
+        if h and lib is not None:   # lib is None during interpreter shutdown
+            lib.dasc_plan_destroy(h)
 
     def __del__(self):
         self.close()
