@@ -137,7 +137,7 @@ void build_tables(dasc_plan* p) {
   }
   // KDA tasks, shape group by shape group.
   for (const auto& s : shapes) {
-    Group g{s.first, s.second, static_cast<uint32_t>(p->kda.size()), 0};
+    Group g{s.first, s.second, static_cast<uint32_t>(p->kda.size()), 0, 0};
     for (const auto& L : p->layers) {
       if (L.kind != kKDA || L.d_k != s.first || L.d_v != s.second) continue;
       const int64_t head_bytes = int64_t(L.d_v) * L.d_k * 4;
@@ -162,6 +162,7 @@ void build_tables(dasc_plan* p) {
           t.map_idx = static_cast<uint32_t>(p->maps.size() / kMapBytes);
           p->maps.insert(p->maps.end(), map, map + kMapBytes);
           p->kda.push_back(t);
+          g.r_max = std::max(g.r_max, static_cast<int32_t>(r));
         }
         j += r;
       }
@@ -182,7 +183,7 @@ void build_tables(dasc_plan* p) {
       rshapes.push_back(s);
   }
   for (const auto& s : rshapes) {
-    Group g{s.first, s.second, static_cast<uint32_t>(p->refresh.size()), 0};
+    Group g{s.first, s.second, static_cast<uint32_t>(p->refresh.size()), 0, 0};
     for (const auto& L : p->layers) {
       if (L.d_k != s.first || L.d_v != s.second) continue;
       const int64_t head_bytes = int64_t(L.d_v) * L.d_k * 4;
@@ -583,7 +584,7 @@ int dasc_ckpt_pack(dasc_plan_t p, const void* dense_base, int64_t dense_stride, 
   uint8_t* dst = static_cast<uint8_t*>(pool_base);
   int e = 0;
   for (const Group& g : p->kda_groups) {
-    e = launch_kda(true, g.d_k, g.d_v, p->dev.kda + g.first, g.count, p->dev.maps, src_idx,
+    e = launch_kda(true, g.d_k, g.d_v, g.r_max, p->dev.kda + g.first, g.count, p->dev.maps, src_idx,
                    dst_slot, src, dense_stride, n_dense, dst, pool_stride, n_slots, n,
                    p->dev.status, stream);
     if (e) break;
@@ -608,7 +609,7 @@ int dasc_ckpt_unpack_zero_fill(dasc_plan_t p, const void* pool_base, int64_t poo
   uint8_t* dst = static_cast<uint8_t*>(dense_base);
   int e = 0;
   for (const Group& g : p->kda_groups) {
-    e = launch_kda(false, g.d_k, g.d_v, p->dev.kda + g.first, g.count, p->dev.maps, src_slot,
+    e = launch_kda(false, g.d_k, g.d_v, g.r_max, p->dev.kda + g.first, g.count, p->dev.maps, src_slot,
                    dst_idx, src, pool_stride, n_slots, dst, dense_stride, n_dense, n,
                    p->dev.status, stream);
     if (e) break;

@@ -74,10 +74,12 @@ struct DeviceTables {
   uint32_t* status;        // DASC_STATUS_* bits
 };
 
-// A run of tasks that share one kernel instantiation.
+// A run of tasks that share one kernel instantiation.  r_max: the largest
+// retained-channel count of a KDA head in the run (sizes the LDS).
 struct Group {
   int32_t d_k, d_v;
   uint32_t first, count;
+  int32_t r_max;
 };
 
 // Kernel launchers (dasc_kernels.hip).  They return a hipError_t value.
@@ -86,7 +88,7 @@ int launch_copy(bool pack, const CopyTask* tasks, uint32_t n_tasks, const int32_
                 int64_t n_src, uint8_t* dst_base, int64_t dst_stride, int64_t n_dst,
                 int32_t n, uint32_t* status, void* stream);
 
-int launch_kda(bool pack, int d_k, int d_v, const KdaTask* tasks, uint32_t n_tasks,
+int launch_kda(bool pack, int d_k, int d_v, int r_max, const KdaTask* tasks, uint32_t n_tasks,
                const uint8_t* maps, const int32_t* src_idx, const int32_t* dst_idx,
                const uint8_t* src_base, int64_t src_stride, int64_t n_src, uint8_t* dst_base,
                int64_t dst_stride, int64_t n_dst, int32_t n, uint32_t* status, void* stream);

@@ -86,22 +86,20 @@ copy_kernel(const CopyTask* __restrict__ tasks, const int32_t* __restrict__ src_
 // ---------------------------------------------------------------------------
 // KDA heads.  The state S is [d_v][d_k] row-major; the unit (h, k) is the
 // column S[:, k], stored in the pool as d_v contiguous floats ([dasc] §4.1,
-// Appendix B).  LDS holds one head, transposed: row k of T is column k of S.
-// A lane moves 4x4 blocks: four 16-byte row loads, an in-register transpose,
-// four 16-byte LDS stores (and the reverse for unpack).  LDS rows are
-// rotated by whole 16-byte groups so that neither the block stores nor the
-// row reads pile onto the same banks.
+// Appendix B).  LDS holds only the head's r retained columns, as rows
+// U[j][0..d_v) in pool order (j = rank of the channel among the retained
+// ones), so its size is r_max * d_v floats for the task group instead of a
+// whole head.  A lane moves 4x4 blocks of S: four 16-byte row accesses and an
+// in-register transpose.  Each LDS row is rotated by whole 16-byte groups
+// (by its row index) so that lanes touching different rows spread over the
+// banks; lanes walking one row touch consecutive groups.
 // ---------------------------------------------------------------------------
-template <int DK, int DV>
-struct KdaShape {
-  static constexpr int kLds = (DK && DV) ? DK * DV : 128 * 128;
-};
-
 __device__ __forceinline__ int rot(int g, int by, int groups) {
   int x = g + by;
   return x >= groups ? x - groups : x;  // by < groups, g < groups
 }
 
+// pack: dense head -> LDS (retained columns only) -> contiguous pool units
 template <int DK, int DV>
 __global__ void __launch_bounds__(kThreads)
 kda_pack_kernel(const KdaTask* __restrict__ tasks, const uint8_t* __restrict__ maps,
@@ -109,7 +107,7 @@ kda_pack_kernel(const KdaTask* __restrict__ tasks, const uint8_t* __restrict__ m
                 const uint8_t* __restrict__ src_base, int64_t src_stride, int64_t n_src,
                 uint8_t* __restrict__ dst_base, int64_t dst_stride, int64_t n_dst,
                 uint32_t* __restrict__ status, int dk_rt, int dv_rt) {
-  __shared__ __attribute__((aligned(16))) float T[KdaShape<DK, DV>::kLds];
+  extern __shared__ __attribute__((aligned(16))) float U[];
   const int dk = DK ? DK : dk_rt;
   const int dv = DV ? DV : dv_rt;
   const KdaTask t = tasks[blockIdx.x];
@@ -121,8 +119,10 @@ kda_pack_kernel(const KdaTask* __restrict__ tasks, const uint8_t* __restrict__ m
   }
   const int KG = dk / 4, VG = dv / 4, NB = KG * VG;
   const int tid = threadIdx.x;
+  const uint8_t* rank_of = maps + static_cast<uint64_t>(t.map_idx) * kMapBytes + 128;
   const float* S = reinterpret_cast<const float*>(src_base + s * src_stride + t.dense_off);
-  // Phase 1: whole head into LDS, transposed.
+  // Phase 1: read the whole head (strided columns force whole rows), keep
+  // the retained columns.
 #pragma unroll 4
   for (int b = tid; b < NB; b += kThreads) {
     const int kg = b % KG, vg = b / KG;
@@ -130,26 +130,29 @@ kda_pack_kernel(const KdaTask* __restrict__ tasks, const uint8_t* __restrict__ m
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       x[i] = ld_stream(reinterpret_cast<const f32x4*>(S + (4 * vg + i) * dk + 4 * kg));
-    const int pg = rot(vg, kg % VG, VG);
+    const uint32_t ranks = *reinterpret_cast<const uint32_t*>(rank_of + 4 * kg);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f32x4 col = {x[0][j], x[1][j], x[2][j], x[3][j]};
-      *reinterpret_cast<f32x4*>(&T[(4 * kg + j) * dv + 4 * pg]) = col;
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t rk = (ranks >> (8 * c)) & 0xFFu;
+      if (rk != kLocal) {
+        f32x4 col = {x[0][c], x[1][c], x[2][c], x[3][c]};
+        *reinterpret_cast<f32x4*>(&U[rk * dv + 4 * rot(vg, rk % VG, VG)]) = col;
+      }
     }
   }
   __syncthreads();
-  // Phase 2: retained columns, each one contiguous unit of d_v floats.
-  const uint8_t* ret = maps + static_cast<uint64_t>(t.map_idx) * kMapBytes;
+  // Phase 2: the r units, contiguous in the pool slot.
   float* P = reinterpret_cast<float*>(dst_base + d * dst_stride + t.pool_off);
   const int total = static_cast<int>(t.r) * VG;
   for (int q = tid; q < total; q += kThreads) {
     const int j = q / VG, g = q % VG;
-    const int k = ret[j];
-    const f32x4 val = *reinterpret_cast<const f32x4*>(&T[k * dv + 4 * rot(g, (k / 4) % VG, VG)]);
+    const f32x4 val = *reinterpret_cast<const f32x4*>(&U[j * dv + 4 * rot(g, j % VG, VG)]);
     st_stream(val, reinterpret_cast<f32x4*>(P + j * dv + 4 * g));
   }
 }
 
+// unpack: contiguous pool units -> LDS -> every element of the dense head,
+// +0.0 in omitted channels
 template <int DK, int DV>
 __global__ void __launch_bounds__(kThreads)
 kda_unpack_kernel(const KdaTask* __restrict__ tasks, const uint8_t* __restrict__ maps,
@@ -157,7 +160,7 @@ kda_unpack_kernel(const KdaTask* __restrict__ tasks, const uint8_t* __restrict__
                   const uint8_t* __restrict__ src_base, int64_t src_stride, int64_t n_src,
                   uint8_t* __restrict__ dst_base, int64_t dst_stride, int64_t n_dst,
                   uint32_t* __restrict__ status, int dk_rt, int dv_rt) {
-  __shared__ __attribute__((aligned(16))) float U[KdaShape<DK, DV>::kLds];
+  extern __shared__ __attribute__((aligned(16))) float U[];
   const int dk = DK ? DK : dk_rt;
   const int dv = DV ? DV : dv_rt;
   const KdaTask t = tasks[blockIdx.x];
@@ -206,25 +209,35 @@ kda_unpack_kernel(const KdaTask* __restrict__ tasks, const uint8_t* __restrict__
 // ---------------------------------------------------------------------------
 // Bounded-suffix refresh ([dasc] §4.2), one workgroup per (head, request).
 //
-// Eq. 1 in rank-1 form: with A = S Diag(alpha_t),
-//   S_t = A + beta_t (v_t - A k_t) k_t^T,
-// so per token each state element takes one multiply (decay), one FMA
-// (the readout A k_t) and one FMA (the rank-1 write).  A lane owns 4 rows x
-// 16 columns of S; the D/16 lanes that share rows sit next to each other and
-// finish A k_t with DPP butterflies.  Tokens are staged through LDS in
-// blocks of kTB (double-buffered): k, v widened from bf16, beta, and the
-// decay alpha = exp(-exp(A_log) softplus(a_t + dt_bias)) (Eq. 2), each
-// computed once per (token, channel).
+// Eq. 1 ([dasc] §3.1) is replayed in chunks of C tokens.  Inside a chunk
+// that starts from S_0, with the running decay gamma_t = alpha_1 ... alpha_t
+// and the pairwise decay D_{t,s} = alpha_{s+1} ... alpha_t (s < t), the
+// recurrence unrolls exactly to
+//   S_t = S_0 Diag(gamma_t) + sum_{s<=t} c_s (k_s o D_{t,s})^T,
+//   c_t = beta_t (v_t - S_0 (gamma_t o k_t) - sum_{s<t} M_{t,s} c_s),
+//   M_{t,s} = sum_j k_t[j] k_s[j] D_{t,s}[j],
+// so a chunk costs one product S_0 Q (Q = [gamma_t o k_t]), a C x C
+// forward substitution for the c_t, and one rank-C update
+// S_C = S_0 Diag(gamma_C) + sum_s c_s (k_s o D_{C,s})^T: two FMAs per state
+// element and token instead of a multiply and two FMAs, and every factor is a
+// product of decays (no division, so fast-decaying channels cannot overflow).
+// Tokens past the end of a request pad the last chunk as exact no-ops
+// (alpha = 1, k = 0, v = 0, beta = 0).
+//
+// Lanes: each lane owns 4 rows x 16 columns of S; the D/16 lanes sharing rows
+// are adjacent and finish the readout with DPP butterflies.  Chunk inputs are
+// staged through LDS (double-buffered): the decay alpha = exp(-exp(A_log)
+// softplus(a_t + dt_bias)) ([dasc] §3.3 Eq. 2) once per (token, channel),
+// then gamma, Q, W = [k_s o D_{C,s}] and M.
 // ---------------------------------------------------------------------------
-constexpr int kTB = 16;
-
-template <int D>
+template <int D, int C>
 struct RefreshShape {
   static constexpr int kG = D / 16;             // lanes per row group
   static constexpr int kNS = D * D / 64;        // lanes that hold state
   static constexpr int kNT = kNS < 64 ? 64 : kNS;
-  static constexpr int kPer = kTB * D / kNT;    // staged entries per lane per block
+  static constexpr int kPer = C * D / kNT;      // staged entries per lane per chunk
   static_assert(kNT % D == 0, "staging assumes a fixed channel per lane");
+  static_assert(C * D % kNT == 0, "staging covers a chunk exactly");
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
@@ -246,19 +259,30 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ float softplus_f32(float x) {
-  return x > 20.f ? x : log1pf(expf(x));
+// alpha = exp(-exp(A_log) softplus(x)) with x = a_t + dt_bias (Eq. 2);
+// expA = exp(A_log) is precomputed per unit.
+__device__ __forceinline__ float decay(float x, float expA) {
+  const float sp = fmaxf(x, 0.f) + log1pf(__builtin_amdgcn_exp2f(-fabsf(x) * 1.44269504088896341f));
+  return __builtin_amdgcn_exp2f(-expA * sp * 1.44269504088896341f);
 }
 
-template <int D>
-__global__ void __launch_bounds__(RefreshShape<D>::kNT)
+constexpr int kChunk = 8;
+
+template <int D, int C>
+__global__ void __launch_bounds__((RefreshShape<D, C>::kNT))
 refresh_kernel(RefreshArgs a) {
-  using Sh = RefreshShape<D>;
-  constexpr int G = Sh::kG, NS = Sh::kNS, NT = Sh::kNT;
-  __shared__ __attribute__((aligned(16))) float sA[2][kTB][D];
-  __shared__ __attribute__((aligned(16))) float sK[2][kTB][D];
-  __shared__ __attribute__((aligned(16))) float sV[2][kTB][D];
-  __shared__ float sB[2][kTB];
+  using Sh = RefreshShape<D, C>;
+  constexpr int G = Sh::kG, NS = Sh::kNS, NT = Sh::kNT, PER = Sh::kPer;
+  // per chunk (double-buffered): Q = gamma o k, W = k o D_{C,.}, v, gamma_C, beta, M
+  __shared__ __attribute__((aligned(16))) float sQ[2][C][D];
+  __shared__ __attribute__((aligned(16))) float sW[2][C][D];
+  __shared__ __attribute__((aligned(16))) float sV[2][C][D];
+  __shared__ __attribute__((aligned(16))) float sG[2][D];
+  __shared__ float sB[2][C];
+  __shared__ float sM[2][C][C];
+  // staging scratch (single): k and alpha of the chunk being staged
+  __shared__ __attribute__((aligned(16))) float sK[C][D];
+  __shared__ __attribute__((aligned(16))) float sA[C][D];
 
   const RefreshTask t = a.tasks[blockIdx.x];
   const int req = blockIdx.y;
@@ -278,7 +302,7 @@ refresh_kernel(RefreshArgs a) {
   const int c0 = (tid % G) * 16;
   const int r0 = (tid / G) * 4;
 
-  // Staging: lane `tid` always handles channel jj of tokens tid/D + m*NT/D.
+  // Staging: lane `tid` handles channel jj of tokens tid/D + m*NT/D.
   const int jj = tid % D;
   const bool kda = t.kind == static_cast<uint32_t>(kKDA);
   const uint32_t pidx = t.param_off + (kda ? jj : 0);
@@ -288,17 +312,89 @@ refresh_kernel(RefreshArgs a) {
   const int64_t kcol = t.k_off + jj;
   const int64_t vcol = t.v_off + jj;
 
-  auto stage = [&](int buf, int64_t tok0, int nt) {
+  const int64_t W = t1 - t0;
+  const int64_t nchunks = (W + C - 1) / C;
+
+  uint16_t ra[PER], rk[PER], rv[PER];
+  float rb[PER];
+  auto fetch = [&](int64_t n) {  // raw inputs of chunk n into registers
 #pragma unroll
-    for (int m = 0; m < Sh::kPer; ++m) {
+    for (int m = 0; m < PER; ++m) {
       const int tt = tid / D + m * (NT / D);
-      if (tt < nt) {
-        const int64_t tok = tok0 + tt;
-        const float x = bf16_to_f32(a.a[tok * a.g_row + gcol]) + dtb;
-        sA[buf][tt][jj] = expf(-expA * softplus_f32(x));
-        sK[buf][tt][jj] = bf16_to_f32(a.k[tok * a.k_row + kcol]);
-        sV[buf][tt][jj] = bf16_to_f32(a.v[tok * a.v_row + vcol]);
-        if (jj == 0) sB[buf][tt] = a.beta[tok * a.b_row + t.b_off];
+      const int64_t tok = t0 + n * C + tt;
+      if (tok < t1) {
+        ra[m] = a.a[tok * a.g_row + gcol];
+        rk[m] = a.k[tok * a.k_row + kcol];
+        rv[m] = a.v[tok * a.v_row + vcol];
+        rb[m] = jj == 0 ? a.beta[tok * a.b_row + t.b_off] : 0.f;
+      } else {  // padding: an exact no-op step
+        ra[m] = 0;
+        rk[m] = 0;
+        rv[m] = 0;
+        rb[m] = 0.f;
+      }
+    }
+  };
+  auto stage_a = [&](int buf, int64_t n) {  // decay, k, v, beta
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int tt = tid / D + m * (NT / D);
+      const bool real = t0 + n * C + tt < t1;
+      sA[tt][jj] = real ? decay(bf16_to_f32(ra[m]) + dtb, expA) : 1.f;
+      sK[tt][jj] = bf16_to_f32(rk[m]);
+      sV[buf][tt][jj] = bf16_to_f32(rv[m]);
+      if (jj == 0) sB[buf][tt] = rb[m];
+    }
+  };
+  auto stage_b = [&](int buf) {  // gamma, Q, W, gamma_C and M from sK, sA
+    for (int j = tid; j < D; j += NT) {
+      float g = 1.f;
+#pragma unroll
+      for (int tt = 0; tt < C; ++tt) {
+        g *= sA[tt][j];
+        sQ[buf][tt][j] = g * sK[tt][j];
+      }
+      sG[buf][j] = g;
+      float dd = 1.f;
+#pragma unroll
+      for (int s = C - 1; s >= 0; --s) {
+        sW[buf][s][j] = sK[s][j] * dd;
+        dd *= sA[s][j];
+      }
+    }
+    if constexpr (D == 128 && NT == 256 && C == 8) {
+      // threads 128..255: (token t, block of 8 channels); M_{t,s} summed
+      // over the 16 blocks with DPP inside each 16-lane row
+      if (tid >= 128) {
+        const int u = tid - 128;
+        const int tt = u >> 4, j0 = (u & 15) * 8;
+        float p[8], kt[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) p[c] = kt[c] = sK[tt][j0 + c];
+        (void)kt;
+        for (int s = tt - 1; s >= 0; --s) {
+          float part = 0.f;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            p[c] *= sA[s + 1][j0 + c];
+            part = fmaf(p[c], sK[s][j0 + c], part);
+          }
+          part = group_sum<16>(part);
+          if ((u & 15) == 0) sM[buf][tt][s] = part;
+        }
+      }
+    } else {
+      for (int e = tid; e < C * C; e += NT) {
+        const int tt = e / C, s = e % C;
+        if (s < tt) {
+          float acc = 0.f;
+          for (int j = 0; j < D; ++j) {
+            float p = sK[tt][j];
+            for (int r = s + 1; r <= tt; ++r) p *= sA[r][j];
+            acc = fmaf(p, sK[s][j], acc);
+          }
+          sM[buf][tt][s] = acc;
+        }
       }
     }
   };
@@ -309,58 +405,86 @@ refresh_kernel(RefreshArgs a) {
 #pragma unroll
     for (int c = 0; c < 16; ++c) S[i][c] = 0.f;
 
-  const int64_t W = t1 - t0;
-  const int64_t nb = (W + kTB - 1) / kTB;
-  if (nb > 0) stage(0, t0, static_cast<int>(W < kTB ? W : kTB));
+  if (nchunks > 0) {
+    fetch(0);
+    stage_a(0, 0);
+  }
   __syncthreads();
-  for (int64_t b = 0; b < nb; ++b) {
-    const int buf = static_cast<int>(b & 1);
-    const int64_t left = W - b * kTB;
-    const int nt = static_cast<int>(left < kTB ? left : kTB);
-    if (b + 1 < nb) {
-      const int64_t left2 = left - kTB;
-      stage(buf ^ 1, t0 + (b + 1) * kTB, static_cast<int>(left2 < kTB ? left2 : kTB));
-    }
+  if (nchunks > 0) stage_b(0);
+  __syncthreads();
+  for (int64_t n = 0; n < nchunks; ++n) {
+    const int b = static_cast<int>(n & 1);
+    const bool more = n + 1 < nchunks;
+    if (more) fetch(n + 1);
     if (has_state) {
-      for (int tt = 0; tt < nt; ++tt) {
-        float al[16], kk[16], vv[4];
+      float U[4][C];
+      // readout of the chunk-start state: U[i][t] = (S_0 q_t)_i
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(&sA[buf][tt][c0 + 4 * q]);
-          const f32x4 y = *reinterpret_cast<const f32x4*>(&sK[buf][tt][c0 + 4 * q]);
+      for (int tt = 0; tt < C; ++tt) {
+        float q[16];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            al[4 * q + e] = x[e];
-            kk[4 * q + e] = y[e];
-          }
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(&sQ[b][tt][c0 + 4 * v4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) q[4 * v4 + e] = x[e];
         }
-        {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(&sV[buf][tt][r0]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vv[e] = x[e];
-        }
-        const float beta = sB[buf][tt];
-        float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float acc = 0.f;
 #pragma unroll
-          for (int c = 0; c < 16; ++c) {
-            S[i][c] *= al[c];                 // A = S Diag(alpha_t)
-            acc = fmaf(S[i][c], kk[c], acc);  // (A k_t), partial over 16 columns
-          }
-          p[i] = acc;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = group_sum<G>(p[i]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float ci = beta * (vv[i] - p[i]);  // beta_t (v_t - A k_t)
-#pragma unroll
-          for (int c = 0; c < 16; ++c) S[i][c] = fmaf(ci, kk[c], S[i][c]);
+          for (int c = 0; c < 16; ++c) acc = fmaf(S[i][c], q[c], acc);
+          U[i][tt] = acc;
         }
       }
+#pragma unroll
+      for (int tt = 0; tt < C; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) U[i][tt] = group_sum<G>(U[i][tt]);
+      // forward substitution: U[i][t] <- c_t for the lane's rows
+#pragma unroll
+      for (int tt = 0; tt < C; ++tt) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&sV[b][tt][r0]);
+        const float beta = sB[b][tt];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = v[i] - U[i][tt];
+#pragma unroll
+          for (int s = 0; s < tt; ++s) x = fmaf(-sM[b][tt][s], U[i][s], x);
+          U[i][tt] = beta * x;
+        }
+      }
+      // S <- S Diag(gamma_C) + sum_s c_s w_s^T
+      {
+        float g[16];
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(&sG[b][c0 + 4 * v4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) g[4 * v4 + e] = x[e];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int c = 0; c < 16; ++c) S[i][c] *= g[c];
+      }
+#pragma unroll
+      for (int s = 0; s < C; ++s) {
+        float w[16];
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(&sW[b][s][c0 + 4 * v4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[4 * v4 + e] = x[e];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int c = 0; c < 16; ++c) S[i][c] = fmaf(U[i][s], w[c], S[i][c]);
+      }
     }
+    if (more) stage_a(b ^ 1, n + 1);
+    __syncthreads();
+    if (more) stage_b(b ^ 1);
     __syncthreads();
   }
 
@@ -414,33 +538,36 @@ bool kda_shape_supported(int d_k, int d_v) {
   return d_k >= 4 && d_v >= 4 && d_k <= 128 && d_v <= 128 && d_k % 4 == 0 && d_v % 4 == 0;
 }
 
-int launch_kda(bool pack, int d_k, int d_v, const KdaTask* tasks, uint32_t n_tasks,
+int launch_kda(bool pack, int d_k, int d_v, int r_max, const KdaTask* tasks, uint32_t n_tasks,
                const uint8_t* maps, const int32_t* src_idx, const int32_t* dst_idx,
                const uint8_t* src_base, int64_t src_stride, int64_t n_src, uint8_t* dst_base,
                int64_t dst_stride, int64_t n_dst, int32_t n, uint32_t* status, void* stream) {
   if (n_tasks == 0 || n == 0) return hipSuccess;
-  if (!kda_shape_supported(d_k, d_v)) return static_cast<int>(hipErrorInvalidValue);
+  if (!kda_shape_supported(d_k, d_v) || r_max < 1 || r_max > d_k)
+    return static_cast<int>(hipErrorInvalidValue);
   dim3 grid(n_tasks, static_cast<uint32_t>(n));
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t lds = static_cast<size_t>(r_max) * d_v * sizeof(float);  // <= 64 KiB
   const bool fixed = d_k == 128 && d_v == 128;
   if (pack) {
     if (fixed)
-      kda_pack_kernel<128, 128><<<grid, kThreads, 0, s>>>(tasks, maps, src_idx, dst_idx, src_base,
-                                                          src_stride, n_src, dst_base, dst_stride,
-                                                          n_dst, status, d_k, d_v);
-    else
-      kda_pack_kernel<0, 0><<<grid, kThreads, 0, s>>>(tasks, maps, src_idx, dst_idx, src_base,
-                                                      src_stride, n_src, dst_base, dst_stride,
-                                                      n_dst, status, d_k, d_v);
-  } else {
-    if (fixed)
-      kda_unpack_kernel<128, 128><<<grid, kThreads, 0, s>>>(tasks, maps, src_idx, dst_idx,
+      kda_pack_kernel<128, 128><<<grid, kThreads, lds, s>>>(tasks, maps, src_idx, dst_idx,
                                                             src_base, src_stride, n_src, dst_base,
                                                             dst_stride, n_dst, status, d_k, d_v);
     else
-      kda_unpack_kernel<0, 0><<<grid, kThreads, 0, s>>>(tasks, maps, src_idx, dst_idx, src_base,
+      kda_pack_kernel<0, 0><<<grid, kThreads, lds, s>>>(tasks, maps, src_idx, dst_idx, src_base,
                                                         src_stride, n_src, dst_base, dst_stride,
                                                         n_dst, status, d_k, d_v);
+  } else {
+    if (fixed)
+      kda_unpack_kernel<128, 128><<<grid, kThreads, lds, s>>>(tasks, maps, src_idx, dst_idx,
+                                                              src_base, src_stride, n_src,
+                                                              dst_base, dst_stride, n_dst, status,
+                                                              d_k, d_v);
+    else
+      kda_unpack_kernel<0, 0><<<grid, kThreads, lds, s>>>(tasks, maps, src_idx, dst_idx,
+                                                          src_base, src_stride, n_src, dst_base,
+                                                          dst_stride, n_dst, status, d_k, d_v);
   }
   return static_cast<int>(hipGetLastError());
 }
@@ -455,16 +582,16 @@ int launch_refresh(int d, const RefreshArgs& args, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (d) {
     case 16:
-      refresh_kernel<16><<<grid, RefreshShape<16>::kNT, 0, s>>>(args);
+      refresh_kernel<16, kChunk><<<grid, RefreshShape<16, kChunk>::kNT, 0, s>>>(args);
       break;
     case 32:
-      refresh_kernel<32><<<grid, RefreshShape<32>::kNT, 0, s>>>(args);
+      refresh_kernel<32, kChunk><<<grid, RefreshShape<32, kChunk>::kNT, 0, s>>>(args);
       break;
     case 64:
-      refresh_kernel<64><<<grid, RefreshShape<64>::kNT, 0, s>>>(args);
+      refresh_kernel<64, kChunk><<<grid, RefreshShape<64, kChunk>::kNT, 0, s>>>(args);
       break;
     case 128:
-      refresh_kernel<128><<<grid, RefreshShape<128>::kNT, 0, s>>>(args);
+      refresh_kernel<128, kChunk><<<grid, RefreshShape<128, kChunk>::kNT, 0, s>>>(args);
       break;
     default:
       return static_cast<int>(hipErrorInvalidValue);
