@@ -213,6 +213,8 @@ int dasc_ckpt_unpack_zero_fill(dasc_plan_t plan, const void* pool_base,
  *   k     [T, sum_l H_l d_k]  bf16 bits      v    [T, sum_l H_l d_v] bf16 bits
  *   a     [T, sum_l (H_l d_k for KDA, H_l for GDN)] bf16 bits
  *   beta  [T, sum_l H_l]      fp32
+ *   k, v and a must be 16-byte aligned; the k and v rows must be multiples
+ *   of 8 elements (DASC_EUNSUPPORTED otherwise).
  *   tok_offsets [n+1] int64, device: request r owns tokens
  *     [tok_offsets[r], tok_offsets[r+1]); must be non-decreasing within
  *     [0, n_tokens] (a request that breaks this is skipped and flagged).

@@ -639,6 +639,11 @@ int dasc_ckpt_refresh_suffix(dasc_plan_t p, const uint16_t* k, const uint16_t* v
   if (n_tokens < 0) return fail(DASC_EINVAL, std::string(w) + ": n_tokens must be >= 0");
   if (n_tokens > 0 && (!k || !v || !a || !beta))
     return fail(DASC_EINVAL, std::string(w) + ": null input pointer");
+  if (p->k_row % 8 || p->v_row % 8)
+    return fail(DASC_EUNSUPPORTED, std::string(w) + ": k and v rows must be multiples of 8 elements");
+  if (n_tokens > 0 && (!aligned16(k) || !aligned16(v) || !aligned16(a) ||
+                       reinterpret_cast<uintptr_t>(beta) % 4))
+    return fail(DASC_EINVAL, std::string(w) + ": k, v and a must be 16-byte aligned");
   if (!aligned16(dense_base) || dense_stride < p->info.dense_bytes || dense_stride % 16)
     return fail(DASC_EINVAL, std::string(w) + ": dense base/stride misaligned or too small");
   if (n_dense <= 0) return fail(DASC_EINVAL, std::string(w) + ": n_dense must be > 0");

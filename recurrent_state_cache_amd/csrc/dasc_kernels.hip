@@ -209,54 +209,52 @@ kda_unpack_kernel(const KdaTask* __restrict__ tasks, const uint8_t* __restrict__
 // ---------------------------------------------------------------------------
 // Bounded-suffix refresh ([dasc] §4.2), one workgroup per (head, request).
 //
-// Eq. 1 ([dasc] §3.1) is replayed in chunks of C tokens.  Inside a chunk
+// Eq. 1 ([dasc] §3.1) is replayed in chunks of 16 tokens.  Inside a chunk
 // that starts from S_0, with the running decay gamma_t = alpha_1 ... alpha_t
 // and the pairwise decay D_{t,s} = alpha_{s+1} ... alpha_t (s < t), the
 // recurrence unrolls exactly to
 //   S_t = S_0 Diag(gamma_t) + sum_{s<=t} c_s (k_s o D_{t,s})^T,
-//   c_t = beta_t (v_t - S_0 (gamma_t o k_t) - sum_{s<t} M_{t,s} c_s),
-//   M_{t,s} = sum_j k_t[j] k_s[j] D_{t,s}[j],
-// so a chunk costs one product S_0 Q (Q = [gamma_t o k_t]), a C x C
-// forward substitution for the c_t, and one rank-C update
-// S_C = S_0 Diag(gamma_C) + sum_s c_s (k_s o D_{C,s})^T: two FMAs per state
-// element and token instead of a multiply and two FMAs, and every factor is a
-// product of decays (no division, so fast-decaying channels cannot overflow).
-// Tokens past the end of a request pad the last chunk as exact no-ops
-// (alpha = 1, k = 0, v = 0, beta = 0).
+//   c_t = beta_t (v_t - S_0 (gamma_t o k_t)) - sum_{s<t} L_{t,s} c_s,
+//   L_{t,s} = beta_t sum_j k_t[j] k_s[j] D_{t,s}[j],
+// so a chunk is one product U0 = S_0 Q (Q = [gamma_t o k_t]), a 16 x 16
+// unit-lower-triangular solve for the c_t, and one rank-16 update
+// S_16 = S_0 Diag(gamma_16) + sum_s c_s w_s^T (w_s = k_s o D_{16,s}).  Every
+// factor is a product of decays, so nothing is divided (fast-decaying
+// channels cannot overflow).  Tokens past the end of a request pad the last
+// chunk as exact no-ops (alpha = 1, k = 0, v = 0, beta = 0).
 //
-// Lanes: each lane owns 4 rows x 16 columns of S; the D/16 lanes sharing rows
-// are adjacent and finish the readout with DPP butterflies.  Chunk inputs are
-// staged through LDS (double-buffered): the decay alpha = exp(-exp(A_log)
+// The two products run on fp32 MFMA (v_mfma_f32_16x16x4f32).  The state is
+// kept transposed, S^T [k][v], in 16 x 16 accumulator tiles: lane (g, m)
+// (g = lane / 16, m = lane % 16) of tile (kt, vt) holds
+// S^T[16 kt + 4 g + r][16 vt + m], r = 0..3.  Those same registers are the B
+// operand of both products when lane group g stands for the k (or token)
+// index 4 g + r of the k-step r, so the state never moves:
+//   P1  U0^T[t][v] = sum_k Q[t][k] S^T[k][v]   (A = Q from LDS, B = S^T)
+//   P2  S^T[k][v] += sum_t W[k][t] C^T[t][v]   (A = W from LDS, B = C^T)
+// and P1's output U0^T (lane group g holds tokens 4 g .. 4 g + 3) is, after
+// the triangular solve, exactly the B operand C^T of P2.  Each wave owns all
+// k tiles of its v tiles, so P1 needs no cross-wave reduction.  The solve
+// walks the 4 lane groups in order, passing finished c's with lane shuffles.
+// Chunk inputs are staged through LDS: decay alpha = exp(-exp(A_log)
 // softplus(a_t + dt_bias)) ([dasc] §3.3 Eq. 2) once per (token, channel),
-// then gamma, Q, W = [k_s o D_{C,s}] and M.
+// then gamma, Q, W, gamma_16 and L.
 // ---------------------------------------------------------------------------
-template <int D, int C>
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kC = 16;  // tokens per chunk (the MFMA tile edge)
+
+template <int D>
 struct RefreshShape {
-  static constexpr int kG = D / 16;             // lanes per row group
-  static constexpr int kNS = D * D / 64;        // lanes that hold state
-  static constexpr int kNT = kNS < 64 ? 64 : kNS;
-  static constexpr int kPer = C * D / kNT;      // staged entries per lane per chunk
-  static_assert(kNT % D == 0, "staging assumes a fixed channel per lane");
-  static_assert(C * D % kNT == 0, "staging covers a chunk exactly");
+  static constexpr int kKT = D / 16;                  // k tiles
+  static constexpr int kVTW = D >= 32 ? 2 : 1;        // v tiles per wave
+  static constexpr int kNW = (D / 16) / kVTW;         // waves per head
+  static constexpr int kNT = 64 * kNW;                // threads
+  static constexpr int kJB = D / 8;                   // 8-channel blocks per token
+  static_assert(2 * D <= kNT, "one staged item per lane");
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
-}
-
-template <int kCtrl>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, true));
-}
-
-// Sum over the G consecutive lanes of a row group (G in {1, 2, 4, 8, 16}).
-template <int G>
-__device__ __forceinline__ float group_sum(float x) {
-  if constexpr (G >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
-  if constexpr (G >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
-  if constexpr (G >= 8) x += dpp<0x141>(x);  // row_half_mirror
-  if constexpr (G >= 16) x += dpp<0x140>(x); // row_mirror
-  return x;
 }
 
 // alpha = exp(-exp(A_log) softplus(x)) with x = a_t + dt_bias (Eq. 2);
@@ -266,25 +264,41 @@ __device__ __forceinline__ float decay(float x, float expA) {
   return __builtin_amdgcn_exp2f(-expA * sp * 1.44269504088896341f);
 }
 
-constexpr int kChunk = 8;
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, true));
+}
 
-template <int D, int C>
-__global__ void __launch_bounds__((RefreshShape<D, C>::kNT))
+// Sum over the G consecutive lanes of a 16-lane row (G in {1, 2, 4, 8, 16});
+// every lane of the group gets the sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (G >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  if constexpr (G >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  if constexpr (G >= 8) x += dpp<0x141>(x);  // row_half_mirror
+  if constexpr (G >= 16) x += dpp<0x140>(x); // row_mirror
+  return x;
+}
+
+__device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+__global__ void __launch_bounds__(RefreshShape<D>::kNT) __attribute__((amdgpu_waves_per_eu(2)))
 refresh_kernel(RefreshArgs a) {
-  using Sh = RefreshShape<D, C>;
-  constexpr int G = Sh::kG, NS = Sh::kNS, NT = Sh::kNT, PER = Sh::kPer;
-  // per chunk (double-buffered): Q = gamma o k, W = k o D_{C,.}, v, gamma_C, beta, M
-  __shared__ __attribute__((aligned(16))) float sQ[2][C][D];
-  __shared__ __attribute__((aligned(16))) float sW[2][C][D];
-  __shared__ __attribute__((aligned(16))) float sV[2][C][D];
-  __shared__ __attribute__((aligned(16))) float sG[2][D];
-  __shared__ float sB[2][C];
-  __shared__ float sM[2][C][C];
-  // staging scratch (single): k and alpha of the chunk being staged
-  __shared__ __attribute__((aligned(16))) float sK[C][D];
-  __shared__ __attribute__((aligned(16))) float sA[C][D];
+  using Sh = RefreshShape<D>;
+  constexpr int KT = Sh::kKT, VTW = Sh::kVTW, NT = Sh::kNT, JB = Sh::kJB;
+  __shared__ __attribute__((aligned(16))) float sK[kC][D];     // k (staging)
+  __shared__ __attribute__((aligned(16))) float sA[kC][D];     // alpha (staging)
+  __shared__ __attribute__((aligned(16))) float sQ[kC][D + 4]; // gamma_t o k_t
+  __shared__ __attribute__((aligned(16))) float sW[D][kC + 4]; // k_s o D_{16,s}, [k][s]
+  __shared__ __attribute__((aligned(16))) float sVT[D][kC + 4];// v, [v][t]
+  __shared__ __attribute__((aligned(16))) float sL[kC][kC + 4];// beta_t M_{t,s}, s < t
+  __shared__ __attribute__((aligned(16))) float sG[D];         // gamma_16
+  __shared__ __attribute__((aligned(16))) float sB[kC];        // beta
 
-  const RefreshTask t = a.tasks[blockIdx.x];
+  const RefreshTask task = a.tasks[blockIdx.x];
   const int req = blockIdx.y;
   const int64_t t0 = a.tok_off[req];
   const int64_t t1 = a.tok_off[req + 1];
@@ -298,216 +312,237 @@ refresh_kernel(RefreshArgs a) {
     return;
   }
   const int tid = threadIdx.x;
-  const bool has_state = tid < NS;
-  const int c0 = (tid % G) * 16;
-  const int r0 = (tid / G) * 4;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, m = lane & 15;
+  const bool kda = task.kind == static_cast<uint32_t>(kKDA);
 
-  // Staging: lane `tid` handles channel jj of tokens tid/D + m*NT/D.
-  const int jj = tid % D;
-  const bool kda = t.kind == static_cast<uint32_t>(kKDA);
-  const uint32_t pidx = t.param_off + (kda ? jj : 0);
-  const float expA = a.gate_expA[pidx];
-  const float dtb = a.gate_dt[pidx];
-  const int64_t gcol = t.g_off + (kda ? jj : 0);
-  const int64_t kcol = t.k_off + jj;
-  const int64_t vcol = t.v_off + jj;
+  // Staged item of this lane: token it_t, channels 8 it_jb .. 8 it_jb + 7.
+  const bool it_on = tid < 2 * D;
+  const int it_t = tid / JB, it_jb = tid % JB, j0 = 8 * it_jb;
+  float expA[8], dtb[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint32_t u = task.param_off + (kda ? j0 + c : 0);
+    expA[c] = it_on ? a.gate_expA[u] : 0.f;
+    dtb[c] = it_on ? a.gate_dt[u] : 0.f;
+  }
+  const bool a_vec = kda && ((task.g_off | a.g_row) % 8 == 0);
+
+  u32x4 rk = {0u, 0u, 0u, 0u}, rv = rk, ra = rk;  // 8 bf16 each, packed
+  float rb = 0.f;
+  bool r_real = false;
+  auto fetch = [&](int64_t n) {
+    const int64_t tok = t0 + n * kC + it_t;
+    r_real = it_on && tok < t1;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    rk = rv = ra = z;
+    rb = 0.f;
+    if (r_real) {
+      rk = *reinterpret_cast<const u32x4*>(a.k + tok * a.k_row + task.k_off + j0);
+      rv = *reinterpret_cast<const u32x4*>(a.v + tok * a.v_row + task.v_off + j0);
+      const uint16_t* ap = a.a + tok * a.g_row + task.g_off;
+      if (a_vec) {
+        ra = *reinterpret_cast<const u32x4*>(ap + j0);
+      } else if (kda) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          ra[q] = static_cast<uint32_t>(ap[j0 + 2 * q]) | (static_cast<uint32_t>(ap[j0 + 2 * q + 1]) << 16);
+      } else {
+        ra[0] = ap[0];
+      }
+      if (it_jb == 0) rb = a.beta[tok * a.b_row + task.b_off];
+    }
+  };
+  auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
+  auto hi = [](uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); };
+
+  v4f acc[KT][VTW];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+    for (int vv = 0; vv < VTW; ++vv) acc[kt][vv] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const int64_t W = t1 - t0;
-  const int64_t nchunks = (W + C - 1) / C;
-
-  uint16_t ra[PER], rk[PER], rv[PER];
-  float rb[PER];
-  auto fetch = [&](int64_t n) {  // raw inputs of chunk n into registers
-#pragma unroll
-    for (int m = 0; m < PER; ++m) {
-      const int tt = tid / D + m * (NT / D);
-      const int64_t tok = t0 + n * C + tt;
-      if (tok < t1) {
-        ra[m] = a.a[tok * a.g_row + gcol];
-        rk[m] = a.k[tok * a.k_row + kcol];
-        rv[m] = a.v[tok * a.v_row + vcol];
-        rb[m] = jj == 0 ? a.beta[tok * a.b_row + t.b_off] : 0.f;
-      } else {  // padding: an exact no-op step
-        ra[m] = 0;
-        rk[m] = 0;
-        rv[m] = 0;
-        rb[m] = 0.f;
-      }
-    }
-  };
-  auto stage_a = [&](int buf, int64_t n) {  // decay, k, v, beta
-#pragma unroll
-    for (int m = 0; m < PER; ++m) {
-      const int tt = tid / D + m * (NT / D);
-      const bool real = t0 + n * C + tt < t1;
-      sA[tt][jj] = real ? decay(bf16_to_f32(ra[m]) + dtb, expA) : 1.f;
-      sK[tt][jj] = bf16_to_f32(rk[m]);
-      sV[buf][tt][jj] = bf16_to_f32(rv[m]);
-      if (jj == 0) sB[buf][tt] = rb[m];
-    }
-  };
-  auto stage_b = [&](int buf) {  // gamma, Q, W, gamma_C and M from sK, sA
-    for (int j = tid; j < D; j += NT) {
-      float g = 1.f;
-#pragma unroll
-      for (int tt = 0; tt < C; ++tt) {
-        g *= sA[tt][j];
-        sQ[buf][tt][j] = g * sK[tt][j];
-      }
-      sG[buf][j] = g;
-      float dd = 1.f;
-#pragma unroll
-      for (int s = C - 1; s >= 0; --s) {
-        sW[buf][s][j] = sK[s][j] * dd;
-        dd *= sA[s][j];
-      }
-    }
-    if constexpr (D == 128 && NT == 256 && C == 8) {
-      // threads 128..255: (token t, block of 8 channels); M_{t,s} summed
-      // over the 16 blocks with DPP inside each 16-lane row
-      if (tid >= 128) {
-        const int u = tid - 128;
-        const int tt = u >> 4, j0 = (u & 15) * 8;
-        float p[8], kt[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) p[c] = kt[c] = sK[tt][j0 + c];
-        (void)kt;
-        for (int s = tt - 1; s >= 0; --s) {
-          float part = 0.f;
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            p[c] *= sA[s + 1][j0 + c];
-            part = fmaf(p[c], sK[s][j0 + c], part);
-          }
-          part = group_sum<16>(part);
-          if ((u & 15) == 0) sM[buf][tt][s] = part;
-        }
-      }
-    } else {
-      for (int e = tid; e < C * C; e += NT) {
-        const int tt = e / C, s = e % C;
-        if (s < tt) {
-          float acc = 0.f;
-          for (int j = 0; j < D; ++j) {
-            float p = sK[tt][j];
-            for (int r = s + 1; r <= tt; ++r) p *= sA[r][j];
-            acc = fmaf(p, sK[s][j], acc);
-          }
-          sM[buf][tt][s] = acc;
-        }
-      }
-    }
-  };
-
-  float S[4][16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int c = 0; c < 16; ++c) S[i][c] = 0.f;
-
-  if (nchunks > 0) {
-    fetch(0);
-    stage_a(0, 0);
-  }
-  __syncthreads();
-  if (nchunks > 0) stage_b(0);
-  __syncthreads();
+  const int64_t nchunks = (W + kC - 1) / kC;
+  if (nchunks > 0) fetch(0);
   for (int64_t n = 0; n < nchunks; ++n) {
-    const int b = static_cast<int>(n & 1);
-    const bool more = n + 1 < nchunks;
-    if (more) fetch(n + 1);
-    if (has_state) {
-      float U[4][C];
-      // readout of the chunk-start state: U[i][t] = (S_0 q_t)_i
+    // ---- stage 1: decay, k, v, beta of this chunk into LDS
+    if (it_on) {
+      float al[8], kf[8], vf[8];
 #pragma unroll
-      for (int tt = 0; tt < C; ++tt) {
-        float q[16];
-#pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(&sQ[b][tt][c0 + 4 * v4]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) q[4 * v4 + e] = x[e];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float acc = 0.f;
-#pragma unroll
-          for (int c = 0; c < 16; ++c) acc = fmaf(S[i][c], q[c], acc);
-          U[i][tt] = acc;
-        }
+      for (int q = 0; q < 4; ++q) {
+        kf[2 * q] = lo(rk[q]);
+        kf[2 * q + 1] = hi(rk[q]);
+        vf[2 * q] = lo(rv[q]);
+        vf[2 * q + 1] = hi(rv[q]);
       }
+      if (!r_real) {
 #pragma unroll
-      for (int tt = 0; tt < C; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) U[i][tt] = group_sum<G>(U[i][tt]);
-      // forward substitution: U[i][t] <- c_t for the lane's rows
-#pragma unroll
-      for (int tt = 0; tt < C; ++tt) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(&sV[b][tt][r0]);
-        const float beta = sB[b][tt];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float x = v[i] - U[i][tt];
-#pragma unroll
-          for (int s = 0; s < tt; ++s) x = fmaf(-sM[b][tt][s], U[i][s], x);
-          U[i][tt] = beta * x;
-        }
-      }
-      // S <- S Diag(gamma_C) + sum_s c_s w_s^T
-      {
-        float g[16];
-#pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(&sG[b][c0 + 4 * v4]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) g[4 * v4 + e] = x[e];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int c = 0; c < 16; ++c) S[i][c] *= g[c];
-      }
-#pragma unroll
-      for (int s = 0; s < C; ++s) {
-        float w[16];
-#pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(&sW[b][s][c0 + 4 * v4]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[4 * v4 + e] = x[e];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int c = 0; c < 16; ++c) S[i][c] = fmaf(U[i][s], w[c], S[i][c]);
-      }
-    }
-    if (more) stage_a(b ^ 1, n + 1);
-    __syncthreads();
-    if (more) stage_b(b ^ 1);
-    __syncthreads();
-  }
-
-  // Write back the local units only ([dasc] §4.2): whole GDN heads, or the
-  // local columns of a KDA head.
-  if (has_state) {
-    float* out = reinterpret_cast<float*>(a.dense + dst * a.dense_stride + t.dense_off);
-    // select the mask word without a dynamic index (keeps `t` in registers)
-    const uint32_t lw = c0 < 32 ? t.local[0] : c0 < 64 ? t.local[1] : c0 < 96 ? t.local[2] : t.local[3];
-    const uint32_t m16 = (lw >> (c0 & 31)) & 0xFFFFu;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float* row = out + (r0 + i) * D + c0;
-      if (m16 == 0xFFFFu) {
+        for (int c = 0; c < 8; ++c) al[c] = 1.f;
+      } else if (kda) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const f32x4 x = {S[i][4 * q], S[i][4 * q + 1], S[i][4 * q + 2], S[i][4 * q + 3]};
-          *reinterpret_cast<f32x4*>(row + 4 * q) = x;
+          al[2 * q] = decay(lo(ra[q]) + dtb[2 * q], expA[2 * q]);
+          al[2 * q + 1] = decay(hi(ra[q]) + dtb[2 * q + 1], expA[2 * q + 1]);
         }
-      } else if (m16 != 0u) {
+      } else {
+        const float x = decay(lo(ra[0]) + dtb[0], expA[0]);
 #pragma unroll
-        for (int c = 0; c < 16; ++c)
-          if ((m16 >> c) & 1u) row[c] = S[i][c];
+        for (int c = 0; c < 8; ++c) al[c] = x;
+      }
+      *reinterpret_cast<v4f*>(&sA[it_t][j0]) = v4f{al[0], al[1], al[2], al[3]};
+      *reinterpret_cast<v4f*>(&sA[it_t][j0 + 4]) = v4f{al[4], al[5], al[6], al[7]};
+      *reinterpret_cast<v4f*>(&sK[it_t][j0]) = v4f{kf[0], kf[1], kf[2], kf[3]};
+      *reinterpret_cast<v4f*>(&sK[it_t][j0 + 4]) = v4f{kf[4], kf[5], kf[6], kf[7]};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) sVT[j0 + c][it_t] = vf[c];
+      if (it_jb == 0) sB[it_t] = rb;
+    }
+    if (n + 1 < nchunks) fetch(n + 1);
+    __syncthreads();
+    // ---- stage 2: L (pairs of rows p, 15 - p over 4-channel blocks), then
+    //      gamma / Q (forward) and W (backward) per channel
+    if (tid < 2 * D) {
+      // rows p and 15 - p (15 pairs in all), 4 channels per lane, summed over
+      // the D/4 lanes of the row pair right away
+      constexpr int NB4 = D / 4;
+      const int p = tid / NB4, c4 = 4 * (tid % NB4);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = h == 0 ? p : kC - 1 - p;
+        v4f pk = *reinterpret_cast<const v4f*>(&sK[t][c4]);
+        for (int s = t - 1; s >= 0; --s) {
+          const v4f al = *reinterpret_cast<const v4f*>(&sA[s + 1][c4]);
+          const v4f ks = *reinterpret_cast<const v4f*>(&sK[s][c4]);
+          float part = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pk[e] *= al[e];
+            part = fmaf(pk[e], ks[e], part);
+          }
+          part = group_sum<(NB4 < 16 ? NB4 : 16)>(part);
+          if constexpr (NB4 == 32) part += __shfl_xor(part, 16, 64);
+          if (tid % NB4 == 0) sL[t][s] = sB[t] * part;
+        }
+      }
+      // per-channel decays: tid < D forward, D <= tid < 2D backward
+      const int j = tid % D;
+      if (tid < D) {
+        float gam = 1.f;
+#pragma unroll
+        for (int t = 0; t < kC; ++t) {
+          gam *= sA[t][j];
+          sQ[t][j] = gam * sK[t][j];
+        }
+        sG[j] = gam;
+      } else {
+        float dd = 1.f;
+#pragma unroll
+        for (int s = kC - 1; s >= 0; --s) {
+          sW[j][s] = sK[s][j] * dd;
+          dd *= sA[s][j];
+        }
+      }
+    }
+    __syncthreads();
+    // ---- compute: P1, solve, fold, P2
+    {
+      v4f U[VTW];
+#pragma unroll
+      for (int vv = 0; vv < VTW; ++vv) U[vv] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const v4f qa = *reinterpret_cast<const v4f*>(&sQ[m][16 * kt + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int vv = 0; vv < VTW; ++vv) U[vv] = mfma4(qa[r], acc[kt][vv][r], U[vv]);
+      }
+      const v4f b4 = *reinterpret_cast<const v4f*>(&sB[4 * g]);
+      v4f Cc[VTW];
+#pragma unroll
+      for (int vv = 0; vv < VTW; ++vv) {
+        const int v = 16 * (wave * VTW + vv) + m;
+        const v4f vt = *reinterpret_cast<const v4f*>(&sVT[v][4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) U[vv][r] = b4[r] * (vt[r] - U[vv][r]);  // R_t
+      }
+      // forward substitution over the lane groups: c_t = R_t - sum_{s<t} L_{t,s} c_s
+#pragma unroll
+      for (int pgrp = 0; pgrp < 4; ++pgrp) {
+        if (g == pgrp) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const v4f Lr = *reinterpret_cast<const v4f*>(&sL[4 * g + r][4 * g]);
+#pragma unroll
+            for (int vv = 0; vv < VTW; ++vv) {
+              float x = U[vv][r];
+#pragma unroll
+              for (int q = 0; q < r; ++q) x = fmaf(-Lr[q], Cc[vv][q], x);
+              Cc[vv][r] = x;
+            }
+          }
+        }
+        if (pgrp < 3) {
+          v4f cp[VTW];
+#pragma unroll
+          for (int vv = 0; vv < VTW; ++vv)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) cp[vv][q] = __shfl(Cc[vv][q], m + 16 * pgrp, 64);
+          if (g > pgrp) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const v4f Lr = *reinterpret_cast<const v4f*>(&sL[4 * g + r][4 * pgrp]);
+#pragma unroll
+              for (int vv = 0; vv < VTW; ++vv) {
+                float x = U[vv][r];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) x = fmaf(-Lr[q], cp[vv][q], x);
+                U[vv][r] = x;
+              }
+            }
+          }
+        }
+      }
+      // S^T <- Diag(gamma_16) S^T, then S^T += W C^T
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const v4f g4 = *reinterpret_cast<const v4f*>(&sG[16 * kt + 4 * g]);
+        const v4f wa = *reinterpret_cast<const v4f*>(&sW[16 * kt + m][4 * g]);
+#pragma unroll
+        for (int vv = 0; vv < VTW; ++vv) {
+          v4f x = acc[kt][vv];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x[r] *= g4[r];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) x = mfma4(wa[r], Cc[vv][r], x);
+          acc[kt][vv] = x;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // Write back the local units only ([dasc] §4.2).  Lane (g, m) of tile
+  // (kt, vt) holds S[v][k .. k + 3] with v = 16 vt + m, k = 16 kt + 4 g.
+  float* out = reinterpret_cast<float*>(a.dense + dst * a.dense_stride + task.dense_off);
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    const int k0 = 16 * kt + 4 * g;
+    const uint32_t lw = k0 < 32 ? task.local[0] : k0 < 64 ? task.local[1]
+                      : k0 < 96 ? task.local[2] : task.local[3];
+    const uint32_t m4 = (lw >> (k0 & 31)) & 0xFu;
+#pragma unroll
+    for (int vv = 0; vv < VTW; ++vv) {
+      const int v = 16 * (wave * VTW + vv) + m;
+      float* row = out + v * D + k0;
+      const v4f x = acc[kt][vv];
+      if (m4 == 0xFu) {
+        *reinterpret_cast<v4f*>(row) = x;
+      } else if (m4) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if ((m4 >> r) & 1u) row[r] = x[r];
       }
     }
   }
@@ -582,16 +617,16 @@ int launch_refresh(int d, const RefreshArgs& args, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (d) {
     case 16:
-      refresh_kernel<16, kChunk><<<grid, RefreshShape<16, kChunk>::kNT, 0, s>>>(args);
+      refresh_kernel<16><<<grid, RefreshShape<16>::kNT, 0, s>>>(args);
       break;
     case 32:
-      refresh_kernel<32, kChunk><<<grid, RefreshShape<32, kChunk>::kNT, 0, s>>>(args);
+      refresh_kernel<32><<<grid, RefreshShape<32>::kNT, 0, s>>>(args);
       break;
     case 64:
-      refresh_kernel<64, kChunk><<<grid, RefreshShape<64, kChunk>::kNT, 0, s>>>(args);
+      refresh_kernel<64><<<grid, RefreshShape<64>::kNT, 0, s>>>(args);
       break;
     case 128:
-      refresh_kernel<128, kChunk><<<grid, RefreshShape<128, kChunk>::kNT, 0, s>>>(args);
+      refresh_kernel<128><<<grid, RefreshShape<128>::kNT, 0, s>>>(args);
       break;
     default:
       return static_cast<int>(hipErrorInvalidValue);
