@@ -258,10 +258,18 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 }
 
 // alpha = exp(-exp(A_log) softplus(x)) with x = a_t + dt_bias (Eq. 2);
-// expA = exp(A_log) is precomputed per unit.
+// expA = exp(A_log) is precomputed per unit.  softplus(x) = max(x, 0) +
+// log(1 + z) with z = exp(-|x|) in (0, 1]; u = 1 + z is rounded, and the
+// first-order term (z - (u - 1)) / u restores what the rounding lost, so
+// log(1 + z) keeps full relative precision for small z.  Hardware exp2 /
+// log2 / reciprocal, a few ulp overall.
 __device__ __forceinline__ float decay(float x, float expA) {
-  const float sp = fmaxf(x, 0.f) + log1pf(__builtin_amdgcn_exp2f(-fabsf(x) * 1.44269504088896341f));
-  return __builtin_amdgcn_exp2f(-expA * sp * 1.44269504088896341f);
+  constexpr float kLog2e = 1.44269504088896341f, kLn2 = 0.693147180559945309f;
+  const float z = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
+  const float u = 1.f + z;
+  const float l1p = __builtin_amdgcn_logf(u) * kLn2 + (z - (u - 1.f)) * __builtin_amdgcn_rcpf(u);
+  const float sp = fmaxf(x, 0.f) + l1p;
+  return __builtin_amdgcn_exp2f(-expA * sp * kLog2e);
 }
 
 template <int kCtrl>
@@ -293,7 +301,7 @@ refresh_kernel(RefreshArgs a) {
   __shared__ __attribute__((aligned(16))) float sA[kC][D];     // alpha (staging)
   __shared__ __attribute__((aligned(16))) float sQ[kC][D + 4]; // gamma_t o k_t
   __shared__ __attribute__((aligned(16))) float sW[D][kC + 4]; // k_s o D_{16,s}, [k][s]
-  __shared__ __attribute__((aligned(16))) float sVT[D][kC + 4];// v, [v][t]
+  __shared__ __attribute__((aligned(16))) float sV[kC][D];     // v, [t][v]
   __shared__ __attribute__((aligned(16))) float sL[kC][kC + 4];// beta_t M_{t,s}, s < t
   __shared__ __attribute__((aligned(16))) float sG[D];         // gamma_16
   __shared__ __attribute__((aligned(16))) float sB[kC];        // beta
@@ -394,8 +402,8 @@ refresh_kernel(RefreshArgs a) {
       *reinterpret_cast<v4f*>(&sA[it_t][j0 + 4]) = v4f{al[4], al[5], al[6], al[7]};
       *reinterpret_cast<v4f*>(&sK[it_t][j0]) = v4f{kf[0], kf[1], kf[2], kf[3]};
       *reinterpret_cast<v4f*>(&sK[it_t][j0 + 4]) = v4f{kf[4], kf[5], kf[6], kf[7]};
-#pragma unroll
-      for (int c = 0; c < 8; ++c) sVT[j0 + c][it_t] = vf[c];
+      *reinterpret_cast<v4f*>(&sV[it_t][j0]) = v4f{vf[0], vf[1], vf[2], vf[3]};
+      *reinterpret_cast<v4f*>(&sV[it_t][j0 + 4]) = v4f{vf[4], vf[5], vf[6], vf[7]};
       if (it_jb == 0) sB[it_t] = rb;
     }
     if (n + 1 < nchunks) fetch(n + 1);
@@ -463,9 +471,8 @@ refresh_kernel(RefreshArgs a) {
 #pragma unroll
       for (int vv = 0; vv < VTW; ++vv) {
         const int v = 16 * (wave * VTW + vv) + m;
-        const v4f vt = *reinterpret_cast<const v4f*>(&sVT[v][4 * g]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) U[vv][r] = b4[r] * (vt[r] - U[vv][r]);  // R_t
+        for (int r = 0; r < 4; ++r) U[vv][r] = b4[r] * (sV[4 * g + r][v] - U[vv][r]);  // R_t
       }
       // forward substitution over the lane groups: c_t = R_t - sum_{s<t} L_{t,s} c_s
 #pragma unroll
