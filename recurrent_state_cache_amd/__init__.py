@@ -1,7 +1,7 @@
 """MI355X-native state-checkpoint hot path of decay-aware state compression.
 
 A thin Python binding over the C ABI in include/dasc.h (libdasc.so, built for
-gfx950 by `python -m recurrent_state_cache_amd._build`).  This module only
+gfx950 by `python recurrent_state_cache_amd/_build.py`).  This module only
 marshals arguments: every step of the plan runs in the library's host code
 and every step of pack, unpack and refresh runs in its HIP kernels.  There is
 no fallback: if the library is missing, importing this package fails.
@@ -64,7 +64,7 @@ class _LayerInfo(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built: run `python -m recurrent_state_cache_amd._build`")
+        raise ImportError(f"{LIB_PATH} is not built: run `python recurrent_state_cache_amd/_build.py`")
     L = ctypes.CDLL(LIB_PATH)
     sig = {
         "dasc_plan_build": (_c_i32, [ctypes.POINTER(_LayerDesc), _c_i32, _c_f64, _c_f64, _c_i32,

@@ -1,6 +1,6 @@
 """Builds libdasc.so in-tree with hipcc for gfx950.
 
-    python -m recurrent_state_cache_amd._build
+    python recurrent_state_cache_amd/_build.py
 """
 from __future__ import annotations
 
