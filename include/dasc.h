@@ -150,7 +150,7 @@ int dasc_plan_units(dasc_plan_t plan, int32_t layer, uint8_t* retained,
  * for a null plan or a negative budget. */
 int64_t dasc_plan_slots(dasc_plan_t plan, int64_t budget_bytes, int32_t dense);
 
-/* Copy the plan's device tables (task lists, channel maps, gate parameters,
+/* Copy the plan's device tables (task lists, retained-channel masks, gate parameters,
  * status word) into a caller-allocated device buffer of at least
  * info.device_bytes bytes, 256-byte aligned, on `stream`; the copy is
  * complete when this call returns.  Later data calls use that buffer, which

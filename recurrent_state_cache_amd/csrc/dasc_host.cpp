@@ -71,14 +71,14 @@ struct dasc_plan {
   int64_t k_row = 0, v_row = 0, g_row = 0, b_row = 0;
 
   // host image of the device tables
-  std::vector<CopyTask> pack_copy, unpack_copy;
-  std::vector<KdaTask> kda;
-  std::vector<uint8_t> maps;
+  std::vector<Piece> pack, unpack;
   std::vector<RefreshTask> refresh;
   std::vector<float> gate_expA, gate_dt;
-  std::vector<Group> kda_groups, refresh_groups;
-  int64_t off_pack = 0, off_unpack = 0, off_kda = 0, off_maps = 0, off_refresh = 0,
-          off_expA = 0, off_dt = 0, off_status = 0, table_bytes = 0;
+  std::vector<Group> refresh_groups;
+  int32_t kda_r_max = 0;  // largest retained-channel count of a KDA head
+  bool kda_128 = true;    // every KDA layer has d_k = d_v = 128
+  int64_t off_pack = 0, off_unpack = 0, off_refresh = 0, off_expA = 0, off_dt = 0,
+          off_status = 0, table_bytes = 0;
 
   uint8_t* device = nullptr;  // caller-owned upload target
   DeviceTables dev{};
@@ -86,11 +86,11 @@ struct dasc_plan {
 
 namespace {
 
-void push_range(std::vector<CopyTask>& out, uint64_t dense_off, uint64_t pool_off, uint64_t bytes,
+void push_range(std::vector<Piece>& out, uint64_t dense_off, uint64_t pool_off, uint64_t bytes,
                 uint32_t type) {
   while (bytes > 0) {
     uint32_t b = static_cast<uint32_t>(std::min<uint64_t>(bytes, kCopyChunk));
-    CopyTask t{};
+    Piece t{};
     t.dense_off = dense_off;
     t.pool_off = pool_off;
     t.bytes = b;
@@ -102,78 +102,62 @@ void push_range(std::vector<CopyTask>& out, uint64_t dense_off, uint64_t pool_of
   }
 }
 
-// Turn the mask into task lists and lay out the device tables.
+// Turn the mask into piece lists and lay out the device tables.  Pieces
+// follow the dense checkpoint's order (layers, heads, then conv), which is
+// also the pool slot's order.
 void build_tables(dasc_plan* p) {
-  // KDA heads are grouped by shape so that each group uses one kernel.
-  std::vector<std::pair<int, int>> shapes;
   for (const auto& L : p->layers) {
-    if (L.kind != kKDA) continue;
-    auto s = std::make_pair(L.d_k, L.d_v);
-    if (std::find(shapes.begin(), shapes.end(), s) == shapes.end()) shapes.push_back(s);
-  }
-  for (const auto& L : p->layers) {
+    int64_t j = 0;  // retained units of the layer seen so far
     if (L.kind == kGDN) {
-      int64_t j = 0;
       for (int h = 0; h < L.n_heads; ++h) {
-        uint64_t d_off = L.dense_off + h * L.unit_bytes;
+        const uint64_t d_off = L.dense_off + h * L.unit_bytes;
         if (L.retained[h]) {
-          uint64_t p_off = L.pool_off + j * L.unit_bytes;
-          push_range(p->pack_copy, d_off, p_off, L.unit_bytes, kTaskCopy);
-          push_range(p->unpack_copy, d_off, p_off, L.unit_bytes, kTaskCopy);
+          const uint64_t p_off = L.pool_off + j * L.unit_bytes;
+          push_range(p->pack, d_off, p_off, L.unit_bytes, kPieceCopy);
+          push_range(p->unpack, d_off, p_off, L.unit_bytes, kPieceCopy);
           ++j;
         } else {
-          push_range(p->unpack_copy, d_off, 0, L.unit_bytes, kTaskZero);
+          push_range(p->unpack, d_off, 0, L.unit_bytes, kPieceZero);
         }
       }
-    } else {
-      // Fully omitted KDA heads have no task of their own: unpack clears them.
-      const int64_t head_bytes = int64_t(L.d_v) * L.d_k * 4;
-      for (int h = 0; h < L.n_heads; ++h) {
-        int r = 0;
-        for (int k = 0; k < L.d_k; ++k) r += L.retained[h * L.d_k + k];
-        if (r == 0) push_range(p->unpack_copy, L.dense_off + h * head_bytes, 0, head_bytes, kTaskZero);
-      }
+      continue;
     }
-  }
-  // KDA tasks, shape group by shape group.
-  for (const auto& s : shapes) {
-    Group g{s.first, s.second, static_cast<uint32_t>(p->kda.size()), 0, 0};
-    for (const auto& L : p->layers) {
-      if (L.kind != kKDA || L.d_k != s.first || L.d_v != s.second) continue;
-      const int64_t head_bytes = int64_t(L.d_v) * L.d_k * 4;
-      int64_t j = 0;  // retained units of the layer seen so far
-      for (int h = 0; h < L.n_heads; ++h) {
-        uint8_t map[kMapBytes];
-        std::memset(map, 0, 128);
-        std::memset(map + 128, kLocal, 128);
-        uint32_t r = 0;
-        for (int k = 0; k < L.d_k; ++k) {
-          if (L.retained[h * L.d_k + k]) {
-            map[r] = static_cast<uint8_t>(k);
-            map[128 + k] = static_cast<uint8_t>(r);
-            ++r;
-          }
+    p->kda_128 = p->kda_128 && L.d_k == 128 && L.d_v == 128;
+    const int64_t head_bytes = int64_t(L.d_v) * L.d_k * 4;
+    const int row_blocks = (L.d_v + kKdaRows - 1) / kKdaRows;
+    for (int h = 0; h < L.n_heads; ++h) {
+      Piece t{};
+      uint32_t r = 0;
+      for (int k = 0; k < L.d_k; ++k) {
+        if (L.retained[h * L.d_k + k]) {
+          t.mask[k >> 5] |= 1u << (k & 31);
+          ++r;
         }
-        if (r > 0) {
-          KdaTask t{};
-          t.dense_off = L.dense_off + h * head_bytes;
-          t.pool_off = L.pool_off + j * L.unit_bytes;
-          t.r = r;
-          t.map_idx = static_cast<uint32_t>(p->maps.size() / kMapBytes);
-          p->maps.insert(p->maps.end(), map, map + kMapBytes);
-          p->kda.push_back(t);
-          g.r_max = std::max(g.r_max, static_cast<int32_t>(r));
-        }
-        j += r;
       }
+      const uint64_t d_off = L.dense_off + h * head_bytes;
+      if (r == 0) {  // fully omitted head: unpack clears it
+        push_range(p->unpack, d_off, 0, head_bytes, kPieceZero);
+        continue;
+      }
+      t.type = kPieceKda;
+      t.dense_off = d_off;
+      t.pool_off = L.pool_off + j * L.unit_bytes;
+      t.d_k = static_cast<uint16_t>(L.d_k);
+      t.d_v = static_cast<uint16_t>(L.d_v);
+      t.r = static_cast<uint16_t>(r);
+      for (int rb = 0; rb < row_blocks; ++rb) {
+        t.rb = static_cast<uint16_t>(rb);
+        p->pack.push_back(t);
+        p->unpack.push_back(t);
+      }
+      p->kda_r_max = std::max(p->kda_r_max, static_cast<int32_t>(r));
+      j += r;
     }
-    g.count = static_cast<uint32_t>(p->kda.size()) - g.first;
-    if (g.count) p->kda_groups.push_back(g);
   }
   // Conv state: one contiguous block after the temporal payload on both sides.
   const dasc_plan_info& I = p->info;
-  push_range(p->pack_copy, I.temporal_dense_bytes, I.temporal_rag_bytes, I.conv_bytes, kTaskCopy);
-  push_range(p->unpack_copy, I.temporal_dense_bytes, I.temporal_rag_bytes, I.conv_bytes, kTaskCopy);
+  push_range(p->pack, I.temporal_dense_bytes, I.temporal_rag_bytes, I.conv_bytes, kPieceCopy);
+  push_range(p->unpack, I.temporal_dense_bytes, I.temporal_rag_bytes, I.conv_bytes, kPieceCopy);
 
   // Refresh tasks, grouped by head width.
   std::vector<std::pair<int, int>> rshapes;
@@ -183,7 +167,7 @@ void build_tables(dasc_plan* p) {
       rshapes.push_back(s);
   }
   for (const auto& s : rshapes) {
-    Group g{s.first, s.second, static_cast<uint32_t>(p->refresh.size()), 0, 0};
+    Group g{s.first, s.second, static_cast<uint32_t>(p->refresh.size()), 0};
     for (const auto& L : p->layers) {
       if (L.d_k != s.first || L.d_v != s.second) continue;
       const int64_t head_bytes = int64_t(L.d_v) * L.d_k * 4;
@@ -227,10 +211,8 @@ void build_tables(dasc_plan* p) {
     o = align_up(o + bytes, 256);
     return at;
   };
-  p->off_pack = section(p->pack_copy.size() * sizeof(CopyTask));
-  p->off_unpack = section(p->unpack_copy.size() * sizeof(CopyTask));
-  p->off_kda = section(p->kda.size() * sizeof(KdaTask));
-  p->off_maps = section(p->maps.size());
+  p->off_pack = section(p->pack.size() * sizeof(Piece));
+  p->off_unpack = section(p->unpack.size() * sizeof(Piece));
   p->off_refresh = section(p->refresh.size() * sizeof(RefreshTask));
   p->off_expA = section(p->gate_expA.size() * sizeof(float));
   p->off_dt = section(p->gate_dt.size() * sizeof(float));
@@ -492,10 +474,8 @@ int dasc_plan_upload(dasc_plan_t p, void* device_buffer, int64_t bytes, void* st
   auto put = [&](int64_t off, const void* src, size_t n) {
     if (n) std::memcpy(img.data() + off, src, n);
   };
-  put(p->off_pack, p->pack_copy.data(), p->pack_copy.size() * sizeof(CopyTask));
-  put(p->off_unpack, p->unpack_copy.data(), p->unpack_copy.size() * sizeof(CopyTask));
-  put(p->off_kda, p->kda.data(), p->kda.size() * sizeof(KdaTask));
-  put(p->off_maps, p->maps.data(), p->maps.size());
+  put(p->off_pack, p->pack.data(), p->pack.size() * sizeof(Piece));
+  put(p->off_unpack, p->unpack.data(), p->unpack.size() * sizeof(Piece));
   put(p->off_refresh, p->refresh.data(), p->refresh.size() * sizeof(RefreshTask));
   put(p->off_expA, p->gate_expA.data(), p->gate_expA.size() * sizeof(float));
   put(p->off_dt, p->gate_dt.data(), p->gate_dt.size() * sizeof(float));
@@ -505,10 +485,8 @@ int dasc_plan_upload(dasc_plan_t p, void* device_buffer, int64_t bytes, void* st
   if (e != hipSuccess) return fail(DASC_EHIP, std::string("plan_upload: ") + hipGetErrorString(e));
   uint8_t* d = static_cast<uint8_t*>(device_buffer);
   p->device = d;
-  p->dev.pack_copy = reinterpret_cast<const CopyTask*>(d + p->off_pack);
-  p->dev.unpack_copy = reinterpret_cast<const CopyTask*>(d + p->off_unpack);
-  p->dev.kda = reinterpret_cast<const KdaTask*>(d + p->off_kda);
-  p->dev.maps = d + p->off_maps;
+  p->dev.pack = reinterpret_cast<const Piece*>(d + p->off_pack);
+  p->dev.unpack = reinterpret_cast<const Piece*>(d + p->off_unpack);
   p->dev.refresh = reinterpret_cast<const RefreshTask*>(d + p->off_refresh);
   p->dev.gate_expA = reinterpret_cast<const float*>(d + p->off_expA);
   p->dev.gate_dt = reinterpret_cast<const float*>(d + p->off_dt);
@@ -570,6 +548,29 @@ int check_move(const dasc_plan* p, const char* what, const void* dense, int64_t 
   return DASC_OK;
 }
 
+// One pack or unpack: a single launch over the direction's piece list.
+int run_move(const dasc_plan* p, bool pack, const void* src_base, int64_t src_stride,
+             int64_t n_src, const int32_t* src_idx, void* dst_base, int64_t dst_stride,
+             int64_t n_dst, const int32_t* dst_idx, int32_t n, void* stream) {
+  const std::vector<Piece>& pieces = pack ? p->pack : p->unpack;
+  MoveArgs m{};
+  m.pieces = pack ? p->dev.pack : p->dev.unpack;
+  m.n_pieces = static_cast<uint32_t>(pieces.size());
+  m.kda_r_max = p->kda_r_max;
+  m.kda_128 = p->kda_128;
+  m.src_idx = src_idx;
+  m.dst_idx = dst_idx;
+  m.src_base = static_cast<const uint8_t*>(src_base);
+  m.src_stride = src_stride;
+  m.n_src = n_src;
+  m.dst_base = static_cast<uint8_t*>(dst_base);
+  m.dst_stride = dst_stride;
+  m.n_dst = n_dst;
+  m.n = n;
+  m.status = p->dev.status;
+  return launch_move(pack, m, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -580,19 +581,8 @@ int dasc_ckpt_pack(dasc_plan_t p, const void* dense_base, int64_t dense_stride, 
   int rc = check_move(p, "ckpt_pack", dense_base, dense_stride, n_dense, pool_base, pool_stride,
                       n_slots, src_idx, dst_slot, n);
   if (rc != DASC_OK || n == 0) return rc;
-  const uint8_t* src = static_cast<const uint8_t*>(dense_base);
-  uint8_t* dst = static_cast<uint8_t*>(pool_base);
-  int e = 0;
-  for (const Group& g : p->kda_groups) {
-    e = launch_kda(true, g.d_k, g.d_v, g.r_max, p->dev.kda + g.first, g.count, p->dev.maps, src_idx,
-                   dst_slot, src, dense_stride, n_dense, dst, pool_stride, n_slots, n,
-                   p->dev.status, stream);
-    if (e) break;
-  }
-  if (!e && !p->pack_copy.empty())
-    e = launch_copy(true, p->dev.pack_copy, static_cast<uint32_t>(p->pack_copy.size()), src_idx,
-                    dst_slot, src, dense_stride, n_dense, dst, pool_stride, n_slots, n,
-                    p->dev.status, stream);
+  int e = run_move(p, true, dense_base, dense_stride, n_dense, src_idx, pool_base, pool_stride,
+                   n_slots, dst_slot, n, stream);
   if (e) return fail(DASC_EHIP, std::string("ckpt_pack: launch failed: ") +
                                     hipGetErrorString(static_cast<hipError_t>(e)));
   return DASC_OK;
@@ -605,19 +595,8 @@ int dasc_ckpt_unpack_zero_fill(dasc_plan_t p, const void* pool_base, int64_t poo
   int rc = check_move(p, "ckpt_unpack_zero_fill", dense_base, dense_stride, n_dense, pool_base,
                       pool_stride, n_slots, src_slot, dst_idx, n);
   if (rc != DASC_OK || n == 0) return rc;
-  const uint8_t* src = static_cast<const uint8_t*>(pool_base);
-  uint8_t* dst = static_cast<uint8_t*>(dense_base);
-  int e = 0;
-  for (const Group& g : p->kda_groups) {
-    e = launch_kda(false, g.d_k, g.d_v, g.r_max, p->dev.kda + g.first, g.count, p->dev.maps, src_slot,
-                   dst_idx, src, pool_stride, n_slots, dst, dense_stride, n_dense, n,
-                   p->dev.status, stream);
-    if (e) break;
-  }
-  if (!e && !p->unpack_copy.empty())
-    e = launch_copy(false, p->dev.unpack_copy, static_cast<uint32_t>(p->unpack_copy.size()),
-                    src_slot, dst_idx, src, pool_stride, n_slots, dst, dense_stride, n_dense, n,
-                    p->dev.status, stream);
+  int e = run_move(p, false, pool_base, pool_stride, n_slots, src_slot, dense_base, dense_stride,
+                   n_dense, dst_idx, n, stream);
   if (e) return fail(DASC_EHIP, std::string("ckpt_unpack_zero_fill: launch failed: ") +
                                     hipGetErrorString(static_cast<hipError_t>(e)));
   return DASC_OK;

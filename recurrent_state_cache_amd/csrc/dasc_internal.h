@@ -12,37 +12,36 @@ namespace dasc {
 constexpr int kGDN = 0;
 constexpr int kKDA = 1;
 
-constexpr uint32_t kTaskCopy = 0;  // move `bytes` between dense and pool
-constexpr uint32_t kTaskZero = 1;  // clear `bytes` of the dense checkpoint
+// Pack and unpack walk one flat list of pieces per direction, in the order
+// of the dense checkpoint (layer by layer, head by head, conv last), so that
+// the workgroups resident at once sweep a narrow address window.
+constexpr uint32_t kPieceCopy = 0;  // move `bytes` between dense and pool
+constexpr uint32_t kPieceZero = 1;  // clear `bytes` of the dense checkpoint (unpack)
+constexpr uint32_t kPieceKda = 2;   // kKdaRows rows of a KDA head with >= 1 retained channel
 
-// Largest byte range one workgroup moves in a copy task (one GDN head at
-// d_k = d_v = 128).
-constexpr uint32_t kCopyChunk = 65536;
+// Largest byte range one copy / zero piece covers: 256 lanes x 16 B.  Small
+// pieces stream HBM markedly faster on MI355X than 64 KiB pieces do.
+constexpr uint32_t kCopyChunk = 4096;
 
-// Bytes of per-head channel maps: ret_list[128] (the r retained channel
-// indices, ascending) then rank_of[128] (a channel's position among the
-// retained ones, or kLocal).
-constexpr uint32_t kMapBytes = 256;
-constexpr uint8_t kLocal = 0xFF;
+// Rows of a KDA head one piece moves: 32 rows make every unit segment a
+// whole 128-byte line (32 fp32).
+constexpr int kKdaRows = 32;
+// LDS floats per staged unit segment (kKdaRows + 4 of padding).
+constexpr int kKdaLdsRow = kKdaRows + 4;
 
-// A contiguous byte range: pack moves dense -> pool, unpack pool -> dense
-// (or clears the dense range for kTaskZero).
-struct alignas(32) CopyTask {
-  uint64_t dense_off;  // byte offset inside a dense checkpoint
-  uint64_t pool_off;   // byte offset inside a pool slot
-  uint32_t bytes;      // multiple of 16, at most kCopyChunk
-  uint32_t type;       // kTaskCopy or kTaskZero
-  uint64_t pad;
-};
-
-// One KDA head with at least one retained channel.  Its r retained
-// columns are the units pool[pool_off + j * d_v * 4], j < r.
-struct alignas(32) KdaTask {
-  uint64_t dense_off;  // the head's state [d_v][d_k] fp32
-  uint64_t pool_off;   // the head's first retained unit
-  uint32_t r;          // retained channels of the head
-  uint32_t map_idx;    // channel maps at maps + map_idx * kMapBytes
-  uint32_t pad[2];
+// One workgroup's work for one (checkpoint, slot) pair.  For a KDA piece the
+// head's r retained columns (r = popcount of mask) are the units
+// pool[pool_off + j d_v 4], j < r, in ascending channel order: channel k
+// goes to j = the number of retained channels below k.
+struct alignas(64) Piece {
+  uint64_t dense_off;  // copy / zero: the range; KDA: the head's state [d_v][d_k] fp32
+  uint64_t pool_off;   // copy: the range; KDA: the head's first retained unit
+  uint32_t type;       // kPieceCopy, kPieceZero or kPieceKda
+  uint32_t bytes;      // copy / zero: multiple of 16, at most kCopyChunk
+  uint16_t d_k, d_v;   // KDA: head shape
+  uint16_t rb, r;      // KDA: row block (rows kKdaRows rb ..), retained channels
+  uint32_t mask[4];    // KDA: bit k set = channel k retained
+  uint32_t pad[4];
 };
 
 // One (layer, head) that a bounded-suffix refresh replays.
@@ -58,40 +57,46 @@ struct alignas(64) RefreshTask {
   uint32_t pad[4];
 };
 
-static_assert(sizeof(CopyTask) == 32, "CopyTask layout");
-static_assert(sizeof(KdaTask) == 32, "KdaTask layout");
+static_assert(sizeof(Piece) == 64, "Piece layout");
 static_assert(sizeof(RefreshTask) == 64, "RefreshTask layout");
 
 // Device pointers of an uploaded plan's sections.
 struct DeviceTables {
-  const CopyTask* pack_copy;
-  const CopyTask* unpack_copy;
-  const KdaTask* kda;
-  const uint8_t* maps;
+  const Piece* pack;
+  const Piece* unpack;
   const RefreshTask* refresh;
   const float* gate_expA;  // exp(A_log) per unit, fp32
   const float* gate_dt;    // dt_bias per unit, fp32
   uint32_t* status;        // DASC_STATUS_* bits
 };
 
-// A run of tasks that share one kernel instantiation.  r_max: the largest
-// retained-channel count of a KDA head in the run (sizes the LDS).
+// A run of refresh tasks that share one kernel instantiation (head width).
 struct Group {
   int32_t d_k, d_v;
   uint32_t first, count;
-  int32_t r_max;
+};
+
+// Arguments of one pack or unpack launch: grid x = the pieces, grid y = the
+// entry i of the (src_idx[i], dst_idx[i]) pairs.
+// pack:   src = dense checkpoints, dst = pool slots
+// unpack: src = pool slots,        dst = dense checkpoints
+struct MoveArgs {
+  const Piece* pieces;
+  uint32_t n_pieces;
+  int32_t kda_r_max;  // largest r of a KDA piece (sizes the LDS); 0 if none
+  bool kda_128;       // every KDA piece has d_k = d_v = 128
+  const int32_t* src_idx;
+  const int32_t* dst_idx;
+  const uint8_t* src_base;
+  int64_t src_stride, n_src;
+  uint8_t* dst_base;
+  int64_t dst_stride, n_dst;
+  int32_t n;
+  uint32_t* status;
 };
 
 // Kernel launchers (dasc_kernels.hip).  They return a hipError_t value.
-int launch_copy(bool pack, const CopyTask* tasks, uint32_t n_tasks, const int32_t* src_idx,
-                const int32_t* dst_idx, const uint8_t* src_base, int64_t src_stride,
-                int64_t n_src, uint8_t* dst_base, int64_t dst_stride, int64_t n_dst,
-                int32_t n, uint32_t* status, void* stream);
-
-int launch_kda(bool pack, int d_k, int d_v, int r_max, const KdaTask* tasks, uint32_t n_tasks,
-               const uint8_t* maps, const int32_t* src_idx, const int32_t* dst_idx,
-               const uint8_t* src_base, int64_t src_stride, int64_t n_src, uint8_t* dst_base,
-               int64_t dst_stride, int64_t n_dst, int32_t n, uint32_t* status, void* stream);
+int launch_move(bool pack, const MoveArgs& args, void* stream);
 
 bool kda_shape_supported(int d_k, int d_v);
 bool refresh_shape_supported(int d_k, int d_v);

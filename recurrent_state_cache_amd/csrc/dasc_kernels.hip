@@ -5,12 +5,12 @@
 //          Serving" (arXiv HTML version): §3.1 Eq. 1, §3.3 Eq. 2, §4.1, §4.2,
 //          Appendix B (ragged Scheme 2).
 //
-// Pack and unpack are pure data movement: every workgroup takes one task of
-// the plan's lists for one (checkpoint, slot) pair and moves raw bits with
-// 16-byte accesses.  KDA units are strided columns of a row-major state, so
-// a KDA task stages its head through LDS as a 4x4-block register transpose.
-// The refresh keeps one head's fp32 state resident in registers (4 rows x 16
-// columns per lane) and replays Eq. 1 token by token.
+// Pack and unpack are pure data movement: every workgroup takes one piece of
+// the plan's task lists for one (checkpoint, slot) pair and moves raw bits
+// with 16-byte accesses.  KDA units are strided columns of a row-major state,
+// so a KDA piece (32 rows of a head) goes through a 4x4-block register
+// transpose and LDS.  The refresh keeps one head's fp32 state resident in
+// MFMA accumulator registers and replays Eq. 1 in exact chunks of 16 tokens.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -41,169 +41,143 @@ __device__ __forceinline__ void st_stream(T v, T* p) {
 }
 
 // ---------------------------------------------------------------------------
-// Contiguous ranges: GDN heads (whole-unit copies), conv bytes, and the
-// zero-fill of omitted GDN heads / fully omitted KDA heads.
-// pack:   src = dense checkpoint, dst = pool slot
-// unpack: src = pool slot,        dst = dense checkpoint
+// Pack and unpack ([dasc] §4.1, §4.2, Appendix B Scheme 2).  One launch per
+// direction moves every byte of n (checkpoint, slot) pairs: grid x walks the
+// plan's piece list (in dense-checkpoint order), grid y the pairs.  Every
+// workgroup touches a small, compact range (at most 16 KiB), so that the
+// workgroups resident at once sweep a narrow address window; on MI355X that
+// streams HBM far better than 64 KiB pieces.  A workgroup issues its three
+// table loads (piece, source index, destination index) together, and one
+// check consumes all of them, so a piece costs one table round trip before
+// its data moves.
+//
+// Copy / zero pieces: GDN heads (whole units), conv bytes, and the
+// zero-fill of omitted GDN heads / fully omitted KDA heads, at most 4 KiB:
+// one 16-byte access per lane.
+//
+// KDA pieces.  The state S is [d_v][d_k] row-major; the unit (h, k) is the
+// column S[:, k], stored in the pool as d_v contiguous floats.  A piece is
+// one block of kKdaRows = 32 rows of one head: lane (vl, kg) with
+// kg = tid % 32, vl = tid / 32 owns the 4x4 block of rows 4 (8 rb + vl) ..
+// + 3 and columns 4 kg .. 4 kg + 3, read as four 16-byte row pieces (lanes
+// 0..31 of a row cover it contiguously) and transposed in registers.  LDS
+// holds only the head's r retained columns, as 32-row segments U[j][..] in
+// pool order (j = rank of the channel among the retained ones, a popcount
+// of the piece's mask), written and read as 16-byte vectors; each segment
+// is one 128-byte line of its unit.
 // ---------------------------------------------------------------------------
-template <bool kPack>
-__global__ void __launch_bounds__(kThreads)
-copy_kernel(const CopyTask* __restrict__ tasks, const int32_t* __restrict__ src_idx,
-            const int32_t* __restrict__ dst_idx, const uint8_t* __restrict__ src_base,
-            int64_t src_stride, int64_t n_src, uint8_t* __restrict__ dst_base,
-            int64_t dst_stride, int64_t n_dst, uint32_t* __restrict__ status) {
-  const CopyTask t = tasks[blockIdx.x];
-  const int64_t s = src_idx[blockIdx.y];
-  const int64_t d = dst_idx[blockIdx.y];
-  if (!in_range(s, n_src) || !in_range(d, n_dst)) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) flag(status, DASC_STATUS_BAD_INDEX);
-    return;
+
+// Retained bits of channels 4 kg .. 4 kg + 3 (low 4 bits) and the number of
+// retained channels below 4 kg, from a head's 128-bit mask.
+__device__ __forceinline__ void lane_ranks(const Piece& t, int kg, uint32_t& bits4,
+                                           uint32_t& below) {
+  const int k0 = 4 * kg, w = k0 >> 5, sh = k0 & 31;
+  const uint32_t m0 = t.mask[0], m1 = t.mask[1], m2 = t.mask[2], m3 = t.mask[3];
+  const uint32_t mw = w == 0 ? m0 : w == 1 ? m1 : w == 2 ? m2 : m3;
+  below = (w > 0 ? __popc(m0) : 0u) + (w > 1 ? __popc(m1) : 0u) + (w > 2 ? __popc(m2) : 0u) +
+          __popc(mw & ((1u << sh) - 1u));
+  bits4 = (mw >> sh) & 0xFu;
+}
+
+template <bool kPack, int DK, int DV>
+__device__ __forceinline__ void kda_piece(const Piece& t, const uint8_t* src, uint8_t* dst,
+                                          float* U) {
+  const int dk = DK ? DK : t.d_k;
+  const int dv = DV ? DV : t.d_v;
+  const int KG = dk / 4, VG = dv / 4;
+  const int rb = t.rb, r = t.r;
+  const int tid = threadIdx.x;
+  const int kg = tid % 32, vl = tid / 32, vg = 8 * rb + vl;
+  const int nseg = min(8, VG - 8 * rb);  // 16-byte pieces per unit segment
+  const bool mine = kg < KG && vl < nseg;
+  uint32_t bits4 = 0, below = 0;
+  lane_ranks(t, kg, bits4, below);
+  if constexpr (kPack) {
+    const float* S = reinterpret_cast<const float*>(src + t.dense_off);
+    if (mine) {
+      f32x4 x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        x[i] = ld_stream(reinterpret_cast<const f32x4*>(S + (4 * vg + i) * dk + 4 * kg));
+      uint32_t rk = below;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if ((bits4 >> c) & 1u) {
+          *reinterpret_cast<f32x4*>(&U[rk * kKdaLdsRow + 4 * vl]) =
+              f32x4{x[0][c], x[1][c], x[2][c], x[3][c]};
+          ++rk;
+        }
+      }
+    }
+    __syncthreads();
+    float* P = reinterpret_cast<float*>(dst + t.pool_off) + kKdaRows * rb;
+    for (int q = tid; q < 8 * r; q += kThreads) {
+      const int j = q / 8, g = q % 8;
+      if (g < nseg)
+        st_stream(*reinterpret_cast<const f32x4*>(&U[j * kKdaLdsRow + 4 * g]),
+                  reinterpret_cast<f32x4*>(P + j * dv + 4 * g));
+    }
+  } else {
+    const float* P = reinterpret_cast<const float*>(src + t.pool_off) + kKdaRows * rb;
+    for (int q = tid; q < 8 * r; q += kThreads) {
+      const int j = q / 8, g = q % 8;
+      if (g < nseg)
+        *reinterpret_cast<f32x4*>(&U[j * kKdaLdsRow + 4 * g]) =
+            ld_stream(reinterpret_cast<const f32x4*>(P + j * dv + 4 * g));
+    }
+    __syncthreads();
+    if (mine) {
+      float* S = reinterpret_cast<float*>(dst + t.dense_off);
+      f32x4 col[4];
+      uint32_t rk = below;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if ((bits4 >> c) & 1u) {
+          col[c] = *reinterpret_cast<const f32x4*>(&U[rk * kKdaLdsRow + 4 * vl]);
+          ++rk;
+        } else {
+          col[c] = f32x4{0.f, 0.f, 0.f, 0.f};  // omitted channel: +0.0
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        st_stream(f32x4{col[0][i], col[1][i], col[2][i], col[3][i]},
+                  reinterpret_cast<f32x4*>(S + (4 * vg + i) * dk + 4 * kg));
+    }
   }
+}
+
+template <bool kPack>
+__device__ __forceinline__ void copy_piece(const Piece& t, const uint8_t* src, uint8_t* dst) {
+  const uint32_t tid = threadIdx.x;
+  if (tid >= (t.bytes >> 4)) return;
   const uint64_t src_off = kPack ? t.dense_off : t.pool_off;
   const uint64_t dst_off = kPack ? t.pool_off : t.dense_off;
-  u32x4* dst = reinterpret_cast<u32x4*>(dst_base + d * dst_stride + dst_off);
-  const uint32_t nv = t.bytes >> 4;
-  const uint32_t tid = threadIdx.x;
-  if (!kPack && t.type == kTaskZero) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    for (uint32_t i = tid; i < nv; i += kThreads) st_stream(z, dst + i);
-    return;
-  }
-  const u32x4* src = reinterpret_cast<const u32x4*>(src_base + s * src_stride + src_off);
-  if (nv == kCopyChunk / 16) {
-    // A full 64 KiB chunk: all 16 loads of a lane in flight before any store.
-    constexpr int kPer = kCopyChunk / 16 / kThreads;
-    u32x4 r[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) r[j] = ld_stream(src + tid + kThreads * j);
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) st_stream(r[j], dst + tid + kThreads * j);
+  u32x4* d = reinterpret_cast<u32x4*>(dst + dst_off) + tid;
+  if (!kPack && t.type == kPieceZero) {
+    st_stream(u32x4{0u, 0u, 0u, 0u}, d);
   } else {
-    for (uint32_t i = tid; i < nv; i += kThreads) st_stream(ld_stream(src + i), dst + i);
+    st_stream(ld_stream(reinterpret_cast<const u32x4*>(src + src_off) + tid), d);
   }
 }
 
-// ---------------------------------------------------------------------------
-// KDA heads.  The state S is [d_v][d_k] row-major; the unit (h, k) is the
-// column S[:, k], stored in the pool as d_v contiguous floats ([dasc] §4.1,
-// Appendix B).  LDS holds only the head's r retained columns, as rows
-// U[j][0..d_v) in pool order (j = rank of the channel among the retained
-// ones), so its size is r_max * d_v floats for the task group instead of a
-// whole head.  A lane moves 4x4 blocks of S: four 16-byte row accesses and an
-// in-register transpose.  Each LDS row is rotated by whole 16-byte groups
-// (by its row index) so that lanes touching different rows spread over the
-// banks; lanes walking one row touch consecutive groups.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int rot(int g, int by, int groups) {
-  int x = g + by;
-  return x >= groups ? x - groups : x;  // by < groups, g < groups
-}
-
-// pack: dense head -> LDS (retained columns only) -> contiguous pool units
-template <int DK, int DV>
-__global__ void __launch_bounds__(kThreads)
-kda_pack_kernel(const KdaTask* __restrict__ tasks, const uint8_t* __restrict__ maps,
-                const int32_t* __restrict__ src_idx, const int32_t* __restrict__ dst_idx,
-                const uint8_t* __restrict__ src_base, int64_t src_stride, int64_t n_src,
-                uint8_t* __restrict__ dst_base, int64_t dst_stride, int64_t n_dst,
-                uint32_t* __restrict__ status, int dk_rt, int dv_rt) {
+template <bool kPack, int DK, int DV>
+__global__ void __launch_bounds__(kThreads) move_kernel(MoveArgs a) {
   extern __shared__ __attribute__((aligned(16))) float U[];
-  const int dk = DK ? DK : dk_rt;
-  const int dv = DV ? DV : dv_rt;
-  const KdaTask t = tasks[blockIdx.x];
-  const int64_t s = src_idx[blockIdx.y];
-  const int64_t d = dst_idx[blockIdx.y];
-  if (!in_range(s, n_src) || !in_range(d, n_dst)) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) flag(status, DASC_STATUS_BAD_INDEX);
+  const Piece t = a.pieces[blockIdx.x];
+  const int64_t s = a.src_idx[blockIdx.y];
+  const int64_t d = a.dst_idx[blockIdx.y];
+  const bool bad_idx = !in_range(s, a.n_src) || !in_range(d, a.n_dst);
+  if (bad_idx | (t.type > kPieceKda)) {
+    if (bad_idx && blockIdx.x == 0 && threadIdx.x == 0) flag(a.status, DASC_STATUS_BAD_INDEX);
     return;
   }
-  const int KG = dk / 4, VG = dv / 4, NB = KG * VG;
-  const int tid = threadIdx.x;
-  const uint8_t* rank_of = maps + static_cast<uint64_t>(t.map_idx) * kMapBytes + 128;
-  const float* S = reinterpret_cast<const float*>(src_base + s * src_stride + t.dense_off);
-  // Phase 1: read the whole head (strided columns force whole rows), keep
-  // the retained columns.
-#pragma unroll 4
-  for (int b = tid; b < NB; b += kThreads) {
-    const int kg = b % KG, vg = b / KG;
-    f32x4 x[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      x[i] = ld_stream(reinterpret_cast<const f32x4*>(S + (4 * vg + i) * dk + 4 * kg));
-    const uint32_t ranks = *reinterpret_cast<const uint32_t*>(rank_of + 4 * kg);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t rk = (ranks >> (8 * c)) & 0xFFu;
-      if (rk != kLocal) {
-        f32x4 col = {x[0][c], x[1][c], x[2][c], x[3][c]};
-        *reinterpret_cast<f32x4*>(&U[rk * dv + 4 * rot(vg, rk % VG, VG)]) = col;
-      }
-    }
-  }
-  __syncthreads();
-  // Phase 2: the r units, contiguous in the pool slot.
-  float* P = reinterpret_cast<float*>(dst_base + d * dst_stride + t.pool_off);
-  const int total = static_cast<int>(t.r) * VG;
-  for (int q = tid; q < total; q += kThreads) {
-    const int j = q / VG, g = q % VG;
-    const f32x4 val = *reinterpret_cast<const f32x4*>(&U[j * dv + 4 * rot(g, j % VG, VG)]);
-    st_stream(val, reinterpret_cast<f32x4*>(P + j * dv + 4 * g));
-  }
-}
-
-// unpack: contiguous pool units -> LDS -> every element of the dense head,
-// +0.0 in omitted channels
-template <int DK, int DV>
-__global__ void __launch_bounds__(kThreads)
-kda_unpack_kernel(const KdaTask* __restrict__ tasks, const uint8_t* __restrict__ maps,
-                  const int32_t* __restrict__ src_idx, const int32_t* __restrict__ dst_idx,
-                  const uint8_t* __restrict__ src_base, int64_t src_stride, int64_t n_src,
-                  uint8_t* __restrict__ dst_base, int64_t dst_stride, int64_t n_dst,
-                  uint32_t* __restrict__ status, int dk_rt, int dv_rt) {
-  extern __shared__ __attribute__((aligned(16))) float U[];
-  const int dk = DK ? DK : dk_rt;
-  const int dv = DV ? DV : dv_rt;
-  const KdaTask t = tasks[blockIdx.x];
-  const int64_t s = src_idx[blockIdx.y];
-  const int64_t d = dst_idx[blockIdx.y];
-  if (!in_range(s, n_src) || !in_range(d, n_dst)) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) flag(status, DASC_STATUS_BAD_INDEX);
-    return;
-  }
-  const int KG = dk / 4, VG = dv / 4, NB = KG * VG;
-  const int tid = threadIdx.x;
-  // Phase 1: the head's r stored units (contiguous) into LDS rows j < r.
-  const float* P = reinterpret_cast<const float*>(src_base + s * src_stride + t.pool_off);
-  const int total = static_cast<int>(t.r) * VG;
-  for (int q = tid; q < total; q += kThreads) {
-    const int j = q / VG, g = q % VG;
-    const f32x4 val = ld_stream(reinterpret_cast<const f32x4*>(P + j * dv + 4 * g));
-    *reinterpret_cast<f32x4*>(&U[j * dv + 4 * rot(g, j % VG, VG)]) = val;
-  }
-  __syncthreads();
-  // Phase 2: every element of the dense head; omitted channels get +0.0.
-  const uint8_t* rank_of = maps + static_cast<uint64_t>(t.map_idx) * kMapBytes + 128;
-  float* S = reinterpret_cast<float*>(dst_base + d * dst_stride + t.dense_off);
-#pragma unroll 4
-  for (int b = tid; b < NB; b += kThreads) {
-    const int kg = b % KG, vg = b / KG;
-    const uint32_t ranks = *reinterpret_cast<const uint32_t*>(rank_of + 4 * kg);
-    f32x4 col[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t rk = (ranks >> (8 * c)) & 0xFFu;
-      if (rk != kLocal) {
-        col[c] = *reinterpret_cast<const f32x4*>(&U[rk * dv + 4 * rot(vg, rk % VG, VG)]);
-      } else {
-        col[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f32x4 row = {col[0][i], col[1][i], col[2][i], col[3][i]};
-      st_stream(row, reinterpret_cast<f32x4*>(S + (4 * vg + i) * dk + 4 * kg));
-    }
-  }
+  const uint8_t* src = a.src_base + s * a.src_stride;
+  uint8_t* dst = a.dst_base + d * a.dst_stride;
+  if (t.type == kPieceKda)  // uniform per workgroup
+    kda_piece<kPack, DK, DV>(t, src, dst, U);
+  else
+    copy_piece<kPack>(t, src, dst);
 }
 
 // ---------------------------------------------------------------------------
@@ -560,56 +534,23 @@ refresh_kernel(RefreshArgs a) {
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
-int launch_copy(bool pack, const CopyTask* tasks, uint32_t n_tasks, const int32_t* src_idx,
-                const int32_t* dst_idx, const uint8_t* src_base, int64_t src_stride,
-                int64_t n_src, uint8_t* dst_base, int64_t dst_stride, int64_t n_dst,
-                int32_t n, uint32_t* status, void* stream) {
-  if (n_tasks == 0 || n == 0) return hipSuccess;
-  dim3 grid(n_tasks, static_cast<uint32_t>(n));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (pack)
-    copy_kernel<true><<<grid, kThreads, 0, s>>>(tasks, src_idx, dst_idx, src_base, src_stride,
-                                                n_src, dst_base, dst_stride, n_dst, status);
-  else
-    copy_kernel<false><<<grid, kThreads, 0, s>>>(tasks, src_idx, dst_idx, src_base, src_stride,
-                                                 n_src, dst_base, dst_stride, n_dst, status);
-  return static_cast<int>(hipGetLastError());
-}
-
 bool kda_shape_supported(int d_k, int d_v) {
   return d_k >= 4 && d_v >= 4 && d_k <= 128 && d_v <= 128 && d_k % 4 == 0 && d_v % 4 == 0;
 }
 
-int launch_kda(bool pack, int d_k, int d_v, int r_max, const KdaTask* tasks, uint32_t n_tasks,
-               const uint8_t* maps, const int32_t* src_idx, const int32_t* dst_idx,
-               const uint8_t* src_base, int64_t src_stride, int64_t n_src, uint8_t* dst_base,
-               int64_t dst_stride, int64_t n_dst, int32_t n, uint32_t* status, void* stream) {
-  if (n_tasks == 0 || n == 0) return hipSuccess;
-  if (!kda_shape_supported(d_k, d_v) || r_max < 1 || r_max > d_k)
+int launch_move(bool pack, const MoveArgs& args, void* stream) {
+  if (args.n == 0 || args.n_pieces == 0) return hipSuccess;
+  if (args.n_pieces > 0x7FFFFFFFu || args.kda_r_max < 0 || args.kda_r_max > 128)
     return static_cast<int>(hipErrorInvalidValue);
-  dim3 grid(n_tasks, static_cast<uint32_t>(n));
+  const size_t lds = static_cast<size_t>(args.kda_r_max) * kKdaLdsRow * sizeof(float);  // <= 18 KiB
+  dim3 grid(args.n_pieces, static_cast<uint32_t>(args.n));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t lds = static_cast<size_t>(r_max) * d_v * sizeof(float);  // <= 64 KiB
-  const bool fixed = d_k == 128 && d_v == 128;
   if (pack) {
-    if (fixed)
-      kda_pack_kernel<128, 128><<<grid, kThreads, lds, s>>>(tasks, maps, src_idx, dst_idx,
-                                                            src_base, src_stride, n_src, dst_base,
-                                                            dst_stride, n_dst, status, d_k, d_v);
-    else
-      kda_pack_kernel<0, 0><<<grid, kThreads, lds, s>>>(tasks, maps, src_idx, dst_idx, src_base,
-                                                        src_stride, n_src, dst_base, dst_stride,
-                                                        n_dst, status, d_k, d_v);
+    if (args.kda_128) move_kernel<true, 128, 128><<<grid, kThreads, lds, s>>>(args);
+    else move_kernel<true, 0, 0><<<grid, kThreads, lds, s>>>(args);
   } else {
-    if (fixed)
-      kda_unpack_kernel<128, 128><<<grid, kThreads, lds, s>>>(tasks, maps, src_idx, dst_idx,
-                                                              src_base, src_stride, n_src,
-                                                              dst_base, dst_stride, n_dst, status,
-                                                              d_k, d_v);
-    else
-      kda_unpack_kernel<0, 0><<<grid, kThreads, lds, s>>>(tasks, maps, src_idx, dst_idx,
-                                                          src_base, src_stride, n_src, dst_base,
-                                                          dst_stride, n_dst, status, d_k, d_v);
+    if (args.kda_128) move_kernel<false, 128, 128><<<grid, kThreads, lds, s>>>(args);
+    else move_kernel<false, 0, 0><<<grid, kThreads, lds, s>>>(args);
   }
   return static_cast<int>(hipGetLastError());
 }
