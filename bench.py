@@ -28,8 +28,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-FP32_VECTOR_PEAK_TF = 157.3    # MI355X fp32 vector (packed FMA), TFLOP/s
-FP32_UNPACKED_PEAK_TF = 78.6   # 256 CU x 64 lanes x 2 flop x 2.4 GHz without packed FMA
+FP32_MFMA_PEAK_TF = 157.3      # MI355X dense fp32 matrix (MFMA), TFLOP/s
+
+# Kernel sources whose hash a traffic summary under profiles/ records: the
+# counters it holds describe these exact kernels and piece lists.
+KERNEL_SOURCES = ["recurrent_state_cache_amd/csrc/dasc_kernels.hip",
+                  "recurrent_state_cache_amd/csrc/dasc_internal.h",
+                  "recurrent_state_cache_amd/csrc/dasc_host.cpp"]
+KERNEL_ROLES = {"move_kernel<true": "pack", "move_kernel<false": "unpack",
+                "refresh_kernel": "refresh"}
 
 
 def _args():
@@ -41,6 +48,14 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--summarize", nargs=5, metavar=("STATS", "FETCH", "WRITE", "FETCH_COPY",
+                                                     "WRITE_COPY"),
+                    help="print a markdown summary of rocprofv3 csv output directories "
+                         "(kernel stats; FETCH_SIZE and WRITE_SIZE of this bench and of "
+                         "--calibrate-copy) and exit")
+    ap.add_argument("--counters", nargs="+", metavar="DIR",
+                    help="print the mean per-dispatch value of every counter in these "
+                         "rocprofv3 csv output directories, per kernel of the library, and exit")
     return ap.parse_args()
 
 
@@ -131,6 +146,122 @@ def _cpu_baseline(cfg, P, dense_cpu, pack_bytes_per_ckpt, unpack_bytes_per_ckpt,
     }
 
 
+def _sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _role(kernel_name):
+    for key, role in KERNEL_ROLES.items():
+        if key in kernel_name:
+            return role
+    return None
+
+
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(directory, f"*{suffix}"))
+    if len(files) != 1:
+        raise SystemExit(f"expected one *{suffix} under {directory}, found {files}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _counter_means(directory, counter, match):
+    """Mean counter value (KiB) per dispatch of each kernel that `match` names."""
+    acc = {}
+    for r in _csv_rows(directory, "_counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        key = match(r["Kernel_Name"])
+        if key:
+            acc.setdefault(key, []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def _summarize(dirs, workload):
+    """Markdown summary of the rocprofv3 runs: kernel durations, and HBM
+    traffic per dispatch from FETCH_SIZE / WRITE_SIZE, each scaled by what the
+    same counter reads for a plain 1 GiB device copy."""
+    stats_d, fetch_d, write_d, fetch_c, write_c = dirs
+    stats = {}
+    for r in _csv_rows(stats_d, "_kernel_stats.csv"):
+        role = _role(r["Name"])
+        if role:
+            stats[role] = (int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]),
+                           float(r["MaxNs"]))
+    copy = lambda name: "copy" if "copyBuffer" in name or "copy_kernel" in name else None
+    cal_f = _counter_means(fetch_c, "FETCH_SIZE", copy).get("copy")
+    cal_w = _counter_means(write_c, "WRITE_SIZE", copy).get("copy")
+    if not cal_f or not cal_w:
+        raise SystemExit("no device-copy dispatch in the calibration runs")
+    kib = (1 << 30) / 1024.0
+    f_scale, w_scale = kib / cal_f, kib / cal_w
+    fetch = _counter_means(fetch_d, "FETCH_SIZE", _role)
+    write = _counter_means(write_d, "WRITE_SIZE", _role)
+    traffic = {k: int(round(fetch[k] * 1024 * f_scale + write[k] * 1024 * w_scale))
+               for k in fetch if k in write}
+    lines = [f"| kernel | calls | average (us) | min (us) | max (us) | FETCH_SIZE (KiB) | "
+             f"WRITE_SIZE (KiB) | HBM bytes per launch (calibrated) |",
+             "|---|---|---|---|---|---|---|---|"]
+    for role in ("pack", "unpack", "refresh"):
+        if role not in stats:
+            continue
+        c, avg, mn, mx = stats[role]
+        lines.append(f"| {role} | {c} | {avg / 1e3:.1f} | {mn / 1e3:.1f} | {mx / 1e3:.1f} | "
+                     f"{fetch.get(role, float('nan')):.0f} | {write.get(role, float('nan')):.0f} | "
+                     f"{traffic.get(role, 'n/a')} |")
+    out = "\n".join(lines)
+    out += (f"\n\nCalibration: a 1 GiB device copy reads FETCH_SIZE {cal_f:.1f} KiB and "
+            f"WRITE_SIZE {cal_w:.1f} KiB per dispatch, so FETCH_SIZE is scaled by "
+            f"{f_scale:.4f} and WRITE_SIZE by {w_scale:.4f}.\n\n")
+    out += "Machine-readable (bench.py reads these lines):\n\n"
+    out += f"    workload: {workload}\n"
+    out += f"    kernel_sources_sha256: {_sources_sha256()}\n"
+    out += f"    traffic_bytes: {json.dumps(traffic, sort_keys=True)}\n"
+    return out
+
+
+def _counter_table(dirs):
+    table = {}
+    for d in dirs:
+        for r in _csv_rows(d, "_counter_collection.csv"):
+            role = _role(r["Kernel_Name"])
+            if role:
+                table.setdefault(r["Counter_Name"], {}).setdefault(role, []).append(
+                    float(r["Counter_Value"]))
+    roles = ("pack", "unpack", "refresh")
+    lines = ["| counter | " + " | ".join(roles) + " |", "|---|---|---|---|"]
+    for c in sorted(table):
+        vals = [table[c].get(r) for r in roles]
+        lines.append(f"| {c} | " + " | ".join(f"{sum(v) / len(v):.4g}" if v else "" for v in vals)
+                     + " |")
+    return "\n".join(lines)
+
+
+def _recorded_traffic(workload):
+    """HBM bytes per launch recorded under profiles/ for this workload, or {}
+    when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return {}
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            for key in ("workload:", "kernel_sources_sha256:", "traffic_bytes:"):
+                if line.startswith(key):
+                    rec[key[:-1]] = line[len(key):].strip()
+    if rec.get("workload") != workload or rec.get("kernel_sources_sha256") != _sources_sha256():
+        return {}
+    return json.loads(rec.get("traffic_bytes", "{}"))
+
+
 def main():
     args = _args()
     if args.gpus != 1:
@@ -142,6 +273,12 @@ def main():
 
     if args.calibrate_copy:
         _calibrate_copy(args.steps)
+        return
+    if args.summarize:
+        print(_summarize(args.summarize, args.workload))
+        return
+    if args.counters:
+        print(_counter_table(args.counters))
         return
 
     import recurrent_state_cache_amd as R
@@ -201,16 +338,18 @@ def main():
     mover_gbs = (pack_total + unpack_total) * args.steps / (t_pack.sum() + t_unpack.sum()) / 1e9
     ref_tf = flops / t_ref.mean() / 1e12
 
-    def hbm(bytes_, secs):
+    traffic = _recorded_traffic(args.workload)
+
+    def hbm(role, bytes_, secs):
         a = bytes_ / secs / 1e9
         return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic.get(role),
+                "kernel": f"move_kernel<{'true' if role == 'pack' else 'false'}>",
                 "ms": round(secs * 1e3, 4), "bytes": int(bytes_)}
 
-    roof_ref = {"bound": "alu", "achieved": round(ref_tf, 3), "peak": FP32_VECTOR_PEAK_TF,
-                "unit": "TFLOP/s", "frac": round(ref_tf / FP32_VECTOR_PEAK_TF, 4),
-                "traffic": None, "kernel": "refresh_kernel<128>",
-                "frac_of_unpacked_fp32": round(ref_tf / FP32_UNPACKED_PEAK_TF, 4),
+    roof_ref = {"bound": "mfma", "achieved": round(ref_tf, 3), "peak": FP32_MFMA_PEAK_TF,
+                "unit": "TFLOP/s", "frac": round(ref_tf / FP32_MFMA_PEAK_TF, 4),
+                "traffic": traffic.get("refresh"), "kernel": "refresh_kernel<128>",
                 "ms": round(t_ref.mean() * 1e3, 4), "flops": int(flops)}
     line = {
         "metric": "checkpoint pack+unpack GB/s (% HBM peak); suffix-refresh tokens/s, 1 MI355X",
@@ -233,8 +372,8 @@ def main():
         "refresh_request_tokens_per_s": round(total_tokens / t_ref.mean(), 1),
         "plan_build_ms": round(plan_ms, 3),
         "roofline": roof_ref,
-        "roofline_pack": hbm(pack_total, t_pack.mean()),
-        "roofline_unpack": hbm(unpack_total, t_unpack.mean()),
+        "roofline_pack": hbm("pack", pack_total, t_pack.mean()),
+        "roofline_unpack": hbm("unpack", unpack_total, t_unpack.mean()),
     }
     if not args.no_cpu_baseline:
         m = min(8, n)
