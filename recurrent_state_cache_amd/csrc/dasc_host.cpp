@@ -14,6 +14,7 @@
 #include <limits>
 #include <new>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "../../include/dasc.h"
@@ -159,41 +160,46 @@ void build_tables(dasc_plan* p) {
   push_range(p->pack, I.temporal_dense_bytes, I.temporal_rag_bytes, I.conv_bytes, kPieceCopy);
   push_range(p->unpack, I.temporal_dense_bytes, I.temporal_rag_bytes, I.conv_bytes, kPieceCopy);
 
-  // Refresh tasks, grouped by head width.
-  std::vector<std::pair<int, int>> rshapes;
+  // Refresh tasks, grouped by head width and gate mode (one kernel each).
+  std::vector<std::tuple<int, int, int>> rkeys;  // (d_k, d_v, gate mode)
+  std::vector<std::vector<RefreshTask>> rtasks;
   for (const auto& L : p->layers) {
-    auto s = std::make_pair(L.d_k, L.d_v);
-    if (L.n_refresh && std::find(rshapes.begin(), rshapes.end(), s) == rshapes.end())
-      rshapes.push_back(s);
-  }
-  for (const auto& s : rshapes) {
-    Group g{s.first, s.second, static_cast<uint32_t>(p->refresh.size()), 0};
-    for (const auto& L : p->layers) {
-      if (L.d_k != s.first || L.d_v != s.second) continue;
-      const int64_t head_bytes = int64_t(L.d_v) * L.d_k * 4;
-      for (int h = 0; h < L.n_heads; ++h) {
-        RefreshTask t{};
-        bool any_local = false;
-        for (int k = 0; k < L.d_k && k < 128; ++k) {
-          bool local = L.kind == kGDN ? !L.retained[h] : !L.retained[h * L.d_k + k];
-          if (local) {
-            t.local[k >> 5] |= 1u << (k & 31);
-            any_local = true;
-          }
+    const int64_t head_bytes = int64_t(L.d_v) * L.d_k * 4;
+    for (int h = 0; h < L.n_heads; ++h) {
+      RefreshTask t{};
+      bool any_local = false;
+      for (int k = 0; k < L.d_k && k < 128; ++k) {
+        bool local = L.kind == kGDN ? !L.retained[h] : !L.retained[h * L.d_k + k];
+        if (local) {
+          t.local[k >> 5] |= 1u << (k & 31);
+          any_local = true;
         }
-        if (!any_local) continue;
-        t.dense_off = L.dense_off + h * head_bytes;
-        t.k_off = static_cast<uint32_t>(L.k_row_off + int64_t(h) * L.d_k);
-        t.v_off = static_cast<uint32_t>(L.v_row_off + int64_t(h) * L.d_v);
-        t.g_off = static_cast<uint32_t>(L.g_row_off + (L.kind == kKDA ? int64_t(h) * L.d_k : h));
-        t.b_off = static_cast<uint32_t>(L.b_row_off + h);
-        t.param_off = static_cast<uint32_t>(L.unit_base + (L.kind == kKDA ? int64_t(h) * L.d_k : h));
-        t.kind = static_cast<uint32_t>(L.kind);
-        p->refresh.push_back(t);
       }
+      if (!any_local) continue;
+      t.dense_off = L.dense_off + h * head_bytes;
+      t.k_off = static_cast<uint32_t>(L.k_row_off + int64_t(h) * L.d_k);
+      t.v_off = static_cast<uint32_t>(L.v_row_off + int64_t(h) * L.d_v);
+      t.g_off = static_cast<uint32_t>(L.g_row_off + (L.kind == kKDA ? int64_t(h) * L.d_k : h));
+      t.b_off = static_cast<uint32_t>(L.b_row_off + h);
+      t.param_off = static_cast<uint32_t>(L.unit_base + (L.kind == kKDA ? int64_t(h) * L.d_k : h));
+      t.kind = static_cast<uint32_t>(L.kind);
+      int gate = kGateHead;
+      if (L.kind == kKDA) gate = (t.g_off % 8 == 0 && p->g_row % 8 == 0) ? kGateChan : kGateChanSplit;
+      const auto key = std::make_tuple(L.d_k, L.d_v, gate);
+      auto it = std::find(rkeys.begin(), rkeys.end(), key);
+      if (it == rkeys.end()) {
+        rkeys.push_back(key);
+        rtasks.emplace_back();
+        it = rkeys.end() - 1;
+      }
+      rtasks[it - rkeys.begin()].push_back(t);
     }
-    g.count = static_cast<uint32_t>(p->refresh.size()) - g.first;
-    if (g.count) p->refresh_groups.push_back(g);
+  }
+  for (size_t i = 0; i < rkeys.size(); ++i) {
+    Group g{std::get<0>(rkeys[i]), std::get<1>(rkeys[i]), static_cast<uint32_t>(p->refresh.size()),
+            static_cast<uint32_t>(rtasks[i].size()), std::get<2>(rkeys[i])};
+    p->refresh.insert(p->refresh.end(), rtasks[i].begin(), rtasks[i].end());
+    p->refresh_groups.push_back(g);
   }
 
   // Gate parameters, per unit in plan order: exp(A_log) rounded once from
@@ -648,7 +654,7 @@ int dasc_ckpt_refresh_suffix(dasc_plan_t p, const uint16_t* k, const uint16_t* v
   for (const Group& g : p->refresh_groups) {
     args.tasks = p->dev.refresh + g.first;
     args.n_tasks = g.count;
-    int e = launch_refresh(g.d_k, args, stream);
+    int e = launch_refresh(g.d_k, g.gate, args, stream);
     if (e) return fail(DASC_EHIP, std::string(w) + ": launch failed: " +
                                       hipGetErrorString(static_cast<hipError_t>(e)));
   }

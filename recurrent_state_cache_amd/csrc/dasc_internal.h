@@ -70,10 +70,17 @@ struct DeviceTables {
   uint32_t* status;        // DASC_STATUS_* bits
 };
 
-// A run of refresh tasks that share one kernel instantiation (head width).
+// How a refresh task reads its gate logits `a`.
+constexpr int kGateHead = 0;       // one logit per head (GDN)
+constexpr int kGateChan = 1;       // one per channel, 16-byte aligned rows of 8 (KDA)
+constexpr int kGateChanSplit = 2;  // one per channel, read element by element (KDA)
+
+// A run of refresh tasks that share one kernel instantiation (head width and
+// gate mode).
 struct Group {
   int32_t d_k, d_v;
   uint32_t first, count;
+  int32_t gate;
 };
 
 // Arguments of one pack or unpack launch: grid x = the pieces, grid y = the
@@ -121,6 +128,6 @@ struct RefreshArgs {
   uint32_t* status;
 };
 
-int launch_refresh(int d, const RefreshArgs& args, void* stream);
+int launch_refresh(int d, int gate, const RefreshArgs& args, void* stream);
 
 }  // namespace dasc

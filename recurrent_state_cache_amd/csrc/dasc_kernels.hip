@@ -184,34 +184,42 @@ __global__ void __launch_bounds__(kThreads) move_kernel(MoveArgs a) {
 // Bounded-suffix refresh ([dasc] §4.2), one workgroup per (head, request).
 //
 // Eq. 1 ([dasc] §3.1) is replayed in chunks of 16 tokens.  Inside a chunk
-// that starts from S_0, with the running decay gamma_t = alpha_1 ... alpha_t
+// that starts from S_0, with the running decay gamma_t = alpha_0 ... alpha_t
 // and the pairwise decay D_{t,s} = alpha_{s+1} ... alpha_t (s < t), the
 // recurrence unrolls exactly to
 //   S_t = S_0 Diag(gamma_t) + sum_{s<=t} c_s (k_s o D_{t,s})^T,
-//   c_t = beta_t (v_t - S_0 (gamma_t o k_t)) - sum_{s<t} L_{t,s} c_s,
-//   L_{t,s} = beta_t sum_j k_t[j] k_s[j] D_{t,s}[j],
-// so a chunk is one product U0 = S_0 Q (Q = [gamma_t o k_t]), a 16 x 16
-// unit-lower-triangular solve for the c_t, and one rank-16 update
-// S_16 = S_0 Diag(gamma_16) + sum_s c_s w_s^T (w_s = k_s o D_{16,s}).  Every
-// factor is a product of decays, so nothing is divided (fast-decaying
-// channels cannot overflow).  Tokens past the end of a request pad the last
-// chunk as exact no-ops (alpha = 1, k = 0, v = 0, beta = 0).
+//   (I + L) c = R,  R_t = beta_t (v_t - S_0 (gamma_t o k_t)),
+//   L_{t,s} = beta_t sum_j k_t[j] k_s[j] D_{t,s}[j]   (s < t),
+// so a chunk is one product U0 = S_0 Q (Q = [gamma_t o k_t]), C = T R with
+// the 16 x 16 unit-lower-triangular inverse T = (I + L)^-1, and one rank-16
+// update S_16 = S_0 Diag(gamma_15) + sum_s c_s w_s^T (w_s = k_s o D_{15,s}).
+// Every factor is a product of decays, so nothing is divided (channels
+// whose decay underflows cannot overflow anything).  Tokens past the end of
+// a request pad the last chunk as exact no-ops (alpha = 1, k = v = 0,
+// beta = 0).
 //
-// The two products run on fp32 MFMA (v_mfma_f32_16x16x4f32).  The state is
+// The three products run on fp32 MFMA (v_mfma_f32_16x16x4f32).  The state is
 // kept transposed, S^T [k][v], in 16 x 16 accumulator tiles: lane (g, m)
 // (g = lane / 16, m = lane % 16) of tile (kt, vt) holds
-// S^T[16 kt + 4 g + r][16 vt + m], r = 0..3.  Those same registers are the B
-// operand of both products when lane group g stands for the k (or token)
-// index 4 g + r of the k-step r, so the state never moves:
-//   P1  U0^T[t][v] = sum_k Q[t][k] S^T[k][v]   (A = Q from LDS, B = S^T)
-//   P2  S^T[k][v] += sum_t W[k][t] C^T[t][v]   (A = W from LDS, B = C^T)
-// and P1's output U0^T (lane group g holds tokens 4 g .. 4 g + 3) is, after
-// the triangular solve, exactly the B operand C^T of P2.  Each wave owns all
-// k tiles of its v tiles, so P1 needs no cross-wave reduction.  The solve
-// walks the 4 lane groups in order, passing finished c's with lane shuffles.
-// Chunk inputs are staged through LDS: decay alpha = exp(-exp(A_log)
-// softplus(a_t + dt_bias)) ([dasc] §3.3 Eq. 2) once per (token, channel),
-// then gamma, Q, W, gamma_16 and L.
+// S^T[16 kt + 4 g + r][16 vt + m], r = 0..3.  With the K index of k-step r
+// read as 4 g + r on both operands, those same registers are the B operand
+// of the readout, and every product's output is the next one's B operand:
+//   U0^T[t][v] = sum_k Q[t][k] S^T[k][v]   (A = Q from LDS, B = S^T)
+//   C[t][v]    = sum_s T[t][s] R[s][v]     (A = T from LDS, B = R)
+//   S^T[k][v] += sum_t W[k][t] C[t][v]     (A = W from LDS, B = C)
+// so the state never moves.  Each wave owns all k tiles of its v tiles: no
+// product needs a cross-wave reduction.
+//
+// Software pipeline.  The chunk inputs (decays from the gate logits by
+// Eq. 2 ([dasc] §3.3), Q, W, gamma_15, L, T) do not depend on the state, so
+// chunk n + 1 is prepared while chunk n runs its products:
+//   phase 1: T(n) = (I + L(n))^-1; U0 = S Q(n)  ||  stage chunk n + 1
+//            (decays, k, v, beta into LDS); fetch chunk n + 2
+//   phase 2: R, C = T R; S <- S Diag(gamma) + W C  ||  L(n + 1), gamma,
+//            Q(n + 1), W(n + 1)
+// with one barrier after each phase.  Both phases are branch-free, and the
+// two workgroups a CU holds overlap each other's phases.  LDS buffers
+// that live across an iteration are double-buffered by chunk parity.
 // ---------------------------------------------------------------------------
 typedef float v4f __attribute__((ext_vector_type(4)));
 
@@ -224,24 +232,39 @@ struct RefreshShape {
   static constexpr int kNW = (D / 16) / kVTW;         // waves per head
   static constexpr int kNT = 64 * kNW;                // threads
   static constexpr int kJB = D / 8;                   // 8-channel blocks per token
+  static constexpr int kNB4 = D / 4;                  // lanes per row pair of L
   static_assert(2 * D <= kNT, "one staged item per lane");
 };
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
-  return __uint_as_float(static_cast<uint32_t>(h) << 16);
-}
+template <int D>
+struct alignas(16) RefreshLds {
+  float K[kC][D];             // k of the chunk being prepared
+  float A[kC][D];             // its decays
+  float V[2][kC][D];          // v, by chunk parity
+  float B[2][kC];             // beta, by chunk parity
+  float Q[kC][D + 4];         // gamma_t o k_t
+  float W[2][D][kC + 4];      // k_s o D_{15,s}, [k][s], by chunk parity
+  float G[2][2][D];           // gamma_15 by chunk parity ([.][1][.] is scratch)
+  float L[kC][kC + 4];        // beta_t M_{t,s}, s < t
+  float T[kC][kC + 4];        // (I + L)^-1
+  float sink[2 * D];          // target of the stores of lanes that hold no result
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // alpha = exp(-exp(A_log) softplus(x)) with x = a_t + dt_bias (Eq. 2);
 // expA = exp(A_log) is precomputed per unit.  softplus(x) = max(x, 0) +
 // log(1 + z) with z = exp(-|x|) in (0, 1]; u = 1 + z is rounded, and the
-// first-order term (z - (u - 1)) / u restores what the rounding lost, so
-// log(1 + z) keeps full relative precision for small z.  Hardware exp2 /
-// log2 / reciprocal, a few ulp overall.
+// term z - (u - 1) restores what the rounding lost (its 1/u factor is at
+// most a factor 2 away from 1 and the term itself is below 2^-24, so the
+// factor is dropped), so log(1 + z) keeps full relative precision for small
+// z.  Hardware exp2 / log2, a few ulp overall.
 __device__ __forceinline__ float decay(float x, float expA) {
   constexpr float kLog2e = 1.44269504088896341f, kLn2 = 0.693147180559945309f;
   const float z = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
   const float u = 1.f + z;
-  const float l1p = __builtin_amdgcn_logf(u) * kLn2 + (z - (u - 1.f)) * __builtin_amdgcn_rcpf(u);
+  const float l1p = __builtin_amdgcn_logf(u) * kLn2 + (z - (u - 1.f));
   const float sp = fmaxf(x, 0.f) + l1p;
   return __builtin_amdgcn_exp2f(-expA * sp * kLog2e);
 }
@@ -266,19 +289,14 @@ __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <int D>
+template <int D, int GATE>
 __global__ void __launch_bounds__(RefreshShape<D>::kNT) __attribute__((amdgpu_waves_per_eu(2)))
 refresh_kernel(RefreshArgs a) {
   using Sh = RefreshShape<D>;
-  constexpr int KT = Sh::kKT, VTW = Sh::kVTW, NT = Sh::kNT, JB = Sh::kJB;
-  __shared__ __attribute__((aligned(16))) float sK[kC][D];     // k (staging)
-  __shared__ __attribute__((aligned(16))) float sA[kC][D];     // alpha (staging)
-  __shared__ __attribute__((aligned(16))) float sQ[kC][D + 4]; // gamma_t o k_t
-  __shared__ __attribute__((aligned(16))) float sW[D][kC + 4]; // k_s o D_{16,s}, [k][s]
-  __shared__ __attribute__((aligned(16))) float sV[kC][D];     // v, [t][v]
-  __shared__ __attribute__((aligned(16))) float sL[kC][kC + 4];// beta_t M_{t,s}, s < t
-  __shared__ __attribute__((aligned(16))) float sG[D];         // gamma_16
-  __shared__ __attribute__((aligned(16))) float sB[kC];        // beta
+  constexpr int KT = Sh::kKT, VTW = Sh::kVTW, JB = Sh::kJB, NB4 = Sh::kNB4;
+  constexpr bool kChan = GATE != kGateHead;
+  constexpr bool kAllStage = Sh::kNT == 2 * D;  // every lane stages an item
+  __shared__ RefreshLds<D> sh;
 
   const RefreshTask task = a.tasks[blockIdx.x];
   const int req = blockIdx.y;
@@ -294,49 +312,155 @@ refresh_kernel(RefreshArgs a) {
     return;
   }
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = tid >> 6;  // wave w owns v tiles w VTW ..
   const int g = lane >> 4, m = lane & 15;
-  const bool kda = task.kind == static_cast<uint32_t>(kKDA);
 
-  // Staged item of this lane: token it_t, channels 8 it_jb .. 8 it_jb + 7.
-  const bool it_on = tid < 2 * D;
-  const int it_t = tid / JB, it_jb = tid % JB, j0 = 8 * it_jb;
+  // Staged item of this lane: token it_t of a chunk, channels j0 .. j0 + 7.
+  const bool it_on = kAllStage || tid < 2 * D;
+  const int it_t = (tid / JB) % kC, it_jb = tid % JB, j0 = 8 * it_jb;
   float expA[8], dtb[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    const uint32_t u = task.param_off + (kda ? j0 + c : 0);
-    expA[c] = it_on ? a.gate_expA[u] : 0.f;
-    dtb[c] = it_on ? a.gate_dt[u] : 0.f;
+    const uint32_t u = task.param_off + (kChan ? j0 + c : 0);
+    expA[c] = a.gate_expA[u];
+    dtb[c] = a.gate_dt[u];
   }
-  const bool a_vec = kda && ((task.g_off | a.g_row) % 8 == 0);
 
-  u32x4 rk = {0u, 0u, 0u, 0u}, rv = rk, ra = rk;  // 8 bf16 each, packed
-  float rb = 0.f;
-  bool r_real = false;
+  // Inputs of one token for this lane (8 bf16 of k, v and the gate logits,
+  // packed, and beta), fetched one chunk ahead of their staging.  The row is
+  // clamped into the request, so every load is in bounds; past the end the
+  // values are replaced by the no-op token when staged.
+  u32x4 rk, rv, ra;
+  float rb;
+  bool r_real;
   auto fetch = [&](int64_t n) {
     const int64_t tok = t0 + n * kC + it_t;
-    r_real = it_on && tok < t1;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    rk = rv = ra = z;
-    rb = 0.f;
-    if (r_real) {
-      rk = *reinterpret_cast<const u32x4*>(a.k + tok * a.k_row + task.k_off + j0);
-      rv = *reinterpret_cast<const u32x4*>(a.v + tok * a.v_row + task.v_off + j0);
-      const uint16_t* ap = a.a + tok * a.g_row + task.g_off;
-      if (a_vec) {
-        ra = *reinterpret_cast<const u32x4*>(ap + j0);
-      } else if (kda) {
+    r_real = tok < t1;
+    const int64_t tc = r_real ? tok : t1 - 1;
+    rk = *reinterpret_cast<const u32x4*>(a.k + tc * a.k_row + task.k_off + j0);
+    rv = *reinterpret_cast<const u32x4*>(a.v + tc * a.v_row + task.v_off + j0);
+    const uint16_t* ap = a.a + tc * a.g_row + task.g_off;
+    if constexpr (GATE == kGateChan) {
+      ra = *reinterpret_cast<const u32x4*>(ap + j0);
+    } else if constexpr (GATE == kGateChanSplit) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          ra[q] = static_cast<uint32_t>(ap[j0 + 2 * q]) | (static_cast<uint32_t>(ap[j0 + 2 * q + 1]) << 16);
-      } else {
-        ra[0] = ap[0];
+      for (int q = 0; q < 4; ++q)
+        ra[q] = static_cast<uint32_t>(ap[j0 + 2 * q]) |
+                (static_cast<uint32_t>(ap[j0 + 2 * q + 1]) << 16);
+    } else {
+      ra = u32x4{static_cast<uint32_t>(ap[0]), 0u, 0u, 0u};
+    }
+    rb = a.beta[tc * a.b_row + task.b_off];
+  };
+
+  // Stage the fetched token into LDS buffer vb: decays (Eq. 2), k, v, beta.
+  // A token past the end becomes the no-op token: k = v = 0 words, beta = 0,
+  // and a zero gate scale, which makes the decay exp2(-0) = 1 exactly.  (The
+  // padding is applied to inputs, not by selecting results, so the code has
+  // no branch.)
+  auto stage1 = [&](int vb) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const u32x4 wk = r_real ? rk : zero, wv = r_real ? rv : zero;
+    float kf[8], vf[8], al[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      kf[2 * q] = bf16_lo(wk[q]);
+      kf[2 * q + 1] = bf16_hi(wk[q]);
+      vf[2 * q] = bf16_lo(wv[q]);
+      vf[2 * q + 1] = bf16_hi(wv[q]);
+    }
+    if constexpr (kChan) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        al[2 * q] = decay(bf16_lo(ra[q]) + dtb[2 * q], r_real ? expA[2 * q] : 0.f);
+        al[2 * q + 1] = decay(bf16_hi(ra[q]) + dtb[2 * q + 1], r_real ? expA[2 * q + 1] : 0.f);
       }
-      if (it_jb == 0) rb = a.beta[tok * a.b_row + task.b_off];
+    } else {
+      const float x = decay(bf16_lo(ra[0]) + dtb[0], r_real ? expA[0] : 0.f);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) al[c] = x;
+    }
+    const float bv = r_real ? rb : 0.f;
+    if (it_on) {
+      *reinterpret_cast<v4f*>(&sh.A[it_t][j0]) = v4f{al[0], al[1], al[2], al[3]};
+      *reinterpret_cast<v4f*>(&sh.A[it_t][j0 + 4]) = v4f{al[4], al[5], al[6], al[7]};
+      *reinterpret_cast<v4f*>(&sh.K[it_t][j0]) = v4f{kf[0], kf[1], kf[2], kf[3]};
+      *reinterpret_cast<v4f*>(&sh.K[it_t][j0 + 4]) = v4f{kf[4], kf[5], kf[6], kf[7]};
+      *reinterpret_cast<v4f*>(&sh.V[vb][it_t][j0]) = v4f{vf[0], vf[1], vf[2], vf[3]};
+      *reinterpret_cast<v4f*>(&sh.V[vb][it_t][j0 + 4]) = v4f{vf[4], vf[5], vf[6], vf[7]};
+      sh.B[vb][it_t] = bv;  // the JB lanes of a token store the same value
     }
   };
-  auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
-  auto hi = [](uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); };
+
+  // From the staged chunk: L (into sh.L), Q (sh.Q), W and gamma_15 (buffer vb).
+  auto stage2 = [&](int vb) {
+    if (kAllStage || tid < 2 * D) {
+      // L, rows p and 15 - p (15 entries in all), 4 channels per lane,
+      // summed over the NB4 lanes of the row pair.  The lane with
+      // tid % NB4 == 0 stores each entry; the others store to sink.
+      const int p = tid / NB4, c4 = 4 * (tid % NB4);
+      const v4f kp = *reinterpret_cast<const v4f*>(&sh.K[p][c4]);
+      const v4f kq = *reinterpret_cast<const v4f*>(&sh.K[kC - 1 - p][c4]);
+      const float bp = sh.B[vb][p], bq = sh.B[vb][kC - 1 - p];
+      float* const sink = &sh.sink[tid];
+      v4f pk = kp;
+#pragma unroll
+      for (int i = 0; i < kC - 1; ++i) {
+        const bool first = i < p;
+        const int t = first ? p : kC - 1 - p;
+        const int s = first ? p - 1 - i : kC - 2 - i;
+        if (i == 0) pk = first ? kp : kq;
+        else pk = i == p ? kq : pk;
+        const v4f al = *reinterpret_cast<const v4f*>(&sh.A[s + 1][c4]);
+        const v4f ks = *reinterpret_cast<const v4f*>(&sh.K[s][c4]);
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pk[e] *= al[e];
+          part = fmaf(pk[e], ks[e], part);
+        }
+        part = group_sum<(NB4 < 16 ? NB4 : 16)>(part);
+        if constexpr (NB4 == 32) part += __shfl_xor(part, 16, 64);
+        float* const at = tid % NB4 == 0 ? &sh.L[t][s] : sink;
+        *at = (first ? bp : bq) * part;
+      }
+      // gamma_t and Q (forward lanes, tid < D) or W (backward lanes)
+      const int j = tid % D;
+      const bool fwd = tid < D;
+      float gm = 1.f;
+#pragma unroll
+      for (int i = 0; i < kC; ++i) {
+        const int t = fwd ? i : kC - 1 - i;
+        const float al = sh.A[t][j], kv = sh.K[t][j];
+        const float before = gm * kv;  // backward: k_s o D_{15,s}
+        gm *= al;
+        const float after = gm * kv;   // forward: gamma_t o k_t
+        float* const at = fwd ? &sh.Q[t][j] : &sh.W[vb][j][t];
+        *at = fwd ? after : before;
+      }
+      sh.G[vb][fwd ? 0 : 1][j] = gm;
+    }
+  };
+
+  // T = (I + L)^-1 by columns: lane s = lane % 16 owns column s,
+  // T[t][s] = delta_{ts} - sum_{u<t} L[t][u] T[u][s].  For t <= s the sum
+  // only meets T[u][s] = 0 (u < s), so one formula serves every row and the
+  // code has no branch.  Every wave computes it (the four lane groups of a
+  // wave hold the same column), so the stores write identical values.
+  auto invert = [&]() {
+    const int sc = lane & 15;
+    float tc[kC];
+    tc[0] = sc == 0 ? 1.f : 0.f;
+#pragma unroll
+    for (int t = 1; t < kC; ++t) {
+      float acc = 0.f;
+#pragma unroll
+      for (int u = 0; u < t; ++u) acc = fmaf(sh.L[t][u], tc[u], acc);
+      tc[t] = (t == sc ? 1.f : 0.f) - acc;
+    }
+#pragma unroll
+    for (int t = 0; t < kC; ++t) sh.T[t][sc] = tc[t];
+  };
 
   v4f acc[KT][VTW];
 #pragma unroll
@@ -346,162 +470,64 @@ refresh_kernel(RefreshArgs a) {
 
   const int64_t W = t1 - t0;
   const int64_t nchunks = (W + kC - 1) / kC;
-  if (nchunks > 0) fetch(0);
-  for (int64_t n = 0; n < nchunks; ++n) {
-    // ---- stage 1: decay, k, v, beta of this chunk into LDS
-    if (it_on) {
-      float al[8], kf[8], vf[8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        kf[2 * q] = lo(rk[q]);
-        kf[2 * q + 1] = hi(rk[q]);
-        vf[2 * q] = lo(rv[q]);
-        vf[2 * q + 1] = hi(rv[q]);
-      }
-      if (!r_real) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) al[c] = 1.f;
-      } else if (kda) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          al[2 * q] = decay(lo(ra[q]) + dtb[2 * q], expA[2 * q]);
-          al[2 * q + 1] = decay(hi(ra[q]) + dtb[2 * q + 1], expA[2 * q + 1]);
-        }
-      } else {
-        const float x = decay(lo(ra[0]) + dtb[0], expA[0]);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) al[c] = x;
-      }
-      *reinterpret_cast<v4f*>(&sA[it_t][j0]) = v4f{al[0], al[1], al[2], al[3]};
-      *reinterpret_cast<v4f*>(&sA[it_t][j0 + 4]) = v4f{al[4], al[5], al[6], al[7]};
-      *reinterpret_cast<v4f*>(&sK[it_t][j0]) = v4f{kf[0], kf[1], kf[2], kf[3]};
-      *reinterpret_cast<v4f*>(&sK[it_t][j0 + 4]) = v4f{kf[4], kf[5], kf[6], kf[7]};
-      *reinterpret_cast<v4f*>(&sV[it_t][j0]) = v4f{vf[0], vf[1], vf[2], vf[3]};
-      *reinterpret_cast<v4f*>(&sV[it_t][j0 + 4]) = v4f{vf[4], vf[5], vf[6], vf[7]};
-      if (it_jb == 0) sB[it_t] = rb;
-    }
-    if (n + 1 < nchunks) fetch(n + 1);
+  if (nchunks > 0) {
+    fetch(0);
+    stage1(0);
+    fetch(1);
     __syncthreads();
-    // ---- stage 2: L (pairs of rows p, 15 - p over 4-channel blocks), then
-    //      gamma / Q (forward) and W (backward) per channel
-    if (tid < 2 * D) {
-      // rows p and 15 - p (15 pairs in all), 4 channels per lane, summed over
-      // the D/4 lanes of the row pair right away
-      constexpr int NB4 = D / 4;
-      const int p = tid / NB4, c4 = 4 * (tid % NB4);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int t = h == 0 ? p : kC - 1 - p;
-        v4f pk = *reinterpret_cast<const v4f*>(&sK[t][c4]);
-        for (int s = t - 1; s >= 0; --s) {
-          const v4f al = *reinterpret_cast<const v4f*>(&sA[s + 1][c4]);
-          const v4f ks = *reinterpret_cast<const v4f*>(&sK[s][c4]);
-          float part = 0.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pk[e] *= al[e];
-            part = fmaf(pk[e], ks[e], part);
-          }
-          part = group_sum<(NB4 < 16 ? NB4 : 16)>(part);
-          if constexpr (NB4 == 32) part += __shfl_xor(part, 16, 64);
-          if (tid % NB4 == 0) sL[t][s] = sB[t] * part;
-        }
-      }
-      // per-channel decays: tid < D forward, D <= tid < 2D backward
-      const int j = tid % D;
-      if (tid < D) {
-        float gam = 1.f;
-#pragma unroll
-        for (int t = 0; t < kC; ++t) {
-          gam *= sA[t][j];
-          sQ[t][j] = gam * sK[t][j];
-        }
-        sG[j] = gam;
-      } else {
-        float dd = 1.f;
-#pragma unroll
-        for (int s = kC - 1; s >= 0; --s) {
-          sW[j][s] = sK[s][j] * dd;
-          dd *= sA[s][j];
-        }
-      }
-    }
+    stage2(0);
     __syncthreads();
-    // ---- compute: P1, solve, fold, P2
-    {
+    for (int64_t n = 0; n < nchunks; ++n) {
+      const int cb = static_cast<int>(n & 1), nb = cb ^ 1;
+      // ---- phase 1: T(n), U0 = S Q(n)  ||  stage chunk n + 1, fetch n + 2
+      invert();
       v4f U[VTW];
 #pragma unroll
       for (int vv = 0; vv < VTW; ++vv) U[vv] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
-        const v4f qa = *reinterpret_cast<const v4f*>(&sQ[m][16 * kt + 4 * g]);
+        const v4f qa = *reinterpret_cast<const v4f*>(&sh.Q[m][16 * kt + 4 * g]);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
           for (int vv = 0; vv < VTW; ++vv) U[vv] = mfma4(qa[r], acc[kt][vv][r], U[vv]);
       }
-      const v4f b4 = *reinterpret_cast<const v4f*>(&sB[4 * g]);
-      v4f Cc[VTW];
-#pragma unroll
-      for (int vv = 0; vv < VTW; ++vv) {
-        const int v = 16 * (wave * VTW + vv) + m;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) U[vv][r] = b4[r] * (sV[4 * g + r][v] - U[vv][r]);  // R_t
-      }
-      // forward substitution over the lane groups: c_t = R_t - sum_{s<t} L_{t,s} c_s
-#pragma unroll
-      for (int pgrp = 0; pgrp < 4; ++pgrp) {
-        if (g == pgrp) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const v4f Lr = *reinterpret_cast<const v4f*>(&sL[4 * g + r][4 * g]);
-#pragma unroll
-            for (int vv = 0; vv < VTW; ++vv) {
-              float x = U[vv][r];
-#pragma unroll
-              for (int q = 0; q < r; ++q) x = fmaf(-Lr[q], Cc[vv][q], x);
-              Cc[vv][r] = x;
-            }
-          }
-        }
-        if (pgrp < 3) {
-          v4f cp[VTW];
-#pragma unroll
-          for (int vv = 0; vv < VTW; ++vv)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) cp[vv][q] = __shfl(Cc[vv][q], m + 16 * pgrp, 64);
-          if (g > pgrp) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const v4f Lr = *reinterpret_cast<const v4f*>(&sL[4 * g + r][4 * pgrp]);
-#pragma unroll
-              for (int vv = 0; vv < VTW; ++vv) {
-                float x = U[vv][r];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) x = fmaf(-Lr[q], cp[vv][q], x);
-                U[vv][r] = x;
-              }
-            }
-          }
-        }
-      }
-      // S^T <- Diag(gamma_16) S^T, then S^T += W C^T
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const v4f g4 = *reinterpret_cast<const v4f*>(&sG[16 * kt + 4 * g]);
-        const v4f wa = *reinterpret_cast<const v4f*>(&sW[16 * kt + m][4 * g]);
+      stage1(nb);
+      fetch(n + 2);
+      __syncthreads();
+      // ---- phase 2: R, C = T R, S <- S Diag(gamma) + W C  ||  L, Q, W of n + 1
+      {
+        const v4f b4 = *reinterpret_cast<const v4f*>(&sh.B[cb][4 * g]);
+        const v4f ta = *reinterpret_cast<const v4f*>(&sh.T[m][4 * g]);
+        v4f Cc[VTW];
 #pragma unroll
         for (int vv = 0; vv < VTW; ++vv) {
-          v4f x = acc[kt][vv];
+          const int v = 16 * (wave * VTW + vv) + m;
+          v4f R;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) x[r] *= g4[r];
+          for (int r = 0; r < 4; ++r) R[r] = b4[r] * (sh.V[cb][4 * g + r][v] - U[vv][r]);
+          Cc[vv] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) x = mfma4(wa[r], Cc[vv][r], x);
-          acc[kt][vv] = x;
+          for (int r = 0; r < 4; ++r) Cc[vv] = mfma4(ta[r], R[r], Cc[vv]);
+        }
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          const v4f g4 = *reinterpret_cast<const v4f*>(&sh.G[cb][0][16 * kt + 4 * g]);
+          const v4f wa = *reinterpret_cast<const v4f*>(&sh.W[cb][16 * kt + m][4 * g]);
+#pragma unroll
+          for (int vv = 0; vv < VTW; ++vv) {
+            v4f x = acc[kt][vv];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[r] *= g4[r];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x = mfma4(wa[r], Cc[vv][r], x);
+            acc[kt][vv] = x;
+          }
         }
       }
+      stage2(nb);
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   // Write back the local units only ([dasc] §4.2).  Lane (g, m) of tile
@@ -559,27 +585,35 @@ bool refresh_shape_supported(int d_k, int d_v) {
   return d_k == d_v && (d_k == 16 || d_k == 32 || d_k == 64 || d_k == 128);
 }
 
-int launch_refresh(int d, const RefreshArgs& args, void* stream) {
-  if (args.n_tasks == 0 || args.n == 0) return hipSuccess;
-  dim3 grid(args.n_tasks, static_cast<uint32_t>(args.n));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  switch (d) {
-    case 16:
-      refresh_kernel<16><<<grid, RefreshShape<16>::kNT, 0, s>>>(args);
+template <int D>
+int launch_refresh_d(int gate, const RefreshArgs& args, dim3 grid, hipStream_t s) {
+  switch (gate) {
+    case kGateHead:
+      refresh_kernel<D, kGateHead><<<grid, RefreshShape<D>::kNT, 0, s>>>(args);
       break;
-    case 32:
-      refresh_kernel<32><<<grid, RefreshShape<32>::kNT, 0, s>>>(args);
+    case kGateChan:
+      refresh_kernel<D, kGateChan><<<grid, RefreshShape<D>::kNT, 0, s>>>(args);
       break;
-    case 64:
-      refresh_kernel<64><<<grid, RefreshShape<64>::kNT, 0, s>>>(args);
-      break;
-    case 128:
-      refresh_kernel<128><<<grid, RefreshShape<128>::kNT, 0, s>>>(args);
+    case kGateChanSplit:
+      refresh_kernel<D, kGateChanSplit><<<grid, RefreshShape<D>::kNT, 0, s>>>(args);
       break;
     default:
       return static_cast<int>(hipErrorInvalidValue);
   }
   return static_cast<int>(hipGetLastError());
+}
+
+int launch_refresh(int d, int gate, const RefreshArgs& args, void* stream) {
+  if (args.n_tasks == 0 || args.n == 0) return hipSuccess;
+  dim3 grid(args.n_tasks, static_cast<uint32_t>(args.n));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (d) {
+    case 16: return launch_refresh_d<16>(gate, args, grid, s);
+    case 32: return launch_refresh_d<32>(gate, args, grid, s);
+    case 64: return launch_refresh_d<64>(gate, args, grid, s);
+    case 128: return launch_refresh_d<128>(gate, args, grid, s);
+    default: return static_cast<int>(hipErrorInvalidValue);
+  }
 }
 
 }  // namespace dasc
