@@ -111,6 +111,45 @@ def test_refresh_mixed_sampled():
                     label="mixed")
 
 
+def _odd_refresh_layers(seed):
+    """Every refresh width (16, 32, 64, 128) as GDN and KDA layers.  The
+    GDN layers' one-per-head gate logits shift the KDA layers' gate blocks:
+    the d = 32 and d = 128 KDA layers start on a 16-byte boundary (vector
+    gate reads), the d = 64 and d = 16 ones do not (element reads)."""
+    rng = np.random.default_rng(seed)
+    f = np.float32
+
+    def lay(kind, H, d):
+        n = H * d if kind == W.KDA else H
+        A = rng.uniform(-1, 2, n) if kind == W.GDN else rng.normal(0, 1.5, n)
+        return W.Layer(kind, H, d, d, A.astype(f), rng.normal(0, 1, n).astype(f), 0)
+
+    return [lay(W.KDA, 2, 32), lay(W.GDN, 3, 32), lay(W.KDA, 2, 64), lay(W.GDN, 2, 64),
+            lay(W.KDA, 1, 16), lay(W.GDN, 3, 16), lay(W.KDA, 2, 128), lay(W.GDN, 8, 16)]
+
+
+def test_refresh_every_width_and_unaligned_gate_rows():
+    cfg = W.Config("widths", _odd_refresh_layers(21), w_max=8, n_req=3, seed=21)
+    P, O = _plans(cfg)
+    assert P.info()["gate_row"] % 8 == 0
+    kda_offsets = [P.layer(l)["gate_row_offset"] for l in range(len(cfg.layers))
+                   if cfg.layers[l].kind == W.KDA]
+    assert [o % 8 == 0 for o in kda_offsets] == [True, False, False, True], kda_offsets
+    for li in range(len(cfg.layers)):
+        assert len(O.refreshed_heads(li)) > 0, f"layer {li} replays no head"
+    Wn = np.array([5, 16, 37])
+    log(f"[refresh] widths 16..128, GDN and KDA, gate offsets {kda_offsets}, windows {list(Wn)}")
+    inp = W.refresh_inputs(cfg, Wn, device="cuda")
+    dense = W.dense_states(cfg, 4, device="cuda", seed=8)
+    before = dense.clone()
+    dst = torch.tensor([3, 0, 2], dtype=torch.int32, device="cuda")
+    R.ckpt_refresh_suffix(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, dense, dst)
+    torch.cuda.synchronize()
+    assert P.status() == 0
+    assert torch.equal(dense[1], before[1])                 # not a destination
+    _check_requests(P, O, inp, before, dense, dst.cpu().numpy(), [0, 1, 2], label="widths")
+
+
 def test_zero_window_writes_zero_locals_and_bad_ranges_are_flagged():
     cfg = W.tiny_kda()
     P, O = _plans(cfg)
