@@ -6,8 +6,9 @@ binding) never imports, calls or links it, and it imports nothing from the
 product path: the two share no code.
 
 Everything here is plain and slow on purpose: NumPy in float64 for floating
-point, raw bit copies (uint32 / uint16 views) for data movement, one step of
-each definition per line so that it can be checked against the pages by eye.
+point (float32 where the page fixes it: Eq. 10's INT8 quantization), raw bit
+copies (uint32 / uint16 views) for data movement, one step of each
+definition per line so that it can be checked against the pages by eye.
 
 Pages cited (by title, section / equation / table):
 
@@ -31,6 +32,8 @@ closed forms, invariants, printed numbers and brute force (see the
 from .plan import (GDN, KDA, OraclePlan, build_plan, gate_log_decay, horizon,
                    next_pow2, replay_window, slots_eq8, softplus)
 from .ckpt import pack, unpack_zero_fill
+from .int8 import (Int8Layout, dequantize_columns, pack_int8, quantize_columns,
+                   unpack_int8_zero_fill)
 from .refresh import (bf16_bits_to_f64, delta_rule_step, refresh_expected,
                       replay_dense, replay_rank1)
 
@@ -38,5 +41,6 @@ __all__ = [
     "GDN", "KDA", "OraclePlan", "build_plan", "gate_log_decay", "horizon",
     "next_pow2", "replay_window", "slots_eq8", "softplus", "pack",
     "unpack_zero_fill", "bf16_bits_to_f64", "delta_rule_step",
-    "refresh_expected", "replay_dense", "replay_rank1",
+    "refresh_expected", "replay_dense", "replay_rank1", "Int8Layout",
+    "quantize_columns", "dequantize_columns", "pack_int8", "unpack_int8_zero_fill",
 ]

@@ -14,9 +14,11 @@ import pytest
 
 import oracle
 import oracle.ckpt
+import oracle.int8
 import oracle.plan
 import oracle.refresh
 import test_oracle_ckpt as T_ckpt
+import test_oracle_int8 as T_int8
 import test_oracle_plan as T_plan
 import test_oracle_refresh as T_ref
 
@@ -42,7 +44,7 @@ def _swap(monkeypatch, modname, mod):
     real = getattr(oracle, modname)
     for name, obj in vars(mod).items():
         if callable(obj) and getattr(real, name, None) is not None and not name.startswith("__"):
-            for holder in (oracle, oracle.plan, oracle.ckpt, oracle.refresh):
+            for holder in (oracle, oracle.plan, oracle.ckpt, oracle.refresh, oracle.int8):
                 if getattr(holder, name, None) is getattr(real, name):
                     monkeypatch.setattr(holder, name, obj)
 
@@ -73,6 +75,14 @@ REFRESH_PINS = [T_ref.test_rank1_matches_printed_matrix_form, T_ref.test_beta_on
                 lambda: T_ref.test_refresh_expected_wiring_gate_and_rows(8, 4),
                 T_ref.test_refresh_expected_respects_windows, T_ref.test_gdn_scalar_decay_equals_broadcast]
 
+INT8_PINS = [T_int8.test_pages_8p11_capacity_and_3p88_quantization_only,
+             T_int8.test_scale_is_column_max_over_127_and_rounding_is_half_even,
+             T_int8.test_zero_and_tiny_columns_use_the_floor,
+             T_int8.test_scales_are_per_key_column_over_values,
+             T_int8.test_range_and_error_bound_on_random_columns,
+             T_int8.test_non_finite_entries_quantize_to_zero,
+             T_int8.test_pack_unpack_int8_round_trip]
+
 MUTATIONS = [
     # plan
     ("plan", "np.exp(A_log) * softplus(a + dt_bias)", "np.exp(A_log) * softplus(a - dt_bias)", PLAN_PINS),
@@ -98,6 +108,15 @@ MUTATIONS = [
     ("refresh", "al = np.exp(gate_log_decay(Al, Db, a))", "al = np.exp(-gate_log_decay(Al, Db, a))", REFRESH_PINS),
     ("refresh", "g += lay.n_heads * lay.d_k if lay.kind != GDN else lay.n_heads", "g += lay.n_heads * lay.d_k", REFRESH_PINS),
     ("refresh", "vs = bf16_bits_to_f64(v_bits[t0:t1, vo[li]", "vs = bf16_bits_to_f64(v_bits[t0:t1, ko[li]", REFRESH_PINS),
+    # INT8 (Eq. 10)
+    ("int8", "s = np.fmax(a, SCALE_FLOOR) / QMAX", "s = np.fmax(a, SCALE_FLOOR) / F32(128.0)", INT8_PINS),
+    ("int8", "s = np.fmax(a, SCALE_FLOOR) / QMAX", "s = a / QMAX", INT8_PINS),
+    ("int8", "r = np.rint(X / s[None, :])", "r = np.floor(X / s[None, :] + F32(0.5))", INT8_PINS),
+    ("int8", "a = np.fmax.reduce(np.abs(X), axis=0)", "a = np.full(X.shape[1], np.abs(X).max(), F32)", INT8_PINS),
+    ("int8", "per_unit_s = lay.d_k if lay.kind == GDN else 1", "per_unit_s = 1", INT8_PINS),
+    ("int8", "per_unit_q = lay.d_v * lay.d_k if lay.kind == GDN else lay.d_v", "per_unit_q = lay.d_v * lay.d_k", INT8_PINS),
+    ("int8", "self.scale_base = align16(q)", "self.scale_base = q", INT8_PINS),
+    ("int8", "s = src[so + j * 4:so + (j + 1) * 4].view(F32)", "s = src[so:so + 4].view(F32)", INT8_PINS),
 ]
 
 
