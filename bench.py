@@ -13,7 +13,9 @@ omitted heads) and "mixed" (27 alternating layers, 512 checkpoints, 64
 requests with windows U{64..1024}).
 
 Prints ONE JSON line.  value = pack+unpack GB/s (algorithmic bytes / time);
-refresh request-tokens/s and the per-kernel rooflines ride along.
+refresh request-tokens/s and the per-kernel rooflines ride along, and an
+"int8" object times INT8 checkpoint pack and unpack (Eq. 10) of the same
+checkpoints on their own, after the timed steps.
 """
 from __future__ import annotations
 
@@ -35,7 +37,8 @@ FP32_MFMA_PEAK_TF = 157.3      # MI355X dense fp32 matrix (MFMA), TFLOP/s
 KERNEL_SOURCES = ["recurrent_state_cache_amd/csrc/dasc_kernels.hip",
                   "recurrent_state_cache_amd/csrc/dasc_internal.h",
                   "recurrent_state_cache_amd/csrc/dasc_host.cpp"]
-KERNEL_ROLES = {"move_kernel<true": "pack", "move_kernel<false": "unpack",
+KERNEL_ROLES = {"qmove_kernel<true": "pack_int8", "qmove_kernel<false": "unpack_int8",
+                "move_kernel<true": "pack", "move_kernel<false": "unpack",
                 "refresh_kernel": "refresh"}
 
 
@@ -92,7 +95,10 @@ def _algorithmic_bytes(P):
             read_pack += int(per_head.sum()) * L["d_v"] * L["d_k"] * 4
     pack = read_pack + info["temporal_rag_bytes"] + 2 * info["conv_bytes"]
     unpack = info["temporal_rag_bytes"] + info["temporal_dense_bytes"] + 2 * info["conv_bytes"]
-    return pack, unpack
+    q = info["int8_payload_bytes"] + info["int8_scale_bytes"]
+    pack_q = read_pack + q + 2 * info["conv_bytes"]
+    unpack_q = q + info["temporal_dense_bytes"] + 2 * info["conv_bytes"]
+    return pack, unpack, pack_q, unpack_q
 
 
 def _calibrate_copy(steps):
@@ -209,7 +215,7 @@ def _summarize(dirs, workload):
     lines = [f"| kernel | calls | average (us) | min (us) | max (us) | FETCH_SIZE (KiB) | "
              f"WRITE_SIZE (KiB) | HBM bytes per launch (calibrated) |",
              "|---|---|---|---|---|---|---|---|"]
-    for role in ("pack", "unpack", "refresh"):
+    for role in ("pack", "unpack", "refresh", "pack_int8", "unpack_int8"):
         if role not in stats:
             continue
         c, avg, mn, mx = stats[role]
@@ -235,8 +241,8 @@ def _counter_table(dirs):
             if role:
                 table.setdefault(r["Counter_Name"], {}).setdefault(role, []).append(
                     float(r["Counter_Value"]))
-    roles = ("pack", "unpack", "refresh")
-    lines = ["| counter | " + " | ".join(roles) + " |", "|---|---|---|---|"]
+    roles = ("pack", "unpack", "refresh", "pack_int8", "unpack_int8")
+    lines = ["| counter | " + " | ".join(roles) + " |", "|" + "---|" * (len(roles) + 1)]
     for c in sorted(table):
         vals = [table[c].get(r) for r in roles]
         lines.append(f"| {c} | " + " | ".join(f"{sum(v) / len(v):.4g}" if v else "" for v in vals)
@@ -301,7 +307,7 @@ def main():
     inp = W.refresh_inputs(cfg, Wn, device="cuda")
     dst = torch.arange(cfg.n_req, dtype=torch.int32, device="cuda") % n
     total_tokens = int(Wn.sum())
-    pack_b, unpack_b = _algorithmic_bytes(P)
+    pack_b, unpack_b, pack_qb, unpack_qb = _algorithmic_bytes(P)
     # Eq. 1 per token and replayed head: decay (1), readout (2), rank-1 write (2) flops per element
     flops = total_tokens * sum(5 * P.layer(l)["d_v"] * P.layer(l)["d_k"] * P.layer(l)["n_refresh_heads"]
                                for l in range(info["n_layers"]))
@@ -329,6 +335,22 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     assert P.status() == 0
+
+    # INT8 checkpoints (Eq. 10), timed on their own after the step: pack and
+    # unpack of the same checkpoints through an INT8 pool.
+    pool_q = torch.empty((n, info["int8_slot_bytes"]), dtype=torch.uint8, device="cuda")
+    evq = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.warmup + args.steps):
+        e = evq[i - args.warmup] if i >= args.warmup else None
+        if e: e[0].record(stream)
+        R.ckpt_pack_int8(P, dense, src, pool_q, slot, stream)
+        if e: e[1].record(stream)
+        R.ckpt_unpack_int8_zero_fill(P, pool_q, slot, out, src, stream)
+        if e: e[2].record(stream)
+    torch.cuda.synchronize()
+    assert P.status() == 0
+    t_pack_q = np.array([e[0].elapsed_time(e[1]) for e in evq]) * 1e-3
+    t_unpack_q = np.array([e[1].elapsed_time(e[2]) for e in evq]) * 1e-3
 
     t_pack = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
     t_unpack = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
@@ -374,6 +396,14 @@ def main():
         "roofline": roof_ref,
         "roofline_pack": hbm("pack", pack_total, t_pack.mean()),
         "roofline_unpack": hbm("unpack", unpack_total, t_unpack.mean()),
+        "int8": {
+            "c_ckpt_int8": round(info["c_ckpt_int8"], 4),
+            "pack_unpack_gbs": round(n * (pack_qb + unpack_qb) / (t_pack_q.mean() + t_unpack_q.mean()) / 1e9, 2),
+            "pack": {k: v for k, v in hbm("pack_int8", n * pack_qb, t_pack_q.mean()).items() if k != "kernel"}
+                    | {"kernel": "qmove_kernel<true>"},
+            "unpack": {k: v for k, v in hbm("unpack_int8", n * unpack_qb, t_unpack_q.mean()).items() if k != "kernel"}
+                      | {"kernel": "qmove_kernel<false>"},
+        },
     }
     if not args.no_cpu_baseline:
         m = min(8, n)

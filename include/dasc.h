@@ -39,6 +39,13 @@
  *     [dasc-pp] §4.4).  slot_bytes = sum_l r_l unit_bytes_l + sum conv.
  *   units: a GDN unit is a head (index h); a KDA unit is a key channel
  *     (h, k) with index h*d_k + k ([dasc] §4.1).
+ *   INT8 pool slot ([dasc] Appendix E.1 Eq. 10 on the ragged layout):
+ *     every retained unit's int8 payload, layer by layer in unit order (a
+ *     GDN unit as [d_v][d_k] row-major, a KDA unit as its d_v column
+ *     entries), padded to 16 bytes; then every retained unit's fp32 scales
+ *     in the same order (d_k per GDN unit: one per column k; one per KDA
+ *     unit), padded to 16 bytes; then every layer's conv bytes (bf16,
+ *     raw).  int8_slot_bytes in dasc_plan_info.
  */
 #ifndef DASC_H
 #define DASC_H
@@ -95,6 +102,10 @@ typedef struct {
   int64_t device_bytes;         /* size of the device tables (dasc_plan_upload) */
   int64_t k_row, v_row;         /* refresh row widths (elements): sum H d_k, sum H d_v */
   int64_t gate_row, beta_row;   /* sum (H d_k for KDA, H for GDN), sum H */
+  int64_t int8_payload_bytes;   /* int8 payload of the retained units */
+  int64_t int8_scale_bytes;     /* their fp32 scales */
+  int64_t int8_slot_bytes;      /* bytes of one INT8 pool slot (padded blocks + conv) */
+  double c_ckpt_int8;           /* dense checkpoint bytes / int8_slot_bytes */
 } dasc_plan_info;
 
 typedef struct {
@@ -111,6 +122,8 @@ typedef struct {
   int32_t w_layer;       /* max Eq. 7 window over the layer's local units (0 if none) */
   int32_t n_refresh_heads;
   int64_t k_row_offset, v_row_offset, gate_row_offset, beta_row_offset; /* refresh rows */
+  int64_t int8_pool_offset;   /* byte offset of the layer's int8 payload in an INT8 slot */
+  int64_t int8_scale_offset;  /* ... of its fp32 scales */
 } dasc_layer_info;
 
 /*
@@ -225,6 +238,38 @@ int dasc_ckpt_refresh_suffix(dasc_plan_t plan, const uint16_t* k, const uint16_t
                              const int64_t* tok_offsets, int64_t n_tokens,
                              void* dense_base, int64_t dense_stride, int64_t n_dense,
                              const int32_t* dst_idx, int32_t n, void* stream);
+
+/*
+ * INT8 pack ([dasc] Appendix E.1 Eq. 10 composed with the ragged layout,
+ * §4.1): for i in [0, n), quantize the retained units of dense[src_idx[i]]
+ * into INT8 pool slot pool[dst_slot[i]] and copy its conv bytes raw.  Per
+ * column k of a retained unit (every column of a GDN head, the one column of
+ * a KDA unit), in fp32 with correctly rounded division:
+ *   a = max_v |S[v][k]|,  s = max(a, 1e-8) / 127,
+ *   q[v] = clip(round_half_even(S[v][k] / s), -127, 127)   (0 if S / s is NaN)
+ * Maxima ignore NaN.  Same arguments and rules as dasc_ckpt_pack, except that
+ * pool rows hold int8_slot_bytes (pool_stride >= int8_slot_bytes).
+ * Requires d_k and d_v multiples of 4 and at most 128 for every layer with
+ * a retained unit (DASC_EUNSUPPORTED otherwise).
+ */
+int dasc_ckpt_pack_int8(dasc_plan_t plan, const void* dense_base, int64_t dense_stride,
+                        int64_t n_dense, const int32_t* src_idx, void* pool_base,
+                        int64_t pool_stride, int64_t n_slots, const int32_t* dst_slot,
+                        int32_t n, void* stream);
+
+/*
+ * INT8 unpack with zero-fill, dasc-nr on an INT8 checkpoint ([dasc] §4.2,
+ * Appendix E.1): dense[dst_idx[i]] <- S_hat = q s (fp32 product) in every
+ * retained unit of pool[src_slot[i]], +0.0 in every local unit, and the
+ * stored conv bytes.  Every byte of each destination checkpoint is written;
+ * the pool is read only.  Same arguments and rules as
+ * dasc_ckpt_unpack_zero_fill with INT8 pool rows.
+ */
+int dasc_ckpt_unpack_int8_zero_fill(dasc_plan_t plan, const void* pool_base,
+                                    int64_t pool_stride, int64_t n_slots,
+                                    const int32_t* src_slot, void* dense_base,
+                                    int64_t dense_stride, int64_t n_dense,
+                                    const int32_t* dst_idx, int32_t n, void* stream);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* dasc_last_error(void);

@@ -30,6 +30,8 @@ Readings (the page is silent on them):
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 from .plan import GDN, OraclePlan
@@ -67,8 +69,9 @@ class Int8Layout:
     @property
     def C_ckpt(self) -> float:
         """Checkpoint capacity ratio against the dense mixed-precision
-        checkpoint, the quantity the page's 8.11x measures."""
-        return self.dense_bytes / self.slot_bytes
+        checkpoint, the quantity the page's 8.11x measures; unbounded (inf)
+        when nothing is stored, as for Eq. 6's ratio."""
+        return math.inf if self.slot_bytes == 0 else self.dense_bytes / self.slot_bytes
 
 
 def quantize_columns(X: np.ndarray):
@@ -85,8 +88,10 @@ def quantize_columns(X: np.ndarray):
 
 
 def dequantize_columns(q: np.ndarray, s: np.ndarray) -> np.ndarray:
-    """S_hat = q s in fp32."""
-    return (np.asarray(q, dtype=np.int8).astype(F32) * np.asarray(s, dtype=F32)[None, :]).astype(F32)
+    """S_hat = q s in fp32 (0 * inf = NaN for a column whose maximum was
+    infinite, as the product defines)."""
+    with np.errstate(invalid="ignore"):
+        return (np.asarray(q, dtype=np.int8).astype(F32) * np.asarray(s, dtype=F32)[None, :]).astype(F32)
 
 
 def _state(row: np.ndarray, plan: OraclePlan, li: int) -> np.ndarray:

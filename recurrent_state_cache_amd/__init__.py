@@ -21,7 +21,8 @@ import numpy as np
 import torch  # noqa: F401
 
 __all__ = ["Plan", "DascError", "ckpt_pack", "ckpt_unpack_zero_fill",
-           "ckpt_refresh_suffix", "GDN", "KDA", "STATUS_BAD_INDEX",
+           "ckpt_refresh_suffix", "ckpt_pack_int8", "ckpt_unpack_int8_zero_fill",
+           "GDN", "KDA", "STATUS_BAD_INDEX",
            "STATUS_BAD_TOKENS", "LIB_PATH", "lib"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdasc.so")
@@ -48,7 +49,9 @@ class _PlanInfo(ctypes.Structure):
                 ("r_bar", _c_f64), ("c_temp", _c_f64), ("c_ckpt", _c_f64),
                 ("c_temp_pad", _c_f64), ("layout_gain", _c_f64),
                 ("n_refresh_heads", _c_i64), ("device_bytes", _c_i64), ("k_row", _c_i64),
-                ("v_row", _c_i64), ("gate_row", _c_i64), ("beta_row", _c_i64)]
+                ("v_row", _c_i64), ("gate_row", _c_i64), ("beta_row", _c_i64),
+                ("int8_payload_bytes", _c_i64), ("int8_scale_bytes", _c_i64),
+                ("int8_slot_bytes", _c_i64), ("c_ckpt_int8", _c_f64)]
 
 
 class _LayerInfo(ctypes.Structure):
@@ -59,7 +62,8 @@ class _LayerInfo(ctypes.Structure):
                 ("conv_pool_offset", _c_i64), ("conv_bytes", _c_i64), ("w_layer", _c_i32),
                 ("n_refresh_heads", _c_i32), ("k_row_offset", _c_i64),
                 ("v_row_offset", _c_i64), ("gate_row_offset", _c_i64),
-                ("beta_row_offset", _c_i64)]
+                ("beta_row_offset", _c_i64), ("int8_pool_offset", _c_i64),
+                ("int8_scale_offset", _c_i64)]
 
 
 def _load():
@@ -82,6 +86,10 @@ def _load():
                                                 _c_i64, _c_p, _c_i32, _c_p]),
         "dasc_ckpt_refresh_suffix": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p,
                                               _c_i64, _c_i64, _c_p, _c_i32, _c_p]),
+        "dasc_ckpt_pack_int8": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_i64,
+                                         _c_p, _c_i32, _c_p]),
+        "dasc_ckpt_unpack_int8_zero_fill": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p,
+                                                     _c_i64, _c_i64, _c_p, _c_i32, _c_p]),
         "dasc_last_error": (ctypes.c_char_p, []),
         "dasc_version": (ctypes.c_char_p, []),
     }
@@ -243,6 +251,37 @@ def ckpt_unpack_zero_fill(plan: Plan, pool, src_slot, dense, dst_idx, stream=Non
                                           _dev_ptr(src_slot, "src_slot", torch.int32), dp, ds, dn,
                                           _dev_ptr(dst_idx, "dst_idx", torch.int32), n,
                                           _stream_handle(stream)), "ckpt_unpack_zero_fill")
+
+
+def ckpt_pack_int8(plan: Plan, dense, src_idx, pool, dst_slot, stream=None) -> None:
+    """INT8 pool slot pool[dst_slot[i]] <- Eq. 10 of the retained units of
+    dense[src_idx[i]] (int8 payload, fp32 scales) and its raw conv bytes.
+    pool: [n_slots, >= int8_slot_bytes] uint8 CUDA tensor."""
+    import torch
+    dp, ds, dn = _rows(dense, "dense")
+    pp, ps, pn = _rows(pool, "pool")
+    n = src_idx.numel()
+    if dst_slot.numel() != n:
+        raise ValueError("src_idx and dst_slot differ in length")
+    _check(lib.dasc_ckpt_pack_int8(plan._h, dp, ds, dn, _dev_ptr(src_idx, "src_idx", torch.int32),
+                                   pp, ps, pn, _dev_ptr(dst_slot, "dst_slot", torch.int32), n,
+                                   _stream_handle(stream)), "ckpt_pack_int8")
+
+
+def ckpt_unpack_int8_zero_fill(plan: Plan, pool, src_slot, dense, dst_idx, stream=None) -> None:
+    """dense[dst_idx[i]] <- q s in the retained units of INT8 slot
+    pool[src_slot[i]], +0.0 in local units, and the stored conv bytes."""
+    import torch
+    pp, ps, pn = _rows(pool, "pool")
+    dp, ds, dn = _rows(dense, "dense")
+    n = src_slot.numel()
+    if dst_idx.numel() != n:
+        raise ValueError("src_slot and dst_idx differ in length")
+    _check(lib.dasc_ckpt_unpack_int8_zero_fill(plan._h, pp, ps, pn,
+                                               _dev_ptr(src_slot, "src_slot", torch.int32), dp,
+                                               ds, dn, _dev_ptr(dst_idx, "dst_idx", torch.int32),
+                                               n, _stream_handle(stream)),
+           "ckpt_unpack_int8_zero_fill")
 
 
 def ckpt_refresh_suffix(plan: Plan, k, v, a, beta, tok_off, dense, dst_idx, stream=None) -> None:

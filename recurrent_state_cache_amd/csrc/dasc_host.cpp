@@ -52,6 +52,7 @@ struct LayerPlan {
   int64_t unit_off, dense_off, conv_dense_off, pool_off, conv_pool_off;
   int64_t k_row_off, v_row_off, g_row_off, b_row_off;
   int64_t unit_base;  // first unit of the layer in the plan-wide unit order
+  int64_t q_off, s_off;  // INT8 slot: payload and scale offsets (bytes, scale block relative)
   int32_t w_layer;
   int32_t n_refresh;
   std::vector<uint8_t> retained;
@@ -72,14 +73,17 @@ struct dasc_plan {
   int64_t k_row = 0, v_row = 0, g_row = 0, b_row = 0;
 
   // host image of the device tables
-  std::vector<Piece> pack, unpack;
+  std::vector<Piece> pack, unpack, pack_q, unpack_q;
+  bool int8_ok = true;          // every layer with a retained unit fits the INT8 kernels
+  int64_t int8_scale_base = 0;  // INT8 slot: start of the scale block
+  int64_t int8_conv_base = 0;   // INT8 slot: start of the conv bytes
   std::vector<RefreshTask> refresh;
   std::vector<float> gate_expA, gate_dt;
   std::vector<Group> refresh_groups;
   int32_t kda_r_max = 0;  // largest retained-channel count of a KDA head
   bool kda_128 = true;    // every KDA layer has d_k = d_v = 128
-  int64_t off_pack = 0, off_unpack = 0, off_refresh = 0, off_expA = 0, off_dt = 0,
-          off_status = 0, table_bytes = 0;
+  int64_t off_pack = 0, off_unpack = 0, off_pack_q = 0, off_unpack_q = 0, off_refresh = 0,
+          off_expA = 0, off_dt = 0, off_status = 0, table_bytes = 0;
 
   uint8_t* device = nullptr;  // caller-owned upload target
   DeviceTables dev{};
@@ -160,6 +164,57 @@ void build_tables(dasc_plan* p) {
   push_range(p->pack, I.temporal_dense_bytes, I.temporal_rag_bytes, I.conv_bytes, kPieceCopy);
   push_range(p->unpack, I.temporal_dense_bytes, I.temporal_rag_bytes, I.conv_bytes, kPieceCopy);
 
+  // INT8 pieces ([dasc] Appendix E.1 Eq. 10): pack quantizes each head with a
+  // retained unit whole; unpack dequantizes GDN heads by row blocks and KDA
+  // heads whole, and clears omitted heads as above.
+  for (const auto& L : p->layers) {
+    const int64_t head_bytes = int64_t(L.d_v) * L.d_k * 4;
+    const int row_blocks = (L.d_v + kKdaRows - 1) / kKdaRows;
+    int64_t j = 0;  // retained units of the layer seen so far
+    for (int h = 0; h < L.n_heads; ++h) {
+      const uint64_t d_off = L.dense_off + h * head_bytes;
+      Piece t{};
+      t.dense_off = d_off;
+      t.d_k = static_cast<uint16_t>(L.d_k);
+      t.d_v = static_cast<uint16_t>(L.d_v);
+      uint32_t r = 0;
+      if (L.kind == kGDN) {
+        r = L.retained[h] ? 1 : 0;
+      } else {
+        for (int k = 0; k < L.d_k; ++k) {
+          if (L.retained[h * L.d_k + k]) {
+            t.mask[k >> 5] |= 1u << (k & 31);
+            ++r;
+          }
+        }
+      }
+      if (r == 0) {
+        push_range(p->unpack_q, d_off, 0, head_bytes, kPieceZero);
+        continue;
+      }
+      t.r = static_cast<uint16_t>(r);
+      if (L.kind == kGDN) {
+        t.type = kPieceQGdn;
+        t.pool_off = L.q_off + j * L.d_v * L.d_k;
+        t.scale_off = p->int8_scale_base + L.s_off + j * L.d_k * 4;
+        p->pack_q.push_back(t);
+        for (int rb = 0; rb < row_blocks; ++rb) {
+          t.rb = static_cast<uint16_t>(rb);
+          p->unpack_q.push_back(t);
+        }
+      } else {
+        t.type = kPieceQKda;
+        t.pool_off = L.q_off + j * L.d_v;
+        t.scale_off = p->int8_scale_base + L.s_off + j * 4;
+        p->pack_q.push_back(t);
+        p->unpack_q.push_back(t);
+      }
+      j += r;
+    }
+  }
+  push_range(p->pack_q, I.temporal_dense_bytes, p->int8_conv_base, I.conv_bytes, kPieceCopy);
+  push_range(p->unpack_q, I.temporal_dense_bytes, p->int8_conv_base, I.conv_bytes, kPieceCopy);
+
   // Refresh tasks, grouped by head width and gate mode (one kernel each).
   std::vector<std::tuple<int, int, int>> rkeys;  // (d_k, d_v, gate mode)
   std::vector<std::vector<RefreshTask>> rtasks;
@@ -219,6 +274,8 @@ void build_tables(dasc_plan* p) {
   };
   p->off_pack = section(p->pack.size() * sizeof(Piece));
   p->off_unpack = section(p->unpack.size() * sizeof(Piece));
+  p->off_pack_q = section(p->pack_q.size() * sizeof(Piece));
+  p->off_unpack_q = section(p->unpack_q.size() * sizeof(Piece));
   p->off_refresh = section(p->refresh.size() * sizeof(RefreshTask));
   p->off_expA = section(p->gate_expA.size() * sizeof(float));
   p->off_dt = section(p->gate_dt.size() * sizeof(float));
@@ -396,6 +453,22 @@ int dasc_plan_build(const dasc_layer_desc* layers, int32_t n_layers, double a_s,
       c_dense += L.conv_bytes;
       c_pool += L.conv_bytes;
     }
+    // INT8 slot ([dasc] Appendix E.1 Eq. 10): int8 payload | fp32 scales |
+    // conv, each block 16-byte aligned.
+    int64_t q = 0, sc = 0;
+    for (auto& L : p->layers) {
+      L.q_off = q;
+      L.s_off = sc;
+      q += L.r * (L.kind == kGDN ? int64_t(L.d_v) * L.d_k : L.d_v);
+      sc += L.r * (L.kind == kGDN ? L.d_k : 1) * 4;
+      if (L.r > 0 && (L.d_k % 4 || L.d_v % 4 || L.d_k > 128 || L.d_v > 128)) p->int8_ok = false;
+    }
+    p->int8_scale_base = align_up(q, 16);
+    p->int8_conv_base = p->int8_scale_base + align_up(sc, 16);
+    I.int8_payload_bytes = q;
+    I.int8_scale_bytes = sc;
+    I.int8_slot_bytes = p->int8_conv_base + conv;
+    I.c_ckpt_int8 = static_cast<double>(I.dense_bytes) / static_cast<double>(I.int8_slot_bytes);
     build_tables(p);
   } catch (const std::bad_alloc&) {
     delete p;
@@ -436,6 +509,8 @@ int dasc_plan_layer(dasc_plan_t p, int32_t layer, dasc_layer_info* out) {
   I.v_row_offset = L.v_row_off;
   I.gate_row_offset = L.g_row_off;
   I.beta_row_offset = L.b_row_off;
+  I.int8_pool_offset = L.q_off;
+  I.int8_scale_offset = p->int8_scale_base + L.s_off;
   *out = I;
   return DASC_OK;
 }
@@ -482,6 +557,8 @@ int dasc_plan_upload(dasc_plan_t p, void* device_buffer, int64_t bytes, void* st
   };
   put(p->off_pack, p->pack.data(), p->pack.size() * sizeof(Piece));
   put(p->off_unpack, p->unpack.data(), p->unpack.size() * sizeof(Piece));
+  put(p->off_pack_q, p->pack_q.data(), p->pack_q.size() * sizeof(Piece));
+  put(p->off_unpack_q, p->unpack_q.data(), p->unpack_q.size() * sizeof(Piece));
   put(p->off_refresh, p->refresh.data(), p->refresh.size() * sizeof(RefreshTask));
   put(p->off_expA, p->gate_expA.data(), p->gate_expA.size() * sizeof(float));
   put(p->off_dt, p->gate_dt.data(), p->gate_dt.size() * sizeof(float));
@@ -493,6 +570,8 @@ int dasc_plan_upload(dasc_plan_t p, void* device_buffer, int64_t bytes, void* st
   p->device = d;
   p->dev.pack = reinterpret_cast<const Piece*>(d + p->off_pack);
   p->dev.unpack = reinterpret_cast<const Piece*>(d + p->off_unpack);
+  p->dev.pack_q = reinterpret_cast<const Piece*>(d + p->off_pack_q);
+  p->dev.unpack_q = reinterpret_cast<const Piece*>(d + p->off_unpack_q);
   p->dev.refresh = reinterpret_cast<const RefreshTask*>(d + p->off_refresh);
   p->dev.gate_expA = reinterpret_cast<const float*>(d + p->off_expA);
   p->dev.gate_dt = reinterpret_cast<const float*>(d + p->off_dt);
@@ -536,7 +615,7 @@ bool overlap(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
 // Common checks of pack and unpack; `what` names the call in messages.
 int check_move(const dasc_plan* p, const char* what, const void* dense, int64_t dense_stride,
                int64_t n_dense, const void* pool, int64_t pool_stride, int64_t n_slots,
-               const void* idx_a, const void* idx_b, int32_t n) {
+               const void* idx_a, const void* idx_b, int32_t n, bool int8 = false) {
   const std::string w(what);
   if (!p) return fail(DASC_EINVAL, w + ": null plan");
   if (!p->device) return fail(DASC_ENOTUPLOADED, w + ": plan tables not uploaded");
@@ -546,21 +625,24 @@ int check_move(const dasc_plan* p, const char* what, const void* dense, int64_t 
   if (!aligned16(dense) || !aligned16(pool)) return fail(DASC_EINVAL, w + ": bases must be 16-byte aligned");
   if (dense_stride < p->info.dense_bytes || dense_stride % 16)
     return fail(DASC_EINVAL, w + ": dense_stride must be >= dense_bytes and a multiple of 16");
-  if (pool_stride < p->info.slot_bytes || pool_stride % 16)
-    return fail(DASC_EINVAL, w + ": pool_stride must be >= slot_bytes and a multiple of 16");
+  const int64_t slot_bytes = int8 ? p->info.int8_slot_bytes : p->info.slot_bytes;
+  if (pool_stride < slot_bytes || pool_stride % 16)
+    return fail(DASC_EINVAL, w + ": pool_stride must be >= the slot bytes and a multiple of 16");
   if (n_dense <= 0 || n_slots <= 0) return fail(DASC_EINVAL, w + ": n_dense and n_slots must be > 0");
   if (overlap(dense, dense_stride * n_dense, pool, pool_stride * n_slots))
     return fail(DASC_EINVAL, w + ": pool and dense ranges overlap");
   return DASC_OK;
 }
 
-// One pack or unpack: a single launch over the direction's piece list.
+// One pack or unpack (fp32 or INT8): a single launch over the direction's
+// piece list.
 int run_move(const dasc_plan* p, bool pack, const void* src_base, int64_t src_stride,
              int64_t n_src, const int32_t* src_idx, void* dst_base, int64_t dst_stride,
-             int64_t n_dst, const int32_t* dst_idx, int32_t n, void* stream) {
-  const std::vector<Piece>& pieces = pack ? p->pack : p->unpack;
+             int64_t n_dst, const int32_t* dst_idx, int32_t n, void* stream, bool int8 = false) {
+  const std::vector<Piece>& pieces = int8 ? (pack ? p->pack_q : p->unpack_q)
+                                          : (pack ? p->pack : p->unpack);
   MoveArgs m{};
-  m.pieces = pack ? p->dev.pack : p->dev.unpack;
+  m.pieces = int8 ? (pack ? p->dev.pack_q : p->dev.unpack_q) : (pack ? p->dev.pack : p->dev.unpack);
   m.n_pieces = static_cast<uint32_t>(pieces.size());
   m.kda_r_max = p->kda_r_max;
   m.kda_128 = p->kda_128;
@@ -574,7 +656,7 @@ int run_move(const dasc_plan* p, bool pack, const void* src_base, int64_t src_st
   m.n_dst = n_dst;
   m.n = n;
   m.status = p->dev.status;
-  return launch_move(pack, m, stream);
+  return int8 ? launch_qmove(pack, m, stream) : launch_move(pack, m, stream);
 }
 
 }  // namespace
@@ -604,6 +686,39 @@ int dasc_ckpt_unpack_zero_fill(dasc_plan_t p, const void* pool_base, int64_t poo
   int e = run_move(p, false, pool_base, pool_stride, n_slots, src_slot, dense_base, dense_stride,
                    n_dense, dst_idx, n, stream);
   if (e) return fail(DASC_EHIP, std::string("ckpt_unpack_zero_fill: launch failed: ") +
+                                    hipGetErrorString(static_cast<hipError_t>(e)));
+  return DASC_OK;
+}
+
+int dasc_ckpt_pack_int8(dasc_plan_t p, const void* dense_base, int64_t dense_stride,
+                        int64_t n_dense, const int32_t* src_idx, void* pool_base,
+                        int64_t pool_stride, int64_t n_slots, const int32_t* dst_slot, int32_t n,
+                        void* stream) {
+  int rc = check_move(p, "ckpt_pack_int8", dense_base, dense_stride, n_dense, pool_base,
+                      pool_stride, n_slots, src_idx, dst_slot, n, true);
+  if (rc != DASC_OK || n == 0) return rc;
+  if (!p->int8_ok)
+    return fail(DASC_EUNSUPPORTED, "ckpt_pack_int8: INT8 needs d_k, d_v multiples of 4, at most 128");
+  int e = run_move(p, true, dense_base, dense_stride, n_dense, src_idx, pool_base, pool_stride,
+                   n_slots, dst_slot, n, stream, true);
+  if (e) return fail(DASC_EHIP, std::string("ckpt_pack_int8: launch failed: ") +
+                                    hipGetErrorString(static_cast<hipError_t>(e)));
+  return DASC_OK;
+}
+
+int dasc_ckpt_unpack_int8_zero_fill(dasc_plan_t p, const void* pool_base, int64_t pool_stride,
+                                    int64_t n_slots, const int32_t* src_slot, void* dense_base,
+                                    int64_t dense_stride, int64_t n_dense, const int32_t* dst_idx,
+                                    int32_t n, void* stream) {
+  int rc = check_move(p, "ckpt_unpack_int8_zero_fill", dense_base, dense_stride, n_dense,
+                      pool_base, pool_stride, n_slots, src_slot, dst_idx, n, true);
+  if (rc != DASC_OK || n == 0) return rc;
+  if (!p->int8_ok)
+    return fail(DASC_EUNSUPPORTED,
+                "ckpt_unpack_int8_zero_fill: INT8 needs d_k, d_v multiples of 4, at most 128");
+  int e = run_move(p, false, pool_base, pool_stride, n_slots, src_slot, dense_base, dense_stride,
+                   n_dense, dst_idx, n, stream, true);
+  if (e) return fail(DASC_EHIP, std::string("ckpt_unpack_int8_zero_fill: launch failed: ") +
                                     hipGetErrorString(static_cast<hipError_t>(e)));
   return DASC_OK;
 }

@@ -18,6 +18,11 @@ constexpr int kKDA = 1;
 constexpr uint32_t kPieceCopy = 0;  // move `bytes` between dense and pool
 constexpr uint32_t kPieceZero = 1;  // clear `bytes` of the dense checkpoint (unpack)
 constexpr uint32_t kPieceKda = 2;   // kKdaRows rows of a KDA head with >= 1 retained channel
+// INT8 checkpoints (Eq. 10).  Pack quantizes whole heads (a column's scale
+// spans all d_v rows); unpack dequantizes GDN heads kKdaRows rows at a time
+// and KDA heads whole.
+constexpr uint32_t kPieceQGdn = 3;  // a retained GDN head
+constexpr uint32_t kPieceQKda = 4;  // a KDA head with >= 1 retained channel
 
 // Largest byte range one copy / zero piece covers: 256 lanes x 16 B.  Small
 // pieces stream HBM markedly faster on MI355X than 64 KiB pieces do.
@@ -34,14 +39,15 @@ constexpr int kKdaLdsRow = kKdaRows + 4;
 // pool[pool_off + j d_v 4], j < r, in ascending channel order: channel k
 // goes to j = the number of retained channels below k.
 struct alignas(64) Piece {
-  uint64_t dense_off;  // copy / zero: the range; KDA: the head's state [d_v][d_k] fp32
-  uint64_t pool_off;   // copy: the range; KDA: the head's first retained unit
-  uint32_t type;       // kPieceCopy, kPieceZero or kPieceKda
+  uint64_t dense_off;  // copy / zero: the range; head pieces: the head's state [d_v][d_k] fp32
+  uint64_t pool_off;   // copy: the range; head pieces: the head's first retained unit
+  uint32_t type;       // kPiece*
   uint32_t bytes;      // copy / zero: multiple of 16, at most kCopyChunk
-  uint16_t d_k, d_v;   // KDA: head shape
-  uint16_t rb, r;      // KDA: row block (rows kKdaRows rb ..), retained channels
+  uint16_t d_k, d_v;   // head pieces: head shape
+  uint16_t rb, r;      // row block (rows kKdaRows rb ..), retained channels
   uint32_t mask[4];    // KDA: bit k set = channel k retained
-  uint32_t pad[4];
+  uint64_t scale_off;  // INT8 pieces: byte offset of the first fp32 scale in a slot
+  uint32_t pad[2];
 };
 
 // One (layer, head) that a bounded-suffix refresh replays.
@@ -64,6 +70,8 @@ static_assert(sizeof(RefreshTask) == 64, "RefreshTask layout");
 struct DeviceTables {
   const Piece* pack;
   const Piece* unpack;
+  const Piece* pack_q;     // INT8 pack
+  const Piece* unpack_q;   // INT8 unpack
   const RefreshTask* refresh;
   const float* gate_expA;  // exp(A_log) per unit, fp32
   const float* gate_dt;    // dt_bias per unit, fp32
@@ -104,6 +112,8 @@ struct MoveArgs {
 
 // Kernel launchers (dasc_kernels.hip).  They return a hipError_t value.
 int launch_move(bool pack, const MoveArgs& args, void* stream);
+// INT8 pack / unpack over an INT8 piece list (kda_r_max and kda_128 unused).
+int launch_qmove(bool pack, const MoveArgs& args, void* stream);
 
 bool kda_shape_supported(int d_k, int d_v);
 bool refresh_shape_supported(int d_k, int d_v);

@@ -181,6 +181,206 @@ __global__ void __launch_bounds__(kThreads) move_kernel(MoveArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// INT8 checkpoints ([dasc] Appendix E.1 Eq. 10) on the ragged layout.  Per
+// column k of a retained unit: a = max_v |S[v][k]|, s = max(a, 1e-8) / 127
+// and q = clip(round_half_even(S / s), -127, 127), in fp32 with correctly
+// rounded division; unpack writes q s (fp32 product).  Maxima are taken with
+// `>` so that NaN entries are skipped; a NaN quotient stores 0.
+//
+// Pack pieces are whole heads (a column's scale spans all d_v rows): lane
+// (vl, kg), kg = tid % 32, vl = tid / 32, holds columns 4 kg .. 4 kg + 3 of
+// rows vl + 8 i (i < 16) in registers; the column maxima are combined over
+// the 8 row lanes in LDS.  A GDN head writes its int8 rows directly (32
+// lanes cover a row) and its d_k scales; a KDA head stages the int8 bytes of
+// its retained columns in LDS and writes each unit contiguously.  Unpack
+// pieces are GDN heads by blocks of 32 rows (lane: 4 rows x 4 columns) and
+// KDA heads whole (units and scales through LDS, 4x4 blocks transposed in
+// registers, +0.0 in omitted columns).
+// ---------------------------------------------------------------------------
+constexpr float kScaleFloor = 1e-8f;
+constexpr int kQRows = 16;  // rows a lane holds in a pack piece (d_v <= 128, 8 row lanes)
+
+__device__ __forceinline__ uint32_t quant4(f32x4 x, f32x4 s) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float r = rintf(x[c] / s[c]);
+    const float qf = r != r ? 0.f : fminf(fmaxf(r, -127.f), 127.f);
+    w |= (static_cast<uint32_t>(static_cast<int32_t>(qf)) & 0xFFu) << (8 * c);
+  }
+  return w;
+}
+
+__device__ __forceinline__ f32x4 dequant4(uint32_t w, f32x4 s) {
+  f32x4 x;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    x[c] = static_cast<float>(static_cast<int8_t>((w >> (8 * c)) & 0xFFu)) * s[c];
+  return x;
+}
+
+__device__ __forceinline__ float load_scale(const uint8_t* p) {
+  return *reinterpret_cast<const float*>(p);
+}
+
+template <bool kPack>
+__global__ void __launch_bounds__(kThreads) qmove_kernel(MoveArgs a) {
+  __shared__ __attribute__((aligned(16))) float red[8][128];            // column maxima per row lane
+  __shared__ __attribute__((aligned(16))) uint32_t qbuf[128][128 / 4];  // KDA units, int8 x 4 per word
+  __shared__ float qs[128];                                             // KDA scales
+  const Piece t = a.pieces[blockIdx.x];
+  const int64_t si = a.src_idx[blockIdx.y];
+  const int64_t di = a.dst_idx[blockIdx.y];
+  const bool bad_idx = !in_range(si, a.n_src) || !in_range(di, a.n_dst);
+  if (bad_idx | (t.type > kPieceQKda)) {
+    if (bad_idx && blockIdx.x == 0 && threadIdx.x == 0) flag(a.status, DASC_STATUS_BAD_INDEX);
+    return;
+  }
+  const uint8_t* src = a.src_base + si * a.src_stride;
+  uint8_t* dst = a.dst_base + di * a.dst_stride;
+  if (t.type == kPieceCopy || t.type == kPieceZero) {
+    copy_piece<kPack>(t, src, dst);
+    return;
+  }
+  const int dk = t.d_k, dv = t.d_v, KG = dk / 4, VG = dv / 4;
+  const int tid = threadIdx.x, kg = tid % 32, vl = tid / 32;
+  const bool col_on = kg < KG;
+  const bool kda = t.type == kPieceQKda;
+  uint32_t bits4 = 0, below = 0;
+  if (kda) lane_ranks(t, kg, bits4, below);
+  if constexpr (kPack) {
+    const float* S = reinterpret_cast<const float*>(src + t.dense_off);
+    f32x4 x[kQRows];
+    f32x4 mx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kQRows; ++i) {
+      const int v = vl + 8 * i;
+      x[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (col_on && v < dv) {
+        x[i] = ld_stream(reinterpret_cast<const f32x4*>(S + v * dk + 4 * kg));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float m = fabsf(x[i][c]);
+          mx[c] = m > mx[c] ? m : mx[c];
+        }
+      }
+    }
+    *reinterpret_cast<f32x4*>(&red[vl][4 * kg]) = mx;
+    __syncthreads();
+    f32x4 sc;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float m = 0.f;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) m = red[r][4 * kg + c] > m ? red[r][4 * kg + c] : m;
+      sc[c] = (m > kScaleFloor ? m : kScaleFloor) / 127.f;  // correctly rounded fp32 division
+    }
+    if (!kda) {
+      uint8_t* Q = dst + t.pool_off;
+#pragma unroll
+      for (int i = 0; i < kQRows; ++i) {
+        const int v = vl + 8 * i;
+        if (col_on && v < dv)
+          *reinterpret_cast<uint32_t*>(Q + v * dk + 4 * kg) = quant4(x[i], sc);
+      }
+      if (col_on && vl == 0) {
+        float* Sc = reinterpret_cast<float*>(dst + t.scale_off);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) Sc[4 * kg + c] = sc[c];
+      }
+      return;
+    }
+    // KDA: the retained columns' int8 bytes into LDS as units [rank][v]
+    uint8_t* qb = reinterpret_cast<uint8_t*>(&qbuf[0][0]);
+    if (col_on) {
+#pragma unroll
+      for (int i = 0; i < kQRows; ++i) {
+        const int v = vl + 8 * i;
+        if (v < dv) {
+          const uint32_t w = quant4(x[i], sc);
+          uint32_t rk = below;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            if ((bits4 >> c) & 1u) {
+              qb[rk * 128 + v] = static_cast<uint8_t>((w >> (8 * c)) & 0xFFu);
+              ++rk;
+            }
+          }
+        }
+      }
+      if (vl == 0) {
+        float* Sc = reinterpret_cast<float*>(dst + t.scale_off);
+        uint32_t rk = below;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if ((bits4 >> c) & 1u) {
+            Sc[rk] = sc[c];
+            ++rk;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const int r = t.r, wpu = dv / 4;  // 4-byte words per unit
+    uint32_t* U = reinterpret_cast<uint32_t*>(dst + t.pool_off);
+    for (int q = tid; q < r * wpu; q += kThreads) {
+      const int j = q / wpu, o = q % wpu;
+      U[j * wpu + o] = qbuf[j][o];
+    }
+  } else {
+    float* S = reinterpret_cast<float*>(dst + t.dense_off);
+    if (!kda) {
+      // 32 rows of a GDN head: lane holds rows 32 rb + 4 vl + i, columns 4 kg ..
+      if (!col_on) return;
+      const uint8_t* Sc = src + t.scale_off;
+      const f32x4 sc = {load_scale(Sc + 16 * kg), load_scale(Sc + 16 * kg + 4),
+                        load_scale(Sc + 16 * kg + 8), load_scale(Sc + 16 * kg + 12)};
+      const uint8_t* Q = src + t.pool_off;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int v = kKdaRows * t.rb + 4 * vl + i;
+        if (v < dv) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(Q + v * dk + 4 * kg);
+          st_stream(dequant4(w, sc), reinterpret_cast<f32x4*>(S + v * dk + 4 * kg));
+        }
+      }
+      return;
+    }
+    // KDA head: units and scales into LDS, then every element of the head
+    const int r = t.r, wpu = dv / 4;
+    const uint32_t* U = reinterpret_cast<const uint32_t*>(src + t.pool_off);
+    for (int q = tid; q < r * wpu; q += kThreads) {
+      const int j = q / wpu, o = q % wpu;
+      qbuf[j][o] = U[j * wpu + o];
+    }
+    if (tid < r) qs[tid] = load_scale(src + t.scale_off + 4 * tid);
+    __syncthreads();
+    if (!col_on) return;
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const int vg = vl + 8 * blk;  // rows 4 vg .. 4 vg + 3
+      if (vg >= VG) break;
+      f32x4 col[4];
+      uint32_t rk = below;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if ((bits4 >> c) & 1u) {
+          const float s = qs[rk];
+          col[c] = dequant4(qbuf[rk][vg], f32x4{s, s, s, s});
+          ++rk;
+        } else {
+          col[c] = f32x4{0.f, 0.f, 0.f, 0.f};  // omitted channel: +0.0
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        st_stream(f32x4{col[0][i], col[1][i], col[2][i], col[3][i]},
+                  reinterpret_cast<f32x4*>(S + (4 * vg + i) * dk + 4 * kg));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Bounded-suffix refresh ([dasc] §4.2), one workgroup per (head, request).
 //
 // Eq. 1 ([dasc] §3.1) is replayed in chunks of 16 tokens.  Inside a chunk
@@ -578,6 +778,16 @@ int launch_move(bool pack, const MoveArgs& args, void* stream) {
     if (args.kda_128) move_kernel<false, 128, 128><<<grid, kThreads, lds, s>>>(args);
     else move_kernel<false, 0, 0><<<grid, kThreads, lds, s>>>(args);
   }
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_qmove(bool pack, const MoveArgs& args, void* stream) {
+  if (args.n == 0 || args.n_pieces == 0) return hipSuccess;
+  if (args.n_pieces > 0x7FFFFFFFu) return static_cast<int>(hipErrorInvalidValue);
+  dim3 grid(args.n_pieces, static_cast<uint32_t>(args.n));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (pack) qmove_kernel<true><<<grid, kThreads, 0, s>>>(args);
+  else qmove_kernel<false><<<grid, kThreads, 0, s>>>(args);
   return static_cast<int>(hipGetLastError());
 }
 

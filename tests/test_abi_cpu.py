@@ -25,7 +25,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 15
     out = subprocess.run(["nm", "-D", "--defined-only", R.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\b[TW]\s+(dasc_[a-z0-9_]+)\b", out))
@@ -38,6 +38,7 @@ def test_every_declared_symbol_is_exported():
 def _compare(cfg_layers, a_s, eps, w_max):
     P = R.Plan(cfg_layers, a_s, eps, w_max)
     O = oracle.build_plan(cfg_layers, a_s, eps, w_max)
+    lo = oracle.Int8Layout(O)
     info = P.info()
     for l, L in enumerate(O.layers):
         r, H, w = P.units(l)
@@ -56,7 +57,13 @@ def _compare(cfg_layers, a_s, eps, w_max):
         assert li["unit_bytes"] == L.unit_bytes
         assert li["w_layer"] == O.W_layer[l]
         assert li["n_refresh_heads"] == len(O.refreshed_heads(l))
+        assert li["int8_pool_offset"] == lo.q_off[l]
+        assert li["int8_scale_offset"] == lo.scale_base + lo.s_off[l]
     assert info["n_retained"] == sum(L.r for L in O.layers)
+    assert info["int8_payload_bytes"] == lo.payload_bytes
+    assert info["int8_scale_bytes"] == lo.scale_bytes
+    assert info["int8_slot_bytes"] == lo.slot_bytes
+    assert info["c_ckpt_int8"] == lo.C_ckpt or (math.isinf(lo.C_ckpt) and math.isinf(info["c_ckpt_int8"]))
     assert info["temporal_dense_bytes"] == O.B_temp_dense
     assert info["temporal_rag_bytes"] == O.B_temp_rag
     assert info["conv_bytes"] == O.B_conv
