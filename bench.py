@@ -101,6 +101,24 @@ def _algorithmic_bytes(P):
     return pack, unpack, pack_q, unpack_q
 
 
+def _windowed_work(P, Wn):
+    """(flops, head-token replays) of the refresh with per-head Eq. 7
+    windows: head (l, h) replays min(W_lh, n_r) tokens of request r, W_lh
+    being the largest window over the head's local units."""
+    import numpy as np
+    flops = head_tokens = 0
+    for l in range(P.info()["n_layers"]):
+        L = P.layer(l)
+        ret, _, win = P.units(l)
+        per = 1 if L["kind"] == 0 else L["d_k"]
+        local = ~ret.reshape(L["n_heads"], per).astype(bool)
+        w = np.where(local, win.reshape(L["n_heads"], per), 0).max(axis=1)[local.any(axis=1)]
+        ht = int(np.minimum(w[:, None], np.asarray(Wn)[None, :]).sum())
+        head_tokens += ht
+        flops += 5 * L["d_v"] * L["d_k"] * ht
+    return flops, head_tokens
+
+
 def _calibrate_copy(steps):
     import torch
     n = 1 << 30
@@ -352,6 +370,19 @@ def main():
     t_pack_q = np.array([e[0].elapsed_time(e[1]) for e in evq]) * 1e-3
     t_unpack_q = np.array([e[1].elapsed_time(e[2]) for e in evq]) * 1e-3
 
+    # Refresh with per-head Eq. 7 windows on the same suffixes, timed on its own.
+    evw = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.warmup + args.steps):
+        e = evw[i - args.warmup] if i >= args.warmup else None
+        if e: e[0].record(stream)
+        R.ckpt_refresh_suffix_windowed(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, out, dst,
+                                       stream)
+        if e: e[1].record(stream)
+    torch.cuda.synchronize()
+    assert P.status() == 0
+    t_win = np.array([e[0].elapsed_time(e[1]) for e in evw]) * 1e-3
+    win_flops, win_head_tokens = _windowed_work(P, Wn)
+
     t_pack = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
     t_unpack = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
     t_ref = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
@@ -403,6 +434,14 @@ def main():
                     | {"kernel": "qmove_kernel<true>"},
             "unpack": {k: v for k, v in hbm("unpack_int8", n * unpack_qb, t_unpack_q.mean()).items() if k != "kernel"}
                       | {"kernel": "qmove_kernel<false>"},
+        },
+        "refresh_eq7_windows": {
+            "kernel": "refresh_kernel<128> (per-head window)",
+            "ms": round(t_win.mean() * 1e3, 4),
+            "head_tokens": int(win_head_tokens),
+            "flops": int(win_flops),
+            "achieved_tflops": round(win_flops / t_win.mean() / 1e12, 3),
+            "speedup_vs_full_suffix": round(t_ref.mean() / t_win.mean(), 3),
         },
     }
     if not args.no_cpu_baseline:

@@ -240,6 +240,24 @@ int dasc_ckpt_refresh_suffix(dasc_plan_t plan, const uint16_t* k, const uint16_t
                              const int32_t* dst_idx, int32_t n, void* stream);
 
 /*
+ * Bounded-suffix refresh with per-head Eq. 7 windows ([dasc-sum]
+ * "Methodology" Eq. 7, [dasc] §4.2): as dasc_ckpt_refresh_suffix, except
+ * that head (l, h) of request r replays only the last min(W_lh, n_r) of the
+ * request's n_r tokens, where W_lh is the largest Eq. 7 window
+ * W_u = clamp(next_pow2(H_s,u), 4, w_max) over the head's local units (a
+ * KDA head's local channels share one replay because (I - beta k k^T)
+ * couples its columns).  The caller passes the suffix for the model-wide
+ * window (dasc_plan_info.w_replay, or any longer one); heads whose local
+ * units have short horizons then skip the tokens they do not need.  Same
+ * arguments, rules and errors as dasc_ckpt_refresh_suffix.
+ */
+int dasc_ckpt_refresh_suffix_windowed(dasc_plan_t plan, const uint16_t* k, const uint16_t* v,
+                                      const uint16_t* a, const float* beta,
+                                      const int64_t* tok_offsets, int64_t n_tokens,
+                                      void* dense_base, int64_t dense_stride, int64_t n_dense,
+                                      const int32_t* dst_idx, int32_t n, void* stream);
+
+/*
  * INT8 pack ([dasc] Appendix E.1 Eq. 10 composed with the ragged layout,
  * §4.1): for i in [0, n), quantize the retained units of dense[src_idx[i]]
  * into INT8 pool slot pool[dst_slot[i]] and copy its conv bytes raw.  Per

@@ -172,6 +172,18 @@ class OraclePlan:
         per_head = lay.retained.reshape(lay.n_heads, lay.d_k)
         return np.flatnonzero(~per_head.all(axis=1))
 
+    def head_window(self, li: int, h: int) -> int:
+        """Eq. 7 window of one replayed head: the largest W_u over the
+        head's local units (a GDN local head is one unit; a KDA head's local
+        channels share one replay, because (I - beta k k^T) couples the
+        columns).  0 for a head with no local unit."""
+        lay = self.layers[li]
+        if lay.kind == GDN:
+            sel = lay.local_idx == h
+        else:
+            sel = (lay.local_idx // lay.d_k) == h
+        return int(lay.W_u[sel].max()) if sel.any() else 0
+
 
 def build_plan(layers, a_s: float = -0.3, eps: float = 1e-3,
                w_max: int = 16) -> OraclePlan:

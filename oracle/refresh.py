@@ -91,13 +91,16 @@ def _row_offsets(plan: OraclePlan):
 
 
 def refresh_expected(plan: OraclePlan, k_bits, v_bits, a_bits, beta, tok_off,
-                     requests=None, layers=None, heads=None):
+                     requests=None, layers=None, heads=None, head_windows=False):
     """Scratch states of the bounded-suffix refresh, float64.
 
     For each request r (all, or the given subset), each layer (all, or the
     given subset) and each head the plan replays in that layer (optionally
     restricted to `heads`), start from S = 0 and apply Eq. 1 over the
-    request's tokens tok_off[r] .. tok_off[r+1]-1.
+    request's tokens tok_off[r] .. tok_off[r+1]-1.  With head_windows, head
+    (l, h) replays only the last min(W_lh, n_r) of them, W_lh being the
+    head's own Eq. 7 window ([dasc-sum] "Methodology" Eq. 7, taken per head
+    rather than as one W_replay for the whole model).
 
     Returns {(r, layer, head): S [d_v, d_k] float64}.  Only the local units
     of each S are written into the active state by the refresh.
@@ -108,28 +111,42 @@ def refresh_expected(plan: OraclePlan, k_bits, v_bits, a_bits, beta, tok_off,
     n = len(tok_off) - 1
     out = {}
     for r in (range(n) if requests is None else requests):
-        t0, t1 = int(tok_off[r]), int(tok_off[r + 1])
         for li in (range(len(plan.layers)) if layers is None else layers):
-            lay = plan.layers[li]
-            hs = plan.refreshed_heads(li)
+            hs_all = plan.refreshed_heads(li)
             if heads is not None:
-                hs = np.array([h for h in hs if h in set(heads)], dtype=np.int64)
-            if len(hs) == 0:
+                hs_all = np.array([h for h in hs_all if h in set(heads)], dtype=np.int64)
+            if len(hs_all) == 0:
                 continue
-            H, dk, dv = lay.n_heads, lay.d_k, lay.d_v
-            ks = bf16_bits_to_f64(k_bits[t0:t1, ko[li]:ko[li] + H * dk]).reshape(-1, H, dk)[:, hs]
-            vs = bf16_bits_to_f64(v_bits[t0:t1, vo[li]:vo[li] + H * dv]).reshape(-1, H, dv)[:, hs]
-            bs = beta[t0:t1, bo[li]:bo[li] + H].astype(np.float64)[:, hs]
-            if lay.kind == GDN:
-                a = bf16_bits_to_f64(a_bits[t0:t1, go[li]:go[li] + H])[:, hs]
-                g = gate_log_decay(lay.A_log[hs], lay.dt_bias[hs], a)      # [W, nh]
-                al = np.repeat(np.exp(g)[:, :, None], dk, axis=2)          # alpha_t I
-            else:
-                a = bf16_bits_to_f64(a_bits[t0:t1, go[li]:go[li] + H * dk]).reshape(-1, H, dk)[:, hs]
-                Al = lay.A_log.reshape(H, dk)[hs]
-                Db = lay.dt_bias.reshape(H, dk)[hs]
-                al = np.exp(gate_log_decay(Al, Db, a))                    # [W, nh, dk]
-            S = replay_rank1(al, bs, ks, vs)
-            for i, h in enumerate(hs):
-                out[(r, li, int(h))] = S[i]
+            # heads that share a token range are replayed together
+            t1 = int(tok_off[r + 1])
+            starts = np.full(len(hs_all), int(tok_off[r]), dtype=np.int64)
+            if head_windows:
+                w = np.array([plan.head_window(li, int(h)) for h in hs_all], dtype=np.int64)
+                starts = np.maximum(starts, t1 - w)
+            for t0 in np.unique(starts):
+                out.update(_replay_heads(plan, li, hs_all[starts == t0], int(t0), t1, r,
+                                         k_bits, v_bits, a_bits, beta, ko, vo, go, bo))
+    return out
+
+
+def _replay_heads(plan, li, hs, t0, t1, r, k_bits, v_bits, a_bits, beta, ko, vo, go, bo):
+    """Eq. 1 from S = 0 over tokens t0 .. t1-1 for heads hs of layer li."""
+    out = {}
+    lay = plan.layers[li]
+    H, dk, dv = lay.n_heads, lay.d_k, lay.d_v
+    ks = bf16_bits_to_f64(k_bits[t0:t1, ko[li]:ko[li] + H * dk]).reshape(-1, H, dk)[:, hs]
+    vs = bf16_bits_to_f64(v_bits[t0:t1, vo[li]:vo[li] + H * dv]).reshape(-1, H, dv)[:, hs]
+    bs = beta[t0:t1, bo[li]:bo[li] + H].astype(np.float64)[:, hs]
+    if lay.kind == GDN:
+        a = bf16_bits_to_f64(a_bits[t0:t1, go[li]:go[li] + H])[:, hs]
+        g = gate_log_decay(lay.A_log[hs], lay.dt_bias[hs], a)      # [W, nh]
+        al = np.repeat(np.exp(g)[:, :, None], dk, axis=2)          # alpha_t I
+    else:
+        a = bf16_bits_to_f64(a_bits[t0:t1, go[li]:go[li] + H * dk]).reshape(-1, H, dk)[:, hs]
+        Al = lay.A_log.reshape(H, dk)[hs]
+        Db = lay.dt_bias.reshape(H, dk)[hs]
+        al = np.exp(gate_log_decay(Al, Db, a))                    # [W, nh, dk]
+    S = replay_rank1(al, bs, ks, vs)
+    for i, h in enumerate(hs):
+        out[(r, li, int(h))] = S[i]
     return out

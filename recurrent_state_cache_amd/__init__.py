@@ -21,7 +21,8 @@ import numpy as np
 import torch  # noqa: F401
 
 __all__ = ["Plan", "DascError", "ckpt_pack", "ckpt_unpack_zero_fill",
-           "ckpt_refresh_suffix", "ckpt_pack_int8", "ckpt_unpack_int8_zero_fill",
+           "ckpt_refresh_suffix", "ckpt_refresh_suffix_windowed", "ckpt_pack_int8",
+           "ckpt_unpack_int8_zero_fill",
            "GDN", "KDA", "STATUS_BAD_INDEX",
            "STATUS_BAD_TOKENS", "LIB_PATH", "lib"]
 
@@ -86,6 +87,8 @@ def _load():
                                                 _c_i64, _c_p, _c_i32, _c_p]),
         "dasc_ckpt_refresh_suffix": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_p,
                                               _c_i64, _c_i64, _c_p, _c_i32, _c_p]),
+        "dasc_ckpt_refresh_suffix_windowed": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
+                                                       _c_p, _c_i64, _c_i64, _c_p, _c_i32, _c_p]),
         "dasc_ckpt_pack_int8": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_i64,
                                          _c_p, _c_i32, _c_p]),
         "dasc_ckpt_unpack_int8_zero_fill": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p,
@@ -284,26 +287,37 @@ def ckpt_unpack_int8_zero_fill(plan: Plan, pool, src_slot, dense, dst_idx, strea
            "ckpt_unpack_int8_zero_fill")
 
 
-def ckpt_refresh_suffix(plan: Plan, k, v, a, beta, tok_off, dense, dst_idx, stream=None) -> None:
-    """Bounded-suffix refresh: replay each request's tokens from a zero
-    scratch state and write the local units into dense[dst_idx[r]].
-    k, v, a: bf16 CUDA tensors [T, row]; beta: fp32 [T, row]; tok_off: int64
-    [n+1]; dense: [n_dense, >= dense_bytes] uint8; dst_idx: int32 [n]."""
+def _refresh(fn, name, plan, k, v, a, beta, tok_off, dense, dst_idx, stream):
     import torch
     n = dst_idx.numel()
     if tok_off.numel() != n + 1:
         raise ValueError("tok_off must have n+1 entries")
     T = k.shape[0]
     info = plan.info()
-    for name, t, w in (("k", k, info["k_row"]), ("v", v, info["v_row"]),
-                       ("a", a, info["gate_row"]), ("beta", beta, info["beta_row"])):
+    for nm, t, w in (("k", k, info["k_row"]), ("v", v, info["v_row"]),
+                     ("a", a, info["gate_row"]), ("beta", beta, info["beta_row"])):
         if t.dim() != 2 or t.shape[0] != T or t.shape[1] != w:
-            raise ValueError(f"{name} must be [{T}, {w}], got {tuple(t.shape)}")
+            raise ValueError(f"{nm} must be [{T}, {w}], got {tuple(t.shape)}")
     dp, ds, dn = _rows(dense, "dense")
-    _check(lib.dasc_ckpt_refresh_suffix(plan._h, _dev_ptr(k, "k", torch.bfloat16),
-                                        _dev_ptr(v, "v", torch.bfloat16),
-                                        _dev_ptr(a, "a", torch.bfloat16),
-                                        _dev_ptr(beta, "beta", torch.float32),
-                                        _dev_ptr(tok_off, "tok_off", torch.int64), T, dp, ds, dn,
-                                        _dev_ptr(dst_idx, "dst_idx", torch.int32), n,
-                                        _stream_handle(stream)), "ckpt_refresh_suffix")
+    _check(fn(plan._h, _dev_ptr(k, "k", torch.bfloat16), _dev_ptr(v, "v", torch.bfloat16),
+              _dev_ptr(a, "a", torch.bfloat16), _dev_ptr(beta, "beta", torch.float32),
+              _dev_ptr(tok_off, "tok_off", torch.int64), T, dp, ds, dn,
+              _dev_ptr(dst_idx, "dst_idx", torch.int32), n, _stream_handle(stream)), name)
+
+
+def ckpt_refresh_suffix(plan: Plan, k, v, a, beta, tok_off, dense, dst_idx, stream=None) -> None:
+    """Bounded-suffix refresh: replay each request's tokens from a zero
+    scratch state and write the local units into dense[dst_idx[r]].
+    k, v, a: bf16 CUDA tensors [T, row]; beta: fp32 [T, row]; tok_off: int64
+    [n+1]; dense: [n_dense, >= dense_bytes] uint8; dst_idx: int32 [n]."""
+    _refresh(lib.dasc_ckpt_refresh_suffix, "ckpt_refresh_suffix", plan, k, v, a, beta, tok_off,
+             dense, dst_idx, stream)
+
+
+def ckpt_refresh_suffix_windowed(plan: Plan, k, v, a, beta, tok_off, dense, dst_idx,
+                                 stream=None) -> None:
+    """As ckpt_refresh_suffix, but each replayed head uses only the last
+    min(W_lh, n_r) tokens of its request, W_lh being the head's own Eq. 7
+    window (the largest W_u over its local units)."""
+    _refresh(lib.dasc_ckpt_refresh_suffix_windowed, "ckpt_refresh_suffix_windowed", plan, k, v,
+             a, beta, tok_off, dense, dst_idx, stream)

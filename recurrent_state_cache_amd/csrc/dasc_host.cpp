@@ -224,9 +224,10 @@ void build_tables(dasc_plan* p) {
       RefreshTask t{};
       bool any_local = false;
       for (int k = 0; k < L.d_k && k < 128; ++k) {
-        bool local = L.kind == kGDN ? !L.retained[h] : !L.retained[h * L.d_k + k];
-        if (local) {
+        const int64_t u = L.kind == kGDN ? h : int64_t(h) * L.d_k + k;
+        if (!L.retained[u]) {
           t.local[k >> 5] |= 1u << (k & 31);
+          t.window = std::max(t.window, static_cast<uint32_t>(L.window[u]));
           any_local = true;
         }
       }
@@ -723,11 +724,11 @@ int dasc_ckpt_unpack_int8_zero_fill(dasc_plan_t p, const void* pool_base, int64_
   return DASC_OK;
 }
 
-int dasc_ckpt_refresh_suffix(dasc_plan_t p, const uint16_t* k, const uint16_t* v,
-                             const uint16_t* a, const float* beta, const int64_t* tok_offsets,
-                             int64_t n_tokens, void* dense_base, int64_t dense_stride,
-                             int64_t n_dense, const int32_t* dst_idx, int32_t n, void* stream) {
-  const char* w = "ckpt_refresh_suffix";
+static int run_refresh(const char* w, bool head_windows, dasc_plan_t p, const uint16_t* k,
+                       const uint16_t* v, const uint16_t* a, const float* beta,
+                       const int64_t* tok_offsets, int64_t n_tokens, void* dense_base,
+                       int64_t dense_stride, int64_t n_dense, const int32_t* dst_idx, int32_t n,
+                       void* stream) {
   if (!p) return fail(DASC_EINVAL, std::string(w) + ": null plan");
   if (!p->device) return fail(DASC_ENOTUPLOADED, std::string(w) + ": plan tables not uploaded");
   if (n < 0 || n > 65535) return fail(DASC_EINVAL, std::string(w) + ": n must be in [0, 65535]");
@@ -765,6 +766,7 @@ int dasc_ckpt_refresh_suffix(dasc_plan_t p, const uint16_t* k, const uint16_t* v
   args.n_dense = n_dense;
   args.dst_idx = dst_idx;
   args.n = n;
+  args.head_windows = head_windows ? 1 : 0;
   args.status = p->dev.status;
   for (const Group& g : p->refresh_groups) {
     args.tasks = p->dev.refresh + g.first;
@@ -774,6 +776,23 @@ int dasc_ckpt_refresh_suffix(dasc_plan_t p, const uint16_t* k, const uint16_t* v
                                       hipGetErrorString(static_cast<hipError_t>(e)));
   }
   return DASC_OK;
+}
+
+int dasc_ckpt_refresh_suffix(dasc_plan_t p, const uint16_t* k, const uint16_t* v,
+                             const uint16_t* a, const float* beta, const int64_t* tok_offsets,
+                             int64_t n_tokens, void* dense_base, int64_t dense_stride,
+                             int64_t n_dense, const int32_t* dst_idx, int32_t n, void* stream) {
+  return run_refresh("ckpt_refresh_suffix", false, p, k, v, a, beta, tok_offsets, n_tokens,
+                     dense_base, dense_stride, n_dense, dst_idx, n, stream);
+}
+
+int dasc_ckpt_refresh_suffix_windowed(dasc_plan_t p, const uint16_t* k, const uint16_t* v,
+                                      const uint16_t* a, const float* beta,
+                                      const int64_t* tok_offsets, int64_t n_tokens,
+                                      void* dense_base, int64_t dense_stride, int64_t n_dense,
+                                      const int32_t* dst_idx, int32_t n, void* stream) {
+  return run_refresh("ckpt_refresh_suffix_windowed", true, p, k, v, a, beta, tok_offsets,
+                     n_tokens, dense_base, dense_stride, n_dense, dst_idx, n, stream);
 }
 
 }  // extern "C"

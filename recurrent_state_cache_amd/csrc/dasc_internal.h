@@ -60,7 +60,8 @@ struct alignas(64) RefreshTask {
   uint32_t param_off;  // index of the head's first unit in the gate arrays
   uint32_t kind;       // kGDN: one gate per head; kKDA: one per channel
   uint32_t local[4];   // bit k set: column k is local and gets written
-  uint32_t pad[4];
+  uint32_t window;     // Eq. 7 window of the head: max W_u over its local units
+  uint32_t pad[3];
 };
 
 static_assert(sizeof(Piece) == 64, "Piece layout");
@@ -135,6 +136,7 @@ struct RefreshArgs {
   int64_t n_dense;
   const int32_t* dst_idx;
   int32_t n;
+  int32_t head_windows;  // nonzero: each head replays only its last `window` tokens
   uint32_t* status;
 };
 

@@ -500,13 +500,15 @@ refresh_kernel(RefreshArgs a) {
 
   const RefreshTask task = a.tasks[blockIdx.x];
   const int req = blockIdx.y;
-  const int64_t t0 = a.tok_off[req];
+  int64_t t0 = a.tok_off[req];
   const int64_t t1 = a.tok_off[req + 1];
   const int64_t dst = a.dst_idx[req];
   if (t0 < 0 || t1 < t0 || t1 > a.n_tokens) {
     if (blockIdx.x == 0 && threadIdx.x == 0) flag(a.status, DASC_STATUS_BAD_TOKENS);
     return;
   }
+  // Per-head Eq. 7 window: replay only the request's last `window` tokens.
+  if (a.head_windows) t0 = t1 - t0 > task.window ? t1 - task.window : t0;
   if (!in_range(dst, a.n_dense)) {
     if (blockIdx.x == 0 && threadIdx.x == 0) flag(a.status, DASC_STATUS_BAD_INDEX);
     return;

@@ -31,7 +31,8 @@ def _bits16(t):
     return t.contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
-def _check_requests(P, O, inp, before, after, dst, reqs, layers=None, label=""):
+def _check_requests(P, O, inp, before, after, dst, reqs, layers=None, label="",
+                    head_windows=False):
     """Compare the refreshed heads of the given requests (and layers) with
     the oracle; check untouched bytes of those destinations bit-exactly."""
     tok = inp.tok_off.cpu().numpy()
@@ -43,7 +44,8 @@ def _check_requests(P, O, inp, before, after, dst, reqs, layers=None, label=""):
         v = _bits16(_host_rows(inp.v, (t0, t1)))
         a = _bits16(_host_rows(inp.a, (t0, t1)))
         b = _host_rows(inp.beta, (t0, t1)).numpy()
-        ref = oracle.refresh_expected(O, k, v, a, b, np.array([0, t1 - t0]), layers=layers)
+        ref = oracle.refresh_expected(O, k, v, a, b, np.array([0, t1 - t0]), layers=layers,
+                                      head_windows=head_windows)
         d = int(dst[r])
         got = after[d].cpu().numpy()
         old = before[d].cpu().numpy()
@@ -218,3 +220,44 @@ def test_unsupported_refresh_shape_is_rejected():
                               torch.tensor([0, T], device="cuda"), dense,
                               torch.zeros(1, dtype=torch.int32, device="cuda"))
     assert e.value.code == -5
+
+
+def test_windowed_refresh_every_width():
+    # W_max = 64: head windows from 4 to 64, requests shorter and longer
+    cfg = W.Config("widths", _odd_refresh_layers(22), w_max=64, n_req=5, seed=22)
+    P, O = _plans(cfg)
+    wins = sorted({O.head_window(li, int(h)) for li in range(len(cfg.layers))
+                   for h in O.refreshed_heads(li)})
+    Wn = np.array([0, 3, 17, 70, 130])
+    log(f"[refresh] windowed, widths 16..128: head windows {wins}, requests {list(Wn)}")
+    assert len(wins) >= 3
+    inp = W.refresh_inputs(cfg, Wn, device="cuda")
+    dense = W.dense_states(cfg, 6, device="cuda", seed=9)
+    before = dense.clone()
+    dst = torch.tensor([5, 0, 2, 1, 3], dtype=torch.int32, device="cuda")
+    R.ckpt_refresh_suffix_windowed(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, dense, dst)
+    torch.cuda.synchronize()
+    assert P.status() == 0
+    assert torch.equal(dense[4], before[4])                 # not a destination
+    _check_requests(P, O, inp, before, dense, dst.cpu().numpy(), range(5), label="windowed",
+                    head_windows=True)
+
+
+def test_windowed_refresh_kda_and_mixed_sampled():
+    for cfg, reqs, layers in ((W.kda_refresh(n_req=8), [0, 7], [0, 19]),
+                              (W.mixed(n_ckpt=16, n_req=16), [0, 5], [0, 1, 26])):
+        P, O = _plans(cfg)
+        Wn = W.windows(cfg)
+        wins = sorted({O.head_window(li, int(h)) for li in layers for h in O.refreshed_heads(li)})
+        log(f"[refresh] windowed {cfg.name}: W_max {cfg.w_max}, head windows {wins}, "
+            f"requests of {Wn.min()}..{Wn.max()} tokens")
+        inp = W.refresh_inputs(cfg, Wn, device="cuda")
+        dense = W.dense_states(cfg, cfg.n_req, device="cuda", seed=10)
+        before = dense.clone()
+        dst = torch.arange(cfg.n_req, dtype=torch.int32, device="cuda")
+        R.ckpt_refresh_suffix_windowed(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, dense,
+                                       dst)
+        torch.cuda.synchronize()
+        assert P.status() == 0
+        _check_requests(P, O, inp, before, dense, dst.cpu().numpy(), reqs, layers=layers,
+                        label=f"windowed {cfg.name}", head_windows=True)

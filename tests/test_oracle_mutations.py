@@ -65,7 +65,8 @@ PLAN_PINS = [T_plan.test_half_decay_gives_log2_1000, T_plan.test_exact_tie_is_om
              T_plan.test_ragged_offsets_order_and_bytes,
              T_plan.test_c1_budget_decomposition_and_eq8,
              T_plan.test_eq6_reproduces_kda_2p63_and_eq8_2p64,
-             T_plan.test_refreshed_heads_rule, T_plan.test_mask_equals_decay_threshold_rule]
+             T_plan.test_refreshed_heads_rule, T_plan.test_mask_equals_decay_threshold_rule,
+             T_plan.test_head_window_worked_by_hand]
 CKPT_PINS = [T_ckpt.test_round_trip_equals_masked_state, T_ckpt.test_pack_is_bijection_onto_payload,
              T_ckpt.test_raw_bits_survive, T_ckpt.test_unpack_overwrites_every_byte_and_zero_is_positive,
              T_ckpt.test_conv_bytes_follow_payload]
@@ -73,7 +74,8 @@ REFRESH_PINS = [T_ref.test_rank1_matches_printed_matrix_form, T_ref.test_beta_on
                 T_ref.test_beta_zero_is_pure_column_decay, T_ref.test_one_hot_write_then_decay_closed_form,
                 T_ref.test_contraction_bound, lambda: T_ref.test_refresh_expected_wiring_gate_and_rows(8, 8),
                 lambda: T_ref.test_refresh_expected_wiring_gate_and_rows(8, 4),
-                T_ref.test_refresh_expected_respects_windows, T_ref.test_gdn_scalar_decay_equals_broadcast]
+                T_ref.test_refresh_expected_respects_windows, T_ref.test_gdn_scalar_decay_equals_broadcast,
+                T_ref.test_head_windows_replay_each_heads_last_tokens]
 
 INT8_PINS = [T_int8.test_pages_8p11_capacity_and_3p88_quantization_only,
              T_int8.test_scale_is_column_max_over_127_and_rounding_is_half_even,
@@ -108,6 +110,9 @@ MUTATIONS = [
     ("refresh", "al = np.exp(gate_log_decay(Al, Db, a))", "al = np.exp(-gate_log_decay(Al, Db, a))", REFRESH_PINS),
     ("refresh", "g += lay.n_heads * lay.d_k if lay.kind != GDN else lay.n_heads", "g += lay.n_heads * lay.d_k", REFRESH_PINS),
     ("refresh", "vs = bf16_bits_to_f64(v_bits[t0:t1, vo[li]", "vs = bf16_bits_to_f64(v_bits[t0:t1, ko[li]", REFRESH_PINS),
+    ("refresh", "starts = np.maximum(starts, t1 - w)", "starts = np.maximum(starts, t1 - w + 1)", REFRESH_PINS),
+    ("plan", "return int(lay.W_u[sel].max()) if sel.any() else 0", "return int(lay.W_u[sel].min()) if sel.any() else 0", PLAN_PINS),
+    ("plan", "sel = (lay.local_idx // lay.d_k) == h", "sel = (lay.local_idx % lay.d_k) == h", PLAN_PINS),
     # INT8 (Eq. 10)
     ("int8", "s = np.fmax(a, SCALE_FLOOR) / QMAX", "s = np.fmax(a, SCALE_FLOOR) / F32(128.0)", INT8_PINS),
     ("int8", "s = np.fmax(a, SCALE_FLOOR) / QMAX", "s = a / QMAX", INT8_PINS),

@@ -247,3 +247,26 @@ def test_refreshed_heads_rule():
     assert list(p.refreshed_heads(0)) == [1, 2, 3]
     g = oracle.build_plan([_layer(GDN, 4, 8, 8, [-8.0, 3.0, -8.0, 3.0], np.zeros(4))], w_max=16)
     assert list(g.refreshed_heads(0)) == [1, 3]
+
+
+def test_head_window_worked_by_hand():
+    # a_s + dt_bias = 0 makes softplus = ln 2, so H_s = log2(1000) / exp(A_log)
+    # and A_log = ln(log2(1000) / H) puts each horizon where the table says.
+    # Per head, W_lh = max over local units of clamp(next_pow2(H_s), 4, 16),
+    # worked by hand (Eq. 7 per head; 0 = no local unit, head not replayed).
+    lg = math.log2(1000.0)
+    kda_H = [[3.0, 5.0, 100.0, 2.0],      # W_u 4, 8, retained, 4      -> 8
+             [50.0, 60.0, 70.0, 80.0],    # all retained               -> 0
+             [12.0, 0.5, 7.0, 16.5],      # 16, 4, 8, retained         -> 16
+             [1.5, 2.5, 3.5, 3.9]]        # 4, 4, 4, 4                 -> 4
+    gdn_H = [6.0, 20.0, 2.2, 9.0]         # 8, retained, 4, 16
+    A_k = [math.log(lg / h) for row in kda_H for h in row]
+    A_g = [math.log(lg / h) for h in gdn_H]
+    kda = _layer(KDA, 4, 4, 4, A_k, np.full(16, 0.25))
+    gdn = _layer(GDN, 4, 4, 4, A_g, np.full(4, 0.25))
+    p = oracle.build_plan([kda, gdn], a_s=-0.25, eps=1e-3, w_max=16)
+    assert [p.head_window(0, h) for h in range(4)] == [8, 0, 16, 4]
+    assert [p.head_window(1, h) for h in range(4)] == [8, 0, 4, 16]
+    assert list(p.refreshed_heads(0)) == [0, 2, 3]
+    assert list(p.refreshed_heads(1)) == [0, 2, 3]
+    assert p.W_layer == [16, 16] and p.W_replay == 16

@@ -195,3 +195,47 @@ def test_refresh_expected_respects_windows():
     assert (1, 0, 0) in out and not np.any(out[(1, 0, 0)])          # W = 0
     solo = oracle.refresh_expected(plan, k[3:], v[3:], a[3:], beta[3:], np.array([0, 4]))
     np.testing.assert_array_equal(out[(2, 0, 0)], solo[(0, 0, 0)])
+
+
+def _windowed_plan():
+    # a_s + dt_bias = 0: H_s = log2(1000) / exp(A_log).  KDA heads with
+    # windows 8, 16 and 4 (one fully retained head), GDN heads 8, 4, 16.
+    lg = math.log2(1000.0)
+    kda_H = [3.0, 5.0, 100.0, 2.0, 50.0, 60.0, 70.0, 80.0, 12.0, 0.5, 7.0, 16.5,
+             1.5, 2.5, 3.5, 3.9]
+    gdn_H = [6.0, 20.0, 2.2, 9.0]
+    A_k = np.array([math.log(lg / h) for h in kda_H], np.float32)
+    A_g = np.array([math.log(lg / h) for h in gdn_H], np.float32)
+    return oracle.build_plan([Layer(KDA, 4, 4, 4, A_k, np.full(16, 0.25, np.float32)),
+                              Layer(GDN, 4, 4, 4, A_g, np.full(4, 0.25, np.float32))],
+                             a_s=-0.25, eps=1e-3, w_max=16)
+
+
+def test_head_windows_replay_each_heads_last_tokens():
+    plan = _windowed_plan()
+    rng = np.random.default_rng(29)
+    lens = [0, 3, 4, 5, 8, 9, 16, 23]
+    tok = np.concatenate([[0], np.cumsum(lens)])
+    T = int(tok[-1])
+    trunc = lambda x: (x.astype(np.float32).view(np.uint32) & 0xFFFF0000).view(np.float32)
+    k = _bf16_bits(trunc(rng.normal(0, 0.5, (T, 32))))
+    v = _bf16_bits(trunc(rng.normal(0, 1, (T, 32))))
+    a = _bf16_bits(trunc(rng.normal(0, 1, (T, 20))))
+    beta = rng.uniform(0, 1, (T, 8)).astype(np.float32)
+    win = oracle.refresh_expected(plan, k, v, a, beta, tok, head_windows=True)
+    full = oracle.refresh_expected(plan, k, v, a, beta, tok)
+    assert win.keys() == full.keys()
+    for (r, li, h), S in win.items():
+        W = {(0, 0): 8, (0, 2): 16, (0, 3): 4, (1, 0): 8, (1, 2): 4, (1, 3): 16}[(li, h)]
+        t1 = int(tok[r + 1])
+        t0 = max(int(tok[r]), t1 - W)
+        # the same head replayed alone over its last W tokens
+        solo = oracle.refresh_expected(plan, k, v, a, beta, np.array([t0, t1]), layers=[li],
+                                       heads=[h])
+        np.testing.assert_array_equal(S, solo[(0, li, h)])
+        if lens[r] <= W:
+            np.testing.assert_array_equal(S, full[(r, li, h)])
+        else:
+            assert not np.array_equal(S, full[(r, li, h)])
+        if lens[r] == 0:
+            assert not np.any(S)
