@@ -17,7 +17,8 @@ Pages cited (by title, section / equation / table):
              (log-decay gate), Eq. 3 (static horizon), §4.1 (selection mask,
              byte accounting), §4.2 (load policies), Appendix B (padded and
              ragged layouts), Appendix C.1 (Eq. 8, per-rank budgets),
-             Appendix E.1 (Eq. 10, INT8).
+             Appendix E.1 (Eq. 10, INT8), §4.3 and Appendix B.1(b) (TP
+             storage balancing).
 * [dasc-pp]  the same paper's paperpeel version: Appendix B.2 (insertion and
              reuse, transactional demotion), "Ragged (Scheme 2)".
 * [dasc-sum] the picx.dev summary of dasc, "Methodology": the only page that
@@ -36,6 +37,9 @@ from .int8 import (Int8Layout, dequantize_columns, pack_int8, quantize_columns,
                    unpack_int8_zero_fill)
 from .refresh import (bf16_bits_to_f64, delta_rule_step, refresh_expected,
                       replay_dense, replay_rank1)
+from .balance import (Balance, exchange_load, exchange_store, pack_tp, plans_balance,
+                      rank_layers, rank_plans, send_bytes_tp, slot_bytes_tp, storage_balance,
+                      unpack_tp)
 
 __all__ = [
     "GDN", "KDA", "OraclePlan", "build_plan", "gate_log_decay", "horizon",
@@ -43,4 +47,6 @@ __all__ = [
     "unpack_zero_fill", "bf16_bits_to_f64", "delta_rule_step",
     "refresh_expected", "replay_dense", "replay_rank1", "Int8Layout",
     "quantize_columns", "dequantize_columns", "pack_int8", "unpack_int8_zero_fill",
+    "Balance", "storage_balance", "plans_balance", "rank_layers", "rank_plans", "pack_tp",
+    "unpack_tp", "exchange_store", "exchange_load", "slot_bytes_tp", "send_bytes_tp",
 ]

@@ -13,10 +13,12 @@ import sys
 import pytest
 
 import oracle
+import oracle.balance
 import oracle.ckpt
 import oracle.int8
 import oracle.plan
 import oracle.refresh
+import test_oracle_balance as T_bal
 import test_oracle_ckpt as T_ckpt
 import test_oracle_int8 as T_int8
 import test_oracle_plan as T_plan
@@ -44,7 +46,8 @@ def _swap(monkeypatch, modname, mod):
     real = getattr(oracle, modname)
     for name, obj in vars(mod).items():
         if callable(obj) and getattr(real, name, None) is not None and not name.startswith("__"):
-            for holder in (oracle, oracle.plan, oracle.ckpt, oracle.refresh, oracle.int8):
+            for holder in (oracle, oracle.plan, oracle.ckpt, oracle.refresh, oracle.int8,
+                           oracle.balance):
                 if getattr(holder, name, None) is getattr(real, name):
                     monkeypatch.setattr(holder, name, obj)
 
@@ -85,6 +88,12 @@ INT8_PINS = [T_int8.test_pages_8p11_capacity_and_3p88_quantization_only,
              T_int8.test_non_finite_entries_quantize_to_zero,
              T_int8.test_pack_unpack_int8_round_trip]
 
+BAL_PINS = [T_bal.test_hand_worked_even_split, T_bal.test_hand_worked_remainder_and_tie_order,
+            T_bal.test_indivisible_head_forces_remote_traffic, T_bal.test_target_invariants_random,
+            lambda: T_bal.test_store_load_round_trip(T_bal.KDA, 4, 12),
+            lambda: T_bal.test_store_load_round_trip(T_bal.GDN, 2, 8),
+            T_bal.test_tp1_is_the_plain_ragged_slot, T_bal.test_rank_layers_split_heads_and_parameters]
+
 MUTATIONS = [
     # plan
     ("plan", "np.exp(A_log) * softplus(a + dt_bias)", "np.exp(A_log) * softplus(a - dt_bias)", PLAN_PINS),
@@ -114,6 +123,15 @@ MUTATIONS = [
     ("plan", "return int(lay.W_u[sel].max()) if sel.any() else 0", "return int(lay.W_u[sel].min()) if sel.any() else 0", PLAN_PINS),
     ("plan", "sel = (lay.local_idx // lay.d_k) == h", "sel = (lay.local_idx % lay.d_k) == h", PLAN_PINS),
     # INT8 (Eq. 10)
+    ("balance", "key=lambda r: (-n[r], r))", "key=lambda r: (n[r], r))", BAL_PINS),
+    ("balance", "key=lambda r: (-n[r], r))", "key=lambda r: (-n[r], -r))", BAL_PINS),
+    ("balance", "t[r] = q + 1 if pos < m else q", "t[r] = q + 1 if pos >= P - m else q", BAL_PINS),
+    ("balance", "b.keep = [min(n[r], t[r]) for r in range(P)]", "b.keep = [min(n[r], t[r] - 1) if t[r] else 0 for r in range(P)]", BAL_PINS),
+    ("balance", "b.excess = [(r, i) for r in range(P) for i in range(b.keep[r], n[r])]", "b.excess = [(r, i) for i in range(max(n + [0])) for r in range(P) if b.keep[r] <= i < n[r]]", BAL_PINS),
+    ("balance", "b.slot_units = math.ceil(N / P) if P else 0", "b.slot_units = N // P if P else 0", BAL_PINS),
+    ("balance", "if d2 < d_i or (d2 == d_i and i2 < i):", "if d2 > d_i or (d2 == d_i and i2 < i):", BAL_PINS),
+    ("balance", "D = np.asarray(lay.dt_bias, np.float32).reshape(lay.n_heads, per)[r * Hr:(r + 1) * Hr]", "D = np.asarray(lay.dt_bias, np.float32).reshape(lay.n_heads, per)[r:r + Hr]", BAL_PINS),
+    ("balance", "A = np.asarray(lay.A_log, np.float32).reshape(lay.n_heads, per)[r * Hr:(r + 1) * Hr]", "A = np.asarray(lay.A_log, np.float32).reshape(per, lay.n_heads).T[r * Hr:(r + 1) * Hr]", BAL_PINS),
     ("int8", "s = np.fmax(a, SCALE_FLOOR) / QMAX", "s = np.fmax(a, SCALE_FLOOR) / F32(128.0)", INT8_PINS),
     ("int8", "s = np.fmax(a, SCALE_FLOOR) / QMAX", "s = a / QMAX", INT8_PINS),
     ("int8", "r = np.rint(X / s[None, :])", "r = np.floor(X / s[None, :] + F32(0.5))", INT8_PINS),
