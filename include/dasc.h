@@ -126,6 +126,26 @@ typedef struct {
   int64_t int8_scale_offset;  /* ... of its fp32 scales */
 } dasc_layer_info;
 
+/* Tensor-parallel storage balancing of one rank ([dasc] §4.3, Appendix
+ * B.1(b)); units counted in one store of equal-size units. */
+typedef struct {
+  int32_t tp, rank;
+  int32_t one_store;     /* 1: every layer has the same unit size (balancing available) */
+  int32_t reserved;
+  int64_t unit_bytes;    /* bytes of one unit */
+  int64_t n_total;       /* N = sum_r n_r */
+  int64_t slot_units;    /* ceil(N / tp): unit positions of every rank's storage slot */
+  int64_t m_remote;      /* units crossing ranks: sum_r max(0, n_r - t_r) */
+  int64_t max_local;     /* max_r n_r: the worst rank's units without balancing */
+  int64_t n_local;       /* n_r: this rank's compute-local (retained) units */
+  int64_t target;        /* t_r */
+  int64_t keep;          /* min(n_r, t_r): units this rank keeps, at positions 0 .. keep-1 */
+  int64_t send_units;    /* n_r - keep: units this rank stores elsewhere */
+  int64_t recv_units;    /* t_r - keep: units it stores for other ranks */
+  int64_t slot_bytes;    /* slot_units * unit_bytes + this rank's conv bytes */
+  int64_t send_bytes;    /* send_units * unit_bytes: one send / receive row */
+} dasc_tp_info;
+
 /*
  * Build the static selection plan ([dasc] §4.1).  For every unit u:
  *   g_u   = -exp(A_log_u) * softplus(a_s + dt_bias_u)      ([dasc] §3.3 Eq. 2)
@@ -144,6 +164,40 @@ typedef struct {
  */
 int dasc_plan_build(const dasc_layer_desc* layers, int32_t n_layers, double a_s,
                     double eps, int32_t w_max, dasc_plan_t* out);
+
+/*
+ * Plan of one tensor-parallel rank with storage balancing ([dasc] §4.3,
+ * Appendix B.1(b)).  `layers` describes the whole model; rank `rank` of `tp`
+ * owns heads [rank H/tp, (rank+1) H/tp) of every layer and conv_bytes/tp of
+ * each layer's conv state, and the returned plan is the plan_build plan of
+ * those heads (its dense checkpoint is the rank's compute-local state;
+ * every other call works on it as on any plan).  In addition it holds the
+ * storage-balancing map over all tp ranks, from the whole model's
+ * selection: with n_r the compute-local retained units of rank r,
+ * N = sum n_r and (q, m) = divmod(N, tp), ranks sorted by (-n_r, r) get the
+ * targets t_r = q + 1 (first m) or q; rank r keeps its first min(n_r, t_r)
+ * units; the excess units (by source rank, then local index) are paired in
+ * order with the deficit positions (by destination rank, then position);
+ * every rank's storage slot has ceil(N/tp) unit positions.
+ * Requirements: 1 <= tp, 0 <= rank < tp, n_heads divisible by tp and
+ * conv_bytes by 16 tp for every layer (DASC_EINVAL), and one unit size over
+ * all layers (DASC_EUNSUPPORTED).  A plan from dasc_plan_build is rank 0 of 1.
+ */
+int dasc_plan_build_tp(const dasc_layer_desc* layers, int32_t n_layers, double a_s,
+                       double eps, int32_t w_max, int32_t tp, int32_t rank, dasc_plan_t* out);
+
+/* This rank's balancing figures (host only). */
+int dasc_plan_tp_info(dasc_plan_t plan, dasc_tp_info* out);
+
+/* The whole map (host only; any pointer may be NULL): send_units[s*tp + d] =
+ * units rank s sends to rank d (the variable all-to-all splits), n_local[r]
+ * = n_r and target[r] = t_r.  Rank s's send row holds its excess units in
+ * its local order, which groups them by destination rank (ascending); rank
+ * d receives the group from rank s at slot unit position
+ * keep_d + sum_{s' < s} send_units[s'*tp + d].  The load runs the inverse:
+ * owners send the same slot ranges back, received in the send-row layout. */
+int dasc_plan_tp_splits(dasc_plan_t plan, int64_t* send_units, int64_t* n_local,
+                        int64_t* target);
 
 /* Totals and ratios of a plan (host only). */
 int dasc_plan_query(dasc_plan_t plan, dasc_plan_info* out);
@@ -256,6 +310,43 @@ int dasc_ckpt_refresh_suffix_windowed(dasc_plan_t plan, const uint16_t* k, const
                                       const int64_t* tok_offsets, int64_t n_tokens,
                                       void* dense_base, int64_t dense_stride, int64_t n_dense,
                                       const int32_t* dst_idx, int32_t n, void* stream);
+
+/*
+ * Store with TP storage balancing, this rank's part before the exchange
+ * ([dasc] §4.3, Appendix B.1(b): pack and partition): for i in [0, n), the
+ * rank's compute-local units of dense[src_idx[i]] in its ragged order
+ * (layer by layer, unit by unit) go to
+ *   unit j < keep:  pool[dst_slot[i]] at unit position j,
+ *   unit j >= keep: send[send_idx[i]] at unit position j - keep,
+ * and the rank's conv bytes to pool[dst_slot[i]] at slot_units * unit_bytes.
+ * Pool rows hold tp.slot_bytes (pool_stride >= it); unit positions
+ * keep .. slot_units-1 are not written (the exchange fills keep .. t_r-1).
+ * Send rows hold tp.send_bytes (send_stride >= it, 16-byte aligned) and are
+ * ignored (may be NULL) when tp.send_units == 0.  Same rules as
+ * dasc_ckpt_pack otherwise; DASC_EUNSUPPORTED if the plan is not one store.
+ */
+int dasc_ckpt_pack_tp(dasc_plan_t plan, const void* dense_base, int64_t dense_stride,
+                      int64_t n_dense, const int32_t* src_idx, void* pool_base,
+                      int64_t pool_stride, int64_t n_slots, const int32_t* dst_slot,
+                      void* send_base, int64_t send_stride, int64_t n_send,
+                      const int32_t* send_idx, int32_t n, void* stream);
+
+/*
+ * Load with TP storage balancing, this rank's part after the inverse
+ * exchange (gather and zero-fill unpack, dasc-nr, [dasc] §4.2, §4.3): for i
+ * in [0, n), dense[dst_idx[i]] <- unit j of the rank's ragged order from
+ * pool[src_slot[i]] at position j (j < keep) or from recv[recv_idx[i]] at
+ * position j - keep (j >= keep), +0.0 in every local unit, and the conv
+ * bytes stored in the slot.  Every byte of each destination is written.
+ * Receive rows as the send rows of dasc_ckpt_pack_tp (ignored when
+ * tp.send_units == 0).
+ */
+int dasc_ckpt_unpack_tp_zero_fill(dasc_plan_t plan, const void* pool_base, int64_t pool_stride,
+                                  int64_t n_slots, const int32_t* src_slot,
+                                  const void* recv_base, int64_t recv_stride, int64_t n_recv,
+                                  const int32_t* recv_idx, void* dense_base,
+                                  int64_t dense_stride, int64_t n_dense,
+                                  const int32_t* dst_idx, int32_t n, void* stream);
 
 /*
  * INT8 pack ([dasc] Appendix E.1 Eq. 10 composed with the ragged layout,

@@ -22,7 +22,7 @@ import torch  # noqa: F401
 
 __all__ = ["Plan", "DascError", "ckpt_pack", "ckpt_unpack_zero_fill",
            "ckpt_refresh_suffix", "ckpt_refresh_suffix_windowed", "ckpt_pack_int8",
-           "ckpt_unpack_int8_zero_fill",
+           "ckpt_unpack_int8_zero_fill", "ckpt_pack_tp", "ckpt_unpack_tp_zero_fill",
            "GDN", "KDA", "STATUS_BAD_INDEX",
            "STATUS_BAD_TOKENS", "LIB_PATH", "lib"]
 
@@ -67,6 +67,14 @@ class _LayerInfo(ctypes.Structure):
                 ("int8_scale_offset", _c_i64)]
 
 
+class _TpInfo(ctypes.Structure):
+    _fields_ = [("tp", _c_i32), ("rank", _c_i32), ("one_store", _c_i32), ("reserved", _c_i32),
+                ("unit_bytes", _c_i64), ("n_total", _c_i64), ("slot_units", _c_i64),
+                ("m_remote", _c_i64), ("max_local", _c_i64), ("n_local", _c_i64),
+                ("target", _c_i64), ("keep", _c_i64), ("send_units", _c_i64),
+                ("recv_units", _c_i64), ("slot_bytes", _c_i64), ("send_bytes", _c_i64)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built: run `python recurrent_state_cache_amd/_build.py`")
@@ -74,6 +82,15 @@ def _load():
     sig = {
         "dasc_plan_build": (_c_i32, [ctypes.POINTER(_LayerDesc), _c_i32, _c_f64, _c_f64, _c_i32,
                                      ctypes.POINTER(_c_p)]),
+        "dasc_plan_build_tp": (_c_i32, [ctypes.POINTER(_LayerDesc), _c_i32, _c_f64, _c_f64,
+                                        _c_i32, _c_i32, _c_i32, ctypes.POINTER(_c_p)]),
+        "dasc_plan_tp_info": (_c_i32, [_c_p, ctypes.POINTER(_TpInfo)]),
+        "dasc_plan_tp_splits": (_c_i32, [_c_p, _c_p, _c_p, _c_p]),
+        "dasc_ckpt_pack_tp": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_i64,
+                                       _c_p, _c_p, _c_i64, _c_i64, _c_p, _c_i32, _c_p]),
+        "dasc_ckpt_unpack_tp_zero_fill": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p,
+                                                   _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_i64,
+                                                   _c_p, _c_i32, _c_p]),
         "dasc_plan_query": (_c_i32, [_c_p, ctypes.POINTER(_PlanInfo)]),
         "dasc_plan_layer": (_c_i32, [_c_p, _c_i32, ctypes.POINTER(_LayerInfo)]),
         "dasc_plan_units": (_c_i32, [_c_p, _c_i32, _c_p, _c_p, _c_p]),
@@ -153,10 +170,13 @@ class Plan:
     """The static selection plan (host object owned by the library).
 
     `layers`: objects with kind (GDN / KDA), n_heads, d_k, d_v, A_log and
-    dt_bias (float32, one per unit) and conv_bytes.
+    dt_bias (float32, one per unit) and conv_bytes.  With tp > 1 the plan is
+    rank `rank`'s (its own heads) with the storage-balancing map of all tp
+    ranks.
     """
 
-    def __init__(self, layers, a_s: float = -0.3, eps: float = 1e-3, w_max: int = 16):
+    def __init__(self, layers, a_s: float = -0.3, eps: float = 1e-3, w_max: int = 16,
+                 tp: int = 1, rank: int = 0):
         descs = (_LayerDesc * len(layers))()
         keep = []
         for d, L in zip(descs, layers):
@@ -168,8 +188,13 @@ class Plan:
             d.dt_bias = D.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
             d.conv_bytes = int(L.conv_bytes)
         h = _c_p()
-        _check(lib.dasc_plan_build(descs, len(layers), float(a_s), float(eps), int(w_max),
-                                   ctypes.byref(h)), "plan_build")
+        if tp == 1 and rank == 0:
+            _check(lib.dasc_plan_build(descs, len(layers), float(a_s), float(eps), int(w_max),
+                                       ctypes.byref(h)), "plan_build")
+        else:
+            _check(lib.dasc_plan_build_tp(descs, len(layers), float(a_s), float(eps),
+                                          int(w_max), int(tp), int(rank), ctypes.byref(h)),
+                   "plan_build_tp")
         self._h = h
         self._table = None
         self.n_layers = len(layers)
@@ -179,6 +204,21 @@ class Plan:
         i = _PlanInfo()
         _check(lib.dasc_plan_query(self._h, ctypes.byref(i)), "plan_query")
         return {f: getattr(i, f) for f, _ in _PlanInfo._fields_}
+
+    def tp_info(self) -> dict:
+        i = _TpInfo()
+        _check(lib.dasc_plan_tp_info(self._h, ctypes.byref(i)), "plan_tp_info")
+        return {f: getattr(i, f) for f, _ in _TpInfo._fields_}
+
+    def tp_splits(self):
+        """(send_units [tp, tp], n_local [tp], target [tp]) int64 arrays."""
+        tp = self.tp_info()["tp"]
+        M = np.zeros((tp, tp), np.int64)
+        n = np.zeros(tp, np.int64)
+        t = np.zeros(tp, np.int64)
+        _check(lib.dasc_plan_tp_splits(self._h, M.ctypes.data, n.ctypes.data, t.ctypes.data),
+               "plan_tp_splits")
+        return M, n, t
 
     def layer(self, l: int) -> dict:
         i = _LayerInfo()
@@ -285,6 +325,52 @@ def ckpt_unpack_int8_zero_fill(plan: Plan, pool, src_slot, dense, dst_idx, strea
                                                ds, dn, _dev_ptr(dst_idx, "dst_idx", torch.int32),
                                                n, _stream_handle(stream)),
            "ckpt_unpack_int8_zero_fill")
+
+
+def _alt_rows(plan, t, name):
+    if t is None:
+        if plan.tp_info()["send_units"] > 0:
+            raise ValueError(f"{name} rows are required: this rank stores units elsewhere")
+        return ctypes.c_void_p(0), 0, 0
+    return _rows(t, name)
+
+
+def ckpt_pack_tp(plan: Plan, dense, src_idx, pool, dst_slot, send, send_idx,
+                 stream=None) -> None:
+    """Store with TP storage balancing, this rank's part: kept units and
+    conv into pool[dst_slot[i]], the rest into send[send_idx[i]]."""
+    import torch
+    dp, ds, dn = _rows(dense, "dense")
+    pp, ps, pn = _rows(pool, "pool")
+    sp, ss, sn = _alt_rows(plan, send, "send")
+    n = src_idx.numel()
+    if dst_slot.numel() != n or (send_idx is not None and send_idx.numel() != n):
+        raise ValueError("index arrays must have the same length")
+    sidx = _dev_ptr(send_idx, "send_idx", torch.int32) if send_idx is not None else None
+    _check(lib.dasc_ckpt_pack_tp(plan._h, dp, ds, dn, _dev_ptr(src_idx, "src_idx", torch.int32),
+                                 pp, ps, pn, _dev_ptr(dst_slot, "dst_slot", torch.int32),
+                                 sp, ss, sn, sidx, n, _stream_handle(stream)), "ckpt_pack_tp")
+
+
+def ckpt_unpack_tp_zero_fill(plan: Plan, pool, src_slot, recv, recv_idx, dense, dst_idx,
+                             stream=None) -> None:
+    """Load with TP storage balancing, this rank's part after the inverse
+    exchange: kept units from pool[src_slot[i]], the rest from
+    recv[recv_idx[i]], zero-fill, conv from the slot, into dense[dst_idx[i]]."""
+    import torch
+    dp, ds, dn = _rows(dense, "dense")
+    pp, ps, pn = _rows(pool, "pool")
+    rp, rs, rn = _alt_rows(plan, recv, "recv")
+    n = src_slot.numel()
+    if dst_idx.numel() != n or (recv_idx is not None and recv_idx.numel() != n):
+        raise ValueError("index arrays must have the same length")
+    ridx = _dev_ptr(recv_idx, "recv_idx", torch.int32) if recv_idx is not None else None
+    _check(lib.dasc_ckpt_unpack_tp_zero_fill(plan._h, pp, ps, pn,
+                                             _dev_ptr(src_slot, "src_slot", torch.int32),
+                                             rp, rs, rn, ridx, dp, ds, dn,
+                                             _dev_ptr(dst_idx, "dst_idx", torch.int32), n,
+                                             _stream_handle(stream)),
+           "ckpt_unpack_tp_zero_fill")
 
 
 def _refresh(fn, name, plan, k, v, a, beta, tok_off, dense, dst_idx, stream):

@@ -5,6 +5,7 @@
 //   [dasc]     "dasc: Decay-Aware State Compression for Hybrid Linear-Attention
 //              Serving" (arXiv HTML version)
 //   [dasc-sum] the picx.dev summary of dasc, "Methodology" (Eq. 6, Eq. 7)
+//   TP storage balancing: [dasc] §4.3 and Appendix B.1(b).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -73,7 +74,7 @@ struct dasc_plan {
   int64_t k_row = 0, v_row = 0, g_row = 0, b_row = 0;
 
   // host image of the device tables
-  std::vector<Piece> pack, unpack, pack_q, unpack_q;
+  std::vector<Piece> pack, unpack, pack_q, unpack_q, pack_tp, unpack_tp;
   bool int8_ok = true;          // every layer with a retained unit fits the INT8 kernels
   int64_t int8_scale_base = 0;  // INT8 slot: start of the scale block
   int64_t int8_conv_base = 0;   // INT8 slot: start of the conv bytes
@@ -82,8 +83,15 @@ struct dasc_plan {
   std::vector<Group> refresh_groups;
   int32_t kda_r_max = 0;  // largest retained-channel count of a KDA head
   bool kda_128 = true;    // every KDA layer has d_k = d_v = 128
-  int64_t off_pack = 0, off_unpack = 0, off_pack_q = 0, off_unpack_q = 0, off_refresh = 0,
-          off_expA = 0, off_dt = 0, off_status = 0, table_bytes = 0;
+  int64_t off_pack = 0, off_unpack = 0, off_pack_q = 0, off_unpack_q = 0, off_pack_tp = 0,
+          off_unpack_tp = 0, off_refresh = 0, off_expA = 0, off_dt = 0, off_status = 0,
+          table_bytes = 0;
+
+  // TP storage balancing of this rank ([dasc] Appendix B.1(b)); a plan from
+  // dasc_plan_build is rank 0 of 1 (everything kept).
+  dasc_tp_info tp{};
+  std::vector<int64_t> tp_counts;  // [tp][tp]: units rank s sends to rank d
+  std::vector<int64_t> tp_n, tp_t;  // per rank: compute-local units, target
 
   uint8_t* device = nullptr;  // caller-owned upload target
   DeviceTables dev{};
@@ -105,6 +113,72 @@ void push_range(std::vector<Piece>& out, uint64_t dense_off, uint64_t pool_off, 
     pool_off += b;
     bytes -= b;
   }
+}
+
+// [dasc] Appendix B.1(b): storage targets and the all-to-all splits for
+// compute-local unit counts n (one per rank), seen from rank `rank`.
+// Returns false if the model is not one store (units of different sizes) or
+// a send row would exceed 4 GiB.
+bool set_tp(dasc_plan* p, int32_t tp, int32_t rank, const std::vector<int64_t>& n) {
+  dasc_tp_info& T = p->tp;
+  T = dasc_tp_info{};
+  T.tp = tp;
+  T.rank = rank;
+  int64_t ub = -1;
+  bool one = true;
+  for (const auto& L : p->layers) {
+    if (ub < 0) ub = L.unit_bytes;
+    else if (L.unit_bytes != ub) one = false;
+  }
+  int64_t N = 0, nmax = 0;
+  for (int64_t x : n) {
+    N += x;
+    nmax = std::max(nmax, x);
+  }
+  const int64_t q = N / tp, m = N % tp;
+  std::vector<int32_t> order(tp);
+  for (int32_t r = 0; r < tp; ++r) order[r] = r;
+  std::sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+    return n[a] != n[b] ? n[a] > n[b] : a < b;  // (-n_r, r)
+  });
+  p->tp_n = n;
+  p->tp_t.assign(tp, q);
+  for (int64_t i = 0; i < m; ++i) p->tp_t[order[i]] = q + 1;
+  // Pair the excess list (by source rank, then local index) with the deficit
+  // list (by destination rank, then position), in order, run by run.
+  auto keep = [&](int32_t r) { return std::min(n[r], p->tp_t[r]); };
+  std::vector<int64_t> ex(tp), de(tp);
+  for (int32_t r = 0; r < tp; ++r) {
+    ex[r] = n[r] - keep(r);
+    de[r] = p->tp_t[r] - keep(r);
+  }
+  p->tp_counts.assign(int64_t(tp) * tp, 0);
+  int64_t moved = 0;
+  for (int32_t s = 0, d = 0;;) {
+    while (s < tp && ex[s] == 0) ++s;
+    while (d < tp && de[d] == 0) ++d;
+    if (s == tp || d == tp) break;
+    const int64_t c = std::min(ex[s], de[d]);
+    p->tp_counts[int64_t(s) * tp + d] += c;
+    ex[s] -= c;
+    de[d] -= c;
+    moved += c;
+  }
+  T.one_store = one && ub > 0;
+  T.unit_bytes = ub > 0 ? ub : 0;
+  T.n_total = N;
+  T.slot_units = tp ? (N + tp - 1) / tp : 0;
+  T.m_remote = moved;
+  T.max_local = nmax;
+  T.n_local = n[rank];
+  T.target = p->tp_t[rank];
+  T.keep = keep(rank);
+  T.send_units = n[rank] - T.keep;
+  T.recv_units = p->tp_t[rank] - T.keep;
+  T.slot_bytes = T.slot_units * T.unit_bytes + p->info.conv_bytes;
+  T.send_bytes = T.send_units * T.unit_bytes;
+  if (T.send_bytes > int64_t(std::numeric_limits<uint32_t>::max())) T.one_store = 0;
+  return T.one_store != 0;
 }
 
 // Turn the mask into piece lists and lay out the device tables.  Pieces
@@ -215,6 +289,54 @@ void build_tables(dasc_plan* p) {
   push_range(p->pack_q, I.temporal_dense_bytes, p->int8_conv_base, I.conv_bytes, kPieceCopy);
   push_range(p->unpack_q, I.temporal_dense_bytes, p->int8_conv_base, I.conv_bytes, kPieceCopy);
 
+  // TP storage-balancing lists: the fp32 lists with the pool side remapped.
+  // Units of the rank's ragged order below keep stay at their slot
+  // position; the rest go to the send row in order (the pairing of excess
+  // units with deficit positions is monotone, so the send row, grouped by
+  // destination rank, is exactly the ragged tail); conv moves behind the
+  // slot's slot_units unit positions.
+  if (p->tp.one_store) {
+    const uint64_t ub = p->tp.unit_bytes, keep = p->tp.keep, keep_b = keep * ub;
+    const uint64_t rag = I.temporal_rag_bytes, conv_tp = p->tp.slot_units * ub;
+    auto remap = [&](const std::vector<Piece>& in, std::vector<Piece>& out) {
+      for (Piece t : in) {
+        if (t.type == kPieceZero) {
+          out.push_back(t);
+        } else if (t.type == kPieceCopy && t.pool_off >= rag) {  // conv bytes
+          t.pool_off = t.pool_off - rag + conv_tp;
+          t.split = 1;
+          out.push_back(t);
+        } else if (t.type == kPieceCopy) {  // GDN unit bytes: split at the keep boundary
+          const uint64_t a = t.pool_off, b = t.pool_off + t.bytes;
+          if (a < keep_b) {
+            Piece u = t;
+            u.bytes = static_cast<uint32_t>(std::min(b, keep_b) - a);
+            u.split = 1;
+            out.push_back(u);
+          }
+          if (b > keep_b) {
+            Piece u = t;
+            const uint64_t a2 = std::max(a, keep_b);
+            u.dense_off = t.dense_off + (a2 - a);
+            u.pool_off = a2;
+            u.bytes = static_cast<uint32_t>(b - a2);
+            u.split = 0;
+            u.alt_off = static_cast<uint32_t>(a2 - keep_b);
+            out.push_back(u);
+          }
+        } else {  // KDA piece: units j0 .. j0 + r - 1
+          const int64_t j0 = static_cast<int64_t>(t.pool_off / ub);
+          const int64_t sp = std::min<int64_t>(std::max<int64_t>(int64_t(keep) - j0, 0), t.r);
+          t.split = static_cast<uint32_t>(sp);
+          t.alt_off = sp < t.r ? static_cast<uint32_t>((j0 + sp - int64_t(keep)) * ub) : 0u;
+          out.push_back(t);
+        }
+      }
+    };
+    remap(p->pack, p->pack_tp);
+    remap(p->unpack, p->unpack_tp);
+  }
+
   // Refresh tasks, grouped by head width and gate mode (one kernel each).
   std::vector<std::tuple<int, int, int>> rkeys;  // (d_k, d_v, gate mode)
   std::vector<std::vector<RefreshTask>> rtasks;
@@ -277,6 +399,8 @@ void build_tables(dasc_plan* p) {
   p->off_unpack = section(p->unpack.size() * sizeof(Piece));
   p->off_pack_q = section(p->pack_q.size() * sizeof(Piece));
   p->off_unpack_q = section(p->unpack_q.size() * sizeof(Piece));
+  p->off_pack_tp = section(p->pack_tp.size() * sizeof(Piece));
+  p->off_unpack_tp = section(p->unpack_tp.size() * sizeof(Piece));
   p->off_refresh = section(p->refresh.size() * sizeof(RefreshTask));
   p->off_expA = section(p->gate_expA.size() * sizeof(float));
   p->off_dt = section(p->gate_dt.size() * sizeof(float));
@@ -293,8 +417,8 @@ const char* dasc_last_error(void) { return g_error.c_str(); }
 
 const char* dasc_version(void) { return "dasc-hip 0.1 (gfx950)"; }
 
-int dasc_plan_build(const dasc_layer_desc* layers, int32_t n_layers, double a_s, double eps,
-                    int32_t w_max, dasc_plan_t* out) {
+static int plan_build_impl(const dasc_layer_desc* layers, int32_t n_layers, double a_s,
+                           double eps, int32_t w_max, dasc_plan_t* out) {
   if (!out) return fail(DASC_EINVAL, "plan_build: out is null");
   *out = nullptr;
   if (!layers || n_layers <= 0) return fail(DASC_EINVAL, "plan_build: no layers");
@@ -470,12 +594,93 @@ int dasc_plan_build(const dasc_layer_desc* layers, int32_t n_layers, double a_s,
     I.int8_scale_bytes = sc;
     I.int8_slot_bytes = p->int8_conv_base + conv;
     I.c_ckpt_int8 = static_cast<double>(I.dense_bytes) / static_cast<double>(I.int8_slot_bytes);
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return fail(DASC_ENOMEM, "plan_build: out of host memory");
+  }
+  *out = p;
+  return DASC_OK;
+}
+
+static int finish_plan(dasc_plan_t p, int32_t tp, int32_t rank, const std::vector<int64_t>& n,
+                       dasc_plan_t* out) {
+  try {
+    set_tp(p, tp, rank, n);
     build_tables(p);
   } catch (const std::bad_alloc&) {
     delete p;
     return fail(DASC_ENOMEM, "plan_build: out of host memory");
   }
   *out = p;
+  return DASC_OK;
+}
+
+int dasc_plan_build(const dasc_layer_desc* layers, int32_t n_layers, double a_s, double eps,
+                    int32_t w_max, dasc_plan_t* out) {
+  dasc_plan_t p = nullptr;
+  int rc = plan_build_impl(layers, n_layers, a_s, eps, w_max, &p);
+  if (rc != DASC_OK) return rc;
+  return finish_plan(p, 1, 0, {p->info.n_retained}, out);
+}
+
+int dasc_plan_build_tp(const dasc_layer_desc* layers, int32_t n_layers, double a_s, double eps,
+                       int32_t w_max, int32_t tp, int32_t rank, dasc_plan_t* out) {
+  if (!out) return fail(DASC_EINVAL, "plan_build_tp: out is null");
+  *out = nullptr;
+  if (tp < 1 || rank < 0 || rank >= tp) return fail(DASC_EINVAL, "plan_build_tp: need 0 <= rank < tp");
+  if (!layers || n_layers <= 0) return fail(DASC_EINVAL, "plan_build_tp: no layers");
+  for (int32_t l = 0; l < n_layers; ++l)
+    if (layers[l].n_heads % tp != 0 || layers[l].conv_bytes % (16 * int64_t(tp)) != 0)
+      return fail(DASC_EINVAL, "plan_build_tp: layer " + std::to_string(l) +
+                                   ": n_heads must divide by tp and conv_bytes by 16 tp");
+  // The whole model's selection gives every rank's compute-local unit count.
+  dasc_plan_t full = nullptr;
+  int rc = plan_build_impl(layers, n_layers, a_s, eps, w_max, &full);
+  if (rc != DASC_OK) return rc;
+  std::vector<int64_t> n(tp, 0);
+  for (const auto& L : full->layers) {
+    const int64_t per = L.kind == kGDN ? 1 : L.d_k, hr = L.n_heads / tp;
+    for (int64_t u = 0; u < L.n; ++u) n[(u / per) / hr] += L.retained[u];
+  }
+  delete full;
+  // Rank `rank` owns heads [rank H / tp, (rank + 1) H / tp) of every layer.
+  std::vector<dasc_layer_desc> mine(layers, layers + n_layers);
+  for (auto& d : mine) {
+    const int64_t per = d.kind == kGDN ? 1 : d.d_k;
+    d.n_heads /= tp;
+    d.A_log += int64_t(rank) * d.n_heads * per;
+    d.dt_bias += int64_t(rank) * d.n_heads * per;
+    d.conv_bytes /= tp;
+  }
+  dasc_plan_t p = nullptr;
+  rc = plan_build_impl(mine.data(), n_layers, a_s, eps, w_max, &p);
+  if (rc != DASC_OK) return rc;
+  if (p->info.n_retained != n[rank]) {
+    delete p;
+    return fail(DASC_EINVAL, "plan_build_tp: inconsistent rank selection");
+  }
+  rc = finish_plan(p, tp, rank, n, out);
+  if (rc != DASC_OK) return rc;
+  if (!(*out)->tp.one_store) {
+    delete *out;
+    *out = nullptr;
+    return fail(DASC_EUNSUPPORTED, "plan_build_tp: balancing needs one unit size across layers");
+  }
+  return DASC_OK;
+}
+
+int dasc_plan_tp_info(dasc_plan_t p, dasc_tp_info* out) {
+  if (!p || !out) return fail(DASC_EINVAL, "plan_tp_info: null argument");
+  *out = p->tp;
+  return DASC_OK;
+}
+
+int dasc_plan_tp_splits(dasc_plan_t p, int64_t* send_units, int64_t* n_local, int64_t* target) {
+  if (!p) return fail(DASC_EINVAL, "plan_tp_splits: null plan");
+  const size_t tp = static_cast<size_t>(p->tp.tp);
+  if (send_units) std::memcpy(send_units, p->tp_counts.data(), tp * tp * sizeof(int64_t));
+  if (n_local) std::memcpy(n_local, p->tp_n.data(), tp * sizeof(int64_t));
+  if (target) std::memcpy(target, p->tp_t.data(), tp * sizeof(int64_t));
   return DASC_OK;
 }
 
@@ -560,6 +765,8 @@ int dasc_plan_upload(dasc_plan_t p, void* device_buffer, int64_t bytes, void* st
   put(p->off_unpack, p->unpack.data(), p->unpack.size() * sizeof(Piece));
   put(p->off_pack_q, p->pack_q.data(), p->pack_q.size() * sizeof(Piece));
   put(p->off_unpack_q, p->unpack_q.data(), p->unpack_q.size() * sizeof(Piece));
+  put(p->off_pack_tp, p->pack_tp.data(), p->pack_tp.size() * sizeof(Piece));
+  put(p->off_unpack_tp, p->unpack_tp.data(), p->unpack_tp.size() * sizeof(Piece));
   put(p->off_refresh, p->refresh.data(), p->refresh.size() * sizeof(RefreshTask));
   put(p->off_expA, p->gate_expA.data(), p->gate_expA.size() * sizeof(float));
   put(p->off_dt, p->gate_dt.data(), p->gate_dt.size() * sizeof(float));
@@ -573,6 +780,8 @@ int dasc_plan_upload(dasc_plan_t p, void* device_buffer, int64_t bytes, void* st
   p->dev.unpack = reinterpret_cast<const Piece*>(d + p->off_unpack);
   p->dev.pack_q = reinterpret_cast<const Piece*>(d + p->off_pack_q);
   p->dev.unpack_q = reinterpret_cast<const Piece*>(d + p->off_unpack_q);
+  p->dev.pack_tp = reinterpret_cast<const Piece*>(d + p->off_pack_tp);
+  p->dev.unpack_tp = reinterpret_cast<const Piece*>(d + p->off_unpack_tp);
   p->dev.refresh = reinterpret_cast<const RefreshTask*>(d + p->off_refresh);
   p->dev.gate_expA = reinterpret_cast<const float*>(d + p->off_expA);
   p->dev.gate_dt = reinterpret_cast<const float*>(d + p->off_dt);
@@ -616,7 +825,8 @@ bool overlap(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
 // Common checks of pack and unpack; `what` names the call in messages.
 int check_move(const dasc_plan* p, const char* what, const void* dense, int64_t dense_stride,
                int64_t n_dense, const void* pool, int64_t pool_stride, int64_t n_slots,
-               const void* idx_a, const void* idx_b, int32_t n, bool int8 = false) {
+               const void* idx_a, const void* idx_b, int32_t n, bool int8 = false,
+               int64_t slot_override = 0) {
   const std::string w(what);
   if (!p) return fail(DASC_EINVAL, w + ": null plan");
   if (!p->device) return fail(DASC_ENOTUPLOADED, w + ": plan tables not uploaded");
@@ -626,7 +836,8 @@ int check_move(const dasc_plan* p, const char* what, const void* dense, int64_t 
   if (!aligned16(dense) || !aligned16(pool)) return fail(DASC_EINVAL, w + ": bases must be 16-byte aligned");
   if (dense_stride < p->info.dense_bytes || dense_stride % 16)
     return fail(DASC_EINVAL, w + ": dense_stride must be >= dense_bytes and a multiple of 16");
-  const int64_t slot_bytes = int8 ? p->info.int8_slot_bytes : p->info.slot_bytes;
+  const int64_t slot_bytes = slot_override ? slot_override
+                            : int8 ? p->info.int8_slot_bytes : p->info.slot_bytes;
   if (pool_stride < slot_bytes || pool_stride % 16)
     return fail(DASC_EINVAL, w + ": pool_stride must be >= the slot bytes and a multiple of 16");
   if (n_dense <= 0 || n_slots <= 0) return fail(DASC_EINVAL, w + ": n_dense and n_slots must be > 0");
@@ -722,6 +933,76 @@ int dasc_ckpt_unpack_int8_zero_fill(dasc_plan_t p, const void* pool_base, int64_
   if (e) return fail(DASC_EHIP, std::string("ckpt_unpack_int8_zero_fill: launch failed: ") +
                                     hipGetErrorString(static_cast<hipError_t>(e)));
   return DASC_OK;
+}
+
+// TP pack / unpack: the remapped lists, with the send (pack) or receive
+// (unpack) rows as the second row of each pair.
+static int run_move_tp(const char* w, dasc_plan_t p, bool pack, const void* dense,
+                       int64_t dense_stride, int64_t n_dense, const int32_t* dense_idx,
+                       const void* pool, int64_t pool_stride, int64_t n_slots,
+                       const int32_t* slot_idx, const void* alt, int64_t alt_stride,
+                       int64_t n_alt, const int32_t* alt_idx, int32_t n, void* stream) {
+  const std::string what(w);
+  if (p && !p->tp.one_store)
+    return fail(DASC_EUNSUPPORTED, what + ": balancing needs one unit size across layers");
+  int rc = check_move(p, w, dense, dense_stride, n_dense, pool, pool_stride, n_slots,
+                      dense_idx, slot_idx, n, false, p ? p->tp.slot_bytes : 0);
+  if (rc != DASC_OK || n == 0) return rc;
+  const bool use_alt = p->tp.send_units > 0;
+  if (use_alt) {
+    if (!alt || !alt_idx) return fail(DASC_EINVAL, what + ": null send / receive rows");
+    if (!aligned16(alt) || alt_stride < p->tp.send_bytes || alt_stride % 16 || n_alt <= 0)
+      return fail(DASC_EINVAL, what + ": send / receive rows misaligned or too small");
+    if (overlap(alt, alt_stride * n_alt, dense, dense_stride * n_dense) ||
+        overlap(alt, alt_stride * n_alt, pool, pool_stride * n_slots))
+      return fail(DASC_EINVAL, what + ": send / receive rows overlap dense or pool");
+  }
+  MoveArgs m{};
+  m.pieces = pack ? p->dev.pack_tp : p->dev.unpack_tp;
+  m.n_pieces = static_cast<uint32_t>((pack ? p->pack_tp : p->unpack_tp).size());
+  m.kda_r_max = p->kda_r_max;
+  m.kda_128 = p->kda_128;
+  m.src_idx = pack ? dense_idx : slot_idx;
+  m.dst_idx = pack ? slot_idx : dense_idx;
+  m.src_base = static_cast<const uint8_t*>(pack ? dense : pool);
+  m.src_stride = pack ? dense_stride : pool_stride;
+  m.n_src = pack ? n_dense : n_slots;
+  m.dst_base = static_cast<uint8_t*>(const_cast<void*>(pack ? pool : dense));
+  m.dst_stride = pack ? pool_stride : dense_stride;
+  m.n_dst = pack ? n_slots : n_dense;
+  m.n = n;
+  m.status = p->dev.status;
+  if (use_alt) {
+    m.alt_base = static_cast<uint8_t*>(const_cast<void*>(alt));
+    m.alt_stride = alt_stride;
+    m.n_alt = n_alt;
+    m.alt_idx = alt_idx;
+  }
+  int e = launch_move(pack, m, stream);
+  if (e) return fail(DASC_EHIP, what + ": launch failed: " +
+                                    hipGetErrorString(static_cast<hipError_t>(e)));
+  return DASC_OK;
+}
+
+int dasc_ckpt_pack_tp(dasc_plan_t p, const void* dense_base, int64_t dense_stride,
+                      int64_t n_dense, const int32_t* src_idx, void* pool_base,
+                      int64_t pool_stride, int64_t n_slots, const int32_t* dst_slot,
+                      void* send_base, int64_t send_stride, int64_t n_send,
+                      const int32_t* send_idx, int32_t n, void* stream) {
+  return run_move_tp("ckpt_pack_tp", p, true, dense_base, dense_stride, n_dense, src_idx,
+                     pool_base, pool_stride, n_slots, dst_slot, send_base, send_stride, n_send,
+                     send_idx, n, stream);
+}
+
+int dasc_ckpt_unpack_tp_zero_fill(dasc_plan_t p, const void* pool_base, int64_t pool_stride,
+                                  int64_t n_slots, const int32_t* src_slot,
+                                  const void* recv_base, int64_t recv_stride, int64_t n_recv,
+                                  const int32_t* recv_idx, void* dense_base,
+                                  int64_t dense_stride, int64_t n_dense,
+                                  const int32_t* dst_idx, int32_t n, void* stream) {
+  return run_move_tp("ckpt_unpack_tp_zero_fill", p, false, dense_base, dense_stride, n_dense,
+                     dst_idx, pool_base, pool_stride, n_slots, src_slot, recv_base, recv_stride,
+                     n_recv, recv_idx, n, stream);
 }
 
 static int run_refresh(const char* w, bool head_windows, dasc_plan_t p, const uint16_t* k,

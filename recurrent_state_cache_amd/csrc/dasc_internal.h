@@ -47,7 +47,13 @@ struct alignas(64) Piece {
   uint16_t rb, r;      // row block (rows kKdaRows rb ..), retained channels
   uint32_t mask[4];    // KDA: bit k set = channel k retained
   uint64_t scale_off;  // INT8 pieces: byte offset of the first fp32 scale in a slot
-  uint32_t pad[2];
+  // TP storage balancing (pieces of the pack_tp / unpack_tp lists): units
+  // j < split of a KDA piece live in the storage slot at pool_off + j unit;
+  // units j >= split live in the rank's send / receive row at
+  // alt_off + (j - split) unit.  A copy piece lies wholly on one side:
+  // split = 1 (slot, pool_off) or 0 (send / receive row, alt_off).
+  uint32_t split;
+  uint32_t alt_off;
 };
 
 // One (layer, head) that a bounded-suffix refresh replays.
@@ -73,6 +79,8 @@ struct DeviceTables {
   const Piece* unpack;
   const Piece* pack_q;     // INT8 pack
   const Piece* unpack_q;   // INT8 unpack
+  const Piece* pack_tp;    // TP storage balancing: pack and partition
+  const Piece* unpack_tp;  // ... and the gather of a load
   const RefreshTask* refresh;
   const float* gate_expA;  // exp(A_log) per unit, fp32
   const float* gate_dt;    // dt_bias per unit, fp32
@@ -109,6 +117,11 @@ struct MoveArgs {
   int64_t dst_stride, n_dst;
   int32_t n;
   uint32_t* status;
+  // Second row per pair for TP pieces with split < r: the send row (pack) or
+  // the receive row (unpack).  alt_base == nullptr: no such pieces.
+  uint8_t* alt_base;
+  int64_t alt_stride, n_alt;
+  const int32_t* alt_idx;
 };
 
 // Kernel launchers (dasc_kernels.hip).  They return a hipError_t value.

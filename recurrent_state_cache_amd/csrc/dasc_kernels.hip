@@ -79,9 +79,21 @@ __device__ __forceinline__ void lane_ranks(const Piece& t, int kg, uint32_t& bit
   bits4 = (mw >> sh) & 0xFu;
 }
 
-template <bool kPack, int DK, int DV>
+// Address of unit segment j of a KDA piece on the pool side: the slot row,
+// or (TP pieces, j >= split) the send / receive row.
+template <bool kAlt>
+__device__ __forceinline__ float* unit_seg(const Piece& t, uint8_t* row, uint8_t* alt, int j,
+                                           int dv) {
+  if constexpr (kAlt) {
+    if (j >= static_cast<int>(t.split))
+      return reinterpret_cast<float*>(alt + t.alt_off) + (j - static_cast<int>(t.split)) * dv;
+  }
+  return reinterpret_cast<float*>(row + t.pool_off) + j * dv;
+}
+
+template <bool kPack, int DK, int DV, bool kAlt>
 __device__ __forceinline__ void kda_piece(const Piece& t, const uint8_t* src, uint8_t* dst,
-                                          float* U) {
+                                          uint8_t* alt, float* U) {
   const int dk = DK ? DK : t.d_k;
   const int dv = DV ? DV : t.d_v;
   const int KG = dk / 4, VG = dv / 4;
@@ -110,20 +122,21 @@ __device__ __forceinline__ void kda_piece(const Piece& t, const uint8_t* src, ui
       }
     }
     __syncthreads();
-    float* P = reinterpret_cast<float*>(dst + t.pool_off) + kKdaRows * rb;
     for (int q = tid; q < 8 * r; q += kThreads) {
       const int j = q / 8, g = q % 8;
       if (g < nseg)
         st_stream(*reinterpret_cast<const f32x4*>(&U[j * kKdaLdsRow + 4 * g]),
-                  reinterpret_cast<f32x4*>(P + j * dv + 4 * g));
+                  reinterpret_cast<f32x4*>(unit_seg<kAlt>(t, dst, alt, j, dv) +
+                                           kKdaRows * rb + 4 * g));
     }
   } else {
-    const float* P = reinterpret_cast<const float*>(src + t.pool_off) + kKdaRows * rb;
     for (int q = tid; q < 8 * r; q += kThreads) {
       const int j = q / 8, g = q % 8;
       if (g < nseg)
         *reinterpret_cast<f32x4*>(&U[j * kKdaLdsRow + 4 * g]) =
-            ld_stream(reinterpret_cast<const f32x4*>(P + j * dv + 4 * g));
+            ld_stream(reinterpret_cast<const f32x4*>(
+                unit_seg<kAlt>(t, const_cast<uint8_t*>(src), alt, j, dv) + kKdaRows * rb +
+                4 * g));
     }
     __syncthreads();
     if (mine) {
@@ -147,12 +160,21 @@ __device__ __forceinline__ void kda_piece(const Piece& t, const uint8_t* src, ui
   }
 }
 
-template <bool kPack>
-__device__ __forceinline__ void copy_piece(const Piece& t, const uint8_t* src, uint8_t* dst) {
+template <bool kPack, bool kAlt = false>
+__device__ __forceinline__ void copy_piece(const Piece& t, const uint8_t* src, uint8_t* dst,
+                                           uint8_t* alt = nullptr) {
   const uint32_t tid = threadIdx.x;
   if (tid >= (t.bytes >> 4)) return;
-  const uint64_t src_off = kPack ? t.dense_off : t.pool_off;
-  const uint64_t dst_off = kPack ? t.pool_off : t.dense_off;
+  uint64_t pool_off = t.pool_off;
+  if constexpr (kAlt) {
+    if (t.split == 0 && t.type == kPieceCopy) {  // the unit lives in the send / receive row
+      pool_off = t.alt_off;
+      if (kPack) dst = alt;
+      else src = alt;
+    }
+  }
+  const uint64_t src_off = kPack ? t.dense_off : pool_off;
+  const uint64_t dst_off = kPack ? pool_off : t.dense_off;
   u32x4* d = reinterpret_cast<u32x4*>(dst + dst_off) + tid;
   if (!kPack && t.type == kPieceZero) {
     st_stream(u32x4{0u, 0u, 0u, 0u}, d);
@@ -161,23 +183,28 @@ __device__ __forceinline__ void copy_piece(const Piece& t, const uint8_t* src, u
   }
 }
 
-template <bool kPack, int DK, int DV>
+// kAlt: the TP storage-balancing lists, whose pieces may address a second
+// row per pair (the send row of a pack, the receive row of an unpack).
+template <bool kPack, int DK, int DV, bool kAlt>
 __global__ void __launch_bounds__(kThreads) move_kernel(MoveArgs a) {
   extern __shared__ __attribute__((aligned(16))) float U[];
   const Piece t = a.pieces[blockIdx.x];
   const int64_t s = a.src_idx[blockIdx.y];
   const int64_t d = a.dst_idx[blockIdx.y];
-  const bool bad_idx = !in_range(s, a.n_src) || !in_range(d, a.n_dst);
+  const int64_t x = kAlt ? a.alt_idx[blockIdx.y] : 0;
+  const bool bad_idx = !in_range(s, a.n_src) || !in_range(d, a.n_dst) ||
+                       (kAlt && !in_range(x, a.n_alt));
   if (bad_idx | (t.type > kPieceKda)) {
     if (bad_idx && blockIdx.x == 0 && threadIdx.x == 0) flag(a.status, DASC_STATUS_BAD_INDEX);
     return;
   }
   const uint8_t* src = a.src_base + s * a.src_stride;
   uint8_t* dst = a.dst_base + d * a.dst_stride;
+  uint8_t* alt = kAlt ? a.alt_base + x * a.alt_stride : nullptr;
   if (t.type == kPieceKda)  // uniform per workgroup
-    kda_piece<kPack, DK, DV>(t, src, dst, U);
+    kda_piece<kPack, DK, DV, kAlt>(t, src, dst, alt, U);
   else
-    copy_piece<kPack>(t, src, dst);
+    copy_piece<kPack, kAlt>(t, src, dst, alt);
 }
 
 // ---------------------------------------------------------------------------
@@ -773,12 +800,24 @@ int launch_move(bool pack, const MoveArgs& args, void* stream) {
   const size_t lds = static_cast<size_t>(args.kda_r_max) * kKdaLdsRow * sizeof(float);  // <= 18 KiB
   dim3 grid(args.n_pieces, static_cast<uint32_t>(args.n));
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool alt = args.alt_base != nullptr;
+  if (alt && !args.alt_idx) return static_cast<int>(hipErrorInvalidValue);
   if (pack) {
-    if (args.kda_128) move_kernel<true, 128, 128><<<grid, kThreads, lds, s>>>(args);
-    else move_kernel<true, 0, 0><<<grid, kThreads, lds, s>>>(args);
+    if (alt) {
+      if (args.kda_128) move_kernel<true, 128, 128, true><<<grid, kThreads, lds, s>>>(args);
+      else move_kernel<true, 0, 0, true><<<grid, kThreads, lds, s>>>(args);
+    } else {
+      if (args.kda_128) move_kernel<true, 128, 128, false><<<grid, kThreads, lds, s>>>(args);
+      else move_kernel<true, 0, 0, false><<<grid, kThreads, lds, s>>>(args);
+    }
   } else {
-    if (args.kda_128) move_kernel<false, 128, 128><<<grid, kThreads, lds, s>>>(args);
-    else move_kernel<false, 0, 0><<<grid, kThreads, lds, s>>>(args);
+    if (alt) {
+      if (args.kda_128) move_kernel<false, 128, 128, true><<<grid, kThreads, lds, s>>>(args);
+      else move_kernel<false, 0, 0, true><<<grid, kThreads, lds, s>>>(args);
+    } else {
+      if (args.kda_128) move_kernel<false, 128, 128, false><<<grid, kThreads, lds, s>>>(args);
+      else move_kernel<false, 0, 0, false><<<grid, kThreads, lds, s>>>(args);
+    }
   }
   return static_cast<int>(hipGetLastError());
 }

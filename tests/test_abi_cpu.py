@@ -25,7 +25,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 21
     out = subprocess.run(["nm", "-D", "--defined-only", R.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\b[TW]\s+(dasc_[a-z0-9_]+)\b", out))
@@ -173,3 +173,66 @@ def test_refresh_rows_reported():
     info = R.Plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max).info()
     assert info["k_row"] == 27 * 32 * 128 and info["v_row"] == 27 * 32 * 128
     assert info["gate_row"] == 14 * 32 + 13 * 32 * 128 and info["beta_row"] == 27 * 32
+
+
+def _tp_compare(cfg_layers, a_s, eps, w_max, tp):
+    orac = oracle.rank_plans(cfg_layers, tp, a_s, eps, w_max)
+    b = oracle.plans_balance(orac)
+    for rank in range(tp):
+        P = R.Plan(cfg_layers, a_s, eps, w_max, tp=tp, rank=rank)
+        O = orac[rank]
+        ti = P.tp_info()
+        M, n, t = P.tp_splits()
+        assert n.tolist() == b.n and t.tolist() == b.t
+        assert np.array_equal(M, b.send_units())
+        ub = O.layers[0].unit_bytes
+        assert (ti["tp"], ti["rank"], ti["one_store"]) == (tp, rank, 1)
+        assert ti["unit_bytes"] == ub and ti["n_total"] == b.N
+        assert ti["slot_units"] == b.slot_units and ti["m_remote"] == b.M_remote
+        assert ti["max_local"] == max(b.n) and ti["n_local"] == b.n[rank]
+        assert ti["target"] == b.t[rank] and ti["keep"] == b.keep[rank]
+        assert ti["send_units"] == b.n[rank] - b.keep[rank]
+        assert ti["recv_units"] == b.t[rank] - b.keep[rank]
+        assert ti["slot_bytes"] == oracle.slot_bytes_tp(O, b)
+        assert ti["send_bytes"] == oracle.send_bytes_tp(O, b, rank)
+        # the rank's own plan is the plan of its heads
+        info = P.info()
+        assert info["dense_bytes"] == O.dense_bytes and info["slot_bytes"] == O.slot_bytes
+        for l, L in enumerate(O.layers):
+            assert np.array_equal(P.units(l)[0].astype(bool), L.retained)
+    return b
+
+
+@pytest.mark.parametrize("tp", [1, 2, 4, 8])
+def test_tp_balance_matches_oracle_kda(tp):
+    cfg = W.kda()
+    b = _tp_compare(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max, tp)
+    assert b.slot_units == math.ceil(b.N / tp)
+
+
+@pytest.mark.parametrize("tp", [2, 8])
+def test_tp_balance_matches_oracle_gdn(tp):
+    cfg = W.gdn()
+    b = _tp_compare(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max, tp)
+    if tp == 8:
+        assert b.M_remote > 0          # head-wise selection leaves ranks uneven
+
+
+def test_plain_plan_is_rank_zero_of_one():
+    cfg = W.tiny_kda()
+    P = R.Plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max)
+    ti = P.tp_info()
+    assert (ti["tp"], ti["rank"], ti["keep"], ti["send_units"]) == (1, 0, ti["n_local"], 0)
+    assert ti["slot_bytes"] == P.info()["slot_bytes"]
+
+
+def test_tp_build_rejects():
+    cfg = W.tiny_kda()                  # 4 heads
+    with pytest.raises(R.DascError):
+        R.Plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max, tp=3, rank=0)
+    with pytest.raises(R.DascError):
+        R.Plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max, tp=2, rank=2)
+    mixed = W.mixed(n_ckpt=4, n_req=4)  # GDN and KDA units differ in size
+    with pytest.raises(R.DascError) as e:
+        R.Plan(mixed.layers, mixed.a_s, mixed.eps, mixed.w_max, tp=2, rank=0)
+    assert e.value.code == -5
