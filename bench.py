@@ -119,6 +119,66 @@ def _windowed_work(P, Wn):
     return flops, head_tokens
 
 
+def _bench_tp(cfg, args, stream):
+    """Store and load with TP storage balancing at TP = 8, all eight ranks'
+    shares on this GPU (one launch per rank and direction): pack / partition
+    of the checkpoints into slot and send rows, and the gather / zero-fill
+    unpack from slot and receive rows.  The exchange between ranks is not
+    timed (one GPU); its volume is reported."""
+    import numpy as np
+    import torch
+    import recurrent_state_cache_amd as R
+    import workloads as W
+    tp, n = 8, cfg.n_ckpt
+    plans = [R.Plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max, tp=tp, rank=r).upload()
+             for r in range(tp)]
+    infos = [p.tp_info() for p in plans]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed + 101)
+    dense = [torch.randint(0, 256, (n, p.info()["dense_bytes"]), generator=g, dtype=torch.uint8,
+                           device="cuda") for p in plans]
+    pools = [torch.empty((n, i["slot_bytes"]), dtype=torch.uint8, device="cuda") for i in infos]
+    rows = [torch.empty((n, max(16, i["send_bytes"])), dtype=torch.uint8, device="cuda")
+            for i in infos]
+    out = [torch.empty_like(d) for d in dense]
+    idx = torch.arange(n, dtype=torch.int32, device="cuda")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.warmup + args.steps):
+        e = ev[i - args.warmup] if i >= args.warmup else None
+        if e: e[0].record(stream)
+        for r, p in enumerate(plans):
+            R.ckpt_pack_tp(p, dense[r], idx, pools[r], idx, rows[r], idx, stream)
+        if e: e[1].record(stream)
+        for r, p in enumerate(plans):
+            R.ckpt_unpack_tp_zero_fill(p, pools[r], idx, rows[r], idx, out[r], idx, stream)
+        if e: e[2].record(stream)
+    torch.cuda.synchronize()
+    assert all(p.status() == 0 for p in plans)
+    t_pack = np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
+    t_unpack = np.mean([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
+    moved = 0
+    for p in plans:
+        pk, upk, _, _ = _algorithmic_bytes(p)
+        moved += n * (pk + upk)
+    ub, conv = infos[0]["unit_bytes"], plans[0].info()["conv_bytes"]
+    slot_off = infos[0]["max_local"] * ub + conv      # worst rank's slot without balancing
+    slot_on = infos[0]["slot_units"] * ub + conv
+    return {
+        "tp": tp,
+        "n_local": [i["n_local"] for i in infos],
+        "slot_units": infos[0]["slot_units"],
+        "m_remote_units": infos[0]["m_remote"],
+        "exchange_bytes_per_checkpoint": infos[0]["m_remote"] * ub,
+        "worst_rank_slot_bytes_off": slot_off,
+        "worst_rank_slot_bytes_balanced": slot_on,
+        "slot_capacity_gain": round(slot_off / slot_on, 4),
+        "pack_tp_ms": round(t_pack * 1e3, 4),
+        "unpack_tp_ms": round(t_unpack * 1e3, 4),
+        "pack_unpack_gbs": round(moved / (t_pack + t_unpack) / 1e9, 2),
+        "kernel": "move_kernel<*, kAlt> (8 launches per direction)",
+    }
+
+
 def _calibrate_copy(steps):
     import torch
     n = 1 << 30
@@ -383,6 +443,8 @@ def main():
     t_win = np.array([e[0].elapsed_time(e[1]) for e in evw]) * 1e-3
     win_flops, win_head_tokens = _windowed_work(P, Wn)
 
+    tp8 = _bench_tp(cfg, args, stream) if args.workload in ("kda", "gdn") else None
+
     t_pack = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
     t_unpack = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
     t_ref = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
@@ -435,6 +497,7 @@ def main():
             "unpack": {k: v for k, v in hbm("unpack_int8", n * unpack_qb, t_unpack_q.mean()).items() if k != "kernel"}
                       | {"kernel": "qmove_kernel<false>"},
         },
+        **({"tp8_storage_balancing": tp8} if tp8 else {}),
         "refresh_eq7_windows": {
             "kernel": "refresh_kernel<128> (per-head window)",
             "ms": round(t_win.mean() * 1e3, 4),
