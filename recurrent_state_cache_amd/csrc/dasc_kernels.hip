@@ -455,6 +455,7 @@ constexpr int kC = 16;  // tokens per chunk (the MFMA tile edge)
 template <int D>
 struct RefreshShape {
   static constexpr int kKT = D / 16;                  // k tiles
+  static constexpr bool kSplit = D >= 64;             // big products on split bf16 MFMA
   static constexpr int kVTW = D >= 32 ? 2 : 1;        // v tiles per wave
   static constexpr int kNW = (D / 16) / kVTW;         // waves per head
   static constexpr int kNT = 64 * kNW;                // threads
@@ -463,19 +464,51 @@ struct RefreshShape {
   static_assert(2 * D <= kNT, "one staged item per lane");
 };
 
+// Q and W in fp32 (d = 16) or as bf16 hi / lo pairs (the split products).
+template <int D, bool SPLIT>
+struct RefreshQW {
+  float Q[kC][D + 4];         // gamma_t o k_t
+  float W[2][D][kC + 4];      // k_s o D_{15,s}, [k][s], by chunk parity
+};
+template <int D>
+struct RefreshQW<D, true> {
+  uint16_t Qh[kC][D + 16];    // gamma_t o k_t: bf16 hi, then lo (rows padded to
+  uint16_t Ql[kC][D + 16];    // 8 banks mod 64, so an A-operand read is 2 passes)
+  uint16_t Wh[2][D][kC];      // k_s o D_{15,s}, [k][s]: bf16 hi and lo, by
+  uint16_t Wl[2][D][kC];      // chunk parity
+};
+
 template <int D>
 struct alignas(16) RefreshLds {
   float K[kC][D];             // k of the chunk being prepared
   float A[kC][D];             // its decays
   float V[2][kC][D];          // v, by chunk parity
   float B[2][kC];             // beta, by chunk parity
-  float Q[kC][D + 4];         // gamma_t o k_t
-  float W[2][D][kC + 4];      // k_s o D_{15,s}, [k][s], by chunk parity
+  RefreshQW<D, RefreshShape<D>::kSplit> qw;
   float G[2][2][D];           // gamma_15 by chunk parity ([.][1][.] is scratch)
   float L[kC][kC + 4];        // beta_t M_{t,s}, s < t
   float T[kC][kC + 4];        // (I + L)^-1
   float sink[2 * D];          // target of the stores of lanes that hold no result
 };
+
+// Split of an fp32 value into bf16 hi + lo (hi = x truncated to bf16, lo =
+// the remainder x - hi, exact in fp32, truncated to bf16): x = hi + lo to a
+// relative 2^-16.  A product of two split values is taken as
+// hi hi + hi lo + lo hi on bf16 MFMA with fp32 accumulation; the dropped
+// lo lo term and the truncations are below 2^-15 of each product term.
+__device__ __forceinline__ uint32_t hi_bits(float x) { return __float_as_uint(x) & 0xFFFF0000u; }
+__device__ __forceinline__ uint32_t lo_bits(float x) {
+  return __float_as_uint(x - __uint_as_float(hi_bits(x)));
+}
+// Two bf16 (the upper halves of a and b) in one word: a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ v4f mfma_bf16(u32x4 a, u32x4 b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a),
+                                                 __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -657,15 +690,47 @@ refresh_kernel(RefreshArgs a) {
       const int j = tid % D;
       const bool fwd = tid < D;
       float gm = 1.f;
+      if constexpr (Sh::kSplit) {
+        float qw[kC];  // step i: token i (forward) or token 15 - i (backward)
 #pragma unroll
-      for (int i = 0; i < kC; ++i) {
-        const int t = fwd ? i : kC - 1 - i;
-        const float al = sh.A[t][j], kv = sh.K[t][j];
-        const float before = gm * kv;  // backward: k_s o D_{15,s}
-        gm *= al;
-        const float after = gm * kv;   // forward: gamma_t o k_t
-        float* const at = fwd ? &sh.Q[t][j] : &sh.W[vb][j][t];
-        *at = fwd ? after : before;
+        for (int i = 0; i < kC; ++i) {
+          const int t = fwd ? i : kC - 1 - i;
+          const float al = sh.A[t][j], kv = sh.K[t][j];
+          const float before = gm * kv;  // backward: k_s o D_{15,s}
+          gm *= al;
+          qw[i] = fwd ? gm * kv : before;  // forward: gamma_t o k_t
+        }
+        if (fwd) {
+#pragma unroll
+          for (int t = 0; t < kC; ++t) {
+            sh.qw.Qh[t][j] = static_cast<uint16_t>(hi_bits(qw[t]) >> 16);
+            sh.qw.Ql[t][j] = static_cast<uint16_t>(lo_bits(qw[t]) >> 16);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < kC / 8; ++q) {
+            u32x4 h, l;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float w0 = qw[kC - 1 - (8 * q + 2 * e)], w1 = qw[kC - 2 - (8 * q + 2 * e)];
+              h[e] = pack_bf16(hi_bits(w0), hi_bits(w1));
+              l[e] = pack_bf16(lo_bits(w0), lo_bits(w1));
+            }
+            *reinterpret_cast<u32x4*>(&sh.qw.Wh[vb][j][8 * q]) = h;
+            *reinterpret_cast<u32x4*>(&sh.qw.Wl[vb][j][8 * q]) = l;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kC; ++i) {
+          const int t = fwd ? i : kC - 1 - i;
+          const float al = sh.A[t][j], kv = sh.K[t][j];
+          const float before = gm * kv;  // backward: k_s o D_{15,s}
+          gm *= al;
+          const float after = gm * kv;   // forward: gamma_t o k_t
+          float* const at = fwd ? &sh.qw.Q[t][j] : &sh.qw.W[vb][j][t];
+          *at = fwd ? after : before;
+        }
       }
       sh.G[vb][fwd ? 0 : 1][j] = gm;
     }
@@ -713,13 +778,42 @@ refresh_kernel(RefreshArgs a) {
       v4f U[VTW];
 #pragma unroll
       for (int vv = 0; vv < VTW; ++vv) U[vv] = v4f{0.f, 0.f, 0.f, 0.f};
+      if constexpr (Sh::kSplit) {
+        // K slots of lane group g: 4 g + e of k tile 2p (e < 4), then of
+        // tile 2p + 1, on both operands.
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const v4f qa = *reinterpret_cast<const v4f*>(&sh.Q[m][16 * kt + 4 * g]);
+        for (int kp = 0; kp < KT / 2; ++kp) {
+          const uint32_t* qh0 = reinterpret_cast<const uint32_t*>(&sh.qw.Qh[m][32 * kp + 4 * g]);
+          const uint32_t* qh1 = reinterpret_cast<const uint32_t*>(&sh.qw.Qh[m][32 * kp + 16 + 4 * g]);
+          const uint32_t* ql0 = reinterpret_cast<const uint32_t*>(&sh.qw.Ql[m][32 * kp + 4 * g]);
+          const uint32_t* ql1 = reinterpret_cast<const uint32_t*>(&sh.qw.Ql[m][32 * kp + 16 + 4 * g]);
+          const u32x4 ah = {qh0[0], qh0[1], qh1[0], qh1[1]};
+          const u32x4 al = {ql0[0], ql0[1], ql1[0], ql1[1]};
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+          for (int vv = 0; vv < VTW; ++vv) {
+            const v4f x0 = acc[2 * kp][vv], x1 = acc[2 * kp + 1][vv];
+            const u32x4 bh = {pack_bf16(hi_bits(x0[0]), hi_bits(x0[1])),
+                              pack_bf16(hi_bits(x0[2]), hi_bits(x0[3])),
+                              pack_bf16(hi_bits(x1[0]), hi_bits(x1[1])),
+                              pack_bf16(hi_bits(x1[2]), hi_bits(x1[3]))};
+            const u32x4 bl = {pack_bf16(lo_bits(x0[0]), lo_bits(x0[1])),
+                              pack_bf16(lo_bits(x0[2]), lo_bits(x0[3])),
+                              pack_bf16(lo_bits(x1[0]), lo_bits(x1[1])),
+                              pack_bf16(lo_bits(x1[2]), lo_bits(x1[3]))};
+            U[vv] = mfma_bf16(ah, bh, U[vv]);
+            U[vv] = mfma_bf16(ah, bl, U[vv]);
+            U[vv] = mfma_bf16(al, bh, U[vv]);
+          }
+        }
+      } else {
 #pragma unroll
-          for (int vv = 0; vv < VTW; ++vv) U[vv] = mfma4(qa[r], acc[kt][vv][r], U[vv]);
+        for (int kt = 0; kt < KT; ++kt) {
+          const v4f qa = *reinterpret_cast<const v4f*>(&sh.qw.Q[m][16 * kt + 4 * g]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int vv = 0; vv < VTW; ++vv) U[vv] = mfma4(qa[r], acc[kt][vv][r], U[vv]);
+        }
       }
       stage1(nb);
       fetch(n + 2);
@@ -739,18 +833,47 @@ refresh_kernel(RefreshArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) Cc[vv] = mfma4(ta[r], R[r], Cc[vv]);
         }
+        if constexpr (Sh::kSplit) {
+          // K slots of lane group g: token 4 g + e paired with C hi (e < 4)
+          // and with C lo (e >= 4); W hi meets both, W lo meets C hi.
+          u32x4 cb4[VTW];
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-          const v4f g4 = *reinterpret_cast<const v4f*>(&sh.G[cb][0][16 * kt + 4 * g]);
-          const v4f wa = *reinterpret_cast<const v4f*>(&sh.W[cb][16 * kt + m][4 * g]);
+          for (int vv = 0; vv < VTW; ++vv)
+            cb4[vv] = u32x4{pack_bf16(hi_bits(Cc[vv][0]), hi_bits(Cc[vv][1])),
+                            pack_bf16(hi_bits(Cc[vv][2]), hi_bits(Cc[vv][3])),
+                            pack_bf16(lo_bits(Cc[vv][0]), lo_bits(Cc[vv][1])),
+                            pack_bf16(lo_bits(Cc[vv][2]), lo_bits(Cc[vv][3]))};
 #pragma unroll
-          for (int vv = 0; vv < VTW; ++vv) {
-            v4f x = acc[kt][vv];
+          for (int kt = 0; kt < KT; ++kt) {
+            const v4f g4 = *reinterpret_cast<const v4f*>(&sh.G[cb][0][16 * kt + 4 * g]);
+            const uint32_t* wh = reinterpret_cast<const uint32_t*>(&sh.qw.Wh[cb][16 * kt + m][4 * g]);
+            const uint32_t* wl = reinterpret_cast<const uint32_t*>(&sh.qw.Wl[cb][16 * kt + m][4 * g]);
+            const u32x4 a1 = {wh[0], wh[1], wh[0], wh[1]};
+            const u32x4 a2 = {wl[0], wl[1], 0u, 0u};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) x[r] *= g4[r];
+            for (int vv = 0; vv < VTW; ++vv) {
+              v4f x = acc[kt][vv];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) x = mfma4(wa[r], Cc[vv][r], x);
-            acc[kt][vv] = x;
+              for (int r = 0; r < 4; ++r) x[r] *= g4[r];
+              x = mfma_bf16(a1, cb4[vv], x);
+              x = mfma_bf16(a2, cb4[vv], x);
+              acc[kt][vv] = x;
+            }
+          }
+        } else {
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt) {
+            const v4f g4 = *reinterpret_cast<const v4f*>(&sh.G[cb][0][16 * kt + 4 * g]);
+            const v4f wa = *reinterpret_cast<const v4f*>(&sh.qw.W[cb][16 * kt + m][4 * g]);
+#pragma unroll
+            for (int vv = 0; vv < VTW; ++vv) {
+              v4f x = acc[kt][vv];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) x[r] *= g4[r];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) x = mfma4(wa[r], Cc[vv][r], x);
+              acc[kt][vv] = x;
+            }
           }
         }
       }
