@@ -456,6 +456,7 @@ template <int D>
 struct RefreshShape {
   static constexpr int kKT = D / 16;                  // k tiles
   static constexpr bool kSplit = D >= 64;             // big products on split bf16 MFMA
+  static constexpr int kWavesPerSimd = 2;  // occupancy target
   static constexpr int kVTW = D >= 32 ? 2 : 1;        // v tiles per wave
   static constexpr int kNW = (D / 16) / kVTW;         // waves per head
   static constexpr int kNT = 64 * kNW;                // threads
@@ -482,13 +483,12 @@ template <int D>
 struct alignas(16) RefreshLds {
   float K[kC][D];             // k of the chunk being prepared
   float A[kC][D];             // its decays
-  float V[2][kC][D];          // v, by chunk parity
+  uint16_t V[2][kC][D];       // v (bf16 bits as given), by chunk parity
   float B[2][kC];             // beta, by chunk parity
   RefreshQW<D, RefreshShape<D>::kSplit> qw;
-  float G[2][2][D];           // gamma_15 by chunk parity ([.][1][.] is scratch)
+  float G[2][D];              // gamma_15 by chunk parity
   float L[kC][kC + 4];        // beta_t M_{t,s}, s < t
   float T[kC][kC + 4];        // (I + L)^-1
-  float sink[2 * D];          // target of the stores of lanes that hold no result
 };
 
 // Split of an fp32 value into bf16 hi + lo (hi = x truncated to bf16, lo =
@@ -550,7 +550,8 @@ __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
 }
 
 template <int D, int GATE>
-__global__ void __launch_bounds__(RefreshShape<D>::kNT) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(RefreshShape<D>::kNT)
+    __attribute__((amdgpu_waves_per_eu(RefreshShape<D>::kWavesPerSimd)))
 refresh_kernel(RefreshArgs a) {
   using Sh = RefreshShape<D>;
   constexpr int KT = Sh::kKT, VTW = Sh::kVTW, JB = Sh::kJB, NB4 = Sh::kNB4;
@@ -623,13 +624,11 @@ refresh_kernel(RefreshArgs a) {
   auto stage1 = [&](int vb) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
     const u32x4 wk = r_real ? rk : zero, wv = r_real ? rv : zero;
-    float kf[8], vf[8], al[8];
+    float kf[8], al[8];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       kf[2 * q] = bf16_lo(wk[q]);
       kf[2 * q + 1] = bf16_hi(wk[q]);
-      vf[2 * q] = bf16_lo(wv[q]);
-      vf[2 * q + 1] = bf16_hi(wv[q]);
     }
     if constexpr (kChan) {
 #pragma unroll
@@ -648,8 +647,7 @@ refresh_kernel(RefreshArgs a) {
       *reinterpret_cast<v4f*>(&sh.A[it_t][j0 + 4]) = v4f{al[4], al[5], al[6], al[7]};
       *reinterpret_cast<v4f*>(&sh.K[it_t][j0]) = v4f{kf[0], kf[1], kf[2], kf[3]};
       *reinterpret_cast<v4f*>(&sh.K[it_t][j0 + 4]) = v4f{kf[4], kf[5], kf[6], kf[7]};
-      *reinterpret_cast<v4f*>(&sh.V[vb][it_t][j0]) = v4f{vf[0], vf[1], vf[2], vf[3]};
-      *reinterpret_cast<v4f*>(&sh.V[vb][it_t][j0 + 4]) = v4f{vf[4], vf[5], vf[6], vf[7]};
+      *reinterpret_cast<u32x4*>(&sh.V[vb][it_t][j0]) = wv;
       sh.B[vb][it_t] = bv;  // the JB lanes of a token store the same value
     }
   };
@@ -659,12 +657,11 @@ refresh_kernel(RefreshArgs a) {
     if (kAllStage || tid < 2 * D) {
       // L, rows p and 15 - p (15 entries in all), 4 channels per lane,
       // summed over the NB4 lanes of the row pair.  The lane with
-      // tid % NB4 == 0 stores each entry; the others store to sink.
+      // tid % NB4 == 0 stores each entry.
       const int p = tid / NB4, c4 = 4 * (tid % NB4);
       const v4f kp = *reinterpret_cast<const v4f*>(&sh.K[p][c4]);
       const v4f kq = *reinterpret_cast<const v4f*>(&sh.K[kC - 1 - p][c4]);
       const float bp = sh.B[vb][p], bq = sh.B[vb][kC - 1 - p];
-      float* const sink = &sh.sink[tid];
       v4f pk = kp;
 #pragma unroll
       for (int i = 0; i < kC - 1; ++i) {
@@ -683,8 +680,7 @@ refresh_kernel(RefreshArgs a) {
         }
         part = group_sum<(NB4 < 16 ? NB4 : 16)>(part);
         if constexpr (NB4 == 32) part += __shfl_xor(part, 16, 64);
-        float* const at = tid % NB4 == 0 ? &sh.L[t][s] : sink;
-        *at = (first ? bp : bq) * part;
+        if (tid % NB4 == 0) sh.L[t][s] = (first ? bp : bq) * part;
       }
       // gamma_t and Q (forward lanes, tid < D) or W (backward lanes)
       const int j = tid % D;
@@ -732,25 +728,28 @@ refresh_kernel(RefreshArgs a) {
           *at = fwd ? after : before;
         }
       }
-      sh.G[vb][fwd ? 0 : 1][j] = gm;
+      if (fwd) sh.G[vb][j] = gm;
     }
   };
 
   // T = (I + L)^-1 by columns: lane s = lane % 16 owns column s,
   // T[t][s] = delta_{ts} - sum_{u<t} L[t][u] T[u][s].  For t <= s the sum
   // only meets T[u][s] = 0 (u < s), so one formula serves every row and the
-  // code has no branch.  Every wave computes it (the four lane groups of a
-  // wave hold the same column), so the stores write identical values.
+  // code has no branch.  The sums are built right-looking: as soon as
+  // T[u][s] is known it is added into the running sums of every later row,
+  // so the dependent chain is one multiply-add per row, not one per term.
+  // Every wave computes it (the four lane groups of a wave hold the same
+  // column), so the stores write identical values.
   auto invert = [&]() {
     const int sc = lane & 15;
-    float tc[kC];
-    tc[0] = sc == 0 ? 1.f : 0.f;
+    float tc[kC], run[kC];
 #pragma unroll
-    for (int t = 1; t < kC; ++t) {
-      float acc = 0.f;
+    for (int t = 0; t < kC; ++t) run[t] = 0.f;
 #pragma unroll
-      for (int u = 0; u < t; ++u) acc = fmaf(sh.L[t][u], tc[u], acc);
-      tc[t] = (t == sc ? 1.f : 0.f) - acc;
+    for (int u = 0; u < kC; ++u) {
+      tc[u] = (u == sc ? 1.f : 0.f) - run[u];
+#pragma unroll
+      for (int t = u + 1; t < kC; ++t) run[t] = fmaf(sh.L[t][u], tc[u], run[t]);
     }
 #pragma unroll
     for (int t = 0; t < kC; ++t) sh.T[t][sc] = tc[t];
@@ -828,7 +827,8 @@ refresh_kernel(RefreshArgs a) {
           const int v = 16 * (wave * VTW + vv) + m;
           v4f R;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) R[r] = b4[r] * (sh.V[cb][4 * g + r][v] - U[vv][r]);
+          for (int r = 0; r < 4; ++r)
+            R[r] = b4[r] * (__uint_as_float(uint32_t(sh.V[cb][4 * g + r][v]) << 16) - U[vv][r]);
           Cc[vv] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int r = 0; r < 4; ++r) Cc[vv] = mfma4(ta[r], R[r], Cc[vv]);
@@ -845,7 +845,7 @@ refresh_kernel(RefreshArgs a) {
                             pack_bf16(lo_bits(Cc[vv][2]), lo_bits(Cc[vv][3]))};
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt) {
-            const v4f g4 = *reinterpret_cast<const v4f*>(&sh.G[cb][0][16 * kt + 4 * g]);
+            const v4f g4 = *reinterpret_cast<const v4f*>(&sh.G[cb][16 * kt + 4 * g]);
             const uint32_t* wh = reinterpret_cast<const uint32_t*>(&sh.qw.Wh[cb][16 * kt + m][4 * g]);
             const uint32_t* wl = reinterpret_cast<const uint32_t*>(&sh.qw.Wl[cb][16 * kt + m][4 * g]);
             const u32x4 a1 = {wh[0], wh[1], wh[0], wh[1]};
@@ -863,7 +863,7 @@ refresh_kernel(RefreshArgs a) {
         } else {
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt) {
-            const v4f g4 = *reinterpret_cast<const v4f*>(&sh.G[cb][0][16 * kt + 4 * g]);
+            const v4f g4 = *reinterpret_cast<const v4f*>(&sh.G[cb][16 * kt + 4 * g]);
             const v4f wa = *reinterpret_cast<const v4f*>(&sh.qw.W[cb][16 * kt + m][4 * g]);
 #pragma unroll
             for (int vv = 0; vv < VTW; ++vv) {
