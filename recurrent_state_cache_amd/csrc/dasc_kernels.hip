@@ -738,8 +738,9 @@ refresh_kernel(RefreshArgs a) {
   // code has no branch.  The sums are built right-looking: as soon as
   // T[u][s] is known it is added into the running sums of every later row,
   // so the dependent chain is one multiply-add per row, not one per term.
-  // Every wave computes it (the four lane groups of a wave hold the same
-  // column), so the stores write identical values.
+  // One wave per chunk computes it (its four lane groups hold the same
+  // column, so their stores write identical values); the others read T
+  // after the barrier that ends the phase.
   auto invert = [&]() {
     const int sc = lane & 15;
     float tc[kC], run[kC];
@@ -773,7 +774,7 @@ refresh_kernel(RefreshArgs a) {
     for (int64_t n = 0; n < nchunks; ++n) {
       const int cb = static_cast<int>(n & 1), nb = cb ^ 1;
       // ---- phase 1: T(n), U0 = S Q(n)  ||  stage chunk n + 1, fetch n + 2
-      invert();
+      if (wave == static_cast<int>(n % Sh::kNW)) invert();  // one wave, rotating
       v4f U[VTW];
 #pragma unroll
       for (int vv = 0; vv < VTW; ++vv) U[vv] = v4f{0.f, 0.f, 0.f, 0.f};
