@@ -37,9 +37,15 @@ FP32_MFMA_PEAK_TF = 157.3      # MI355X dense fp32 matrix (MFMA), TFLOP/s
 KERNEL_SOURCES = ["recurrent_state_cache_amd/csrc/dasc_kernels.hip",
                   "recurrent_state_cache_amd/csrc/dasc_internal.h",
                   "recurrent_state_cache_amd/csrc/dasc_host.cpp"]
-KERNEL_ROLES = {"qmove_kernel<true": "pack_int8", "qmove_kernel<false": "unpack_int8",
-                "move_kernel<true": "pack", "move_kernel<false": "unpack",
-                "refresh_kernel": "refresh"}
+# kernel name pattern -> role (the TP movers and the windowed refresh are
+# instantiations of their own)
+KERNEL_ROLES = {r"qmove_kernel<true>": "pack_int8", r"qmove_kernel<false>": "unpack_int8",
+                r"(?<!q)move_kernel<true, \d+, \d+, false>": "pack",
+                r"(?<!q)move_kernel<false, \d+, \d+, false>": "unpack",
+                r"(?<!q)move_kernel<true, \d+, \d+, true>": "pack_tp",
+                r"(?<!q)move_kernel<false, \d+, \d+, true>": "unpack_tp",
+                r"refresh_kernel<\d+, \d+, false>": "refresh",
+                r"refresh_kernel<\d+, \d+, true>": "refresh_windowed"}
 
 
 def _args():
@@ -240,8 +246,9 @@ def _sources_sha256():
 
 
 def _role(kernel_name):
+    import re
     for key, role in KERNEL_ROLES.items():
-        if key in kernel_name:
+        if re.search(key, kernel_name):
             return role
     return None
 
@@ -293,7 +300,8 @@ def _summarize(dirs, workload):
     lines = [f"| kernel | calls | average (us) | min (us) | max (us) | FETCH_SIZE (KiB) | "
              f"WRITE_SIZE (KiB) | HBM bytes per launch (calibrated) |",
              "|---|---|---|---|---|---|---|---|"]
-    for role in ("pack", "unpack", "refresh", "pack_int8", "unpack_int8"):
+    for role in ("pack", "unpack", "refresh", "pack_int8", "unpack_int8", "pack_tp", "unpack_tp",
+                 "refresh_windowed"):
         if role not in stats:
             continue
         c, avg, mn, mx = stats[role]
@@ -319,7 +327,8 @@ def _counter_table(dirs):
             if role:
                 table.setdefault(r["Counter_Name"], {}).setdefault(role, []).append(
                     float(r["Counter_Value"]))
-    roles = ("pack", "unpack", "refresh", "pack_int8", "unpack_int8")
+    roles = ("pack", "unpack", "refresh", "pack_int8", "unpack_int8", "pack_tp", "unpack_tp",
+             "refresh_windowed")
     lines = ["| counter | " + " | ".join(roles) + " |", "|" + "---|" * (len(roles) + 1)]
     for c in sorted(table):
         vals = [table[c].get(r) for r in roles]

@@ -534,6 +534,12 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, true));
 }
 
+// Rows 1 and 3 of each wave get lane 15 of rows 0 and 2 (DPP row_bcast:15);
+// rows 0 and 2 get 0.
+__device__ __forceinline__ float row_bcast15_upper(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xA, 0xF, false));
+}
+
 // Sum over the G consecutive lanes of a 16-lane row (G in {1, 2, 4, 8, 16});
 // every lane of the group gets the sum.
 template <int G>
@@ -549,7 +555,9 @@ __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <int D, int GATE>
+// WINDOWED: each task replays only the last `window` tokens of its request
+// (a kernel of its own, so that profiles tell the two refreshes apart).
+template <int D, int GATE, bool WINDOWED>
 __global__ void __launch_bounds__(RefreshShape<D>::kNT)
     __attribute__((amdgpu_waves_per_eu(RefreshShape<D>::kWavesPerSimd)))
 refresh_kernel(RefreshArgs a) {
@@ -569,7 +577,7 @@ refresh_kernel(RefreshArgs a) {
     return;
   }
   // Per-head Eq. 7 window: replay only the request's last `window` tokens.
-  if (a.head_windows) t0 = t1 - t0 > task.window ? t1 - task.window : t0;
+  if constexpr (WINDOWED) t0 = t1 - t0 > task.window ? t1 - task.window : t0;
   if (!in_range(dst, a.n_dense)) {
     if (blockIdx.x == 0 && threadIdx.x == 0) flag(a.status, DASC_STATUS_BAD_INDEX);
     return;
@@ -656,8 +664,10 @@ refresh_kernel(RefreshArgs a) {
   auto stage2 = [&](int vb) {
     if (kAllStage || tid < 2 * D) {
       // L, rows p and 15 - p (15 entries in all), 4 channels per lane,
-      // summed over the NB4 lanes of the row pair.  The lane with
-      // tid % NB4 == 0 stores each entry.
+      // summed over the NB4 lanes of the row pair: within a 16-lane row by
+      // DPP, and for NB4 = 32 across the row pair by a row broadcast, which
+      // leaves the full sum in the upper row.  The last lane of the group
+      // stores each entry.
       const int p = tid / NB4, c4 = 4 * (tid % NB4);
       const v4f kp = *reinterpret_cast<const v4f*>(&sh.K[p][c4]);
       const v4f kq = *reinterpret_cast<const v4f*>(&sh.K[kC - 1 - p][c4]);
@@ -679,8 +689,8 @@ refresh_kernel(RefreshArgs a) {
           part = fmaf(pk[e], ks[e], part);
         }
         part = group_sum<(NB4 < 16 ? NB4 : 16)>(part);
-        if constexpr (NB4 == 32) part += __shfl_xor(part, 16, 64);
-        if (tid % NB4 == 0) sh.L[t][s] = (first ? bp : bq) * part;
+        if constexpr (NB4 == 32) part += row_bcast15_upper(part);
+        if (tid % NB4 == NB4 - 1) sh.L[t][s] = (first ? bp : bq) * part;
       }
       // gamma_t and Q (forward lanes, tid < D) or W (backward lanes)
       const int j = tid % D;
@@ -743,17 +753,16 @@ refresh_kernel(RefreshArgs a) {
   // after the barrier that ends the phase.
   auto invert = [&]() {
     const int sc = lane & 15;
-    float tc[kC], run[kC];
+    float run[kC];
 #pragma unroll
     for (int t = 0; t < kC; ++t) run[t] = 0.f;
 #pragma unroll
     for (int u = 0; u < kC; ++u) {
-      tc[u] = (u == sc ? 1.f : 0.f) - run[u];
+      const float tu = (u == sc ? 1.f : 0.f) - run[u];
+      sh.T[u][sc] = tu;
 #pragma unroll
-      for (int t = u + 1; t < kC; ++t) run[t] = fmaf(sh.L[t][u], tc[u], run[t]);
+      for (int t = u + 1; t < kC; ++t) run[t] = fmaf(sh.L[t][u], tu, run[t]);
     }
-#pragma unroll
-    for (int t = 0; t < kC; ++t) sh.T[t][sc] = tc[t];
   };
 
   v4f acc[KT][VTW];
@@ -962,15 +971,20 @@ bool refresh_shape_supported(int d_k, int d_v) {
 
 template <int D>
 int launch_refresh_d(int gate, const RefreshArgs& args, dim3 grid, hipStream_t s) {
+  constexpr int kNT = RefreshShape<D>::kNT;
+  const bool w = args.head_windows != 0;
   switch (gate) {
     case kGateHead:
-      refresh_kernel<D, kGateHead><<<grid, RefreshShape<D>::kNT, 0, s>>>(args);
+      if (w) refresh_kernel<D, kGateHead, true><<<grid, kNT, 0, s>>>(args);
+      else refresh_kernel<D, kGateHead, false><<<grid, kNT, 0, s>>>(args);
       break;
     case kGateChan:
-      refresh_kernel<D, kGateChan><<<grid, RefreshShape<D>::kNT, 0, s>>>(args);
+      if (w) refresh_kernel<D, kGateChan, true><<<grid, kNT, 0, s>>>(args);
+      else refresh_kernel<D, kGateChan, false><<<grid, kNT, 0, s>>>(args);
       break;
     case kGateChanSplit:
-      refresh_kernel<D, kGateChanSplit><<<grid, RefreshShape<D>::kNT, 0, s>>>(args);
+      if (w) refresh_kernel<D, kGateChanSplit, true><<<grid, kNT, 0, s>>>(args);
+      else refresh_kernel<D, kGateChanSplit, false><<<grid, kNT, 0, s>>>(args);
       break;
     default:
       return static_cast<int>(hipErrorInvalidValue);
