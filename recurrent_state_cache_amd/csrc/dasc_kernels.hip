@@ -487,6 +487,7 @@ struct alignas(16) RefreshLds {
   float B[2][kC];             // beta, by chunk parity
   RefreshQW<D, RefreshShape<D>::kSplit> qw;
   float G[2][D];              // gamma_15 by chunk parity
+  float PA[D], PD[D];         // exp(A_log) and dt_bias per channel (GDN: [0])
   float L[kC][kC + 4];        // beta_t M_{t,s}, s < t
   float T[kC][kC + 4];        // (I + L)^-1
 };
@@ -589,13 +590,12 @@ refresh_kernel(RefreshArgs a) {
   // Staged item of this lane: token it_t of a chunk, channels j0 .. j0 + 7.
   const bool it_on = kAllStage || tid < 2 * D;
   const int it_t = (tid / JB) % kC, it_jb = tid % JB, j0 = 8 * it_jb;
-  float expA[8], dtb[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint32_t u = task.param_off + (kChan ? j0 + c : 0);
-    expA[c] = a.gate_expA[u];
-    dtb[c] = a.gate_dt[u];
+  // The head's gate parameters, once, into LDS (read by every staging).
+  if (tid < (kChan ? D : 1)) {
+    sh.PA[tid] = a.gate_expA[task.param_off + tid];
+    sh.PD[tid] = a.gate_dt[task.param_off + tid];
   }
+  __syncthreads();
 
   // Inputs of one token for this lane (8 bf16 of k, v and the gate logits,
   // packed, and beta), fetched one chunk ahead of their staging.  The row is
@@ -639,13 +639,19 @@ refresh_kernel(RefreshArgs a) {
       kf[2 * q + 1] = bf16_hi(wk[q]);
     }
     if constexpr (kChan) {
+      const v4f e0 = *reinterpret_cast<const v4f*>(&sh.PA[j0]);
+      const v4f e1 = *reinterpret_cast<const v4f*>(&sh.PA[j0 + 4]);
+      const v4f d0 = *reinterpret_cast<const v4f*>(&sh.PD[j0]);
+      const v4f d1 = *reinterpret_cast<const v4f*>(&sh.PD[j0 + 4]);
+      const float expA[8] = {e0[0], e0[1], e0[2], e0[3], e1[0], e1[1], e1[2], e1[3]};
+      const float dtb[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         al[2 * q] = decay(bf16_lo(ra[q]) + dtb[2 * q], r_real ? expA[2 * q] : 0.f);
         al[2 * q + 1] = decay(bf16_hi(ra[q]) + dtb[2 * q + 1], r_real ? expA[2 * q + 1] : 0.f);
       }
     } else {
-      const float x = decay(bf16_lo(ra[0]) + dtb[0], r_real ? expA[0] : 0.f);
+      const float x = decay(bf16_lo(ra[0]) + sh.PD[0], r_real ? sh.PA[0] : 0.f);
 #pragma unroll
       for (int c = 0; c < 8; ++c) al[c] = x;
     }
@@ -661,7 +667,7 @@ refresh_kernel(RefreshArgs a) {
   };
 
   // From the staged chunk: L (into sh.L), Q (sh.Q), W and gamma_15 (buffer vb).
-  auto stage2 = [&](int vb) {
+  auto stage2 = [&](int vb) __attribute__((always_inline)) {
     if (kAllStage || tid < 2 * D) {
       // L, rows p and 15 - p (15 entries in all), 4 channels per lane,
       // summed over the NB4 lanes of the row pair: within a 16-lane row by
