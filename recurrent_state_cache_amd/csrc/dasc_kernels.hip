@@ -673,16 +673,16 @@ refresh_kernel(RefreshArgs a) {
       // summed over the NB4 lanes of the row pair: within a 16-lane row by
       // DPP, and for NB4 = 32 across the row pair by a row broadcast, which
       // leaves the full sum in the upper row.  The last lane of the group
-      // stores each entry.
+      // stores the entries after the loop, so the loop has no branch.
       const int p = tid / NB4, c4 = 4 * (tid % NB4);
       const v4f kp = *reinterpret_cast<const v4f*>(&sh.K[p][c4]);
       const v4f kq = *reinterpret_cast<const v4f*>(&sh.K[kC - 1 - p][c4]);
       const float bp = sh.B[vb][p], bq = sh.B[vb][kC - 1 - p];
       v4f pk = kp;
+      float lv[kC - 1];
 #pragma unroll
       for (int i = 0; i < kC - 1; ++i) {
         const bool first = i < p;
-        const int t = first ? p : kC - 1 - p;
         const int s = first ? p - 1 - i : kC - 2 - i;
         if (i == 0) pk = first ? kp : kq;
         else pk = i == p ? kq : pk;
@@ -696,7 +696,14 @@ refresh_kernel(RefreshArgs a) {
         }
         part = group_sum<(NB4 < 16 ? NB4 : 16)>(part);
         if constexpr (NB4 == 32) part += row_bcast15_upper(part);
-        if (tid % NB4 == NB4 - 1) sh.L[t][s] = (first ? bp : bq) * part;
+        lv[i] = (first ? bp : bq) * part;
+      }
+      if (tid % NB4 == NB4 - 1) {
+#pragma unroll
+        for (int i = 0; i < kC - 1; ++i) {
+          const bool first = i < p;
+          sh.L[first ? p : kC - 1 - p][first ? p - 1 - i : kC - 2 - i] = lv[i];
+        }
       }
       // gamma_t and Q (forward lanes, tid < D) or W (backward lanes)
       const int j = tid % D;
