@@ -475,8 +475,9 @@ template <int D>
 struct RefreshQW<D, true> {
   uint16_t Qh[kC][D + 16];    // gamma_t o k_t: bf16 hi, then lo (rows padded to
   uint16_t Ql[kC][D + 16];    // 8 banks mod 64, so an A-operand read is 2 passes)
-  uint16_t Wh[2][D][kC];      // k_s o D_{15,s}, [k][s]: bf16 hi and lo, by
-  uint16_t Wl[2][D][kC];      // chunk parity
+  // k_s o D_{15,s}, [k][s], by chunk parity: per row k and token group
+  // g (s = 4 g .. 4 g + 3) the four bf16 hi, then the four bf16 lo.
+  uint16_t W[2][D][2 * kC];
 };
 
 template <int D>
@@ -727,16 +728,12 @@ refresh_kernel(RefreshArgs a) {
           }
         } else {
 #pragma unroll
-          for (int q = 0; q < kC / 8; ++q) {
-            u32x4 h, l;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float w0 = qw[kC - 1 - (8 * q + 2 * e)], w1 = qw[kC - 2 - (8 * q + 2 * e)];
-              h[e] = pack_bf16(hi_bits(w0), hi_bits(w1));
-              l[e] = pack_bf16(lo_bits(w0), lo_bits(w1));
-            }
-            *reinterpret_cast<u32x4*>(&sh.qw.Wh[vb][j][8 * q]) = h;
-            *reinterpret_cast<u32x4*>(&sh.qw.Wl[vb][j][8 * q]) = l;
+          for (int gq = 0; gq < kC / 4; ++gq) {  // tokens s = 4 gq .. 4 gq + 3
+            const float w0 = qw[kC - 1 - 4 * gq], w1 = qw[kC - 2 - 4 * gq];
+            const float w2 = qw[kC - 3 - 4 * gq], w3 = qw[kC - 4 - 4 * gq];
+            *reinterpret_cast<u32x4*>(&sh.qw.W[vb][j][8 * gq]) =
+                u32x4{pack_bf16(hi_bits(w0), hi_bits(w1)), pack_bf16(hi_bits(w2), hi_bits(w3)),
+                      pack_bf16(lo_bits(w0), lo_bits(w1)), pack_bf16(lo_bits(w2), lo_bits(w3))};
           }
         }
       } else {
@@ -857,29 +854,30 @@ refresh_kernel(RefreshArgs a) {
           for (int r = 0; r < 4; ++r) Cc[vv] = mfma4(ta[r], R[r], Cc[vv]);
         }
         if constexpr (Sh::kSplit) {
-          // K slots of lane group g: token 4 g + e paired with C hi (e < 4)
-          // and with C lo (e >= 4); W hi meets both, W lo meets C hi.
-          u32x4 cb4[VTW];
+          // K slots of lane group g: token 4 g + e with W hi (e < 4) and
+          // with W lo (e >= 4) on the A side; the B side is C hi for both
+          // in the first product, and C lo against W hi (W lo against 0)
+          // in the second.
+          u32x4 chh[VTW], cl0[VTW];
 #pragma unroll
-          for (int vv = 0; vv < VTW; ++vv)
-            cb4[vv] = u32x4{pack_bf16(hi_bits(Cc[vv][0]), hi_bits(Cc[vv][1])),
-                            pack_bf16(hi_bits(Cc[vv][2]), hi_bits(Cc[vv][3])),
-                            pack_bf16(lo_bits(Cc[vv][0]), lo_bits(Cc[vv][1])),
-                            pack_bf16(lo_bits(Cc[vv][2]), lo_bits(Cc[vv][3]))};
+          for (int vv = 0; vv < VTW; ++vv) {
+            const uint32_t h0 = pack_bf16(hi_bits(Cc[vv][0]), hi_bits(Cc[vv][1]));
+            const uint32_t h1 = pack_bf16(hi_bits(Cc[vv][2]), hi_bits(Cc[vv][3]));
+            chh[vv] = u32x4{h0, h1, h0, h1};
+            cl0[vv] = u32x4{pack_bf16(lo_bits(Cc[vv][0]), lo_bits(Cc[vv][1])),
+                            pack_bf16(lo_bits(Cc[vv][2]), lo_bits(Cc[vv][3])), 0u, 0u};
+          }
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt) {
             const v4f g4 = *reinterpret_cast<const v4f*>(&sh.G[cb][16 * kt + 4 * g]);
-            const uint32_t* wh = reinterpret_cast<const uint32_t*>(&sh.qw.Wh[cb][16 * kt + m][4 * g]);
-            const uint32_t* wl = reinterpret_cast<const uint32_t*>(&sh.qw.Wl[cb][16 * kt + m][4 * g]);
-            const u32x4 a1 = {wh[0], wh[1], wh[0], wh[1]};
-            const u32x4 a2 = {wl[0], wl[1], 0u, 0u};
+            const u32x4 wa = *reinterpret_cast<const u32x4*>(&sh.qw.W[cb][16 * kt + m][8 * g]);
 #pragma unroll
             for (int vv = 0; vv < VTW; ++vv) {
               v4f x = acc[kt][vv];
 #pragma unroll
               for (int r = 0; r < 4; ++r) x[r] *= g4[r];
-              x = mfma_bf16(a1, cb4[vv], x);
-              x = mfma_bf16(a2, cb4[vv], x);
+              x = mfma_bf16(wa, chh[vv], x);
+              x = mfma_bf16(wa, cl0[vv], x);
               acc[kt][vv] = x;
             }
           }
