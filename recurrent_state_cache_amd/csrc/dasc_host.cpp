@@ -972,6 +972,7 @@ static int run_move_tp(const char* w, dasc_plan_t p, bool pack, const void* dens
   m.n_dst = pack ? n_slots : n_dense;
   m.n = n;
   m.status = p->dev.status;
+  m.tp = true;
   if (use_alt) {
     m.alt_base = static_cast<uint8_t*>(const_cast<void*>(alt));
     m.alt_stride = alt_stride;

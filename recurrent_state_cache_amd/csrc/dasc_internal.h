@@ -117,8 +117,10 @@ struct MoveArgs {
   int64_t dst_stride, n_dst;
   int32_t n;
   uint32_t* status;
-  // Second row per pair for TP pieces with split < r: the send row (pack) or
-  // the receive row (unpack).  alt_base == nullptr: no such pieces.
+  // TP storage-balancing lists (their own kernel instantiation).  Second row
+  // per pair for pieces with split < r: the send row (pack) or the receive
+  // row (unpack); alt_base == nullptr when no piece uses one.
+  bool tp;
   uint8_t* alt_base;
   int64_t alt_stride, n_alt;
   const int32_t* alt_idx;

@@ -191,16 +191,17 @@ __global__ void __launch_bounds__(kThreads) move_kernel(MoveArgs a) {
   const Piece t = a.pieces[blockIdx.x];
   const int64_t s = a.src_idx[blockIdx.y];
   const int64_t d = a.dst_idx[blockIdx.y];
-  const int64_t x = kAlt ? a.alt_idx[blockIdx.y] : 0;
+  const bool has_alt = kAlt && a.alt_base != nullptr;
+  const int64_t x = has_alt ? a.alt_idx[blockIdx.y] : 0;
   const bool bad_idx = !in_range(s, a.n_src) || !in_range(d, a.n_dst) ||
-                       (kAlt && !in_range(x, a.n_alt));
+                       (has_alt && !in_range(x, a.n_alt));
   if (bad_idx | (t.type > kPieceKda)) {
     if (bad_idx && blockIdx.x == 0 && threadIdx.x == 0) flag(a.status, DASC_STATUS_BAD_INDEX);
     return;
   }
   const uint8_t* src = a.src_base + s * a.src_stride;
   uint8_t* dst = a.dst_base + d * a.dst_stride;
-  uint8_t* alt = kAlt ? a.alt_base + x * a.alt_stride : nullptr;
+  uint8_t* alt = has_alt ? a.alt_base + x * a.alt_stride : nullptr;
   if (t.type == kPieceKda)  // uniform per workgroup
     kda_piece<kPack, DK, DV, kAlt>(t, src, dst, alt, U);
   else
@@ -944,8 +945,8 @@ int launch_move(bool pack, const MoveArgs& args, void* stream) {
   const size_t lds = static_cast<size_t>(args.kda_r_max) * kKdaLdsRow * sizeof(float);  // <= 18 KiB
   dim3 grid(args.n_pieces, static_cast<uint32_t>(args.n));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool alt = args.alt_base != nullptr;
-  if (alt && !args.alt_idx) return static_cast<int>(hipErrorInvalidValue);
+  const bool alt = args.tp;
+  if (args.alt_base && !args.alt_idx) return static_cast<int>(hipErrorInvalidValue);
   if (pack) {
     if (alt) {
       if (args.kda_128) move_kernel<true, 128, 128, true><<<grid, kThreads, lds, s>>>(args);
