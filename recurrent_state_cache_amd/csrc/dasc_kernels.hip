@@ -677,19 +677,31 @@ refresh_kernel(RefreshArgs a) {
       // leaves the full sum in the upper row.  The last lane of the group
       // stores the entries after the loop, so the loop has no branch.
       const int p = tid / NB4, c4 = 4 * (tid % NB4);
-      const v4f kp = *reinterpret_cast<const v4f*>(&sh.K[p][c4]);
-      const v4f kq = *reinterpret_cast<const v4f*>(&sh.K[kC - 1 - p][c4]);
+      // K and A are adjacent [kC][D] arrays: row r of A is row kC + r here.
+      const float(*KA)[D] = reinterpret_cast<const float(*)[D]>(&sh.K[0][0]);
       const float bp = sh.B[vb][p], bq = sh.B[vb][kC - 1 - p];
+      v4f kp = *reinterpret_cast<const v4f*>(&KA[p][c4]);
+      v4f kq = *reinterpret_cast<const v4f*>(&KA[kC - 1 - p][c4]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {  // beta_t folded into the row's key
+        kp[e] *= bp;
+        kq[e] *= bq;
+      }
+      // Entry i: row p, s = p - 1 - i (i < p), else row 15 - p, s = 14 - i;
+      // both walk down from a base row, so the addresses are a base chosen
+      // per entry plus a constant.
+      const float* const rowP = &KA[p][c4];
+      const float* const rowQ = &KA[kC - 1][c4];
       v4f pk = kp;
       float lv[kC - 1];
 #pragma unroll
       for (int i = 0; i < kC - 1; ++i) {
         const bool first = i < p;
-        const int s = first ? p - 1 - i : kC - 2 - i;
+        const float* const r0 = first ? rowP : rowQ;  // K row s + 1
         if (i == 0) pk = first ? kp : kq;
         else pk = i == p ? kq : pk;
-        const v4f al = *reinterpret_cast<const v4f*>(&sh.A[s + 1][c4]);
-        const v4f ks = *reinterpret_cast<const v4f*>(&sh.K[s][c4]);
+        const v4f al = *reinterpret_cast<const v4f*>(r0 + (kC - i) * D);   // A[s + 1]
+        const v4f ks = *reinterpret_cast<const v4f*>(r0 - (i + 1) * D);    // K[s]
         float part = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -698,14 +710,14 @@ refresh_kernel(RefreshArgs a) {
         }
         part = group_sum<(NB4 < 16 ? NB4 : 16)>(part);
         if constexpr (NB4 == 32) part += row_bcast15_upper(part);
-        lv[i] = (first ? bp : bq) * part;
+        lv[i] = part;
       }
       if (tid % NB4 == NB4 - 1) {
+        // L[p][p - 1 - i] and L[15 - p][14 - i]: two bases, constant steps
+        float* const lP = &sh.L[p][0] + p - 1;
+        float* const lQ = &sh.L[kC - 1 - p][0] + kC - 2;
 #pragma unroll
-        for (int i = 0; i < kC - 1; ++i) {
-          const bool first = i < p;
-          sh.L[first ? p : kC - 1 - p][first ? p - 1 - i : kC - 2 - i] = lv[i];
-        }
+        for (int i = 0; i < kC - 1; ++i) *((i < p ? lP : lQ) - i) = lv[i];
       }
       // gamma_t and Q (forward lanes, tid < D) or W (backward lanes)
       const int j = tid % D;
