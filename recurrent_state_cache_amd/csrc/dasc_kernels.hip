@@ -490,7 +490,7 @@ struct alignas(16) RefreshLds {
   RefreshQW<D, RefreshShape<D>::kSplit> qw;
   float G[2][D];              // gamma_15 by chunk parity
   float PA[D], PD[D];         // exp(A_log) and dt_bias per channel (GDN: [0])
-  float L[kC][kC + 4];        // beta_t M_{t,s}, s < t
+  float LT[kC][kC + 4];       // L transposed: LT[s][t] = beta_t M_{t,s}, s < t
   float T[kC][kC + 4];        // (I + L)^-1
 };
 
@@ -713,11 +713,12 @@ refresh_kernel(RefreshArgs a) {
         lv[i] = part;
       }
       if (tid % NB4 == NB4 - 1) {
-        // L[p][p - 1 - i] and L[15 - p][14 - i]: two bases, constant steps
-        float* const lP = &sh.L[p][0] + p - 1;
-        float* const lQ = &sh.L[kC - 1 - p][0] + kC - 2;
+        // L[p][p - 1 - i] and L[15 - p][14 - i], stored transposed: two
+        // bases, constant steps
+        float* const lP = &sh.LT[0][0] + (p - 1) * (kC + 4) + p;
+        float* const lQ = &sh.LT[0][0] + (kC - 2) * (kC + 4) + (kC - 1 - p);
 #pragma unroll
-        for (int i = 0; i < kC - 1; ++i) *((i < p ? lP : lQ) - i) = lv[i];
+        for (int i = 0; i < kC - 1; ++i) *((i < p ? lP : lQ) - i * (kC + 4)) = lv[i];
       }
       // gamma_t and Q (forward lanes, tid < D) or W (backward lanes)
       const int j = tid % D;
@@ -784,7 +785,12 @@ refresh_kernel(RefreshArgs a) {
       const float tu = (u == sc ? 1.f : 0.f) - run[u];
       sh.T[u][sc] = tu;
 #pragma unroll
-      for (int t = u + 1; t < kC; ++t) run[t] = fmaf(sh.L[t][u], tu, run[t]);
+      for (int q = (u + 1) / 4; q < kC / 4; ++q) {  // row u of L^T, 4 at a time
+        const v4f lt = *reinterpret_cast<const v4f*>(&sh.LT[u][4 * q]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * q + e > u) run[4 * q + e] = fmaf(lt[e], tu, run[4 * q + e]);
+      }
     }
   };
 
