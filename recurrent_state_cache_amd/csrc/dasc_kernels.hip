@@ -805,7 +805,7 @@ refresh_kernel(RefreshArgs a) {
   if (nchunks > 0) {
     fetch(0);
     stage1(0);
-    fetch(1);
+    if (nchunks > 1) fetch(1);
     __syncthreads();
     stage2(0);
     __syncthreads();
@@ -816,7 +816,9 @@ refresh_kernel(RefreshArgs a) {
       v4f U[VTW];
 #pragma unroll
       for (int vv = 0; vv < VTW; ++vv) U[vv] = v4f{0.f, 0.f, 0.f, 0.f};
-      if constexpr (Sh::kSplit) {
+      if (n == 0) {
+        // the scratch state starts at zero: U0 = 0
+      } else if constexpr (Sh::kSplit) {
         // K slots of lane group g: 4 g + e of k tile 2p (e < 4), then of
         // tile 2p + 1, on both operands.
 #pragma unroll
@@ -853,8 +855,9 @@ refresh_kernel(RefreshArgs a) {
             for (int vv = 0; vv < VTW; ++vv) U[vv] = mfma4(qa[r], acc[kt][vv][r], U[vv]);
         }
       }
-      stage1(nb);
-      fetch(n + 2);
+      // staging and fetches past the request's last chunk are skipped
+      if (n + 1 < nchunks) stage1(nb);
+      if (n + 2 < nchunks) fetch(n + 2);
       __syncthreads();
       // ---- phase 2: R, C = T R, S <- S Diag(gamma) + W C  ||  L, Q, W of n + 1
       {
@@ -917,7 +920,7 @@ refresh_kernel(RefreshArgs a) {
           }
         }
       }
-      stage2(nb);
+      if (n + 1 < nchunks) stage2(nb);
       __syncthreads();
     }
   }
