@@ -261,3 +261,23 @@ def test_windowed_refresh_kda_and_mixed_sampled():
         assert P.status() == 0
         _check_requests(P, O, inp, before, dense, dst.cpu().numpy(), reqs, layers=layers,
                         label=f"windowed {cfg.name}", head_windows=True)
+
+
+def test_windowed_equals_full_when_requests_fit_the_windows():
+    # every head window is >= 4 here (W_max = 64), so requests of at most 4
+    # tokens replay the same tokens on both entry points: bit-identical
+    cfg = W.Config("widths", _odd_refresh_layers(23), w_max=64, n_req=4, seed=23)
+    P, O = _plans(cfg)
+    assert min(O.head_window(li, int(h)) for li in range(len(cfg.layers))
+               for h in O.refreshed_heads(li)) >= 4
+    Wn = np.array([0, 1, 3, 4])
+    inp = W.refresh_inputs(cfg, Wn, device="cuda")
+    base = W.dense_states(cfg, 4, device="cuda", seed=11)
+    a, b = base.clone(), base.clone()
+    dst = torch.tensor([2, 0, 3, 1], dtype=torch.int32, device="cuda")
+    R.ckpt_refresh_suffix(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, a, dst)
+    R.ckpt_refresh_suffix_windowed(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, b, dst)
+    torch.cuda.synchronize()
+    assert P.status() == 0
+    assert torch.equal(a, b)
+    assert not torch.equal(a, base)
