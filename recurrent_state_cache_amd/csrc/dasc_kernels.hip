@@ -592,12 +592,6 @@ refresh_kernel(RefreshArgs a) {
   // Staged item of this lane: token it_t of a chunk, channels j0 .. j0 + 7.
   const bool it_on = kAllStage || tid < 2 * D;
   const int it_t = (tid / JB) % kC, it_jb = tid % JB, j0 = 8 * it_jb;
-  // The head's gate parameters, once, into LDS (read by every staging).
-  if (tid < (kChan ? D : 1)) {
-    sh.PA[tid] = a.gate_expA[task.param_off + tid];
-    sh.PD[tid] = a.gate_dt[task.param_off + tid];
-  }
-  __syncthreads();
 
   // Inputs of one token for this lane (8 bf16 of k, v and the gate logits,
   // packed, and beta), fetched one chunk ahead of their staging.  The row is
@@ -803,7 +797,14 @@ refresh_kernel(RefreshArgs a) {
   const int64_t W = t1 - t0;
   const int64_t nchunks = (W + kC - 1) / kC;
   if (nchunks > 0) {
+    // The head's gate parameters into LDS (read by every staging), while
+    // the first chunk's inputs are in flight.
+    if (tid < (kChan ? D : 1)) {
+      sh.PA[tid] = a.gate_expA[task.param_off + tid];
+      sh.PD[tid] = a.gate_dt[task.param_off + tid];
+    }
     fetch(0);
+    __syncthreads();
     stage1(0);
     if (nchunks > 1) fetch(1);
     __syncthreads();
