@@ -312,6 +312,26 @@ int dasc_ckpt_refresh_suffix_windowed(dasc_plan_t plan, const uint16_t* k, const
                                       const int32_t* dst_idx, int32_t n, void* stream);
 
 /*
+ * Load with refresh in one pass, dasc-wr ([dasc] §4.2): for each request r
+ * in [0, n), dense[dst_idx[r]] <- exactly what dasc_ckpt_unpack_zero_fill
+ * from pool[src_slot[r]] followed by dasc_ckpt_refresh_suffix (head_windows
+ * == 0) or dasc_ckpt_refresh_suffix_windowed (head_windows != 0) over the
+ * request's tokens would leave, bit for bit.  Each replayed head is written
+ * once, whole: its local columns from the replay and its retained columns
+ * from their units in the slot; the other heads and the conv bytes are
+ * unpacked as usual.  Arguments as in those two calls (pool rows hold
+ * slot_bytes; src_slot and dst_idx: device int32 arrays of n entries).  A
+ * request whose token range or indices are invalid is skipped and flagged;
+ * its replayed heads are then not written.
+ */
+int dasc_ckpt_unpack_refresh(dasc_plan_t plan, const void* pool_base, int64_t pool_stride,
+                             int64_t n_slots, const int32_t* src_slot, const uint16_t* k,
+                             const uint16_t* v, const uint16_t* a, const float* beta,
+                             const int64_t* tok_offsets, int64_t n_tokens, void* dense_base,
+                             int64_t dense_stride, int64_t n_dense, const int32_t* dst_idx,
+                             int32_t n, int32_t head_windows, void* stream);
+
+/*
  * Store with TP storage balancing, this rank's part before the exchange
  * ([dasc] §4.3, Appendix B.1(b): pack and partition): for i in [0, n), the
  * rank's compute-local units of dense[src_idx[i]] in its ragged order

@@ -23,6 +23,7 @@ import torch  # noqa: F401
 __all__ = ["Plan", "DascError", "ckpt_pack", "ckpt_unpack_zero_fill",
            "ckpt_refresh_suffix", "ckpt_refresh_suffix_windowed", "ckpt_pack_int8",
            "ckpt_unpack_int8_zero_fill", "ckpt_pack_tp", "ckpt_unpack_tp_zero_fill",
+           "ckpt_unpack_refresh",
            "GDN", "KDA", "STATUS_BAD_INDEX",
            "STATUS_BAD_TOKENS", "LIB_PATH", "lib"]
 
@@ -106,6 +107,9 @@ def _load():
                                               _c_i64, _c_i64, _c_p, _c_i32, _c_p]),
         "dasc_ckpt_refresh_suffix_windowed": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
                                                        _c_p, _c_i64, _c_i64, _c_p, _c_i32, _c_p]),
+        "dasc_ckpt_unpack_refresh": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p,
+                                              _c_p, _c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_p,
+                                              _c_i32, _c_i32, _c_p]),
         "dasc_ckpt_pack_int8": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_i64,
                                          _c_p, _c_i32, _c_p]),
         "dasc_ckpt_unpack_int8_zero_fill": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p,
@@ -398,6 +402,33 @@ def ckpt_refresh_suffix(plan: Plan, k, v, a, beta, tok_off, dense, dst_idx, stre
     [n+1]; dense: [n_dense, >= dense_bytes] uint8; dst_idx: int32 [n]."""
     _refresh(lib.dasc_ckpt_refresh_suffix, "ckpt_refresh_suffix", plan, k, v, a, beta, tok_off,
              dense, dst_idx, stream)
+
+
+def ckpt_unpack_refresh(plan: Plan, pool, src_slot, k, v, a, beta, tok_off, dense, dst_idx,
+                        head_windows: bool = False, stream=None) -> None:
+    """Load and refresh in one pass: dense[dst_idx[r]] <- what
+    ckpt_unpack_zero_fill from pool[src_slot[r]] followed by the refresh
+    (per-head windows if head_windows) leaves, each replayed head written
+    once."""
+    import torch
+    n = dst_idx.numel()
+    if src_slot.numel() != n or tok_off.numel() != n + 1:
+        raise ValueError("src_slot must have n entries and tok_off n+1")
+    T = k.shape[0]
+    info = plan.info()
+    for nm, t, w in (("k", k, info["k_row"]), ("v", v, info["v_row"]),
+                     ("a", a, info["gate_row"]), ("beta", beta, info["beta_row"])):
+        if t.dim() != 2 or t.shape[0] != T or t.shape[1] != w:
+            raise ValueError(f"{nm} must be [{T}, {w}], got {tuple(t.shape)}")
+    pp, ps, pn = _rows(pool, "pool")
+    dp, ds, dn = _rows(dense, "dense")
+    _check(lib.dasc_ckpt_unpack_refresh(
+        plan._h, pp, ps, pn, _dev_ptr(src_slot, "src_slot", torch.int32),
+        _dev_ptr(k, "k", torch.bfloat16), _dev_ptr(v, "v", torch.bfloat16),
+        _dev_ptr(a, "a", torch.bfloat16), _dev_ptr(beta, "beta", torch.float32),
+        _dev_ptr(tok_off, "tok_off", torch.int64), T, dp, ds, dn,
+        _dev_ptr(dst_idx, "dst_idx", torch.int32), n, 1 if head_windows else 0,
+        _stream_handle(stream)), "ckpt_unpack_refresh")
 
 
 def ckpt_refresh_suffix_windowed(plan: Plan, k, v, a, beta, tok_off, dense, dst_idx,

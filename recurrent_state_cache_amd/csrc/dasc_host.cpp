@@ -74,7 +74,7 @@ struct dasc_plan {
   int64_t k_row = 0, v_row = 0, g_row = 0, b_row = 0;
 
   // host image of the device tables
-  std::vector<Piece> pack, unpack, pack_q, unpack_q, pack_tp, unpack_tp;
+  std::vector<Piece> pack, unpack, pack_q, unpack_q, pack_tp, unpack_tp, unpack_rest;
   bool int8_ok = true;          // every layer with a retained unit fits the INT8 kernels
   int64_t int8_scale_base = 0;  // INT8 slot: start of the scale block
   int64_t int8_conv_base = 0;   // INT8 slot: start of the conv bytes
@@ -84,8 +84,8 @@ struct dasc_plan {
   int32_t kda_r_max = 0;  // largest retained-channel count of a KDA head
   bool kda_128 = true;    // every KDA layer has d_k = d_v = 128
   int64_t off_pack = 0, off_unpack = 0, off_pack_q = 0, off_unpack_q = 0, off_pack_tp = 0,
-          off_unpack_tp = 0, off_refresh = 0, off_expA = 0, off_dt = 0, off_status = 0,
-          table_bytes = 0;
+          off_unpack_tp = 0, off_unpack_rest = 0, off_refresh = 0, off_expA = 0, off_dt = 0,
+          off_status = 0, table_bytes = 0;
 
   // TP storage balancing of this rank ([dasc] Appendix B.1(b)); a plan from
   // dasc_plan_build is rank 0 of 1 (everything kept).
@@ -342,8 +342,15 @@ void build_tables(dasc_plan* p) {
   std::vector<std::vector<RefreshTask>> rtasks;
   for (const auto& L : p->layers) {
     const int64_t head_bytes = int64_t(L.d_v) * L.d_k * 4;
+    int64_t kept = 0;  // retained units of the layer before head h
     for (int h = 0; h < L.n_heads; ++h) {
       RefreshTask t{};
+      t.pool_off = static_cast<uint32_t>(L.pool_off + kept * L.unit_bytes);
+      if (L.kind == kGDN) {
+        kept += L.retained[h];
+      } else {
+        for (int k = 0; k < L.d_k; ++k) kept += L.retained[int64_t(h) * L.d_k + k];
+      }
       bool any_local = false;
       for (int k = 0; k < L.d_k && k < 128; ++k) {
         const int64_t u = L.kind == kGDN ? h : int64_t(h) * L.d_k + k;
@@ -380,6 +387,25 @@ void build_tables(dasc_plan* p) {
     p->refresh_groups.push_back(g);
   }
 
+  // Fused load: the unpack pieces of every head no refresh task writes (and
+  // the conv bytes); pieces never straddle heads.
+  {
+    std::vector<std::pair<uint64_t, uint64_t>> replayed;  // [start, end) in a dense checkpoint
+    for (const auto& L : p->layers) {
+      const uint64_t hb = uint64_t(L.d_v) * L.d_k * 4;
+      for (const RefreshTask& t : p->refresh)
+        if (t.dense_off >= uint64_t(L.dense_off) && t.dense_off < uint64_t(L.dense_off) + L.n_heads * hb)
+          replayed.emplace_back(t.dense_off, t.dense_off + hb);
+    }
+    std::sort(replayed.begin(), replayed.end());
+    for (const Piece& t : p->unpack) {
+      auto it = std::upper_bound(replayed.begin(), replayed.end(),
+                                 std::make_pair(t.dense_off, ~uint64_t(0)));
+      const bool inside = it != replayed.begin() && t.dense_off < std::prev(it)->second;
+      if (!inside) p->unpack_rest.push_back(t);
+    }
+  }
+
   // Gate parameters, per unit in plan order: exp(A_log) rounded once from
   // double, and dt_bias as given.
   for (const auto& L : p->layers) {
@@ -401,6 +427,7 @@ void build_tables(dasc_plan* p) {
   p->off_unpack_q = section(p->unpack_q.size() * sizeof(Piece));
   p->off_pack_tp = section(p->pack_tp.size() * sizeof(Piece));
   p->off_unpack_tp = section(p->unpack_tp.size() * sizeof(Piece));
+  p->off_unpack_rest = section(p->unpack_rest.size() * sizeof(Piece));
   p->off_refresh = section(p->refresh.size() * sizeof(RefreshTask));
   p->off_expA = section(p->gate_expA.size() * sizeof(float));
   p->off_dt = section(p->gate_dt.size() * sizeof(float));
@@ -767,6 +794,7 @@ int dasc_plan_upload(dasc_plan_t p, void* device_buffer, int64_t bytes, void* st
   put(p->off_unpack_q, p->unpack_q.data(), p->unpack_q.size() * sizeof(Piece));
   put(p->off_pack_tp, p->pack_tp.data(), p->pack_tp.size() * sizeof(Piece));
   put(p->off_unpack_tp, p->unpack_tp.data(), p->unpack_tp.size() * sizeof(Piece));
+  put(p->off_unpack_rest, p->unpack_rest.data(), p->unpack_rest.size() * sizeof(Piece));
   put(p->off_refresh, p->refresh.data(), p->refresh.size() * sizeof(RefreshTask));
   put(p->off_expA, p->gate_expA.data(), p->gate_expA.size() * sizeof(float));
   put(p->off_dt, p->gate_dt.data(), p->gate_dt.size() * sizeof(float));
@@ -782,6 +810,7 @@ int dasc_plan_upload(dasc_plan_t p, void* device_buffer, int64_t bytes, void* st
   p->dev.unpack_q = reinterpret_cast<const Piece*>(d + p->off_unpack_q);
   p->dev.pack_tp = reinterpret_cast<const Piece*>(d + p->off_pack_tp);
   p->dev.unpack_tp = reinterpret_cast<const Piece*>(d + p->off_unpack_tp);
+  p->dev.unpack_rest = reinterpret_cast<const Piece*>(d + p->off_unpack_rest);
   p->dev.refresh = reinterpret_cast<const RefreshTask*>(d + p->off_refresh);
   p->dev.gate_expA = reinterpret_cast<const float*>(d + p->off_expA);
   p->dev.gate_dt = reinterpret_cast<const float*>(d + p->off_dt);
@@ -1010,7 +1039,8 @@ static int run_refresh(const char* w, bool head_windows, dasc_plan_t p, const ui
                        const uint16_t* v, const uint16_t* a, const float* beta,
                        const int64_t* tok_offsets, int64_t n_tokens, void* dense_base,
                        int64_t dense_stride, int64_t n_dense, const int32_t* dst_idx, int32_t n,
-                       void* stream) {
+                       void* stream, const void* pool_base = nullptr, int64_t pool_stride = 0,
+                       int64_t n_slots = 0, const int32_t* src_slot = nullptr) {
   if (!p) return fail(DASC_EINVAL, std::string(w) + ": null plan");
   if (!p->device) return fail(DASC_ENOTUPLOADED, std::string(w) + ": plan tables not uploaded");
   if (n < 0 || n > 65535) return fail(DASC_EINVAL, std::string(w) + ": n must be in [0, 65535]");
@@ -1050,6 +1080,10 @@ static int run_refresh(const char* w, bool head_windows, dasc_plan_t p, const ui
   args.n = n;
   args.head_windows = head_windows ? 1 : 0;
   args.status = p->dev.status;
+  args.pool = static_cast<const uint8_t*>(pool_base);
+  args.pool_stride = pool_stride;
+  args.n_slots = n_slots;
+  args.src_slot = src_slot;
   for (const Group& g : p->refresh_groups) {
     args.tasks = p->dev.refresh + g.first;
     args.n_tasks = g.count;
@@ -1075,6 +1109,43 @@ int dasc_ckpt_refresh_suffix_windowed(dasc_plan_t p, const uint16_t* k, const ui
                                       const int32_t* dst_idx, int32_t n, void* stream) {
   return run_refresh("ckpt_refresh_suffix_windowed", true, p, k, v, a, beta, tok_offsets,
                      n_tokens, dense_base, dense_stride, n_dense, dst_idx, n, stream);
+}
+
+int dasc_ckpt_unpack_refresh(dasc_plan_t p, const void* pool_base, int64_t pool_stride,
+                             int64_t n_slots, const int32_t* src_slot, const uint16_t* k,
+                             const uint16_t* v, const uint16_t* a, const float* beta,
+                             const int64_t* tok_offsets, int64_t n_tokens, void* dense_base,
+                             int64_t dense_stride, int64_t n_dense, const int32_t* dst_idx,
+                             int32_t n, int32_t head_windows, void* stream) {
+  const char* w = "ckpt_unpack_refresh";
+  int rc = check_move(p, w, dense_base, dense_stride, n_dense, pool_base, pool_stride, n_slots,
+                      src_slot, dst_idx, n);
+  if (rc != DASC_OK || n == 0) return rc;
+  // every replayed head, whole (validates the refresh arguments first)
+  rc = run_refresh(w, head_windows != 0, p, k, v, a, beta, tok_offsets, n_tokens, dense_base,
+                   dense_stride, n_dense, dst_idx, n, stream, pool_base, pool_stride, n_slots,
+                   src_slot);
+  if (rc != DASC_OK) return rc;
+  // heads no refresh task writes, and the conv bytes: the zero-fill unpack
+  MoveArgs m{};
+  m.pieces = p->dev.unpack_rest;
+  m.n_pieces = static_cast<uint32_t>(p->unpack_rest.size());
+  m.kda_r_max = p->kda_r_max;
+  m.kda_128 = p->kda_128;
+  m.src_idx = src_slot;
+  m.dst_idx = dst_idx;
+  m.src_base = static_cast<const uint8_t*>(pool_base);
+  m.src_stride = pool_stride;
+  m.n_src = n_slots;
+  m.dst_base = static_cast<uint8_t*>(dense_base);
+  m.dst_stride = dense_stride;
+  m.n_dst = n_dense;
+  m.n = n;
+  m.status = p->dev.status;
+  int e = launch_move(false, m, stream);
+  if (e) return fail(DASC_EHIP, std::string(w) + ": launch failed: " +
+                                    hipGetErrorString(static_cast<hipError_t>(e)));
+  return DASC_OK;
 }
 
 }  // extern "C"

@@ -67,7 +67,8 @@ struct alignas(64) RefreshTask {
   uint32_t kind;       // kGDN: one gate per head; kKDA: one per channel
   uint32_t local[4];   // bit k set: column k is local and gets written
   uint32_t window;     // Eq. 7 window of the head: max W_u over its local units
-  uint32_t pad[3];
+  uint32_t pool_off;   // fused load: byte offset of the head's first retained unit in a slot
+  uint32_t pad[2];
 };
 
 static_assert(sizeof(Piece) == 64, "Piece layout");
@@ -81,6 +82,7 @@ struct DeviceTables {
   const Piece* unpack_q;   // INT8 unpack
   const Piece* pack_tp;    // TP storage balancing: pack and partition
   const Piece* unpack_tp;  // ... and the gather of a load
+  const Piece* unpack_rest;  // fused load: the unpack pieces of heads no refresh writes
   const RefreshTask* refresh;
   const float* gate_expA;  // exp(A_log) per unit, fp32
   const float* gate_dt;    // dt_bias per unit, fp32
@@ -153,6 +155,11 @@ struct RefreshArgs {
   int32_t n;
   int32_t head_windows;  // nonzero: each head replays only its last `window` tokens
   uint32_t* status;
+  // Fused load (pool != nullptr): request r reads the retained units of
+  // slot src_slot[r] and writes each replayed head whole.
+  const uint8_t* pool;
+  int64_t pool_stride, n_slots;
+  const int32_t* src_slot;
 };
 
 int launch_refresh(int d, int gate, const RefreshArgs& args, void* stream);

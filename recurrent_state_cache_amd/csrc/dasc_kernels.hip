@@ -560,7 +560,10 @@ __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
 
 // WINDOWED: each task replays only the last `window` tokens of its request
 // (a kernel of its own, so that profiles tell the two refreshes apart).
-template <int D, int GATE, bool WINDOWED>
+// FUSED: the load and the refresh in one pass: the head is written whole,
+// the local columns from the replay and the retained ones from its units in
+// the pool slot (what a zero-fill unpack followed by the refresh leaves).
+template <int D, int GATE, bool WINDOWED, bool FUSED>
 __global__ void __launch_bounds__(RefreshShape<D>::kNT)
     __attribute__((amdgpu_waves_per_eu(RefreshShape<D>::kWavesPerSimd)))
 refresh_kernel(RefreshArgs a) {
@@ -582,6 +585,11 @@ refresh_kernel(RefreshArgs a) {
   // Per-head Eq. 7 window: replay only the request's last `window` tokens.
   if constexpr (WINDOWED) t0 = t1 - t0 > task.window ? t1 - task.window : t0;
   if (!in_range(dst, a.n_dense)) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) flag(a.status, DASC_STATUS_BAD_INDEX);
+    return;
+  }
+  const int64_t slot = FUSED ? a.src_slot[req] : 0;
+  if (FUSED && !in_range(slot, a.n_slots)) {
     if (blockIdx.x == 0 && threadIdx.x == 0) flag(a.status, DASC_STATUS_BAD_INDEX);
     return;
   }
@@ -929,6 +937,41 @@ refresh_kernel(RefreshArgs a) {
   // Write back the local units only ([dasc] §4.2).  Lane (g, m) of tile
   // (kt, vt) holds S[v][k .. k + 3] with v = 16 vt + m, k = 16 kt + 4 g.
   float* out = reinterpret_cast<float*>(a.dense + dst * a.dense_stride + task.dense_off);
+  if constexpr (FUSED) {
+    // Whole rows: retained column c of the head is unit j = (retained
+    // channels below c) in the slot, D floats each from pool_off.
+    const float* units = reinterpret_cast<const float*>(a.pool + slot * a.pool_stride +
+                                                        task.pool_off);
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const int k0 = 16 * kt + 4 * g;
+      const int w = k0 >> 5, sh5 = k0 & 31;
+      const uint32_t lw = w == 0 ? task.local[0] : w == 1 ? task.local[1]
+                        : w == 2 ? task.local[2] : task.local[3];
+      const uint32_t r4 = ~(lw >> sh5) & 0xFu;  // retained columns k0 .. k0 + 3
+      uint32_t below = __popc(~lw & ((1u << sh5) - 1u));
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+        if (q < w) below += __popc(~task.local[q]);
+#pragma unroll
+      for (int vv = 0; vv < VTW; ++vv) {
+        const int v = 16 * (wave * VTW + vv) + m;
+        v4f y = acc[kt][vv];
+        if (r4) {
+          uint32_t j = below;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            if ((r4 >> c) & 1u) {
+              y[c] = units[j * D + v];
+              ++j;
+            }
+          }
+        }
+        *reinterpret_cast<v4f*>(out + v * D + k0) = y;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
     const int k0 = 16 * kt + 4 * g;
@@ -1003,22 +1046,28 @@ bool refresh_shape_supported(int d_k, int d_v) {
   return d_k == d_v && (d_k == 16 || d_k == 32 || d_k == 64 || d_k == 128);
 }
 
+template <int D, int GATE, bool W>
+void launch_refresh_f(const RefreshArgs& args, dim3 grid, hipStream_t s) {
+  constexpr int kNT = RefreshShape<D>::kNT;
+  if (args.pool) refresh_kernel<D, GATE, W, true><<<grid, kNT, 0, s>>>(args);
+  else refresh_kernel<D, GATE, W, false><<<grid, kNT, 0, s>>>(args);
+}
+
 template <int D>
 int launch_refresh_d(int gate, const RefreshArgs& args, dim3 grid, hipStream_t s) {
-  constexpr int kNT = RefreshShape<D>::kNT;
   const bool w = args.head_windows != 0;
   switch (gate) {
     case kGateHead:
-      if (w) refresh_kernel<D, kGateHead, true><<<grid, kNT, 0, s>>>(args);
-      else refresh_kernel<D, kGateHead, false><<<grid, kNT, 0, s>>>(args);
+      if (w) launch_refresh_f<D, kGateHead, true>(args, grid, s);
+      else launch_refresh_f<D, kGateHead, false>(args, grid, s);
       break;
     case kGateChan:
-      if (w) refresh_kernel<D, kGateChan, true><<<grid, kNT, 0, s>>>(args);
-      else refresh_kernel<D, kGateChan, false><<<grid, kNT, 0, s>>>(args);
+      if (w) launch_refresh_f<D, kGateChan, true>(args, grid, s);
+      else launch_refresh_f<D, kGateChan, false>(args, grid, s);
       break;
     case kGateChanSplit:
-      if (w) refresh_kernel<D, kGateChanSplit, true><<<grid, kNT, 0, s>>>(args);
-      else refresh_kernel<D, kGateChanSplit, false><<<grid, kNT, 0, s>>>(args);
+      if (w) launch_refresh_f<D, kGateChanSplit, true>(args, grid, s);
+      else launch_refresh_f<D, kGateChanSplit, false>(args, grid, s);
       break;
     default:
       return static_cast<int>(hipErrorInvalidValue);

@@ -281,3 +281,79 @@ def test_windowed_equals_full_when_requests_fit_the_windows():
     assert P.status() == 0
     assert torch.equal(a, b)
     assert not torch.equal(a, base)
+
+
+def _fused_vs_two_step(cfg, P, n_req, windows, seed, head_windows):
+    Wn = np.asarray(windows)
+    inp = W.refresh_inputs(cfg, Wn, device="cuda")
+    n_ck = n_req + 1
+    dense = W.dense_states(cfg, n_ck, device="cuda", seed=seed)
+    info = P.info()
+    pool = torch.zeros((n_ck, info["slot_bytes"]), dtype=torch.uint8, device="cuda")
+    rng = np.random.default_rng(seed)
+    idx = torch.arange(n_ck, dtype=torch.int32, device="cuda")
+    R.ckpt_pack(P, dense, idx, pool, idx)
+    src_slot = torch.from_numpy(rng.permutation(n_ck)[:n_req].astype(np.int32)).cuda()
+    dst = torch.from_numpy(rng.permutation(n_ck)[:n_req].astype(np.int32)).cuda()
+    two = torch.full_like(dense, 0xA5)
+    R.ckpt_unpack_zero_fill(P, pool, src_slot, two, dst)
+    refresh = R.ckpt_refresh_suffix_windowed if head_windows else R.ckpt_refresh_suffix
+    refresh(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, two, dst)
+    one = torch.full_like(dense, 0x5A)
+    R.ckpt_unpack_refresh(P, pool, src_slot, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, one, dst,
+                          head_windows=head_windows)
+    torch.cuda.synchronize()
+    assert P.status() == 0
+    d = dst.cpu().numpy()
+    for r in range(n_req):
+        assert torch.equal(one[int(d[r])], two[int(d[r])]), f"request {r}"
+    return inp, pool, src_slot, dst, one
+
+
+@pytest.mark.parametrize("head_windows", [False, True])
+def test_fused_load_equals_unpack_then_refresh(head_windows):
+    cases = [(W.tiny_kda(), [8, 3], 1),
+             (W.Config("widths", _odd_refresh_layers(24), w_max=64, n_req=3, seed=24), [0, 21, 70], 2),
+             (W.kda_refresh(n_req=4), [256, 9, 16, 31], 3),
+             (W.mixed(n_ckpt=8, n_req=3), [64, 200, 17], 4)]
+    for cfg, windows, seed in cases:
+        P, O = _plans(cfg)
+        log(f"[fused] {cfg.name}: requests {windows}, head windows {head_windows}")
+        _fused_vs_two_step(cfg, P, len(windows), windows, seed, head_windows)
+
+
+def test_fused_load_against_the_oracle():
+    cfg = W.tiny_kda()
+    P, O = _plans(cfg)
+    inp, pool, src_slot, dst, out = _fused_vs_two_step(cfg, P, 2, [8, 5], 7, False)
+    tok = inp.tok_off.cpu().numpy()
+    host_pool = pool.cpu().numpy()
+    for r in range(2):
+        d, sl = int(dst[r]), int(src_slot[r])
+        exp = np.full((1, O.dense_bytes), 0xEE, np.uint8)
+        oracle.unpack_zero_fill(O, host_pool, [sl], exp, [0])
+        got = out[d].cpu().numpy()
+        mask = mask_words(O)
+        assert np.array_equal(got.view(np.uint32) & mask, exp[0].view(np.uint32) & mask)
+        t0, t1 = int(tok[r]), int(tok[r + 1])
+        ref = oracle.refresh_expected(O, _bits16(_host_rows(inp.k, (t0, t1))),
+                                      _bits16(_host_rows(inp.v, (t0, t1))),
+                                      _bits16(_host_rows(inp.a, (t0, t1))),
+                                      _host_rows(inp.beta, (t0, t1)).numpy(),
+                                      np.array([0, t1 - t0]))
+        for (_, li, h), S64 in ref.items():
+            local = local_mask_of_head(O, li, h)
+            assert refresh_error(head_state(got, O, li, h), S64, local) <= TOL
+
+
+def test_fused_load_bad_slot_is_flagged():
+    cfg = W.tiny_kda()
+    P, O = _plans(cfg)
+    inp = W.refresh_inputs(cfg, np.array([8, 8]), device="cuda")
+    pool = torch.zeros((2, P.info()["slot_bytes"]), dtype=torch.uint8, device="cuda")
+    dense = torch.zeros((2, P.info()["dense_bytes"]), dtype=torch.uint8, device="cuda")
+    bad = torch.tensor([0, 5], dtype=torch.int32, device="cuda")
+    dst = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    R.ckpt_unpack_refresh(P, pool, bad, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, dense, dst)
+    torch.cuda.synchronize()
+    assert P.status() & R.STATUS_BAD_INDEX
