@@ -478,6 +478,37 @@ def main():
     t_win = np.array([e[0].elapsed_time(e[1]) for e in evw]) * 1e-3
     win_flops, win_head_tokens = _windowed_work(P, Wn)
 
+    # dasc-wr load of the refreshed requests: unpack then refresh, against
+    # the fused load, with the full suffixes and with per-head windows.
+    src_slot = slot[:cfg.n_req].contiguous()
+    req_out = torch.arange(cfg.n_req, dtype=torch.int32, device="cuda")
+
+    def timed(fn):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.warmup + args.steps):
+            e = evs[i - args.warmup] if i >= args.warmup else None
+            if e: e[0].record(stream)
+            fn()
+            if e: e[1].record(stream)
+        torch.cuda.synchronize()
+        assert P.status() == 0
+        return float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+
+    wr = {}
+    for hw, name in ((False, "full_suffix"), (True, "eq7_windows")):
+        refresh = R.ckpt_refresh_suffix_windowed if hw else R.ckpt_refresh_suffix
+
+        def two_step():
+            R.ckpt_unpack_zero_fill(P, pool, src_slot, out, req_out, stream)
+            refresh(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, out, req_out, stream)
+
+        def fused():
+            R.ckpt_unpack_refresh(P, pool, src_slot, inp.k, inp.v, inp.a, inp.beta, inp.tok_off,
+                                  out, req_out, head_windows=hw, stream=stream)
+        t2, t1 = timed(two_step), timed(fused)
+        wr[name] = {"unpack_then_refresh_ms": round(t2, 4), "fused_ms": round(t1, 4),
+                    "speedup": round(t2 / t1, 3)}
+
     tp8 = _bench_tp(cfg, args, stream) if args.workload in ("kda", "gdn") else None
 
     t_pack = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
@@ -541,6 +572,7 @@ def main():
                       | {"kernel": "qmove_kernel<false>"},
         },
         **({"tp8_storage_balancing": tp8} if tp8 else {}),
+        "dasc_wr_load": dict(wr, requests=cfg.n_req),
         "refresh_eq7_windows": {
             "kernel": "refresh_kernel<128> (per-head window)",
             "ms": round(t_win.mean() * 1e3, 4),
