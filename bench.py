@@ -44,8 +44,9 @@ KERNEL_ROLES = {r"qmove_kernel<true>": "pack_int8", r"qmove_kernel<false>": "unp
                 r"(?<!q)move_kernel<false, \d+, \d+, false>": "unpack",
                 r"(?<!q)move_kernel<true, \d+, \d+, true>": "pack_tp",
                 r"(?<!q)move_kernel<false, \d+, \d+, true>": "unpack_tp",
-                r"refresh_kernel<\d+, \d+, false>": "refresh",
-                r"refresh_kernel<\d+, \d+, true>": "refresh_windowed"}
+                r"refresh_kernel<\d+, \d+, false, false>": "refresh",
+                r"refresh_kernel<\d+, \d+, true, false>": "refresh_windowed",
+                r"refresh_kernel<\d+, \d+, (true|false), true>": "refresh_fused"}
 
 
 def _args():
@@ -55,6 +56,9 @@ def _args():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", choices=["kda", "gdn", "mixed"], default="kda")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-wr-load", action="store_true",
+                    help="skip the dasc-wr load section (its unpack launches would share the "
+                         "unpack kernel's name in a profile)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--summarize", nargs=5, metavar=("STATS", "FETCH", "WRITE", "FETCH_COPY",
@@ -327,7 +331,7 @@ def _summarize(dirs, workload):
              f"WRITE_SIZE (KiB) | HBM bytes per launch (calibrated) |",
              "|---|---|---|---|---|---|---|---|"]
     for role in ("pack", "unpack", "refresh", "pack_int8", "unpack_int8", "pack_tp", "unpack_tp",
-                 "refresh_windowed"):
+                 "refresh_windowed", "refresh_fused"):
         if role not in stats:
             continue
         c, avg, mn, mx = stats[role]
@@ -495,7 +499,7 @@ def main():
         return float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
 
     wr = {}
-    for hw, name in ((False, "full_suffix"), (True, "eq7_windows")):
+    for hw, name in (() if args.skip_wr_load else ((False, "full_suffix"), (True, "eq7_windows"))):
         refresh = R.ckpt_refresh_suffix_windowed if hw else R.ckpt_refresh_suffix
 
         def two_step():
@@ -572,7 +576,7 @@ def main():
                       | {"kernel": "qmove_kernel<false>"},
         },
         **({"tp8_storage_balancing": tp8} if tp8 else {}),
-        "dasc_wr_load": dict(wr, requests=cfg.n_req),
+        **({"dasc_wr_load": dict(wr, requests=cfg.n_req)} if wr else {}),
         "refresh_eq7_windows": {
             "kernel": "refresh_kernel<128> (per-head window)",
             "ms": round(t_win.mean() * 1e3, 4),
