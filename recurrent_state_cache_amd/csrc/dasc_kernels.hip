@@ -939,9 +939,12 @@ refresh_kernel(RefreshArgs a) {
   float* out = reinterpret_cast<float*>(a.dense + dst * a.dense_stride + task.dense_off);
   if constexpr (FUSED) {
     // Whole rows: retained column c of the head is unit j = (retained
-    // channels below c) in the slot, D floats each from pool_off.
+    // channels below c) in the slot, D floats each from pool_off.  All the
+    // gathers are issued before any store (the slot and the destination are
+    // different buffers, which the compiler cannot know).
     const float* units = reinterpret_cast<const float*>(a.pool + slot * a.pool_stride +
                                                         task.pool_off);
+    v4f y[KT][VTW];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
       const int k0 = 16 * kt + 4 * g;
@@ -956,20 +959,23 @@ refresh_kernel(RefreshArgs a) {
 #pragma unroll
       for (int vv = 0; vv < VTW; ++vv) {
         const int v = 16 * (wave * VTW + vv) + m;
-        v4f y = acc[kt][vv];
-        if (r4) {
-          uint32_t j = below;
+        y[kt][vv] = acc[kt][vv];
+        uint32_t j = below;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            if ((r4 >> c) & 1u) {
-              y[c] = units[j * D + v];
-              ++j;
-            }
+        for (int c = 0; c < 4; ++c) {
+          if ((r4 >> c) & 1u) {
+            y[kt][vv][c] = units[j * D + v];
+            ++j;
           }
         }
-        *reinterpret_cast<v4f*>(out + v * D + k0) = y;
       }
     }
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int vv = 0; vv < VTW; ++vv)
+        *reinterpret_cast<v4f*>(out + (16 * (wave * VTW + vv) + m) * D + 16 * kt + 4 * g) =
+            y[kt][vv];
     return;
   }
 #pragma unroll
