@@ -236,3 +236,37 @@ def test_tp_build_rejects():
     with pytest.raises(R.DascError) as e:
         R.Plan(mixed.layers, mixed.a_s, mixed.eps, mixed.w_max, tp=2, rank=0)
     assert e.value.code == -5
+
+
+def test_every_data_call_needs_uploaded_tables():
+    # The newer entry points reject a plan whose tables are not on a device
+    # (DASC_ENOTUPLOADED) or a null plan (DASC_EINVAL) before any launch.
+    P = R.Plan([_desc()], w_max=16)
+    f = ctypes.c_void_p(16)
+    L = R.lib
+    calls = {
+        "pack_int8": lambda h: L.dasc_ckpt_pack_int8(h, f, 4096, 1, f, f, 4096, 1, f, 1, None),
+        "unpack_int8": lambda h: L.dasc_ckpt_unpack_int8_zero_fill(h, f, 4096, 1, f, f, 4096, 1,
+                                                                 f, 1, None),
+        "refresh_windowed": lambda h: L.dasc_ckpt_refresh_suffix_windowed(h, f, f, f, f, f, 1, f,
+                                                                          4096, 1, f, 1, None),
+        "pack_tp": lambda h: L.dasc_ckpt_pack_tp(h, f, 4096, 1, f, f, 4096, 1, f, f, 4096, 1, f,
+                                                 1, None),
+        "unpack_tp": lambda h: L.dasc_ckpt_unpack_tp_zero_fill(h, f, 4096, 1, f, f, 4096, 1, f,
+                                                               f, 4096, 1, f, 1, None),
+        "unpack_refresh": lambda h: L.dasc_ckpt_unpack_refresh(h, f, 4096, 1, f, f, f, f, f, f, 1,
+                                                               f, 4096, 1, f, 1, 0, None),
+    }
+    for name, call in calls.items():
+        assert call(P._h) == -2, name
+        assert call(None) == -1, name
+
+
+def test_tp_calls_reject_a_mixed_store_plan():
+    # GDN and KDA layers have units of different sizes: no balancing
+    cfg = W.mixed(n_ckpt=2, n_req=2)
+    P = R.Plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max)
+    assert P.tp_info()["one_store"] == 0
+    f = ctypes.c_void_p(16)
+    assert R.lib.dasc_ckpt_pack_tp(P._h, f, 4096, 1, f, f, 4096, 1, f, f, 4096, 1, f, 1,
+                                   None) == -5
