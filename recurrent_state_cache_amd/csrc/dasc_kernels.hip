@@ -426,8 +426,13 @@ __global__ void __launch_bounds__(kThreads) qmove_kernel(MoveArgs a) {
 // a request pad the last chunk as exact no-ops (alpha = 1, k = v = 0,
 // beta = 0).
 //
-// The three products run on fp32 MFMA (v_mfma_f32_16x16x4f32).  The state is
-// kept transposed, S^T [k][v], in 16 x 16 accumulator tiles: lane (g, m)
+// The three products run on MFMA.  For d <= 32 all three are fp32
+// (v_mfma_f32_16x16x4f32); for d >= 64 the readout and the update use bf16
+// hi / lo splits of both operands (v_mfma_f32_16x16x32_bf16, hi hi + hi lo +
+// lo hi with fp32 accumulation: fp32 MFMA runs at the fp32 vector rate on
+// gfx950 and does not overlap the VALU work, bf16 moves 8x the MACs per
+// instruction), and C = T R stays fp32.  The state is kept transposed,
+// S^T [k][v], in 16 x 16 accumulator tiles: lane (g, m)
 // (g = lane / 16, m = lane % 16) of tile (kt, vt) holds
 // S^T[16 kt + 4 g + r][16 vt + m], r = 0..3.  With the K index of k-step r
 // read as 4 g + r on both operands, those same registers are the B operand
@@ -435,7 +440,8 @@ __global__ void __launch_bounds__(kThreads) qmove_kernel(MoveArgs a) {
 //   U0^T[t][v] = sum_k Q[t][k] S^T[k][v]   (A = Q from LDS, B = S^T)
 //   C[t][v]    = sum_s T[t][s] R[s][v]     (A = T from LDS, B = R)
 //   S^T[k][v] += sum_t W[k][t] C[t][v]     (A = W from LDS, B = C)
-// so the state never moves.  Each wave owns all k tiles of its v tiles: no
+// (with bf16 operands two k tiles, or the C hi and lo halves, fill the 8 K
+// slots of a lane group), so the state never moves.  Each wave owns all k tiles of its v tiles: no
 // product needs a cross-wave reduction.
 //
 // Software pipeline.  The chunk inputs (decays from the gate logits by
@@ -445,9 +451,10 @@ __global__ void __launch_bounds__(kThreads) qmove_kernel(MoveArgs a) {
 //            (decays, k, v, beta into LDS); fetch chunk n + 2
 //   phase 2: R, C = T R; S <- S Diag(gamma) + W C  ||  L(n + 1), gamma,
 //            Q(n + 1), W(n + 1)
-// with one barrier after each phase.  Both phases are branch-free, and the
-// two workgroups a CU holds overlap each other's phases.  LDS buffers
-// that live across an iteration are double-buffered by chunk parity.
+// with one barrier after each phase; T(n) is computed by one wave per chunk,
+// rotating.  The two workgroups a CU holds overlap each other's phases.
+// LDS buffers that live across an iteration are double-buffered by chunk
+// parity; staging and fetches past the request's last chunk are skipped.
 // ---------------------------------------------------------------------------
 typedef float v4f __attribute__((ext_vector_type(4)));
 
@@ -466,7 +473,7 @@ struct RefreshShape {
   static_assert(2 * D <= kNT, "one staged item per lane");
 };
 
-// Q and W in fp32 (d = 16) or as bf16 hi / lo pairs (the split products).
+// Q and W in fp32 (d <= 32) or as bf16 hi / lo pairs (the split products).
 template <int D, bool SPLIT>
 struct RefreshQW {
   float Q[kC][D + 4];         // gamma_t o k_t
