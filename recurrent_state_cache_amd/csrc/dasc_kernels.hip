@@ -217,22 +217,53 @@ __global__ void __launch_bounds__(kThreads) move_kernel(MoveArgs a) {
 //
 // Pack pieces are whole heads (a column's scale spans all d_v rows): lane
 // (vl, kg), kg = tid % 32, vl = tid / 32, holds columns 4 kg .. 4 kg + 3 of
-// rows vl + 8 i (i < 16) in registers; the column maxima are combined over
-// the 8 row lanes in LDS.  A GDN head writes its int8 rows directly (32
-// lanes cover a row) and its d_k scales; a KDA head stages the int8 bytes of
-// its retained columns in LDS and writes each unit contiguously.  Unpack
+// the 16 consecutive rows 16 vl .. 16 vl + 15 in registers; the column
+// maxima are combined over the 8 row lanes in LDS.  A GDN head writes its
+// int8 rows directly (32 lanes cover a row) and its d_k scales.  A KDA head
+// transposes each lane's 16 x 4 int8 block in registers, so that a retained
+// column's 16 bytes are one 16-byte LDS store into its unit; the units then
+// leave LDS as 16-byte pieces of contiguous pool bytes.  (Pieces of 32
+// channels x all rows, 16 KiB like the fp32 pieces, read 128-byte segments
+// at the row stride and streamed HBM far worse than whole heads.)  Unpack
 // pieces are GDN heads by blocks of 32 rows (lane: 4 rows x 4 columns) and
-// KDA heads whole (units and scales through LDS, 4x4 blocks transposed in
-// registers, +0.0 in omitted columns).
+// KDA heads whole: the units and scales come into LDS as 16-byte pieces,
+// each lane reads the 16 bytes of its rows for each of its retained columns
+// and writes its 16 rows x 4 columns (+0.0 in omitted columns).  LDS unit
+// rows are padded to 144 bytes so that lanes reading or writing different
+// units at the same row offset fall on different banks.
 // ---------------------------------------------------------------------------
 constexpr float kScaleFloor = 1e-8f;
-constexpr int kQRows = 16;  // rows a lane holds in a pack piece (d_v <= 128, 8 row lanes)
+constexpr int kQRows = 16;     // consecutive rows a lane holds (d_v <= 128, 8 row lanes)
+constexpr int kQStride = 144;  // bytes per unit row of the LDS staging buffer
 
 __device__ __forceinline__ uint32_t quant4(f32x4 x, f32x4 s) {
   uint32_t w = 0;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const float r = rintf(x[c] / s[c]);
+    const float qf = r != r ? 0.f : fminf(fmaxf(r, -127.f), 127.f);
+    w |= (static_cast<uint32_t>(static_cast<int32_t>(qf)) & 0xFFu) << (8 * c);
+  }
+  return w;
+}
+
+// The same codes from the product y = x (1 / s), with 1 / s correctly
+// rounded.  Within one column |x / s| <= 127 (1 + 2^-23), and y and the
+// correctly rounded quotient each lie within a relative 2^-23 + 2^-48 and
+// 2^-24 of x / s, so they differ by less than 2.3e-5: their nearest integers
+// agree unless y lies within that distance of a half-integer, and only such
+// entries (about one in 8000 of random data) take the division.  NaN and
+// infinite entries give the same codes on both routes (an infinite column
+// maximum makes 1 / s = 0 and every product 0 or NaN, as the quotients are).
+constexpr float kHalfGuard = 0.5f - 6e-5f;
+
+__device__ __forceinline__ uint32_t quant4_fast(f32x4 x, f32x4 s, f32x4 inv) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float y = x[c] * inv[c];
+    float r = rintf(y);
+    if (__builtin_expect(fabsf(y - r) > kHalfGuard, 0)) r = rintf(x[c] / s[c]);
     const float qf = r != r ? 0.f : fminf(fmaxf(r, -127.f), 127.f);
     w |= (static_cast<uint32_t>(static_cast<int32_t>(qf)) & 0xFFu) << (8 * c);
   }
@@ -247,15 +278,242 @@ __device__ __forceinline__ f32x4 dequant4(uint32_t w, f32x4 s) {
   return x;
 }
 
+// 4 x 4 byte transpose: byte c of a[i] becomes byte i of b[c].
+__device__ __forceinline__ void transpose4(const uint32_t (&a)[4], uint32_t (&b)[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    uint32_t x = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x |= ((a[i] >> (8 * c)) & 0xFFu) << (8 * i);
+    b[c] = x;
+  }
+}
+
 __device__ __forceinline__ float load_scale(const uint8_t* p) {
   return *reinterpret_cast<const float*>(p);
 }
 
+// Pack of a GDN head: every unit of the head, whole.
+__device__ __forceinline__ void qpack_gdn_head(const Piece& t, const uint8_t* src, uint8_t* dst,
+                                               float (&red)[8][128]) {
+  const int dk = t.d_k, dv = t.d_v, KG = dk / 4;
+  const int tid = threadIdx.x, kg = tid % 32, vl = tid / 32;
+  const bool col_on = kg < KG;
+  const float* S = reinterpret_cast<const float*>(src + t.dense_off);
+  f32x4 x[kQRows];
+  f32x4 mx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kQRows; ++i) {
+    const int v = kQRows * vl + i;
+    x[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (col_on && v < dv) {
+      x[i] = ld_stream(reinterpret_cast<const f32x4*>(S + v * dk + 4 * kg));
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float m = fabsf(x[i][c]);
+        mx[c] = m > mx[c] ? m : mx[c];
+      }
+    }
+  }
+  *reinterpret_cast<f32x4*>(&red[vl][4 * kg]) = mx;
+  __syncthreads();
+  if (!col_on) return;
+  f32x4 sc, inv;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float m = 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) m = red[r][4 * kg + c] > m ? red[r][4 * kg + c] : m;
+    sc[c] = (m > kScaleFloor ? m : kScaleFloor) / 127.f;  // correctly rounded fp32 division
+    inv[c] = 1.f / sc[c];
+  }
+  uint8_t* Q = dst + t.pool_off;
+#pragma unroll
+  for (int i = 0; i < kQRows; ++i) {
+    const int v = kQRows * vl + i;
+    if (v < dv) *reinterpret_cast<uint32_t*>(Q + v * dk + 4 * kg) = quant4_fast(x[i], sc, inv);
+  }
+  if (vl == 0) {
+    float* Sc = reinterpret_cast<float*>(dst + t.scale_off);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) Sc[4 * kg + c] = sc[c];
+  }
+}
+
+// Pack of a KDA head with a retained channel, whole: lane (vl, kg) as for
+// a GDN head; each retained column's bytes of the lane's 16 rows go to its
+// unit in LDS as one 16-byte store, then the head's units leave LDS as
+// 16-byte pieces of contiguous pool bytes.
+__device__ __forceinline__ void qpack_kda_head(const Piece& t, const uint8_t* src, uint8_t* dst,
+                                               float (&red)[8][128], uint8_t* qbuf) {
+  const int dk = t.d_k, dv = t.d_v, KG = dk / 4;
+  const int tid = threadIdx.x, kg = tid % 32, vl = tid / 32;
+  const bool col_on = kg < KG;
+  uint32_t bits4 = 0, below = 0;
+  lane_ranks(t, kg, bits4, below);
+  const float* S = reinterpret_cast<const float*>(src + t.dense_off);
+  f32x4 x[kQRows];
+  f32x4 mx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kQRows; ++i) {
+    const int v = kQRows * vl + i;
+    x[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (col_on && v < dv) {
+      x[i] = ld_stream(reinterpret_cast<const f32x4*>(S + v * dk + 4 * kg));
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float m = fabsf(x[i][c]);
+        mx[c] = m > mx[c] ? m : mx[c];
+      }
+    }
+  }
+  *reinterpret_cast<f32x4*>(&red[vl][4 * kg]) = mx;
+  __syncthreads();
+  if (col_on) {
+    f32x4 sc, inv;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float m = 0.f;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) m = red[r][4 * kg + c] > m ? red[r][4 * kg + c] : m;
+      sc[c] = (m > kScaleFloor ? m : kScaleFloor) / 127.f;  // correctly rounded fp32 division
+      inv[c] = 1.f / sc[c];
+    }
+    uint32_t cw[4][4];  // [column c][row group m]; rows >= d_v hold zeros, never copied out
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t w[4] = {quant4_fast(x[4 * m], sc, inv), quant4_fast(x[4 * m + 1], sc, inv),
+                             quant4_fast(x[4 * m + 2], sc, inv), quant4_fast(x[4 * m + 3], sc, inv)};
+      uint32_t b[4];
+      transpose4(w, b);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) cw[c][m] = b[c];
+    }
+    uint32_t rk = below;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if ((bits4 >> c) & 1u) {
+        *reinterpret_cast<u32x4*>(&qbuf[rk * kQStride + 16 * vl]) =
+            u32x4{cw[c][0], cw[c][1], cw[c][2], cw[c][3]};
+        ++rk;
+      }
+    }
+    if (vl == 0) {
+      float* Sc = reinterpret_cast<float*>(dst + t.scale_off);
+      rk = below;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if ((bits4 >> c) & 1u) {
+          Sc[rk] = sc[c];
+          ++rk;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int r = t.r;
+  uint8_t* U = dst + t.pool_off;
+  if ((dv % 16) == 0 && (t.pool_off % 16) == 0) {
+    const int per = dv / 16;
+    for (int q = tid; q < r * per; q += kThreads) {
+      const int j = q / per, o = q % per;
+      st_stream(*reinterpret_cast<const u32x4*>(&qbuf[j * kQStride + 16 * o]),
+                reinterpret_cast<u32x4*>(U + j * dv + 16 * o));
+    }
+  } else {
+    const int per = dv / 4;
+    for (int q = tid; q < r * per; q += kThreads) {
+      const int j = q / per, o = q % per;
+      *reinterpret_cast<uint32_t*>(U + j * dv + 4 * o) =
+          *reinterpret_cast<const uint32_t*>(&qbuf[j * kQStride + 4 * o]);
+    }
+  }
+}
+
+// Unpack of 32 rows of a GDN head: lane holds rows 32 rb + 4 vl + i, columns 4 kg ..
+__device__ __forceinline__ void qunpack_gdn_rows(const Piece& t, const uint8_t* src, uint8_t* dst) {
+  const int dk = t.d_k, dv = t.d_v, KG = dk / 4;
+  const int tid = threadIdx.x, kg = tid % 32, vl = tid / 32;
+  if (kg >= KG) return;
+  float* S = reinterpret_cast<float*>(dst + t.dense_off);
+  const uint8_t* Sc = src + t.scale_off;
+  const f32x4 sc = {load_scale(Sc + 16 * kg), load_scale(Sc + 16 * kg + 4),
+                    load_scale(Sc + 16 * kg + 8), load_scale(Sc + 16 * kg + 12)};
+  const uint8_t* Q = src + t.pool_off;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int v = kKdaRows * t.rb + 4 * vl + i;
+    if (v < dv) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(Q + v * dk + 4 * kg);
+      st_stream(dequant4(w, sc), reinterpret_cast<f32x4*>(S + v * dk + 4 * kg));
+    }
+  }
+}
+
+// Unpack of a KDA head, whole: units and scales into LDS, then every element.
+__device__ __forceinline__ void qunpack_kda_head(const Piece& t, const uint8_t* src, uint8_t* dst,
+                                                 uint8_t* qbuf, float* qs) {
+  const int dk = t.d_k, dv = t.d_v, KG = dk / 4;
+  const int tid = threadIdx.x, kg = tid % 32, vl = tid / 32;
+  uint32_t bits4 = 0, below = 0;
+  lane_ranks(t, kg, bits4, below);
+  float* S = reinterpret_cast<float*>(dst + t.dense_off);
+  const int r = t.r;
+  const uint8_t* U = src + t.pool_off;
+  if ((dv % 16) == 0 && (t.pool_off % 16) == 0) {
+    const int per = dv / 16;
+    for (int q = tid; q < r * per; q += kThreads) {
+      const int j = q / per, o = q % per;
+      *reinterpret_cast<u32x4*>(&qbuf[j * kQStride + 16 * o]) =
+          ld_stream(reinterpret_cast<const u32x4*>(U + j * dv + 16 * o));
+    }
+  } else {
+    const int per = dv / 4;
+    for (int q = tid; q < r * per; q += kThreads) {
+      const int j = q / per, o = q % per;
+      *reinterpret_cast<uint32_t*>(&qbuf[j * kQStride + 4 * o]) =
+          *reinterpret_cast<const uint32_t*>(U + j * dv + 4 * o);
+    }
+  }
+  if (tid < r) qs[tid] = load_scale(src + t.scale_off + 4 * tid);
+  __syncthreads();
+  if (kg >= KG) return;
+  // the 16 bytes of rows 16 vl .. 16 vl + 15 of each of this lane's columns;
+  // an omitted column reads as q = 0 with scale 0, i.e. +0.0
+  uint32_t cw[4][4];  // [column c][row group m]
+  f32x4 s;
+  uint32_t rk = below;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    u32x4 q = {0u, 0u, 0u, 0u};
+    s[c] = 0.f;
+    if ((bits4 >> c) & 1u) {
+      q = *reinterpret_cast<const u32x4*>(&qbuf[rk * kQStride + 16 * vl]);
+      s[c] = qs[rk];
+      ++rk;
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) cw[c][m] = q[m];
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint32_t w[4] = {cw[0][m], cw[1][m], cw[2][m], cw[3][m]};
+    uint32_t rows[4];
+    transpose4(w, rows);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int v = kQRows * vl + 4 * m + i;
+      if (v < dv)
+        st_stream(dequant4(rows[i], s), reinterpret_cast<f32x4*>(S + v * dk + 4 * kg));
+    }
+  }
+}
+
 template <bool kPack>
 __global__ void __launch_bounds__(kThreads) qmove_kernel(MoveArgs a) {
-  __shared__ __attribute__((aligned(16))) float red[8][128];            // column maxima per row lane
-  __shared__ __attribute__((aligned(16))) uint32_t qbuf[128][128 / 4];  // KDA units, int8 x 4 per word
-  __shared__ float qs[128];                                             // KDA scales
+  __shared__ __attribute__((aligned(16))) float red[kPack ? 8 : 1][128];  // column maxima per row lane
+  __shared__ __attribute__((aligned(16))) uint8_t qbuf[128 * kQStride];   // KDA units, int8
+  __shared__ float qs[kPack ? 1 : 128];                                   // KDA scales (unpack)
   const Piece t = a.pieces[blockIdx.x];
   const int64_t si = a.src_idx[blockIdx.y];
   const int64_t di = a.dst_idx[blockIdx.y];
@@ -270,141 +528,16 @@ __global__ void __launch_bounds__(kThreads) qmove_kernel(MoveArgs a) {
     copy_piece<kPack>(t, src, dst);
     return;
   }
-  const int dk = t.d_k, dv = t.d_v, KG = dk / 4, VG = dv / 4;
-  const int tid = threadIdx.x, kg = tid % 32, vl = tid / 32;
-  const bool col_on = kg < KG;
-  const bool kda = t.type == kPieceQKda;
-  uint32_t bits4 = 0, below = 0;
-  if (kda) lane_ranks(t, kg, bits4, below);
   if constexpr (kPack) {
-    const float* S = reinterpret_cast<const float*>(src + t.dense_off);
-    f32x4 x[kQRows];
-    f32x4 mx = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < kQRows; ++i) {
-      const int v = vl + 8 * i;
-      x[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (col_on && v < dv) {
-        x[i] = ld_stream(reinterpret_cast<const f32x4*>(S + v * dk + 4 * kg));
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float m = fabsf(x[i][c]);
-          mx[c] = m > mx[c] ? m : mx[c];
-        }
-      }
-    }
-    *reinterpret_cast<f32x4*>(&red[vl][4 * kg]) = mx;
-    __syncthreads();
-    f32x4 sc;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      float m = 0.f;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) m = red[r][4 * kg + c] > m ? red[r][4 * kg + c] : m;
-      sc[c] = (m > kScaleFloor ? m : kScaleFloor) / 127.f;  // correctly rounded fp32 division
-    }
-    if (!kda) {
-      uint8_t* Q = dst + t.pool_off;
-#pragma unroll
-      for (int i = 0; i < kQRows; ++i) {
-        const int v = vl + 8 * i;
-        if (col_on && v < dv)
-          *reinterpret_cast<uint32_t*>(Q + v * dk + 4 * kg) = quant4(x[i], sc);
-      }
-      if (col_on && vl == 0) {
-        float* Sc = reinterpret_cast<float*>(dst + t.scale_off);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) Sc[4 * kg + c] = sc[c];
-      }
-      return;
-    }
-    // KDA: the retained columns' int8 bytes into LDS as units [rank][v]
-    uint8_t* qb = reinterpret_cast<uint8_t*>(&qbuf[0][0]);
-    if (col_on) {
-#pragma unroll
-      for (int i = 0; i < kQRows; ++i) {
-        const int v = vl + 8 * i;
-        if (v < dv) {
-          const uint32_t w = quant4(x[i], sc);
-          uint32_t rk = below;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            if ((bits4 >> c) & 1u) {
-              qb[rk * 128 + v] = static_cast<uint8_t>((w >> (8 * c)) & 0xFFu);
-              ++rk;
-            }
-          }
-        }
-      }
-      if (vl == 0) {
-        float* Sc = reinterpret_cast<float*>(dst + t.scale_off);
-        uint32_t rk = below;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if ((bits4 >> c) & 1u) {
-            Sc[rk] = sc[c];
-            ++rk;
-          }
-        }
-      }
-    }
-    __syncthreads();
-    const int r = t.r, wpu = dv / 4;  // 4-byte words per unit
-    uint32_t* U = reinterpret_cast<uint32_t*>(dst + t.pool_off);
-    for (int q = tid; q < r * wpu; q += kThreads) {
-      const int j = q / wpu, o = q % wpu;
-      U[j * wpu + o] = qbuf[j][o];
-    }
+    if (t.type == kPieceQKda)
+      qpack_kda_head(t, src, dst, red, qbuf);
+    else
+      qpack_gdn_head(t, src, dst, red);
   } else {
-    float* S = reinterpret_cast<float*>(dst + t.dense_off);
-    if (!kda) {
-      // 32 rows of a GDN head: lane holds rows 32 rb + 4 vl + i, columns 4 kg ..
-      if (!col_on) return;
-      const uint8_t* Sc = src + t.scale_off;
-      const f32x4 sc = {load_scale(Sc + 16 * kg), load_scale(Sc + 16 * kg + 4),
-                        load_scale(Sc + 16 * kg + 8), load_scale(Sc + 16 * kg + 12)};
-      const uint8_t* Q = src + t.pool_off;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int v = kKdaRows * t.rb + 4 * vl + i;
-        if (v < dv) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(Q + v * dk + 4 * kg);
-          st_stream(dequant4(w, sc), reinterpret_cast<f32x4*>(S + v * dk + 4 * kg));
-        }
-      }
-      return;
-    }
-    // KDA head: units and scales into LDS, then every element of the head
-    const int r = t.r, wpu = dv / 4;
-    const uint32_t* U = reinterpret_cast<const uint32_t*>(src + t.pool_off);
-    for (int q = tid; q < r * wpu; q += kThreads) {
-      const int j = q / wpu, o = q % wpu;
-      qbuf[j][o] = U[j * wpu + o];
-    }
-    if (tid < r) qs[tid] = load_scale(src + t.scale_off + 4 * tid);
-    __syncthreads();
-    if (!col_on) return;
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-      const int vg = vl + 8 * blk;  // rows 4 vg .. 4 vg + 3
-      if (vg >= VG) break;
-      f32x4 col[4];
-      uint32_t rk = below;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if ((bits4 >> c) & 1u) {
-          const float s = qs[rk];
-          col[c] = dequant4(qbuf[rk][vg], f32x4{s, s, s, s});
-          ++rk;
-        } else {
-          col[c] = f32x4{0.f, 0.f, 0.f, 0.f};  // omitted channel: +0.0
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        st_stream(f32x4{col[0][i], col[1][i], col[2][i], col[3][i]},
-                  reinterpret_cast<f32x4*>(S + (4 * vg + i) * dk + 4 * kg));
-    }
+    if (t.type == kPieceQKda)
+      qunpack_kda_head(t, src, dst, qbuf, qs);
+    else
+      qunpack_gdn_rows(t, src, dst);
   }
 }
 

@@ -65,7 +65,7 @@ def _run_and_check(cfg, P, O, dense, n, sample, seed, pool_pad=0, dense_pad=0):
     return pool_full, out_full
 
 
-@pytest.mark.parametrize("name,n_sample", [("tiny_kda", 2), ("gdn", 3), ("kda", 3), ("mixed", 6)])
+@pytest.mark.parametrize("name,n_sample", [("tiny_kda", 2), ("gdn", 3), ("kda", 3), ("mixed", 30)])
 def test_pack_unpack_full_size(name, n_sample):
     cfg = W.CONFIGS[name]()
     log(f"[ckpt] {name}: {cfg.n_ckpt} checkpoints, W_max={cfg.w_max}")

@@ -131,6 +131,45 @@ def test_int8_error_bound_against_the_state():
     assert bool((Sh[~keep] == 0).all())
 
 
+def _tie_states(O, n, seed):
+    """Dense states whose quotients S / s sit on and next to half-integers:
+    each retained column's first row is +-127 s (so the column maximum gives
+    s back), the others (k + 1/2 + delta) s in fp32 for deltas from 0 up to
+    1e-4 (exact ties, one-ulp neighbours and values just inside and outside
+    a few 1e-5 of the tie)."""
+    rng = np.random.default_rng(seed)
+    f = np.float32
+    deltas = np.array([0, 0, 0, 1e-7, -1e-7, 1e-6, -1e-6, 2e-5, -2e-5, 5e-5, -5e-5, 7e-5,
+                       -7e-5, 1e-4, -1e-4], np.float64)
+    host = np.zeros((n, O.dense_bytes), np.uint8)
+    for c in range(n):
+        off = 0
+        parts = []
+        for L in O.layers:
+            H, dv, dk = L.n_heads, L.d_v, L.d_k
+            s = (f(2.0) ** rng.integers(-20, 20, (H, 1, dk))).astype(f) * \
+                rng.uniform(1, 2, (H, 1, dk)).astype(f)
+            k = rng.integers(-127, 127, (H, dv, dk)).astype(np.float64)
+            d = deltas[rng.integers(0, len(deltas), (H, dv, dk))]
+            S = ((k + 0.5 + d) * s.astype(np.float64)).astype(f)
+            if dv > 1:
+                S[:, 0, :] = (f(127.0) * s[:, 0, :]) * np.where(rng.random((H, dk)) < 0.5, f(-1), f(1))
+            parts.append(S.reshape(-1))
+        t = np.concatenate(parts)
+        host[c, :t.nbytes] = t.view(np.uint8)
+        host[c, O.B_temp_dense:] = rng.integers(0, 256, O.B_conv, dtype=np.uint8)
+    return host
+
+
+def test_int8_rounding_ties_and_near_ties():
+    # exercises the exact-division route of the pack on most blocks
+    cfg = W.Config("odd8", _odd_int8_layers(8), w_max=3)
+    P, O = _plans(cfg)
+    n = 3
+    dense = torch.from_numpy(_tie_states(O, n, seed=21)).cuda()
+    _run(P, O, dense, n, list(range(n)), seed=5)
+
+
 def test_int8_rejects_unsupported_widths():
     lay = W.Layer(W.GDN, 2, 128, 160, np.full(2, -8.0, np.float32), np.zeros(2, np.float32), 0)
     cfg = W.Config("wide", [lay], w_max=4)
