@@ -44,9 +44,9 @@ KERNEL_ROLES = {r"qmove_kernel<true>": "pack_int8", r"qmove_kernel<false>": "unp
                 r"(?<!q)move_kernel<false, \d+, \d+, false>": "unpack",
                 r"(?<!q)move_kernel<true, \d+, \d+, true>": "pack_tp",
                 r"(?<!q)move_kernel<false, \d+, \d+, true>": "unpack_tp",
-                r"refresh_kernel<\d+, \d+, false, false>": "refresh",
-                r"refresh_kernel<\d+, \d+, true, false>": "refresh_windowed",
-                r"refresh_kernel<\d+, \d+, (true|false), true>": "refresh_fused"}
+                r"refresh_kernel<\d+, \d+, false, false, false>": "refresh",
+                r"refresh_kernel<\d+, \d+, true, false, (true|false)>": "refresh_windowed",
+                r"refresh_kernel<\d+, \d+, (true|false), true, (true|false)>": "refresh_fused"}
 
 
 def _args():
@@ -535,7 +535,7 @@ def main():
     mm_bf16, mm_f32 = _refresh_mfma_flops(P, Wn)
     roof_ref = {"bound": "mfma", "achieved": round(ref_tf, 3), "peak": FP32_MFMA_PEAK_TF,
                 "unit": "TFLOP/s", "frac": round(ref_tf / FP32_MFMA_PEAK_TF, 4),
-                "traffic": traffic.get("refresh"), "kernel": "refresh_kernel<128, gate, false>",
+                "traffic": traffic.get("refresh"), "kernel": "refresh_kernel<128, gate, false, false, false>",
                 "ms": round(t_ref.mean() * 1e3, 4), "flops": int(flops),
                 "note": "algorithmic fp32 flops (5 d^2 per token-head) against the fp32 matrix "
                         "peak; the big products run as bf16 hi/lo splits on the bf16 matrix "
@@ -578,7 +578,7 @@ def main():
         **({"tp8_storage_balancing": tp8} if tp8 else {}),
         **({"dasc_wr_load": dict(wr, requests=cfg.n_req)} if wr else {}),
         "refresh_eq7_windows": {
-            "kernel": "refresh_kernel<128> (per-head window)",
+            "kernel": "refresh_kernel<128, gate, true, false, one_chunk> (per-head windows; the one-chunk kernel when every window is at most 16 tokens)",
             "ms": round(t_win.mean() * 1e3, 4),
             "head_tokens": int(win_head_tokens),
             "flops": int(win_flops),

@@ -381,8 +381,10 @@ void build_tables(dasc_plan* p) {
     }
   }
   for (size_t i = 0; i < rkeys.size(); ++i) {
+    uint32_t max_window = 0;
+    for (const RefreshTask& t : rtasks[i]) max_window = std::max(max_window, t.window);
     Group g{std::get<0>(rkeys[i]), std::get<1>(rkeys[i]), static_cast<uint32_t>(p->refresh.size()),
-            static_cast<uint32_t>(rtasks[i].size()), std::get<2>(rkeys[i])};
+            static_cast<uint32_t>(rtasks[i].size()), std::get<2>(rkeys[i]), max_window};
     p->refresh.insert(p->refresh.end(), rtasks[i].begin(), rtasks[i].end());
     p->refresh_groups.push_back(g);
   }
@@ -1087,6 +1089,7 @@ static int run_refresh(const char* w, bool head_windows, dasc_plan_t p, const ui
   for (const Group& g : p->refresh_groups) {
     args.tasks = p->dev.refresh + g.first;
     args.n_tasks = g.count;
+    args.one_chunk = head_windows && g.max_window <= static_cast<uint32_t>(kRefreshChunk) ? 1 : 0;
     int e = launch_refresh(g.d_k, g.gate, args, stream);
     if (e) return fail(DASC_EHIP, std::string(w) + ": launch failed: " +
                                       hipGetErrorString(static_cast<hipError_t>(e)));

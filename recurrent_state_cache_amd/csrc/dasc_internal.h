@@ -94,12 +94,15 @@ constexpr int kGateHead = 0;       // one logit per head (GDN)
 constexpr int kGateChan = 1;       // one per channel, 16-byte aligned rows of 8 (KDA)
 constexpr int kGateChanSplit = 2;  // one per channel, read element by element (KDA)
 
+constexpr int kRefreshChunk = 16;  // tokens per refresh chunk (the MFMA tile edge)
+
 // A run of refresh tasks that share one kernel instantiation (head width and
 // gate mode).
 struct Group {
   int32_t d_k, d_v;
   uint32_t first, count;
   int32_t gate;
+  uint32_t max_window;  // largest Eq. 7 window of the run's heads
 };
 
 // Arguments of one pack or unpack launch: grid x = the pieces, grid y = the
@@ -154,6 +157,7 @@ struct RefreshArgs {
   const int32_t* dst_idx;
   int32_t n;
   int32_t head_windows;  // nonzero: each head replays only its last `window` tokens
+  int32_t one_chunk;     // with head_windows: every window of the launch is at most one chunk
   uint32_t* status;
   // Fused load (pool != nullptr): request r reads the retained units of
   // slot src_slot[r] and writes each replayed head whole.

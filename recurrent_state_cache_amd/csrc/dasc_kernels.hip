@@ -591,13 +591,14 @@ __global__ void __launch_bounds__(kThreads) qmove_kernel(MoveArgs a) {
 // ---------------------------------------------------------------------------
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kC = 16;  // tokens per chunk (the MFMA tile edge)
+constexpr int kC = kRefreshChunk;
 
 template <int D>
 struct RefreshShape {
   static constexpr int kKT = D / 16;                  // k tiles
   static constexpr bool kSplit = D >= 64;             // big products on split bf16 MFMA
   static constexpr int kWavesPerSimd = 2;  // occupancy target
+  static constexpr int kWavesPerSimdOne = 4;  // ... of the one-chunk kernel
   static constexpr int kVTW = D >= 32 ? 2 : 1;        // v tiles per wave
   static constexpr int kNW = (D / 16) / kVTW;         // waves per head
   static constexpr int kNT = 64 * kNW;                // threads
@@ -607,28 +608,30 @@ struct RefreshShape {
 };
 
 // Q and W in fp32 (d <= 32) or as bf16 hi / lo pairs (the split products).
-template <int D, bool SPLIT>
+// NB: buffers by chunk parity (2; 1 for the one-chunk kernel, which has no
+// Q: its readout meets the zero state only).
+template <int D, bool SPLIT, int NB>
 struct RefreshQW {
-  float Q[kC][D + 4];         // gamma_t o k_t
-  float W[2][D][kC + 4];      // k_s o D_{15,s}, [k][s], by chunk parity
+  float Q[NB == 2 ? kC : 1][D + 4];  // gamma_t o k_t
+  float W[NB][D][kC + 4];            // k_s o D_{15,s}, [k][s], by chunk parity
 };
-template <int D>
-struct RefreshQW<D, true> {
-  uint16_t Qh[kC][D + 16];    // gamma_t o k_t: bf16 hi, then lo (rows padded to
-  uint16_t Ql[kC][D + 16];    // 8 banks mod 64, so an A-operand read is 2 passes)
+template <int D, int NB>
+struct RefreshQW<D, true, NB> {
+  uint16_t Qh[NB == 2 ? kC : 1][D + 16];  // gamma_t o k_t: bf16 hi, then lo (rows padded
+  uint16_t Ql[NB == 2 ? kC : 1][D + 16];  // to 8 banks mod 64, so an A-operand read is 2 passes)
   // k_s o D_{15,s}, [k][s], by chunk parity: per row k and token group
   // g (s = 4 g .. 4 g + 3) the four bf16 hi, then the four bf16 lo.
-  uint16_t W[2][D][2 * kC];
+  uint16_t W[NB][D][2 * kC];
 };
 
-template <int D>
+template <int D, int NB>
 struct alignas(16) RefreshLds {
   float K[kC][D];             // k of the chunk being prepared
   float A[kC][D];             // its decays
-  uint16_t V[2][kC][D];       // v (bf16 bits as given), by chunk parity
-  float B[2][kC];             // beta, by chunk parity
-  RefreshQW<D, RefreshShape<D>::kSplit> qw;
-  float G[2][D];              // gamma_15 by chunk parity
+  uint16_t V[NB][kC][D];      // v (bf16 bits as given), by chunk parity
+  float B[NB][kC];            // beta, by chunk parity
+  RefreshQW<D, RefreshShape<D>::kSplit, NB> qw;
+  float G[NB][D];             // gamma_15 by chunk parity
   float PA[D], PD[D];         // exp(A_log) and dt_bias per channel (GDN: [0])
   float LT[kC][kC + 4];       // L transposed: LT[s][t] = beta_t M_{t,s}, s < t
   float T[kC][kC + 4];        // (I + L)^-1
@@ -639,8 +642,12 @@ struct alignas(16) RefreshLds {
 // relative 2^-16.  A product of two split values is taken as
 // hi hi + hi lo + lo hi on bf16 MFMA with fp32 accumulation; the dropped
 // lo lo term and the truncations are below 2^-15 of each product term.
+// The remainder is never fused with a product that computes x (fp
+// contraction would split the exact product instead of the rounded x, and
+// kernels that inline the split into different code would then disagree).
 __device__ __forceinline__ uint32_t hi_bits(float x) { return __float_as_uint(x) & 0xFFFF0000u; }
 __device__ __forceinline__ uint32_t lo_bits(float x) {
+#pragma clang fp contract(off)
   return __float_as_uint(x - __uint_as_float(hi_bits(x)));
 }
 // Two bf16 (the upper halves of a and b) in one word: a in the low half.
@@ -703,15 +710,23 @@ __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
 // FUSED: the load and the refresh in one pass: the head is written whole,
 // the local columns from the replay and the retained ones from its units in
 // the pool slot (what a zero-fill unpack followed by the refresh leaves).
-template <int D, int GATE, bool WINDOWED, bool FUSED>
+// ONE (with WINDOWED, chosen when every window of the launch is at most one
+// chunk, so that every head replays at most kC tokens): the pipeline's
+// staging of later chunks and the parity buffers are left out, which frees
+// LDS and registers for a third workgroup per CU; short replays are bound by
+// each head's serial chain (stage, L, T, products, write-back), which more
+// resident heads overlap.
+template <int D, int GATE, bool WINDOWED, bool FUSED, bool ONE>
 __global__ void __launch_bounds__(RefreshShape<D>::kNT)
-    __attribute__((amdgpu_waves_per_eu(RefreshShape<D>::kWavesPerSimd)))
+    __attribute__((amdgpu_waves_per_eu(ONE ? RefreshShape<D>::kWavesPerSimdOne
+                                           : RefreshShape<D>::kWavesPerSimd)))
 refresh_kernel(RefreshArgs a) {
+  static_assert(!ONE || WINDOWED, "the one-chunk kernel serves windowed replays");
   using Sh = RefreshShape<D>;
   constexpr int KT = Sh::kKT, VTW = Sh::kVTW, JB = Sh::kJB, NB4 = Sh::kNB4;
   constexpr bool kChan = GATE != kGateHead;
   constexpr bool kAllStage = Sh::kNT == 2 * D;  // every lane stages an item
-  __shared__ RefreshLds<D> sh;
+  __shared__ RefreshLds<D, ONE ? 1 : 2> sh;
 
   const RefreshTask task = a.tasks[blockIdx.x];
   const int req = blockIdx.y;
@@ -877,10 +892,12 @@ refresh_kernel(RefreshArgs a) {
           qw[i] = fwd ? gm * kv : before;  // forward: gamma_t o k_t
         }
         if (fwd) {
+          if constexpr (!ONE) {
 #pragma unroll
-          for (int t = 0; t < kC; ++t) {
-            sh.qw.Qh[t][j] = static_cast<uint16_t>(hi_bits(qw[t]) >> 16);
-            sh.qw.Ql[t][j] = static_cast<uint16_t>(lo_bits(qw[t]) >> 16);
+            for (int t = 0; t < kC; ++t) {
+              sh.qw.Qh[t][j] = static_cast<uint16_t>(hi_bits(qw[t]) >> 16);
+              sh.qw.Ql[t][j] = static_cast<uint16_t>(lo_bits(qw[t]) >> 16);
+            }
           }
         } else {
 #pragma unroll
@@ -900,11 +917,15 @@ refresh_kernel(RefreshArgs a) {
           const float before = gm * kv;  // backward: k_s o D_{15,s}
           gm *= al;
           const float after = gm * kv;   // forward: gamma_t o k_t
-          float* const at = fwd ? &sh.qw.Q[t][j] : &sh.qw.W[vb][j][t];
-          *at = fwd ? after : before;
+          if constexpr (ONE) {
+            if (!fwd) sh.qw.W[vb][j][t] = before;
+          } else {
+            float* const at = fwd ? &sh.qw.Q[t][j] : &sh.qw.W[vb][j][t];
+            *at = fwd ? after : before;
+          }
         }
       }
-      if (fwd) sh.G[vb][j] = gm;
+      if (!ONE && fwd) sh.G[vb][j] = gm;  // the one-chunk kernel decays a zero state
     }
   };
 
@@ -954,18 +975,22 @@ refresh_kernel(RefreshArgs a) {
     fetch(0);
     __syncthreads();
     stage1(0);
-    if (nchunks > 1) fetch(1);
+    if constexpr (!ONE) {
+      if (nchunks > 1) fetch(1);
+    }
     __syncthreads();
     stage2(0);
     __syncthreads();
+    // ONE: the window bounds W by the task's window, at most kC, so the loop
+    // runs once
     for (int64_t n = 0; n < nchunks; ++n) {
-      const int cb = static_cast<int>(n & 1), nb = cb ^ 1;
+      const int cb = ONE ? 0 : static_cast<int>(n & 1), nb = cb ^ 1;
       // ---- phase 1: T(n), U0 = S Q(n)  ||  stage chunk n + 1, fetch n + 2
       if (wave == static_cast<int>(n % Sh::kNW)) invert();  // one wave, rotating
       v4f U[VTW];
 #pragma unroll
       for (int vv = 0; vv < VTW; ++vv) U[vv] = v4f{0.f, 0.f, 0.f, 0.f};
-      if (n == 0) {
+      if (ONE || n == 0) {
         // the scratch state starts at zero: U0 = 0
       } else if constexpr (Sh::kSplit) {
         // K slots of lane group g: 4 g + e of k tile 2p (e < 4), then of
@@ -1005,8 +1030,10 @@ refresh_kernel(RefreshArgs a) {
         }
       }
       // staging and fetches past the request's last chunk are skipped
-      if (n + 1 < nchunks) stage1(nb);
-      if (n + 2 < nchunks) fetch(n + 2);
+      if constexpr (!ONE) {
+        if (n + 1 < nchunks) stage1(nb);
+        if (n + 2 < nchunks) fetch(n + 2);
+      }
       __syncthreads();
       // ---- phase 2: R, C = T R, S <- S Diag(gamma) + W C  ||  L, Q, W of n + 1
       {
@@ -1040,13 +1067,15 @@ refresh_kernel(RefreshArgs a) {
           }
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt) {
-            const v4f g4 = *reinterpret_cast<const v4f*>(&sh.G[cb][16 * kt + 4 * g]);
             const u32x4 wa = *reinterpret_cast<const u32x4*>(&sh.qw.W[cb][16 * kt + m][8 * g]);
 #pragma unroll
             for (int vv = 0; vv < VTW; ++vv) {
               v4f x = acc[kt][vv];
+              if constexpr (!ONE) {
+                const v4f g4 = *reinterpret_cast<const v4f*>(&sh.G[cb][16 * kt + 4 * g]);
 #pragma unroll
-              for (int r = 0; r < 4; ++r) x[r] *= g4[r];
+                for (int r = 0; r < 4; ++r) x[r] *= g4[r];
+              }
               x = mfma_bf16(wa, chh[vv], x);
               x = mfma_bf16(wa, cl0[vv], x);
               acc[kt][vv] = x;
@@ -1055,13 +1084,15 @@ refresh_kernel(RefreshArgs a) {
         } else {
 #pragma unroll
           for (int kt = 0; kt < KT; ++kt) {
-            const v4f g4 = *reinterpret_cast<const v4f*>(&sh.G[cb][16 * kt + 4 * g]);
             const v4f wa = *reinterpret_cast<const v4f*>(&sh.qw.W[cb][16 * kt + m][4 * g]);
 #pragma unroll
             for (int vv = 0; vv < VTW; ++vv) {
               v4f x = acc[kt][vv];
+              if constexpr (!ONE) {
+                const v4f g4 = *reinterpret_cast<const v4f*>(&sh.G[cb][16 * kt + 4 * g]);
 #pragma unroll
-              for (int r = 0; r < 4; ++r) x[r] *= g4[r];
+                for (int r = 0; r < 4; ++r) x[r] *= g4[r];
+              }
 #pragma unroll
               for (int r = 0; r < 4; ++r) x = mfma4(wa[r], Cc[vv][r], x);
               acc[kt][vv] = x;
@@ -1069,8 +1100,10 @@ refresh_kernel(RefreshArgs a) {
           }
         }
       }
-      if (n + 1 < nchunks) stage2(nb);
-      __syncthreads();
+      if constexpr (!ONE) {
+        if (n + 1 < nchunks) stage2(nb);
+        __syncthreads();
+      }
     }
   }
 
@@ -1195,8 +1228,15 @@ bool refresh_shape_supported(int d_k, int d_v) {
 template <int D, int GATE, bool W>
 void launch_refresh_f(const RefreshArgs& args, dim3 grid, hipStream_t s) {
   constexpr int kNT = RefreshShape<D>::kNT;
-  if (args.pool) refresh_kernel<D, GATE, W, true><<<grid, kNT, 0, s>>>(args);
-  else refresh_kernel<D, GATE, W, false><<<grid, kNT, 0, s>>>(args);
+  if constexpr (W) {
+    if (args.one_chunk) {
+      if (args.pool) refresh_kernel<D, GATE, true, true, true><<<grid, kNT, 0, s>>>(args);
+      else refresh_kernel<D, GATE, true, false, true><<<grid, kNT, 0, s>>>(args);
+      return;
+    }
+  }
+  if (args.pool) refresh_kernel<D, GATE, W, true, false><<<grid, kNT, 0, s>>>(args);
+  else refresh_kernel<D, GATE, W, false, false><<<grid, kNT, 0, s>>>(args);
 }
 
 template <int D>
