@@ -243,7 +243,7 @@ void build_tables(dasc_plan* p) {
   // heads whole, and clears omitted heads as above.
   for (const auto& L : p->layers) {
     const int64_t head_bytes = int64_t(L.d_v) * L.d_k * 4;
-    const int row_blocks = (L.d_v + kKdaRows - 1) / kKdaRows;
+    const int row_blocks = (L.d_v + kQGdnRows - 1) / kQGdnRows;
     int64_t j = 0;  // retained units of the layer seen so far
     for (int h = 0; h < L.n_heads; ++h) {
       const uint64_t d_off = L.dense_off + h * head_bytes;

@@ -19,7 +19,7 @@ constexpr uint32_t kPieceCopy = 0;  // move `bytes` between dense and pool
 constexpr uint32_t kPieceZero = 1;  // clear `bytes` of the dense checkpoint (unpack)
 constexpr uint32_t kPieceKda = 2;   // kKdaRows rows of a KDA head with >= 1 retained channel
 // INT8 checkpoints (Eq. 10).  Pack quantizes whole heads (a column's scale
-// spans all d_v rows); unpack dequantizes GDN heads kKdaRows rows at a time
+// spans all d_v rows); unpack dequantizes GDN heads kQGdnRows rows at a time
 // and KDA heads whole.
 constexpr uint32_t kPieceQGdn = 3;  // a retained GDN head
 constexpr uint32_t kPieceQKda = 4;  // a KDA head with >= 1 retained channel
@@ -33,6 +33,9 @@ constexpr uint32_t kCopyChunk = 4096;
 constexpr int kKdaRows = 32;
 // LDS floats per staged unit segment (kKdaRows + 4 of padding).
 constexpr int kKdaLdsRow = kKdaRows + 4;
+// Rows of a GDN head one INT8 unpack piece writes: 8 rows of 128 fp32 are
+// 4 KiB, one 16-byte store per lane, like the copy pieces.
+constexpr int kQGdnRows = 8;
 
 // One workgroup's work for one (checkpoint, slot) pair.  For a KDA piece the
 // head's r retained columns (r = popcount of mask) are the units
@@ -44,7 +47,8 @@ struct alignas(64) Piece {
   uint32_t type;       // kPiece*
   uint32_t bytes;      // copy / zero: multiple of 16, at most kCopyChunk
   uint16_t d_k, d_v;   // head pieces: head shape
-  uint16_t rb, r;      // row block (rows kKdaRows rb ..), retained channels
+  uint16_t rb, r;      // row block (rows kKdaRows rb .., INT8 GDN unpack kQGdnRows rb ..),
+                       // retained channels
   uint32_t mask[4];    // KDA: bit k set = channel k retained
   uint64_t scale_off;  // INT8 pieces: byte offset of the first fp32 scale in a slot
   // TP storage balancing (pieces of the pack_tp / unpack_tp lists): units

@@ -225,8 +225,8 @@ __global__ void __launch_bounds__(kThreads) move_kernel(MoveArgs a) {
 // leave LDS as 16-byte pieces of contiguous pool bytes.  (Pieces of 32
 // channels x all rows, 16 KiB like the fp32 pieces, read 128-byte segments
 // at the row stride and streamed HBM far worse than whole heads.)  Unpack
-// pieces are GDN heads by blocks of 32 rows (lane: 4 rows x 4 columns) and
-// KDA heads whole: the units and scales come into LDS as 16-byte pieces,
+// pieces are GDN heads by blocks of 8 rows (lane: 4 columns of one row, a
+// 4 KiB piece like the copy pieces) and KDA heads whole: the units and scales come into LDS as 16-byte pieces,
 // each lane reads the 16 bytes of its rows for each of its retained columns
 // and writes its 16 rows x 4 columns (+0.0 in omitted columns).  LDS unit
 // rows are padded to 144 bytes so that lanes reading or writing different
@@ -430,24 +430,19 @@ __device__ __forceinline__ void qpack_kda_head(const Piece& t, const uint8_t* sr
   }
 }
 
-// Unpack of 32 rows of a GDN head: lane holds rows 32 rb + 4 vl + i, columns 4 kg ..
+// Unpack of kQGdnRows rows of a GDN head: lane (vl, kg) writes columns
+// 4 kg .. 4 kg + 3 of row kQGdnRows rb + vl.
 __device__ __forceinline__ void qunpack_gdn_rows(const Piece& t, const uint8_t* src, uint8_t* dst) {
   const int dk = t.d_k, dv = t.d_v, KG = dk / 4;
   const int tid = threadIdx.x, kg = tid % 32, vl = tid / 32;
-  if (kg >= KG) return;
+  const int v = kQGdnRows * t.rb + vl;
+  if (kg >= KG || vl >= kQGdnRows || v >= dv) return;
   float* S = reinterpret_cast<float*>(dst + t.dense_off);
   const uint8_t* Sc = src + t.scale_off;
   const f32x4 sc = {load_scale(Sc + 16 * kg), load_scale(Sc + 16 * kg + 4),
                     load_scale(Sc + 16 * kg + 8), load_scale(Sc + 16 * kg + 12)};
-  const uint8_t* Q = src + t.pool_off;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int v = kKdaRows * t.rb + 4 * vl + i;
-    if (v < dv) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(Q + v * dk + 4 * kg);
-      st_stream(dequant4(w, sc), reinterpret_cast<f32x4*>(S + v * dk + 4 * kg));
-    }
-  }
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(src + t.pool_off + v * dk + 4 * kg);
+  st_stream(dequant4(w, sc), reinterpret_cast<f32x4*>(S + v * dk + 4 * kg));
 }
 
 // Unpack of a KDA head, whole: units and scales into LDS, then every element.
