@@ -243,6 +243,29 @@ def test_windowed_refresh_every_width():
                     head_windows=True)
 
 
+def test_one_chunk_windows_every_width_against_the_oracle():
+    # W_max = 16: every head window is at most one chunk, so every launch
+    # group (widths 16..128, GDN, KDA with vector and element gate reads)
+    # runs the one-chunk kernel; requests shorter than, equal to and longer
+    # than the windows
+    cfg = W.Config("widths", _odd_refresh_layers(25), w_max=16, n_req=5, seed=25)
+    P, O = _plans(cfg)
+    wins = sorted({O.head_window(li, int(h)) for li in range(len(cfg.layers))
+                   for h in O.refreshed_heads(li)})
+    assert max(wins) <= 16 and len(wins) >= 2, wins
+    Wn = np.array([0, 5, 16, 40, 3])
+    log(f"[refresh] one-chunk windows {wins}, requests {list(Wn)}")
+    inp = W.refresh_inputs(cfg, Wn, device="cuda")
+    dense = W.dense_states(cfg, 5, device="cuda", seed=12)
+    before = dense.clone()
+    dst = torch.tensor([3, 1, 4, 0, 2], dtype=torch.int32, device="cuda")
+    R.ckpt_refresh_suffix_windowed(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, dense, dst)
+    torch.cuda.synchronize()
+    assert P.status() == 0
+    _check_requests(P, O, inp, before, dense, dst.cpu().numpy(), range(5), label="one-chunk",
+                    head_windows=True)
+
+
 def test_windowed_refresh_kda_and_mixed_sampled():
     for cfg, reqs, layers in ((W.kda_refresh(n_req=8), [0, 7], [0, 19]),
                               (W.mixed(n_ckpt=16, n_req=16), [0, 5], [0, 1, 26])):
@@ -263,10 +286,13 @@ def test_windowed_refresh_kda_and_mixed_sampled():
                         label=f"windowed {cfg.name}", head_windows=True)
 
 
-def test_windowed_equals_full_when_requests_fit_the_windows():
-    # every head window is >= 4 here (W_max = 64), so requests of at most 4
-    # tokens replay the same tokens on both entry points: bit-identical
-    cfg = W.Config("widths", _odd_refresh_layers(23), w_max=64, n_req=4, seed=23)
+@pytest.mark.parametrize("w_max", [16, 64])
+def test_windowed_equals_full_when_requests_fit_the_windows(w_max):
+    # every head window is >= 4, so requests of at most 4 tokens replay the
+    # same tokens on both entry points: bit-identical.  At W_max = 16 every
+    # launch group's windows fit one chunk (the one-chunk kernel for every
+    # width and gate layout), at 64 some do and some do not.
+    cfg = W.Config("widths", _odd_refresh_layers(23), w_max=w_max, n_req=4, seed=23)
     P, O = _plans(cfg)
     assert min(O.head_window(li, int(h)) for li in range(len(cfg.layers))
                for h in O.refreshed_heads(li)) >= 4
@@ -314,6 +340,7 @@ def _fused_vs_two_step(cfg, P, n_req, windows, seed, head_windows):
 def test_fused_load_equals_unpack_then_refresh(head_windows):
     cases = [(W.tiny_kda(), [8, 3], 1),
              (W.Config("widths", _odd_refresh_layers(24), w_max=64, n_req=3, seed=24), [0, 21, 70], 2),
+             (W.Config("widths", _odd_refresh_layers(26), w_max=16, n_req=3, seed=26), [2, 16, 33], 5),
              (W.kda_refresh(n_req=4), [256, 9, 16, 31], 3),
              (W.mixed(n_ckpt=8, n_req=3), [64, 200, 17], 4)]
     for cfg, windows, seed in cases:
