@@ -236,19 +236,10 @@ constexpr float kScaleFloor = 1e-8f;
 constexpr int kQRows = 16;     // consecutive rows a lane holds (d_v <= 128, 8 row lanes)
 constexpr int kQStride = 144;  // bytes per unit row of the LDS staging buffer
 
-__device__ __forceinline__ uint32_t quant4(f32x4 x, f32x4 s) {
-  uint32_t w = 0;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const float r = rintf(x[c] / s[c]);
-    const float qf = r != r ? 0.f : fminf(fmaxf(r, -127.f), 127.f);
-    w |= (static_cast<uint32_t>(static_cast<int32_t>(qf)) & 0xFFu) << (8 * c);
-  }
-  return w;
-}
-
-// The same codes from the product y = x (1 / s), with 1 / s correctly
-// rounded.  Within one column |x / s| <= 127 (1 + 2^-23), and y and the
+// The int8 codes of four entries of four columns.  Eq. 10 rounds the
+// correctly rounded fp32 quotient x / s (half to even); the code here comes
+// from the product y = x (1 / s), with 1 / s correctly rounded.  Within one
+// column |x / s| <= 127 (1 + 2^-23), and y and the
 // correctly rounded quotient each lie within a relative 2^-23 + 2^-48 and
 // 2^-24 of x / s, so they differ by less than 2.3e-5: their nearest integers
 // agree unless y lies within that distance of a half-integer, and only such
@@ -257,7 +248,7 @@ __device__ __forceinline__ uint32_t quant4(f32x4 x, f32x4 s) {
 // maximum makes 1 / s = 0 and every product 0 or NaN, as the quotients are).
 constexpr float kHalfGuard = 0.5f - 6e-5f;
 
-__device__ __forceinline__ uint32_t quant4_fast(f32x4 x, f32x4 s, f32x4 inv) {
+__device__ __forceinline__ uint32_t quant4(f32x4 x, f32x4 s, f32x4 inv) {
   uint32_t w = 0;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
@@ -331,7 +322,7 @@ __device__ __forceinline__ void qpack_gdn_head(const Piece& t, const uint8_t* sr
 #pragma unroll
   for (int i = 0; i < kQRows; ++i) {
     const int v = kQRows * vl + i;
-    if (v < dv) *reinterpret_cast<uint32_t*>(Q + v * dk + 4 * kg) = quant4_fast(x[i], sc, inv);
+    if (v < dv) *reinterpret_cast<uint32_t*>(Q + v * dk + 4 * kg) = quant4(x[i], sc, inv);
   }
   if (vl == 0) {
     float* Sc = reinterpret_cast<float*>(dst + t.scale_off);
@@ -382,8 +373,8 @@ __device__ __forceinline__ void qpack_kda_head(const Piece& t, const uint8_t* sr
     uint32_t cw[4][4];  // [column c][row group m]; rows >= d_v hold zeros, never copied out
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const uint32_t w[4] = {quant4_fast(x[4 * m], sc, inv), quant4_fast(x[4 * m + 1], sc, inv),
-                             quant4_fast(x[4 * m + 2], sc, inv), quant4_fast(x[4 * m + 3], sc, inv)};
+      const uint32_t w[4] = {quant4(x[4 * m], sc, inv), quant4(x[4 * m + 1], sc, inv),
+                             quant4(x[4 * m + 2], sc, inv), quant4(x[4 * m + 3], sc, inv)};
       uint32_t b[4];
       transpose4(w, b);
 #pragma unroll
