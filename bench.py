@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP32_MFMA_PEAK_TF = 157.3      # MI355X dense fp32 matrix (MFMA), TFLOP/s
+FP32_VALU_UNPACKED_TF = 78.6   # fp32 vector FMA rate without packed (2-wide) FMA, TFLOP/s
 
 # Kernel sources whose hash a traffic summary under profiles/ records: the
 # counters it holds describe these exact kernels and piece lists.
@@ -46,7 +47,8 @@ KERNEL_ROLES = {r"qmove_kernel<true>": "pack_int8", r"qmove_kernel<false>": "unp
                 r"(?<!q)move_kernel<false, \d+, \d+, true>": "unpack_tp",
                 r"refresh_kernel<\d+, \d+, false, false, false>": "refresh",
                 r"refresh_kernel<\d+, \d+, true, false, (true|false)>": "refresh_windowed",
-                r"refresh_kernel<\d+, \d+, (true|false), true, (true|false)>": "refresh_fused"}
+                r"refresh_kernel<\d+, \d+, (true|false), true, (true|false)>": "refresh_fused",
+                r"recurrent_kernel<": "refresh_recurrent"}
 
 
 def _args():
@@ -331,7 +333,7 @@ def _summarize(dirs, workload):
              f"WRITE_SIZE (KiB) | HBM bytes per launch (calibrated) |",
              "|---|---|---|---|---|---|---|---|"]
     for role in ("pack", "unpack", "refresh", "pack_int8", "unpack_int8", "pack_tp", "unpack_tp",
-                 "refresh_windowed", "refresh_fused"):
+                 "refresh_windowed", "refresh_fused", "refresh_recurrent"):
         if role not in stats:
             continue
         c, avg, mn, mx = stats[role]
@@ -358,7 +360,7 @@ def _counter_table(dirs):
                 table.setdefault(r["Counter_Name"], {}).setdefault(role, []).append(
                     float(r["Counter_Value"]))
     roles = ("pack", "unpack", "refresh", "pack_int8", "unpack_int8", "pack_tp", "unpack_tp",
-             "refresh_windowed")
+             "refresh_windowed", "refresh_recurrent")
     lines = ["| counter | " + " | ".join(roles) + " |", "|" + "---|" * (len(roles) + 1)]
     for c in sorted(table):
         vals = [table[c].get(r) for r in roles]
@@ -498,6 +500,11 @@ def main():
         assert P.status() == 0
         return float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
 
+    # The recurrence's own form (token by token on the vector units) on the
+    # same suffixes: the reference point for the chunked kernel.
+    t_rec = timed(lambda: R.ckpt_refresh_suffix_recurrent(P, inp.k, inp.v, inp.a, inp.beta,
+                                                          inp.tok_off, out, dst, stream)) * 1e-3
+
     wr = {}
     for hw, name in (() if args.skip_wr_load else ((False, "full_suffix"), (True, "eq7_windows"))):
         refresh = R.ckpt_refresh_suffix_windowed if hw else R.ckpt_refresh_suffix
@@ -577,6 +584,17 @@ def main():
         },
         **({"tp8_storage_balancing": tp8} if tp8 else {}),
         **({"dasc_wr_load": dict(wr, requests=cfg.n_req)} if wr else {}),
+        "refresh_recurrent_form": {
+            "kernel": "recurrent_kernel<128, gate> (token by token, fp32 vector units)",
+            "ms": round(t_rec * 1e3, 4),
+            "achieved_tflops": round(flops / t_rec / 1e12, 3),
+            "fp32_vector_peak_unpacked": FP32_VALU_UNPACKED_TF,
+            "frac_of_unpacked_peak": round(flops / t_rec / 1e12 / FP32_VALU_UNPACKED_TF, 4),
+            "chunked_speedup": round(t_rec / t_ref.mean(), 3),
+            "note": "same suffixes, output and tolerance as the chunked refresh; the vector "
+                    "units' fp32 rate without packed FMA (not emitted by this build) is half "
+                    "the 157.3 TF/s datasheet figure",
+        },
         "refresh_eq7_windows": {
             "kernel": "refresh_kernel<128, gate, true, false, one_chunk> (per-head windows; the one-chunk kernel when every window is at most 16 tokens)",
             "ms": round(t_win.mean() * 1e3, 4),

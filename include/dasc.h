@@ -294,6 +294,22 @@ int dasc_ckpt_refresh_suffix(dasc_plan_t plan, const uint16_t* k, const uint16_t
                              const int32_t* dst_idx, int32_t n, void* stream);
 
 /*
+ * The same operation as dasc_ckpt_refresh_suffix ([dasc] §3.1 Eq. 1,
+ * §4.2), computed in the recurrence's own form: token by token on the
+ * vector units (u = S (alpha o k), c = beta (v - u), S <- S Diag(alpha)
+ * + c k^T), with the state in registers, instead of in 16-token chunks on
+ * the matrix cores.  It exists as the reference point for the chunked form
+ * (same inputs, same output, same tolerance against an fp64 replay) and is
+ * several times slower.  Same arguments, rules and errors as
+ * dasc_ckpt_refresh_suffix.
+ */
+int dasc_ckpt_refresh_suffix_recurrent(dasc_plan_t plan, const uint16_t* k, const uint16_t* v,
+                                       const uint16_t* a, const float* beta,
+                                       const int64_t* tok_offsets, int64_t n_tokens,
+                                       void* dense_base, int64_t dense_stride, int64_t n_dense,
+                                       const int32_t* dst_idx, int32_t n, void* stream);
+
+/*
  * Bounded-suffix refresh with per-head Eq. 7 windows ([dasc-sum]
  * "Methodology" Eq. 7, [dasc] §4.2): as dasc_ckpt_refresh_suffix, except
  * that head (l, h) of request r replays only the last min(W_lh, n_r) of the

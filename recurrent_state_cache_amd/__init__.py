@@ -21,7 +21,8 @@ import numpy as np
 import torch  # noqa: F401
 
 __all__ = ["Plan", "DascError", "ckpt_pack", "ckpt_unpack_zero_fill",
-           "ckpt_refresh_suffix", "ckpt_refresh_suffix_windowed", "ckpt_pack_int8",
+           "ckpt_refresh_suffix", "ckpt_refresh_suffix_windowed",
+           "ckpt_refresh_suffix_recurrent", "ckpt_pack_int8",
            "ckpt_unpack_int8_zero_fill", "ckpt_pack_tp", "ckpt_unpack_tp_zero_fill",
            "ckpt_unpack_refresh",
            "GDN", "KDA", "STATUS_BAD_INDEX",
@@ -107,6 +108,8 @@ def _load():
                                               _c_i64, _c_i64, _c_p, _c_i32, _c_p]),
         "dasc_ckpt_refresh_suffix_windowed": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
                                                        _c_p, _c_i64, _c_i64, _c_p, _c_i32, _c_p]),
+        "dasc_ckpt_refresh_suffix_recurrent": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
+                                                        _c_p, _c_i64, _c_i64, _c_p, _c_i32, _c_p]),
         "dasc_ckpt_unpack_refresh": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p,
                                               _c_p, _c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_p,
                                               _c_i32, _c_i32, _c_p]),
@@ -429,6 +432,15 @@ def ckpt_unpack_refresh(plan: Plan, pool, src_slot, k, v, a, beta, tok_off, dens
         _dev_ptr(tok_off, "tok_off", torch.int64), T, dp, ds, dn,
         _dev_ptr(dst_idx, "dst_idx", torch.int32), n, 1 if head_windows else 0,
         _stream_handle(stream)), "ckpt_unpack_refresh")
+
+
+def ckpt_refresh_suffix_recurrent(plan: Plan, k, v, a, beta, tok_off, dense, dst_idx,
+                                  stream=None) -> None:
+    """As ckpt_refresh_suffix, computed token by token on the vector units
+    (the recurrence's own form): the reference point for the chunked
+    matrix-core kernel, several times slower."""
+    _refresh(lib.dasc_ckpt_refresh_suffix_recurrent, "ckpt_refresh_suffix_recurrent", plan, k,
+             v, a, beta, tok_off, dense, dst_idx, stream)
 
 
 def ckpt_refresh_suffix_windowed(plan: Plan, k, v, a, beta, tok_off, dense, dst_idx,

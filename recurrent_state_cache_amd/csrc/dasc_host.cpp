@@ -1042,7 +1042,8 @@ static int run_refresh(const char* w, bool head_windows, dasc_plan_t p, const ui
                        const int64_t* tok_offsets, int64_t n_tokens, void* dense_base,
                        int64_t dense_stride, int64_t n_dense, const int32_t* dst_idx, int32_t n,
                        void* stream, const void* pool_base = nullptr, int64_t pool_stride = 0,
-                       int64_t n_slots = 0, const int32_t* src_slot = nullptr) {
+                       int64_t n_slots = 0, const int32_t* src_slot = nullptr,
+                       bool recurrent = false) {
   if (!p) return fail(DASC_EINVAL, std::string(w) + ": null plan");
   if (!p->device) return fail(DASC_ENOTUPLOADED, std::string(w) + ": plan tables not uploaded");
   if (n < 0 || n > 65535) return fail(DASC_EINVAL, std::string(w) + ": n must be in [0, 65535]");
@@ -1090,7 +1091,8 @@ static int run_refresh(const char* w, bool head_windows, dasc_plan_t p, const ui
     args.tasks = p->dev.refresh + g.first;
     args.n_tasks = g.count;
     args.one_chunk = head_windows && g.max_window <= static_cast<uint32_t>(kRefreshChunk) ? 1 : 0;
-    int e = launch_refresh(g.d_k, g.gate, args, stream);
+    int e = recurrent ? launch_recurrent(g.d_k, g.gate, args, stream)
+                      : launch_refresh(g.d_k, g.gate, args, stream);
     if (e) return fail(DASC_EHIP, std::string(w) + ": launch failed: " +
                                       hipGetErrorString(static_cast<hipError_t>(e)));
   }
@@ -1103,6 +1105,16 @@ int dasc_ckpt_refresh_suffix(dasc_plan_t p, const uint16_t* k, const uint16_t* v
                              int64_t n_dense, const int32_t* dst_idx, int32_t n, void* stream) {
   return run_refresh("ckpt_refresh_suffix", false, p, k, v, a, beta, tok_offsets, n_tokens,
                      dense_base, dense_stride, n_dense, dst_idx, n, stream);
+}
+
+int dasc_ckpt_refresh_suffix_recurrent(dasc_plan_t p, const uint16_t* k, const uint16_t* v,
+                                       const uint16_t* a, const float* beta,
+                                       const int64_t* tok_offsets, int64_t n_tokens,
+                                       void* dense_base, int64_t dense_stride, int64_t n_dense,
+                                       const int32_t* dst_idx, int32_t n, void* stream) {
+  return run_refresh("ckpt_refresh_suffix_recurrent", false, p, k, v, a, beta, tok_offsets,
+                     n_tokens, dense_base, dense_stride, n_dense, dst_idx, n, stream, nullptr, 0,
+                     0, nullptr, true);
 }
 
 int dasc_ckpt_refresh_suffix_windowed(dasc_plan_t p, const uint16_t* k, const uint16_t* v,

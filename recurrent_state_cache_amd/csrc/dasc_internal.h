@@ -171,5 +171,6 @@ struct RefreshArgs {
 };
 
 int launch_refresh(int d, int gate, const RefreshArgs& args, void* stream);
+int launch_recurrent(int d, int gate, const RefreshArgs& args, void* stream);
 
 }  // namespace dasc

@@ -1159,6 +1159,132 @@ refresh_kernel(RefreshArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same refresh in the recurrence's own form ([dasc] §3.1 Eq. 1), token
+// by token, on the vector units: the reference point for the chunked
+// kernel above (same inputs, same write-back, same tolerance).  One
+// workgroup of 256 lanes per (head, request); lane (rb, cb) = (tid / 16,
+// tid % 16) holds the B x B block of S (B = d / 16) in rows B rb .. and
+// columns B cb ..; the 16 lanes of a DPP row share the rows, so
+// u = S (alpha o k) is a B x B partial product per lane plus a 16-lane DPP
+// sum.  Per token: u = S (alpha o k), c = beta (v - u), S <- S Diag(alpha)
+// + c k^T.  Tokens are staged 16 at a time (decays by Eq. 2 from the gate
+// logits) by the lanes that stage the chunked kernel's chunks.
+// ---------------------------------------------------------------------------
+template <int D, int GATE>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+recurrent_kernel(RefreshArgs a) {
+  constexpr int B = D / 16;
+  constexpr int JB = D / 8;
+  constexpr bool kChan = GATE != kGateHead;
+  __shared__ __attribute__((aligned(16))) float sK[kC][D];
+  __shared__ __attribute__((aligned(16))) float sA[kC][D];
+  __shared__ __attribute__((aligned(16))) float sV[kC][D];
+  __shared__ float sB[kC];
+  __shared__ float sPA[D], sPD[D];
+
+  const RefreshTask task = a.tasks[blockIdx.x];
+  const int req = blockIdx.y;
+  const int64_t t0 = a.tok_off[req];
+  const int64_t t1 = a.tok_off[req + 1];
+  const int64_t dst = a.dst_idx[req];
+  if (t0 < 0 || t1 < t0 || t1 > a.n_tokens) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) flag(a.status, DASC_STATUS_BAD_TOKENS);
+    return;
+  }
+  if (!in_range(dst, a.n_dense)) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) flag(a.status, DASC_STATUS_BAD_INDEX);
+    return;
+  }
+  const int tid = threadIdx.x;
+  const int rb = tid / 16, cb = tid % 16;
+  const int r0 = B * rb, c0 = B * cb;
+  // staged item of this lane: token it_t of a batch, channels j0 .. j0 + 7
+  const bool it_on = tid < 2 * D;
+  const int it_t = (tid / JB) % kC, j0 = 8 * (tid % JB);
+
+  if (tid < (kChan ? D : 1)) {
+    sPA[tid] = a.gate_expA[task.param_off + tid];
+    sPD[tid] = a.gate_dt[task.param_off + tid];
+  }
+  float S[B][B];
+#pragma unroll
+  for (int r = 0; r < B; ++r)
+#pragma unroll
+    for (int c = 0; c < B; ++c) S[r][c] = 0.f;
+
+  const int64_t W = t1 - t0;
+  for (int64_t n0 = 0; n0 < W; n0 += kC) {
+    __syncthreads();  // the previous batch's reads (and the gate parameters)
+    if (it_on) {
+      const int64_t tok = t0 + n0 + it_t;
+      const bool real = tok < t1;
+      const int64_t tc = real ? tok : t1 - 1;  // in bounds; replaced below
+      const u32x4 rk = *reinterpret_cast<const u32x4*>(a.k + tc * a.k_row + task.k_off + j0);
+      const u32x4 rv = *reinterpret_cast<const u32x4*>(a.v + tc * a.v_row + task.v_off + j0);
+      const uint16_t* ap = a.a + tc * a.g_row + task.g_off;
+      float al[8];
+      if constexpr (GATE == kGateHead) {
+        const float x = decay(__uint_as_float(uint32_t(ap[0]) << 16) + sPD[0], sPA[0]);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) al[c] = x;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          al[c] = decay(__uint_as_float(uint32_t(ap[j0 + c]) << 16) + sPD[j0 + c], sPA[j0 + c]);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sK[it_t][j0 + 2 * q] = real ? bf16_lo(rk[q]) : 0.f;
+        sK[it_t][j0 + 2 * q + 1] = real ? bf16_hi(rk[q]) : 0.f;
+        sV[it_t][j0 + 2 * q] = real ? bf16_lo(rv[q]) : 0.f;
+        sV[it_t][j0 + 2 * q + 1] = real ? bf16_hi(rv[q]) : 0.f;
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) sA[it_t][j0 + c] = real ? al[c] : 1.f;
+      if (tid % JB == 0) sB[it_t] = real ? a.beta[tc * a.b_row + task.b_off] : 0.f;
+    }
+    __syncthreads();
+    const int nt = static_cast<int>(W - n0 < kC ? W - n0 : kC);
+    for (int i = 0; i < nt; ++i) {
+      float al[B], kk[B], ak[B], u[B];
+#pragma unroll
+      for (int c = 0; c < B; ++c) {
+        al[c] = sA[i][c0 + c];
+        kk[c] = sK[i][c0 + c];
+        ak[c] = al[c] * kk[c];
+      }
+#pragma unroll
+      for (int r = 0; r < B; ++r) {
+        float x = 0.f;
+#pragma unroll
+        for (int c = 0; c < B; ++c) x = fmaf(S[r][c], ak[c], x);
+        u[r] = group_sum<16>(x);
+      }
+      const float bt = sB[i];
+#pragma unroll
+      for (int r = 0; r < B; ++r) {
+        const float cr = bt * (sV[i][r0 + r] - u[r]);
+#pragma unroll
+        for (int c = 0; c < B; ++c) S[r][c] = fmaf(cr, kk[c], S[r][c] * al[c]);
+      }
+    }
+  }
+
+  // the local columns of the head ([dasc] §4.2)
+  float* out = reinterpret_cast<float*>(a.dense + dst * a.dense_stride + task.dense_off);
+#pragma unroll
+  for (int c = 0; c < B; ++c) {
+    const int k = c0 + c;
+    const uint32_t lw = k < 32 ? task.local[0] : k < 64 ? task.local[1]
+                      : k < 96 ? task.local[2] : task.local[3];
+    if ((lw >> (k & 31)) & 1u) {
+#pragma unroll
+      for (int r = 0; r < B; ++r) out[(r0 + r) * D + k] = S[r][c];
+    }
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -1245,6 +1371,30 @@ int launch_refresh_d(int gate, const RefreshArgs& args, dim3 grid, hipStream_t s
       return static_cast<int>(hipErrorInvalidValue);
   }
   return static_cast<int>(hipGetLastError());
+}
+
+template <int D>
+int launch_recurrent_d(int gate, const RefreshArgs& args, dim3 grid, hipStream_t s) {
+  switch (gate) {
+    case kGateHead: recurrent_kernel<D, kGateHead><<<grid, kThreads, 0, s>>>(args); break;
+    case kGateChan: recurrent_kernel<D, kGateChan><<<grid, kThreads, 0, s>>>(args); break;
+    case kGateChanSplit: recurrent_kernel<D, kGateChanSplit><<<grid, kThreads, 0, s>>>(args); break;
+    default: return static_cast<int>(hipErrorInvalidValue);
+  }
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_recurrent(int d, int gate, const RefreshArgs& args, void* stream) {
+  if (args.n_tasks == 0 || args.n == 0) return hipSuccess;
+  dim3 grid(args.n_tasks, static_cast<uint32_t>(args.n));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (d) {
+    case 16: return launch_recurrent_d<16>(gate, args, grid, s);
+    case 32: return launch_recurrent_d<32>(gate, args, grid, s);
+    case 64: return launch_recurrent_d<64>(gate, args, grid, s);
+    case 128: return launch_recurrent_d<128>(gate, args, grid, s);
+    default: return static_cast<int>(hipErrorInvalidValue);
+  }
 }
 
 int launch_refresh(int d, int gate, const RefreshArgs& args, void* stream) {

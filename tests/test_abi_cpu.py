@@ -25,7 +25,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 22
+    assert len(names) == 23
     out = subprocess.run(["nm", "-D", "--defined-only", R.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\b[TW]\s+(dasc_[a-z0-9_]+)\b", out))
@@ -250,6 +250,9 @@ def test_every_data_call_needs_uploaded_tables():
                                                                  f, 1, None),
         "refresh_windowed": lambda h: L.dasc_ckpt_refresh_suffix_windowed(h, f, f, f, f, f, 1, f,
                                                                           4096, 1, f, 1, None),
+        "refresh_recurrent": lambda h: L.dasc_ckpt_refresh_suffix_recurrent(h, f, f, f, f, f, 1,
+                                                                            f, 4096, 1, f, 1,
+                                                                            None),
         "pack_tp": lambda h: L.dasc_ckpt_pack_tp(h, f, 4096, 1, f, f, 4096, 1, f, f, 4096, 1, f,
                                                  1, None),
         "unpack_tp": lambda h: L.dasc_ckpt_unpack_tp_zero_fill(h, f, 4096, 1, f, f, 4096, 1, f,

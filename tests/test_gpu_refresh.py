@@ -384,3 +384,57 @@ def test_fused_load_bad_slot_is_flagged():
     R.ckpt_unpack_refresh(P, pool, bad, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, dense, dst)
     torch.cuda.synchronize()
     assert P.status() & R.STATUS_BAD_INDEX
+
+
+# ---------------------------------------------------------------------------
+# The recurrence's own form (token by token on the vector units), the
+# reference point for the chunked kernel: the same tolerance against the
+# fp64 oracle, and close to the chunked kernel's output.
+
+
+def test_recurrent_every_width_against_the_oracle():
+    cfg = W.Config("widths", _odd_refresh_layers(27), w_max=8, n_req=4, seed=27)
+    P, O = _plans(cfg)
+    Wn = np.array([0, 5, 16, 37])
+    log(f"[recurrent] widths 16..128, GDN and KDA, requests {list(Wn)}")
+    inp = W.refresh_inputs(cfg, Wn, device="cuda")
+    dense = W.dense_states(cfg, 5, device="cuda", seed=13)
+    before = dense.clone()
+    dst = torch.tensor([4, 0, 3, 1], dtype=torch.int32, device="cuda")
+    R.ckpt_refresh_suffix_recurrent(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, dense, dst)
+    torch.cuda.synchronize()
+    assert P.status() == 0
+    assert torch.equal(dense[2], before[2])                 # not a destination
+    _check_requests(P, O, inp, before, dense, dst.cpu().numpy(), range(4), label="recurrent")
+
+
+def test_recurrent_kda_full_size_against_oracle_and_chunked():
+    cfg = W.kda_refresh(n_req=16)
+    P, O = _plans(cfg)
+    Wn = W.windows(cfg)
+    inp = W.refresh_inputs(cfg, Wn, device="cuda")
+    base = W.dense_states(cfg, cfg.n_req, device="cuda", seed=15)
+    rec, chk = base.clone(), base.clone()
+    dst = torch.from_numpy(np.random.default_rng(2).permutation(cfg.n_req).astype(np.int32)).cuda()
+    R.ckpt_refresh_suffix_recurrent(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, rec, dst)
+    R.ckpt_refresh_suffix(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, chk, dst)
+    torch.cuda.synchronize()
+    assert P.status() == 0
+    _check_requests(P, O, inp, base, rec, dst.cpu().numpy(), [0, 11], layers=[0, 19],
+                    label="recurrent kda")
+    # both within 1e-4 of the oracle: within 2e-4 of each other, head by head
+    worst = 0.0
+    for li in (3, 12):
+        L = O.layers[li]
+        hb = L.d_v * L.d_k * 4
+        for h in O.refreshed_heads(li)[:8]:
+            local = local_mask_of_head(O, li, int(h))
+            a0 = O.temporal_off[li] + int(h) * hb
+            A = rec[:, a0:a0 + hb].cpu().numpy().view(np.float32).reshape(-1, L.d_v, L.d_k)
+            Bc = chk[:, a0:a0 + hb].cpu().numpy().view(np.float32).reshape(-1, L.d_v, L.d_k)
+            for d in range(cfg.n_req):
+                a_, b_ = A[d].astype(np.float64), Bc[d].astype(np.float64)
+                e = float(np.max(np.abs(a_[local] - b_[local])) / max(np.linalg.norm(b_), 1e-30))
+                worst = max(worst, e)
+    log(f"[recurrent] kda: recurrent vs chunked worst {worst:.3e}")
+    assert worst <= 2 * TOL
