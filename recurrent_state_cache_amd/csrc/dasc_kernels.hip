@@ -1271,16 +1271,28 @@ recurrent_kernel(RefreshArgs a) {
     }
   }
 
-  // the local columns of the head ([dasc] §4.2)
+  // the local columns of the head ([dasc] §4.2): 16-byte stores where four
+  // consecutive columns are all local
   float* out = reinterpret_cast<float*>(a.dense + dst * a.dense_stride + task.dense_off);
 #pragma unroll
-  for (int c = 0; c < B; ++c) {
-    const int k = c0 + c;
-    const uint32_t lw = k < 32 ? task.local[0] : k < 64 ? task.local[1]
-                      : k < 96 ? task.local[2] : task.local[3];
-    if ((lw >> (k & 31)) & 1u) {
+  for (int c4 = 0; c4 < B; c4 += 4) {
+    constexpr int G = B < 4 ? B : 4;  // columns per group
+    const int k0 = c0 + c4;
+    const uint32_t lw = k0 < 32 ? task.local[0] : k0 < 64 ? task.local[1]
+                      : k0 < 96 ? task.local[2] : task.local[3];
+    const uint32_t m = (lw >> (k0 & 31)) & ((1u << G) - 1u);
+    if (G == 4 && m == 0xFu) {
 #pragma unroll
-      for (int r = 0; r < B; ++r) out[(r0 + r) * D + k] = S[r][c];
+      for (int r = 0; r < B; ++r)
+        *reinterpret_cast<v4f*>(out + (r0 + r) * D + k0) =
+            v4f{S[r][c4], S[r][c4 + G / 4], S[r][c4 + 2 * (G / 4)], S[r][c4 + 3 * (G / 4)]};
+    } else if (m) {
+#pragma unroll
+      for (int c = 0; c < G; ++c)
+        if ((m >> c) & 1u) {
+#pragma unroll
+          for (int r = 0; r < B; ++r) out[(r0 + r) * D + k0 + c] = S[r][c4 + c];
+        }
     }
   }
 }
