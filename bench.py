@@ -157,6 +157,27 @@ def _windowed_work(P, Wn):
     return flops, head_tokens
 
 
+def _windowed_bytes(P, Wn):
+    """Algorithmic HBM bytes of the refresh with per-head Eq. 7 windows: the
+    token inputs each replayed head reads (k, v, gate logits bf16, beta
+    fp32 for min(W_lh, n_r) tokens) and the local columns it writes."""
+    import numpy as np
+    total = 0
+    for l in range(P.info()["n_layers"]):
+        L = P.layer(l)
+        ret, _, win = P.units(l)
+        kda = L["kind"] != 0
+        per = L["d_k"] if kda else 1
+        local = ~ret.reshape(L["n_heads"], per).astype(bool)
+        heads = local.any(axis=1)
+        w = np.where(local, win.reshape(L["n_heads"], per), 0).max(axis=1)[heads]
+        ht = int(np.minimum(w[:, None], np.asarray(Wn)[None, :]).sum())
+        per_token = 2 * L["d_k"] + 2 * L["d_v"] + (2 * L["d_k"] if kda else 2) + 4
+        cols = local.sum(axis=1)[heads] if kda else np.full(int(heads.sum()), L["d_k"])
+        total += ht * per_token + int(cols.sum()) * L["d_v"] * 4 * len(Wn)
+    return total
+
+
 def _bench_tp(cfg, args, stream):
     """Store and load with TP storage balancing at TP = 8, all eight ranks'
     shares on this GPU (one launch per rank and direction): pack / partition
@@ -213,7 +234,9 @@ def _bench_tp(cfg, args, stream):
         "pack_tp_ms": round(t_pack * 1e3, 4),
         "unpack_tp_ms": round(t_unpack * 1e3, 4),
         "pack_unpack_gbs": round(moved / (t_pack + t_unpack) / 1e9, 2),
+        "frac_of_hbm_peak": round(moved / (t_pack + t_unpack) / 1e9 / HBM_PEAK_GBS, 4),
         "kernel": "move_kernel<*, kAlt> (8 launches per direction)",
+        "rank0_pack_unpack_bytes_per_checkpoint": int(sum(_algorithmic_bytes(plans[0])[:2])),
     }
 
 
@@ -231,9 +254,11 @@ def _calibrate_copy(steps):
 
 
 def _cpu_baseline(cfg, P, dense_cpu, pack_bytes_per_ckpt, unpack_bytes_per_ckpt, inp_rows,
-                  tokens_per_req):
+                  tokens_per_req, int8_bytes_per_ckpt=None, tp_bytes_per_ckpt=None):
     """The fp64 NumPy oracle, single-threaded, on a bounded sample: pack and
-    unpack of a few checkpoints, refresh of one request over 8 layers."""
+    unpack of a few checkpoints, refresh of one request over 8 layers (full
+    suffix and per-head Eq. 7 windows), INT8 pack and unpack of a few
+    checkpoints, and rank 0's TP8 pack / partition and gather / unpack."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -252,6 +277,40 @@ def _cpu_baseline(cfg, P, dense_cpu, pack_bytes_per_ckpt, unpack_bytes_per_ckpt,
         t = time.perf_counter()
         oracle.refresh_expected(O, k, v, a, b, np.array([0, tokens_per_req]), layers=layers)
         t_ref = time.perf_counter() - t
+        t = time.perf_counter()
+        oracle.refresh_expected(O, k, v, a, b, np.array([0, tokens_per_req]), layers=layers,
+                                head_windows=True)
+        t_win = time.perf_counter() - t
+        win_head_tokens = sum(min(O.head_window(l, int(h)), tokens_per_req)
+                              for l in layers for h in O.refreshed_heads(l))
+        extra = {}
+        if int8_bytes_per_ckpt is not None:
+            m = min(4, n)
+            lo = oracle.Int8Layout(O)
+            pool_q = np.zeros((m, lo.slot_bytes), np.uint8)
+            out_q = np.zeros((m, O.dense_bytes), np.uint8)
+            t = time.perf_counter()
+            oracle.pack_int8(O, dense_cpu[:m], list(range(m)), pool_q, list(range(m)))
+            oracle.unpack_int8_zero_fill(O, pool_q, list(range(m)), out_q, list(range(m)))
+            t_q = time.perf_counter() - t
+            extra["int8_pack_unpack_gbs"] = round(m * int8_bytes_per_ckpt / t_q / 1e9, 4)
+            extra["int8_sample"] = f"INT8 pack+unpack of {m} checkpoints ({t_q:.2f} s)"
+        if tp_bytes_per_ckpt is not None:
+            m = min(8, n)
+            orac = oracle.rank_plans(cfg.layers, 8, cfg.a_s, cfg.eps, cfg.w_max)
+            bal = oracle.plans_balance(orac)
+            O0 = orac[0]
+            d0 = np.random.default_rng(0).integers(0, 256, (m, O0.dense_bytes), dtype=np.uint8)
+            pool0 = np.zeros((m, oracle.slot_bytes_tp(O0, bal)), np.uint8)
+            send0 = np.zeros((m, max(16, oracle.send_bytes_tp(O0, bal, 0))), np.uint8)
+            out0 = np.zeros_like(d0)
+            ix = list(range(m))
+            t = time.perf_counter()
+            oracle.pack_tp(O0, bal, 0, d0, ix, pool0, ix, send0, ix)
+            oracle.unpack_tp(O0, bal, 0, pool0, ix, send0, ix, out0, ix)
+            t_tp = time.perf_counter() - t
+            extra["tp8_rank0_pack_unpack_gbs"] = round(m * tp_bytes_per_ckpt / t_tp / 1e9, 4)
+            extra["tp_sample"] = f"rank 0 of TP8, pack_tp+unpack_tp of {m} checkpoints ({t_tp:.2f} s)"
     heads_sampled = sum(len(O.refreshed_heads(l)) for l in layers)
     heads_all = sum(len(O.refreshed_heads(l)) for l in range(len(O.layers)))
     # one request-token = one token through every refreshed head of every layer
@@ -261,9 +320,12 @@ def _cpu_baseline(cfg, P, dense_cpu, pack_bytes_per_ckpt, unpack_bytes_per_ckpt,
         "value": round(gbs, 4), "unit": "GB/s pack+unpack",
         "refresh_request_tokens_per_s": round(1.0 / sec_per_req_token, 3),
         "cores": 1, "kind": "oracle",
+        "refresh_eq7_windows_head_tokens_per_s": round(win_head_tokens / t_win, 3),
         "sample": (f"pack+unpack of {n} checkpoints ({t_move:.2f} s); refresh of 1 request x "
                    f"{tokens_per_req} tokens over {len(layers)} layers / {heads_sampled} heads "
-                   f"({t_ref:.2f} s), scaled to all {heads_all} refreshed heads"),
+                   f"({t_ref:.2f} s), scaled to all {heads_all} refreshed heads; the same with "
+                   f"per-head windows ({win_head_tokens} head-token replays, {t_win:.2f} s)"),
+        **extra,
         "host_cpus": os.cpu_count(),
     }
 
@@ -483,6 +545,7 @@ def main():
     assert P.status() == 0
     t_win = np.array([e[0].elapsed_time(e[1]) for e in evw]) * 1e-3
     win_flops, win_head_tokens = _windowed_work(P, Wn)
+    win_bytes = _windowed_bytes(P, Wn)
 
     # dasc-wr load of the refreshed requests: unpack then refresh, against
     # the fused load, with the full suffixes and with per-head windows.
@@ -599,9 +662,20 @@ def main():
             "kernel": "refresh_kernel<128, gate, true, false, one_chunk> (per-head windows; the one-chunk kernel when every window is at most 16 tokens)",
             "ms": round(t_win.mean() * 1e3, 4),
             "head_tokens": int(win_head_tokens),
+            "head_tokens_per_s": round(win_head_tokens / t_win.mean(), 1),
             "flops": int(win_flops),
             "achieved_tflops": round(win_flops / t_win.mean() / 1e12, 3),
             "speedup_vs_full_suffix": round(t_ref.mean() / t_win.mean(), 3),
+            "roofline": {"bound": "mfma", "achieved": round(win_flops / t_win.mean() / 1e12, 3),
+                         "peak": FP32_MFMA_PEAK_TF, "unit": "TFLOP/s",
+                         "frac": round(win_flops / t_win.mean() / 1e12 / FP32_MFMA_PEAK_TF, 4),
+                         "traffic": traffic.get("refresh_windowed"),
+                         "hbm_bytes": int(win_bytes),
+                         "hbm_achieved_gbs": round(win_bytes / t_win.mean() / 1e9, 1),
+                         "hbm_frac": round(win_bytes / t_win.mean() / 1e9 / HBM_PEAK_GBS, 4),
+                         "note": "one 16-token chunk per head: neither roof is reached; the "
+                                 "time is each head's serial chain and the partial-line "
+                                 "write-back of the local columns"},
         },
     }
     if not args.no_cpu_baseline:
@@ -610,7 +684,10 @@ def main():
         T0, T1 = int(inp.tok_off[0]), int(inp.tok_off[1])
         bits = lambda x: x[T0:T1].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
         rows = (bits(inp.k), bits(inp.v), bits(inp.a), inp.beta[T0:T1].cpu().numpy())
-        line["cpu_baseline"] = _cpu_baseline(cfg, P, dense_cpu, pack_b, unpack_b, rows, T1 - T0)
+        tp_b = tp8["rank0_pack_unpack_bytes_per_checkpoint"] if tp8 else None
+        line["cpu_baseline"] = _cpu_baseline(cfg, P, dense_cpu, pack_b, unpack_b, rows, T1 - T0,
+                                             int8_bytes_per_ckpt=pack_qb + unpack_qb,
+                                             tp_bytes_per_ckpt=tp_b)
     print(json.dumps(line), flush=True)
 
 

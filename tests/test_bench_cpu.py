@@ -1,0 +1,48 @@
+"""The benchmark's work accounting for the refresh with per-head Eq. 7
+windows, recounted from the oracle plan: head-token replays (each replayed
+head (l, h) of request r replays min(W_lh, n_r) tokens), flops (5 d_v d_k
+per replay) and algorithmic HBM bytes (the replayed tokens' k, v, gate
+logits and beta, plus the local columns written)."""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+R = pytest.importorskip("recurrent_state_cache_amd")
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+import bench  # noqa: E402
+
+
+@pytest.mark.parametrize("name", ["tiny_kda", "widths"])
+def test_windowed_work_and_bytes_recounted_from_the_oracle(name):
+    if name == "tiny_kda":
+        cfg = W.tiny_kda()
+    else:
+        rng = np.random.default_rng(31)
+        f = np.float32
+        cfg = W.Config("widths", [
+            W.Layer(W.KDA, 2, 32, 32, rng.normal(0, 1.5, 64).astype(f), rng.normal(0, 1, 64).astype(f), 0),
+            W.Layer(W.GDN, 6, 16, 16, rng.uniform(-1, 2, 6).astype(f), rng.normal(0, 1, 6).astype(f), 16),
+        ], w_max=16)
+    P = R.Plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max)
+    O = oracle.build_plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max)
+    Wn = np.array([0, 3, 9, 40])
+    ht = flops = nbytes = 0
+    for li, L in enumerate(O.layers):
+        kda = L.kind == oracle.KDA
+        for h in O.refreshed_heads(li):
+            w = O.head_window(li, int(h))
+            cols = int((~L.retained.reshape(L.n_heads, L.d_k)[h]).sum()) if kda else L.d_k
+            for n_r in Wn:
+                t = min(w, int(n_r))
+                ht += t
+                flops += 5 * L.d_v * L.d_k * t
+                nbytes += t * (2 * L.d_k + 2 * L.d_v + (2 * L.d_k if kda else 2) + 4)
+                nbytes += cols * L.d_v * 4
+    assert bench._windowed_work(P, Wn) == (flops, ht)
+    assert bench._windowed_bytes(P, Wn) == nbytes
+    assert ht > 0
