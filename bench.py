@@ -273,7 +273,7 @@ def _cpu_baseline(cfg, P, dense_cpu, pack_bytes_per_ckpt, unpack_bytes_per_ckpt,
         oracle.unpack_zero_fill(O, pool, list(range(n)), out, list(range(n)))
         t_move = time.perf_counter() - t
         k, v, a, b = inp_rows
-        layers = [l for l in range(len(O.layers)) if len(O.refreshed_heads(l))][:8]
+        layers = [l for l in range(len(O.layers)) if len(O.refreshed_heads(l))][:20]
         t = time.perf_counter()
         oracle.refresh_expected(O, k, v, a, b, np.array([0, tokens_per_req]), layers=layers)
         t_ref = time.perf_counter() - t
@@ -285,7 +285,7 @@ def _cpu_baseline(cfg, P, dense_cpu, pack_bytes_per_ckpt, unpack_bytes_per_ckpt,
                               for l in layers for h in O.refreshed_heads(l))
         extra = {}
         if int8_bytes_per_ckpt is not None:
-            m = min(4, n)
+            m = min(16, n)
             lo = oracle.Int8Layout(O)
             pool_q = np.zeros((m, lo.slot_bytes), np.uint8)
             out_q = np.zeros((m, O.dense_bytes), np.uint8)
@@ -296,7 +296,7 @@ def _cpu_baseline(cfg, P, dense_cpu, pack_bytes_per_ckpt, unpack_bytes_per_ckpt,
             extra["int8_pack_unpack_gbs"] = round(m * int8_bytes_per_ckpt / t_q / 1e9, 4)
             extra["int8_sample"] = f"INT8 pack+unpack of {m} checkpoints ({t_q:.2f} s)"
         if tp_bytes_per_ckpt is not None:
-            m = min(8, n)
+            m = min(32, n)
             orac = oracle.rank_plans(cfg.layers, 8, cfg.a_s, cfg.eps, cfg.w_max)
             bal = oracle.plans_balance(orac)
             O0 = orac[0]
@@ -679,7 +679,7 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        m = min(8, n)
+        m = min(32, n)
         dense_cpu = dense[:m].cpu().numpy()
         T0, T1 = int(inp.tok_off[0]), int(inp.tok_off[1])
         bits = lambda x: x[T0:T1].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
