@@ -579,6 +579,11 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kC = kRefreshChunk;
 
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
 template <int D>
 struct RefreshShape {
   static constexpr int kKT = D / 16;                  // k tiles
@@ -603,18 +608,25 @@ struct RefreshQW {
 };
 template <int D, int NB>
 struct RefreshQW<D, true, NB> {
-  uint16_t Qh[NB == 2 ? kC : 1][D + 16];  // gamma_t o k_t: bf16 hi, then lo (rows padded
-  uint16_t Ql[NB == 2 ? kC : 1][D + 16];  // to 8 banks mod 64, so an A-operand read is 2 passes)
+  // gamma_t o k_t: bf16 hi, then lo.  Rows padded by 16 bytes: the 16 rows
+  // m of one 8-byte A-operand read start 4 banks apart.
+  uint16_t Qh[NB == 2 ? kC : 1][D + 8];
+  uint16_t Ql[NB == 2 ? kC : 1][D + 8];
   // k_s o D_{15,s}, [k][s], by chunk parity: per row k and token group
-  // g (s = 4 g .. 4 g + 3) the four bf16 hi, then the four bf16 lo.
-  uint16_t W[NB][D][2 * kC];
+  // g (s = 4 g .. 4 g + 3) the four bf16 hi, then the four bf16 lo.  Rows
+  // are padded to 80 bytes (20 banks), so the 16 rows that one 16-byte
+  // A-operand read spans start on 16 different 4-bank groups.
+  uint16_t W[NB][D][2 * kC + 8];
 };
 
 template <int D, int NB>
 struct alignas(16) RefreshLds {
   float K[kC][D];             // k of the chunk being prepared
   float A[kC][D];             // its decays
-  uint16_t V[NB][kC][D];      // v (bf16 bits as given), by chunk parity
+  // v (bf16 bits as given), by chunk parity; rows padded by 16 bytes, so
+  // the rows 4 g + r that the lane groups g read at once fall on
+  // disjoint banks
+  uint16_t V[NB][kC][D + 8];
   float B[NB][kC];            // beta, by chunk parity
   RefreshQW<D, RefreshShape<D>::kSplit, NB> qw;
   float G[NB][D];             // gamma_15 by chunk parity
@@ -812,14 +824,29 @@ refresh_kernel(RefreshArgs a) {
   };
 
   // From the staged chunk: L (into sh.L), Q (sh.Q), W and gamma_15 (buffer vb).
-  auto stage2 = [&](int vb) __attribute__((always_inline)) {
+  // PW >= 0 (d = 128, four waves): the caller's wave index, a compile-time
+  // constant, so that the row pair of each half-wave (p = 2 PW + h) and the
+  // direction of the Q / W lanes are known to the compiler and the only
+  // per-lane selects left are at the two entries where the half-waves'
+  // rows differ; PW = -1: the same work with p and the direction per lane.
+  auto stage2_body = [&](int vb, auto pw_c) __attribute__((always_inline)) {
+    constexpr int PW = decltype(pw_c)::value;
+    static_assert(PW < 0 || (NB4 == 32 && kAllStage), "wave-uniform rows need d = 128");
     if (kAllStage || tid < 2 * D) {
       // L, rows p and 15 - p (15 entries in all), 4 channels per lane,
       // summed over the NB4 lanes of the row pair: within a 16-lane row by
       // DPP, and for NB4 = 32 across the row pair by a row broadcast, which
       // leaves the full sum in the upper row.  The last lane of the group
       // stores the entries after the loop, so the loop has no branch.
-      const int p = tid / NB4, c4 = 4 * (tid % NB4);
+      const bool h = PW >= 0 && (tid & 32) != 0;  // upper half-wave
+      const int p = PW >= 0 ? 2 * PW + (h ? 1 : 0) : tid / NB4, c4 = 4 * (tid % NB4);
+      // entry i is in row p (i < p), and row 15 - p starts at i = p
+      auto in_row_p = [&](int i) {
+        return PW >= 0 ? (i < 2 * PW || (i == 2 * PW && h)) : i < p;
+      };
+      auto starts_q = [&](int i) {
+        return PW >= 0 ? ((i == 2 * PW && !h) || (i == 2 * PW + 1 && h)) : i == p;
+      };
       // K and A are adjacent [kC][D] arrays: row r of A is row kC + r here.
       const float(*KA)[D] = reinterpret_cast<const float(*)[D]>(&sh.K[0][0]);
       const float bp = sh.B[vb][p], bq = sh.B[vb][kC - 1 - p];
@@ -839,10 +866,10 @@ refresh_kernel(RefreshArgs a) {
       float lv[kC - 1];
 #pragma unroll
       for (int i = 0; i < kC - 1; ++i) {
-        const bool first = i < p;
+        const bool first = in_row_p(i);
         const float* const r0 = first ? rowP : rowQ;  // K row s + 1
         if (i == 0) pk = first ? kp : kq;
-        else pk = i == p ? kq : pk;
+        else pk = starts_q(i) ? kq : pk;
         const v4f al = *reinterpret_cast<const v4f*>(r0 + (kC - i) * D);   // A[s + 1]
         const v4f ks = *reinterpret_cast<const v4f*>(r0 - (i + 1) * D);    // K[s]
         float part = 0.f;
@@ -861,11 +888,11 @@ refresh_kernel(RefreshArgs a) {
         float* const lP = &sh.LT[0][0] + (p - 1) * (kC + 4) + p;
         float* const lQ = &sh.LT[0][0] + (kC - 2) * (kC + 4) + (kC - 1 - p);
 #pragma unroll
-        for (int i = 0; i < kC - 1; ++i) *((i < p ? lP : lQ) - i * (kC + 4)) = lv[i];
+        for (int i = 0; i < kC - 1; ++i) *((in_row_p(i) ? lP : lQ) - i * (kC + 4)) = lv[i];
       }
       // gamma_t and Q (forward lanes, tid < D) or W (backward lanes)
       const int j = tid % D;
-      const bool fwd = tid < D;
+      const bool fwd = PW >= 0 ? PW < 2 : tid < D;
       float gm = 1.f;
       if constexpr (Sh::kSplit) {
         float qw[kC];  // step i: token i (forward) or token 15 - i (backward)
@@ -912,6 +939,22 @@ refresh_kernel(RefreshArgs a) {
         }
       }
       if (!ONE && fwd) sh.G[vb][j] = gm;  // the one-chunk kernel decays a zero state
+    }
+  };
+  auto stage2 = [&](int vb) __attribute__((always_inline)) {
+    stage2_body(vb, IntC<-1>{});
+  };
+  // In the chunk loop: one specialized copy per wave (a uniform branch on
+  // the wave index).
+  auto stage2_waves = [&](int vb) __attribute__((always_inline)) {
+    if constexpr (NB4 == 32 && kAllStage && Sh::kNW == 4) {
+      const int wv = __builtin_amdgcn_readfirstlane(wave);
+      if (wv == 0) stage2_body(vb, IntC<0>{});
+      else if (wv == 1) stage2_body(vb, IntC<1>{});
+      else if (wv == 2) stage2_body(vb, IntC<2>{});
+      else stage2_body(vb, IntC<3>{});
+    } else {
+      stage2_body(vb, IntC<-1>{});
     }
   };
 
@@ -1087,7 +1130,7 @@ refresh_kernel(RefreshArgs a) {
         }
       }
       if constexpr (!ONE) {
-        if (n + 1 < nchunks) stage2(nb);
+        if (n + 1 < nchunks) stage2_waves(nb);
         __syncthreads();
       }
     }
