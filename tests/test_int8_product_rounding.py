@@ -50,3 +50,18 @@ def test_scale_from_column_maximum_keeps_quotients_within_127():
     m = (np.ldexp(1.0, rng.integers(-26, 127, 1_000_000)) * rng.uniform(1, 2, 1_000_000)).astype(np.float32)
     s = m / np.float32(127)
     assert np.all(np.abs(m.astype(np.float64) / s.astype(np.float64)) <= 127 * (1 + 2.0 ** -23))
+
+
+def test_clip_never_binds_on_either_route():
+    # the kernel leaves out Eq. 10's clip to [-127, 127]: for the column
+    # maximum itself (the largest |x| of a column), both the fp32 product
+    # m (1 / s) and the fp32 quotient m / s round to at most 127
+    rng = np.random.default_rng(12)
+    f = np.float32
+    m = (np.ldexp(1.0, rng.integers(-26, 127, 2_000_000)) * rng.uniform(1, 2, 2_000_000)).astype(f)
+    m = np.concatenate([m, np.array([1e-8, np.finfo(f).max, np.finfo(f).tiny], f)])
+    s = np.maximum(m, f(1e-8)) / f(127)
+    inv = f(1) / s
+    assert np.all(np.abs(np.rint(m * inv)) <= 127)
+    assert np.all(np.abs(np.rint(m / s)) <= 127)
+    assert np.all(np.abs(m * inv) < 127.5)
