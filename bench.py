@@ -40,6 +40,9 @@ KERNEL_SOURCES = ["recurrent_state_cache_amd/csrc/dasc_kernels.hip",
                   "recurrent_state_cache_amd/csrc/dasc_host.cpp"]
 # kernel name pattern -> role (the TP movers and the windowed refresh are
 # instantiations of their own)
+# rounds of the rocprofv3 kernel-statistics run (--warmup, --steps)
+PROFILE_WARMUP, PROFILE_STEPS = 3, 10
+
 KERNEL_ROLES = {r"qmove_kernel<true>": "pack_int8", r"qmove_kernel<false>": "unpack_int8",
                 r"(?<!q)move_kernel<true, \d+, \d+, false>": "pack",
                 r"(?<!q)move_kernel<false, \d+, \d+, false>": "unpack",
@@ -380,6 +383,18 @@ def _summarize(dirs, workload):
         if role:
             stats[role] = (int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]),
                            float(r["MaxNs"]))
+    # The timed launches alone: the stats run makes PROFILE_WARMUP + PROFILE_STEPS
+    # rounds of every section, and the first round's launches (cold buffers)
+    # are left out, as the bench's own clock leaves out its warm-up.
+    runs = {}
+    for r in sorted(_csv_rows(stats_d, "_kernel_trace.csv"), key=lambda r: int(r["Dispatch_Id"])):
+        role = _role(r["Kernel_Name"])
+        if role:
+            runs.setdefault(role, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    timed = {}
+    for role, d in runs.items():
+        skip = len(d) // (PROFILE_WARMUP + PROFILE_STEPS) * PROFILE_WARMUP
+        timed[role] = sum(d[skip:]) / max(1, len(d) - skip)
     copy = lambda name: "copy" if "copyBuffer" in name or "copy_kernel" in name else None
     cal_f = _counter_means(fetch_c, "FETCH_SIZE", copy).get("copy")
     cal_w = _counter_means(write_c, "WRITE_SIZE", copy).get("copy")
@@ -391,15 +406,16 @@ def _summarize(dirs, workload):
     write = _counter_means(write_d, "WRITE_SIZE", _role)
     traffic = {k: int(round(fetch[k] * 1024 * f_scale + write[k] * 1024 * w_scale))
                for k in fetch if k in write}
-    lines = [f"| kernel | calls | average (us) | min (us) | max (us) | FETCH_SIZE (KiB) | "
-             f"WRITE_SIZE (KiB) | HBM bytes per launch (calibrated) |",
-             "|---|---|---|---|---|---|---|---|"]
+    lines = [f"| kernel | calls | average (us) | timed launches: average (us) | min (us) | "
+             f"max (us) | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM bytes per launch (calibrated) |",
+             "|---|---|---|---|---|---|---|---|---|"]
     for role in ("pack", "unpack", "refresh", "pack_int8", "unpack_int8", "pack_tp", "unpack_tp",
                  "refresh_windowed", "refresh_fused", "refresh_recurrent"):
         if role not in stats:
             continue
         c, avg, mn, mx = stats[role]
-        lines.append(f"| {role} | {c} | {avg / 1e3:.1f} | {mn / 1e3:.1f} | {mx / 1e3:.1f} | "
+        lines.append(f"| {role} | {c} | {avg / 1e3:.1f} | {timed.get(role, float('nan')) / 1e3:.1f} | "
+                     f"{mn / 1e3:.1f} | {mx / 1e3:.1f} | "
                      f"{fetch.get(role, float('nan')):.0f} | {write.get(role, float('nan')):.0f} | "
                      f"{traffic.get(role, 'n/a')} |")
     out = "\n".join(lines)
