@@ -94,24 +94,33 @@ def _workload(name):
 
 def _algorithmic_bytes(P):
     """Bytes pack and unpack must move, from the plan: pack reads each GDN
-    retained head and every KDA head with a retained channel in full (a
-    strided column forces whole rows), writes the ragged payload, and copies
-    the conv bytes; unpack reads the payload and the conv bytes and writes
-    the whole dense checkpoint."""
+    retained head in full and, of a KDA head, every 32-channel column block
+    (d = 128; the whole head for other widths) with a retained channel (a
+    strided column forces whole 128-byte row segments), writes the ragged
+    payload, and copies the conv bytes; unpack reads the payload and the conv
+    bytes and writes the whole dense checkpoint.  INT8 pack reads every KDA
+    head with a retained channel whole (a column's scale spans the head)."""
     info = P.info()
-    read_pack = 0
+    read_pack = read_pack_q = 0
     for l in range(info["n_layers"]):
         L = P.layer(l)
         ret = P.units(l)[0]
         if L["kind"] == 0:
             read_pack += int(ret.sum()) * L["unit_bytes"]
+            read_pack_q += int(ret.sum()) * L["unit_bytes"]
         else:
             per_head = ret.reshape(L["n_heads"], L["d_k"]).any(axis=1)
-            read_pack += int(per_head.sum()) * L["d_v"] * L["d_k"] * 4
+            read_pack_q += int(per_head.sum()) * L["d_v"] * L["d_k"] * 4
+            if L["d_k"] == 128 and L["d_v"] == 128:
+                # the fp32 pack reads 32-channel column blocks with a retained channel
+                per_block = ret.reshape(L["n_heads"], 4, 32).any(axis=2)
+                read_pack += int(per_block.sum()) * L["d_v"] * 32 * 4
+            else:
+                read_pack += int(per_head.sum()) * L["d_v"] * L["d_k"] * 4
     pack = read_pack + info["temporal_rag_bytes"] + 2 * info["conv_bytes"]
     unpack = info["temporal_rag_bytes"] + info["temporal_dense_bytes"] + 2 * info["conv_bytes"]
     q = info["int8_payload_bytes"] + info["int8_scale_bytes"]
-    pack_q = read_pack + q + 2 * info["conv_bytes"]
+    pack_q = read_pack_q + q + 2 * info["conv_bytes"]
     unpack_q = q + info["temporal_dense_bytes"] + 2 * info["conv_bytes"]
     return pack, unpack, pack_q, unpack_q
 

@@ -81,7 +81,7 @@ struct dasc_plan {
   std::vector<RefreshTask> refresh;
   std::vector<float> gate_expA, gate_dt;
   std::vector<Group> refresh_groups;
-  int32_t kda_r_max = 0;  // largest retained-channel count of a KDA head
+  int32_t kda_r_max = 0;  // most unit segments one KDA piece stages
   bool kda_128 = true;    // every KDA layer has d_k = d_v = 128
   int64_t off_pack = 0, off_unpack = 0, off_pack_q = 0, off_unpack_q = 0, off_pack_tp = 0,
           off_unpack_tp = 0, off_unpack_rest = 0, off_refresh = 0, off_expA = 0, off_dt = 0,
@@ -185,6 +185,10 @@ bool set_tp(dasc_plan* p, int32_t tp, int32_t rank, const std::vector<int64_t>& 
 // follow the dense checkpoint's order (layers, heads, then conv), which is
 // also the pool slot's order.
 void build_tables(dasc_plan* p) {
+  // The pack list with 32-row pieces for every KDA head: the TP store's list
+  // is made from it (on a rank's eighth of the heads the row pieces measured
+  // faster than the column blocks).
+  std::vector<Piece> pack_rows;
   for (const auto& L : p->layers) {
     int64_t j = 0;  // retained units of the layer seen so far
     if (L.kind == kGDN) {
@@ -193,6 +197,7 @@ void build_tables(dasc_plan* p) {
         if (L.retained[h]) {
           const uint64_t p_off = L.pool_off + j * L.unit_bytes;
           push_range(p->pack, d_off, p_off, L.unit_bytes, kPieceCopy);
+          push_range(pack_rows, d_off, p_off, L.unit_bytes, kPieceCopy);
           push_range(p->unpack, d_off, p_off, L.unit_bytes, kPieceCopy);
           ++j;
         } else {
@@ -224,18 +229,37 @@ void build_tables(dasc_plan* p) {
       t.d_k = static_cast<uint16_t>(L.d_k);
       t.d_v = static_cast<uint16_t>(L.d_v);
       t.r = static_cast<uint16_t>(r);
-      for (int rb = 0; rb < row_blocks; ++rb) {
-        t.rb = static_cast<uint16_t>(rb);
-        p->pack.push_back(t);
-        p->unpack.push_back(t);
+      if (L.d_k == 128 && L.d_v == 128) {
+        // pack: 32 x 32 blocks (4 KiB) with a retained channel; unpack:
+        // 32-row pieces (their contiguous 16 KiB writes measured faster)
+        for (int rb = 0; rb < row_blocks; ++rb) {
+          Piece u = t;
+          u.rb = static_cast<uint16_t>(rb);
+          p->unpack.push_back(u);
+          pack_rows.push_back(u);
+          u.type = kPieceKdaBlock;
+          for (uint32_t cb = 0; cb < 128 / kKdaBlockCols; ++cb) {
+            u.bytes = cb;
+            if (t.mask[cb] != 0) p->pack.push_back(u);
+          }
+        }
+        p->kda_r_max = std::max(p->kda_r_max, static_cast<int32_t>(std::max<uint32_t>(r, kKdaBlockCols)));
+      } else {
+        for (int rb = 0; rb < row_blocks; ++rb) {
+          t.rb = static_cast<uint16_t>(rb);
+          p->pack.push_back(t);
+          pack_rows.push_back(t);
+          p->unpack.push_back(t);
+        }
+        p->kda_r_max = std::max(p->kda_r_max, static_cast<int32_t>(r));
       }
-      p->kda_r_max = std::max(p->kda_r_max, static_cast<int32_t>(r));
       j += r;
     }
   }
   // Conv state: one contiguous block after the temporal payload on both sides.
   const dasc_plan_info& I = p->info;
   push_range(p->pack, I.temporal_dense_bytes, I.temporal_rag_bytes, I.conv_bytes, kPieceCopy);
+  push_range(pack_rows, I.temporal_dense_bytes, I.temporal_rag_bytes, I.conv_bytes, kPieceCopy);
   push_range(p->unpack, I.temporal_dense_bytes, I.temporal_rag_bytes, I.conv_bytes, kPieceCopy);
 
   // INT8 pieces ([dasc] Appendix E.1 Eq. 10): pack quantizes each head with a
@@ -333,7 +357,7 @@ void build_tables(dasc_plan* p) {
         }
       }
     };
-    remap(p->pack, p->pack_tp);
+    remap(pack_rows, p->pack_tp);
     remap(p->unpack, p->unpack_tp);
   }
 

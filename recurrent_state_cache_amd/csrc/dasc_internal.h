@@ -23,6 +23,10 @@ constexpr uint32_t kPieceKda = 2;   // kKdaRows rows of a KDA head with >= 1 ret
 // and KDA heads whole.
 constexpr uint32_t kPieceQGdn = 3;  // a retained GDN head
 constexpr uint32_t kPieceQKda = 4;  // a KDA head with >= 1 retained channel
+// fp32 pack of a d_k = d_v = 128 KDA head: the 32 x 32 block of rows
+// kKdaRows rb .. and channels 32 cb .. (cb in the piece's `bytes` field),
+// 4 KiB of the dense state, for a block with >= 1 retained channel
+constexpr uint32_t kPieceKdaBlock = 5;
 
 // Largest byte range one copy / zero piece covers: 256 lanes x 16 B.  Small
 // pieces stream HBM markedly faster on MI355X than 64 KiB pieces do.
@@ -33,6 +37,8 @@ constexpr uint32_t kCopyChunk = 4096;
 constexpr int kKdaRows = 32;
 // LDS floats per staged unit segment (kKdaRows + 4 of padding).
 constexpr int kKdaLdsRow = kKdaRows + 4;
+// Channels of one KDA block piece (d = 128 heads): 32 rows x 32 channels.
+constexpr int kKdaBlockCols = 32;
 // Rows of a GDN head one INT8 unpack piece writes: 8 rows of 128 fp32 are
 // 4 KiB, one 16-byte store per lane, like the copy pieces.
 constexpr int kQGdnRows = 8;
@@ -45,7 +51,7 @@ struct alignas(64) Piece {
   uint64_t dense_off;  // copy / zero: the range; head pieces: the head's state [d_v][d_k] fp32
   uint64_t pool_off;   // copy: the range; head pieces: the head's first retained unit
   uint32_t type;       // kPiece*
-  uint32_t bytes;      // copy / zero: multiple of 16, at most kCopyChunk
+  uint32_t bytes;      // copy / zero: multiple of 16, at most kCopyChunk; KDA block: cb
   uint16_t d_k, d_v;   // head pieces: head shape
   uint16_t rb, r;      // row block (rows kKdaRows rb .., INT8 GDN unpack kQGdnRows rb ..),
                        // retained channels
@@ -116,7 +122,7 @@ struct Group {
 struct MoveArgs {
   const Piece* pieces;
   uint32_t n_pieces;
-  int32_t kda_r_max;  // largest r of a KDA piece (sizes the LDS); 0 if none
+  int32_t kda_r_max;  // most unit segments a KDA piece stages (sizes the LDS); 0 if none
   bool kda_128;       // every KDA piece has d_k = d_v = 128
   const int32_t* src_idx;
   const int32_t* dst_idx;

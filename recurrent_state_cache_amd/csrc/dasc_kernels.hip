@@ -160,6 +160,50 @@ __device__ __forceinline__ void kda_piece(const Piece& t, const uint8_t* src, ui
   }
 }
 
+// KDA block pieces of the pack list (d_k = d_v = 128): the 32 x 32 block of
+// rows 32 rb .. and channels 32 cb .. of one head, 4 KiB of the dense
+// state, read like a copy piece (workgroups that read 4 KiB stream HBM
+// better than 16 KiB ones; blocks without a retained channel are not in the
+// list).  Lane (v, cg), v = tid / 8, cg = tid % 8, reads row 32 rb + v,
+// channels 32 cb + 4 cg .. + 3 as one 16-byte load (8 lanes cover the
+// block's 128-byte row segment) and stores its retained channels into LDS,
+// which holds the block's retained columns as 32-row segments (one 128-byte
+// line of a unit each); segment j leaves as 16-byte pieces into unit
+// (retained channels below 32 cb) + j of the head.  (Unpack keeps the
+// 32-row pieces: their contiguous 16 KiB writes measured faster than block
+// writes.)
+template <bool kAlt>
+__device__ __forceinline__ void kda_block_pack(const Piece& t, const uint8_t* src, uint8_t* dst,
+                                               uint8_t* alt, float* U) {
+  constexpr int D = 128;
+  const int cb = static_cast<int>(t.bytes);
+  const int tid = threadIdx.x;
+  const int v = tid >> 3, cg = tid & 7;
+  uint32_t bits4 = 0, below = 0;
+  lane_ranks(t, 8 * cb + cg, bits4, below);
+  const uint32_t m0 = t.mask[0], m1 = t.mask[1], m2 = t.mask[2];
+  const int base = (cb > 0 ? __popc(m0) : 0) + (cb > 1 ? __popc(m1) : 0) + (cb > 2 ? __popc(m2) : 0);
+  const uint32_t mc = cb == 0 ? m0 : cb == 1 ? m1 : cb == 2 ? m2 : t.mask[3];
+  const int rc = __popc(mc);  // retained channels of the block
+  const int row = kKdaRows * t.rb + v;
+  const f32x4 x = ld_stream(reinterpret_cast<const f32x4*>(src + t.dense_off) +
+                            (row * D + kKdaBlockCols * cb + 4 * cg) / 4);
+  uint32_t rk = below - base;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if ((bits4 >> c) & 1u) {
+      U[rk * kKdaLdsRow + v] = x[c];
+      ++rk;
+    }
+  }
+  __syncthreads();
+  const int j = tid >> 3, g = tid & 7;  // segment j, 16-byte piece g
+  if (j < rc)
+    st_stream(*reinterpret_cast<const f32x4*>(&U[j * kKdaLdsRow + 4 * g]),
+              reinterpret_cast<f32x4*>(unit_seg<kAlt>(t, dst, alt, base + j, D) +
+                                       kKdaRows * t.rb + 4 * g));
+}
+
 template <bool kPack, bool kAlt = false>
 __device__ __forceinline__ void copy_piece(const Piece& t, const uint8_t* src, uint8_t* dst,
                                            uint8_t* alt = nullptr) {
@@ -195,14 +239,21 @@ __global__ void __launch_bounds__(kThreads) move_kernel(MoveArgs a) {
   const int64_t x = has_alt ? a.alt_idx[blockIdx.y] : 0;
   const bool bad_idx = !in_range(s, a.n_src) || !in_range(d, a.n_dst) ||
                        (has_alt && !in_range(x, a.n_alt));
-  if (bad_idx | (t.type > kPieceKda)) {
+  const bool block = kPack && t.type == kPieceKdaBlock;
+  if (bad_idx | (t.type > kPieceKda && !block)) {
     if (bad_idx && blockIdx.x == 0 && threadIdx.x == 0) flag(a.status, DASC_STATUS_BAD_INDEX);
     return;
   }
   const uint8_t* src = a.src_base + s * a.src_stride;
   uint8_t* dst = a.dst_base + d * a.dst_stride;
   uint8_t* alt = has_alt ? a.alt_base + x * a.alt_stride : nullptr;
-  if (t.type == kPieceKda)  // uniform per workgroup
+  if constexpr (kPack) {
+    if (block) {  // uniform per workgroup
+      kda_block_pack<kAlt>(t, src, dst, alt, U);
+      return;
+    }
+  }
+  if (t.type == kPieceKda)
     kda_piece<kPack, DK, DV, kAlt>(t, src, dst, alt, U);
   else
     copy_piece<kPack, kAlt>(t, src, dst, alt);

@@ -148,6 +148,14 @@ def test_tp_small_kda_skewed(tp):
     assert b.M_remote > 0
 
 
+def test_tp_kda_d128_skewed():
+    # d = 128: the pack list's 32-channel column blocks, some of whose units
+    # straddle the keep boundary into the send row
+    layers = _skewed(W.KDA, 4, 128, 2, 71, conv=64)
+    b = _round_trip(layers, -0.3, 1e-3, 16, 2, 3, "kda d128 tp2", seed=71)
+    assert b.M_remote > 0
+
+
 @pytest.mark.parametrize("tp", [2, 4])
 def test_tp_small_gdn_skewed(tp):
     # 1 KiB units (one copy piece each), some kept, some sent
