@@ -384,26 +384,45 @@ def _counter_means(directory, counter, match):
 def _summarize(dirs, workload):
     """Markdown summary of the rocprofv3 runs: kernel durations, and HBM
     traffic per dispatch from FETCH_SIZE / WRITE_SIZE, each scaled by what the
-    same counter reads for a plain 1 GiB device copy."""
+    same counter reads for a plain 1 GiB device copy.  A role that several
+    kernel instantiations serve in one run (the refresh of a workload with
+    both GDN and KDA layers) gets one row per instantiation, and no
+    machine-readable traffic: its launches are not alike."""
+    import re
     stats_d, fetch_d, write_d, fetch_c, write_c = dirs
+    trace = sorted(_csv_rows(stats_d, "_kernel_trace.csv"), key=lambda r: int(r["Dispatch_Id"]))
+    names = {}
+    for r in trace:
+        role = _role(r["Kernel_Name"])
+        if role:
+            names.setdefault(role, set()).add(r["Kernel_Name"])
+
+    def key(name):
+        role = _role(name)
+        if not role:
+            return None
+        if len(names.get(role, ())) <= 1:
+            return role
+        m = re.search(r"<([^<>]*)>", name)
+        return f"{role} <{m.group(1) if m else name}>"
+
     stats = {}
     for r in _csv_rows(stats_d, "_kernel_stats.csv"):
-        role = _role(r["Name"])
-        if role:
-            stats[role] = (int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]),
-                           float(r["MaxNs"]))
+        k = key(r["Name"])
+        if k:
+            stats[k] = (int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]), float(r["MaxNs"]))
     # The timed launches alone: the stats run makes PROFILE_WARMUP + PROFILE_STEPS
     # rounds of every section, and the first round's launches (cold buffers)
     # are left out, as the bench's own clock leaves out its warm-up.
     runs = {}
-    for r in sorted(_csv_rows(stats_d, "_kernel_trace.csv"), key=lambda r: int(r["Dispatch_Id"])):
-        role = _role(r["Kernel_Name"])
-        if role:
-            runs.setdefault(role, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    for r in trace:
+        k = key(r["Kernel_Name"])
+        if k:
+            runs.setdefault(k, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     timed = {}
-    for role, d in runs.items():
+    for k, d in runs.items():
         skip = len(d) // (PROFILE_WARMUP + PROFILE_STEPS) * PROFILE_WARMUP
-        timed[role] = sum(d[skip:]) / max(1, len(d) - skip)
+        timed[k] = sum(d[skip:]) / max(1, len(d) - skip)
     copy = lambda name: "copy" if "copyBuffer" in name or "copy_kernel" in name else None
     cal_f = _counter_means(fetch_c, "FETCH_SIZE", copy).get("copy")
     cal_w = _counter_means(write_c, "WRITE_SIZE", copy).get("copy")
@@ -411,22 +430,21 @@ def _summarize(dirs, workload):
         raise SystemExit("no device-copy dispatch in the calibration runs")
     kib = (1 << 30) / 1024.0
     f_scale, w_scale = kib / cal_f, kib / cal_w
-    fetch = _counter_means(fetch_d, "FETCH_SIZE", _role)
-    write = _counter_means(write_d, "WRITE_SIZE", _role)
+    fetch = _counter_means(fetch_d, "FETCH_SIZE", key)
+    write = _counter_means(write_d, "WRITE_SIZE", key)
     traffic = {k: int(round(fetch[k] * 1024 * f_scale + write[k] * 1024 * w_scale))
                for k in fetch if k in write}
     lines = [f"| kernel | calls | average (us) | timed launches: average (us) | min (us) | "
              f"max (us) | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM bytes per launch (calibrated) |",
              "|---|---|---|---|---|---|---|---|---|"]
-    for role in ("pack", "unpack", "refresh", "pack_int8", "unpack_int8", "pack_tp", "unpack_tp",
-                 "refresh_windowed", "refresh_fused", "refresh_recurrent"):
-        if role not in stats:
-            continue
-        c, avg, mn, mx = stats[role]
-        lines.append(f"| {role} | {c} | {avg / 1e3:.1f} | {timed.get(role, float('nan')) / 1e3:.1f} | "
+    order = ("pack", "unpack", "refresh", "pack_int8", "unpack_int8", "pack_tp", "unpack_tp",
+             "refresh_windowed", "refresh_fused", "refresh_recurrent")
+    for k in sorted(stats, key=lambda k: (order.index(k.split(" ")[0]), k)):
+        c, avg, mn, mx = stats[k]
+        lines.append(f"| {k} | {c} | {avg / 1e3:.1f} | {timed.get(k, float('nan')) / 1e3:.1f} | "
                      f"{mn / 1e3:.1f} | {mx / 1e3:.1f} | "
-                     f"{fetch.get(role, float('nan')):.0f} | {write.get(role, float('nan')):.0f} | "
-                     f"{traffic.get(role, 'n/a')} |")
+                     f"{fetch.get(k, float('nan')):.0f} | {write.get(k, float('nan')):.0f} | "
+                     f"{traffic.get(k, 'n/a')} |")
     out = "\n".join(lines)
     out += (f"\n\nCalibration: a 1 GiB device copy reads FETCH_SIZE {cal_f:.1f} KiB and "
             f"WRITE_SIZE {cal_w:.1f} KiB per dispatch, so FETCH_SIZE is scaled by "
@@ -434,7 +452,8 @@ def _summarize(dirs, workload):
     out += "Machine-readable (bench.py reads these lines):\n\n"
     out += f"    workload: {workload}\n"
     out += f"    kernel_sources_sha256: {_sources_sha256()}\n"
-    out += f"    traffic_bytes: {json.dumps(traffic, sort_keys=True)}\n"
+    machine = {k: v for k, v in traffic.items() if k in order}
+    out += f"    traffic_bytes: {json.dumps(machine, sort_keys=True)}\n"
     return out
 
 
