@@ -20,8 +20,11 @@ float32, step by step as printed, and compares bit for bit.
 
 Readings (the page is silent on them):
 * "round" is round-half-to-even (numpy rint), the IEEE default.
-* max(., 1e-8) and the column maximum ignore NaN (fmax); a quotient S / s that
-  is NaN (a NaN or infinite state entry) quantizes to 0.
+* max(., 1e-8) and the column maximum ignore NaN: a NaN entry's magnitude
+  counts as 0 (the maximum of the other magnitudes, all >= 0, is then
+  unchanged; numpy's fmax.reduce was seen to miss the maximum when a
+  signaling NaN shares its vector block); a quotient S / s that is NaN (a
+  NaN or infinite state entry) quantizes to 0.
 * INT8 pool slot layout: every retained unit's int8 payload, layer by layer
   in unit order (a GDN unit as [d_v][d_k] row-major, a KDA unit as its d_v
   column entries), padded to 16 bytes; then every retained unit's fp32
@@ -78,8 +81,9 @@ def quantize_columns(X: np.ndarray):
     """Eq. 10 on a block X [d_v, m] of fp32 columns (one scale per column).
     Returns (q int8 [d_v, m], s float32 [m])."""
     X = np.asarray(X, dtype=F32)
-    a = np.fmax.reduce(np.abs(X), axis=0)              # max_v |S|
-    s = np.fmax(a, SCALE_FLOOR) / QMAX                 # fp32 division
+    mag = np.abs(X)
+    a = np.where(np.isnan(mag), F32(0), mag).max(axis=0)  # max_v |S|, NaN entries skipped
+    s = np.maximum(a, SCALE_FLOOR) / QMAX              # fp32 division
     with np.errstate(invalid="ignore", divide="ignore"):
         r = np.rint(X / s[None, :])                    # fp32 quotient, half to even
     r = np.where(np.isnan(r), F32(0), r)

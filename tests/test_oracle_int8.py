@@ -107,6 +107,24 @@ def test_non_finite_entries_quantize_to_zero():
     assert math.isinf(s[1]) and q[:, 1].tolist() == [0, 0, 0]
 
 
+def test_column_maximum_skips_signaling_nans_in_any_position():
+    # Eq. 10's column maximum over entries, NaN skipped: every position of a
+    # quiet or signaling NaN next to a large finite maximum, in columns of the
+    # head length, against the maximum written out in Python
+    rng = np.random.default_rng(31)
+    snan = np.array([0x7F9D2828], np.uint32).view(F32)[0]
+    for nan in (snan, F32(np.nan)):
+        for pos in range(0, 128, 3):
+            col = (rng.standard_normal(128) * 10.0 ** rng.integers(-30, 30, 128)).astype(F32)
+            col[(pos + 1) % 128] = F32(3.3e38)
+            col[pos] = nan
+            X = np.stack([col, col[::-1]], axis=1)
+            q, s = oracle.quantize_columns(X)
+            want = max(abs(float(v)) for v in col if v == v)
+            assert s[0] == F32(F32(want) / F32(127.0)) and s[1] == s[0], (pos, s, want)
+            assert q[pos, 0] == 0 and q[(pos + 1) % 128, 0] == 127
+
+
 def _mixed_plan():
     rng = np.random.default_rng(9)
     lays = [_layer(GDN, 5, 8, 12, rng.uniform(-1, 2, 5), rng.normal(0, 1, 5), 32),
