@@ -86,6 +86,7 @@ INT8_PINS = [T_int8.test_pages_8p11_capacity_and_3p88_quantization_only,
              T_int8.test_scales_are_per_key_column_over_values,
              T_int8.test_range_and_error_bound_on_random_columns,
              T_int8.test_non_finite_entries_quantize_to_zero,
+             T_int8.test_column_maximum_skips_signaling_nans_in_any_position,
              T_int8.test_pack_unpack_int8_round_trip]
 
 BAL_PINS = [T_bal.test_hand_worked_even_split, T_bal.test_hand_worked_remainder_and_tie_order,
@@ -132,10 +133,13 @@ MUTATIONS = [
     ("balance", "if d2 < d_i or (d2 == d_i and i2 < i):", "if d2 > d_i or (d2 == d_i and i2 < i):", BAL_PINS),
     ("balance", "D = np.asarray(lay.dt_bias, np.float32).reshape(lay.n_heads, per)[r * Hr:(r + 1) * Hr]", "D = np.asarray(lay.dt_bias, np.float32).reshape(lay.n_heads, per)[r:r + Hr]", BAL_PINS),
     ("balance", "A = np.asarray(lay.A_log, np.float32).reshape(lay.n_heads, per)[r * Hr:(r + 1) * Hr]", "A = np.asarray(lay.A_log, np.float32).reshape(per, lay.n_heads).T[r * Hr:(r + 1) * Hr]", BAL_PINS),
-    ("int8", "s = np.fmax(a, SCALE_FLOOR) / QMAX", "s = np.fmax(a, SCALE_FLOOR) / F32(128.0)", INT8_PINS),
-    ("int8", "s = np.fmax(a, SCALE_FLOOR) / QMAX", "s = a / QMAX", INT8_PINS),
+    ("int8", "s = np.maximum(a, SCALE_FLOOR) / QMAX", "s = np.maximum(a, SCALE_FLOOR) / F32(128.0)", INT8_PINS),
+    ("int8", "s = np.maximum(a, SCALE_FLOOR) / QMAX", "s = a / QMAX", INT8_PINS),
     ("int8", "r = np.rint(X / s[None, :])", "r = np.floor(X / s[None, :] + F32(0.5))", INT8_PINS),
-    ("int8", "a = np.fmax.reduce(np.abs(X), axis=0)", "a = np.full(X.shape[1], np.abs(X).max(), F32)", INT8_PINS),
+    ("int8", "a = np.where(np.isnan(mag), F32(0), mag).max(axis=0)",
+     "a = np.full(X.shape[1], np.where(np.isnan(mag), F32(0), mag).max(), F32)", INT8_PINS),
+    ("int8", "a = np.where(np.isnan(mag), F32(0), mag).max(axis=0)", "a = np.fmax.reduce(mag, axis=0)",
+     INT8_PINS),
     ("int8", "per_unit_s = lay.d_k if lay.kind == GDN else 1", "per_unit_s = 1", INT8_PINS),
     ("int8", "per_unit_q = lay.d_v * lay.d_k if lay.kind == GDN else lay.d_v", "per_unit_q = lay.d_v * lay.d_k", INT8_PINS),
     ("int8", "self.scale_base = align16(q)", "self.scale_base = q", INT8_PINS),
