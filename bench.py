@@ -43,7 +43,8 @@ KERNEL_SOURCES = ["recurrent_state_cache_amd/csrc/dasc_kernels.hip",
 # rounds of the rocprofv3 kernel-statistics run (--warmup, --steps)
 PROFILE_WARMUP, PROFILE_STEPS = 3, 10
 
-KERNEL_ROLES = {r"qmove_kernel<true>": "pack_int8", r"qmove_kernel<false>": "unpack_int8",
+KERNEL_ROLES = {r"qmove_kernel<true(, (true|false))?>": "pack_int8",
+                r"qmove_kernel<false(, false)?>": "unpack_int8",
                 r"(?<!q)move_kernel<true, \d+, \d+, false>": "pack",
                 r"(?<!q)move_kernel<false, \d+, \d+, false>": "unpack",
                 r"(?<!q)move_kernel<true, \d+, \d+, true>": "pack_tp",
@@ -685,7 +686,7 @@ def main():
             "c_ckpt_int8": round(info["c_ckpt_int8"], 4),
             "pack_unpack_gbs": round(n * (pack_qb + unpack_qb) / (t_pack_q.mean() + t_unpack_q.mean()) / 1e9, 2),
             "pack": {k: v for k, v in hbm("pack_int8", n * pack_qb, t_pack_q.mean()).items() if k != "kernel"}
-                    | {"kernel": "qmove_kernel<true>"},
+                    | {"kernel": "qmove_kernel<true, *> (column blocks when the list has no whole head)"},
             "unpack": {k: v for k, v in hbm("unpack_int8", n * unpack_qb, t_unpack_q.mean()).items() if k != "kernel"}
                       | {"kernel": "qmove_kernel<false>"},
         },

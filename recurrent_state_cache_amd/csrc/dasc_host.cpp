@@ -82,6 +82,7 @@ struct dasc_plan {
   std::vector<float> gate_expA, gate_dt;
   std::vector<Group> refresh_groups;
   int32_t kda_r_max = 0;  // most unit segments one KDA piece stages
+  bool int8_pack_blocks_only = false;  // the INT8 pack list has no whole-head piece
   bool kda_128 = true;    // every KDA layer has d_k = d_v = 128
   int64_t off_pack = 0, off_unpack = 0, off_pack_q = 0, off_unpack_q = 0, off_pack_tp = 0,
           off_unpack_tp = 0, off_unpack_rest = 0, off_refresh = 0, off_expA = 0, off_dt = 0,
@@ -304,13 +305,27 @@ void build_tables(dasc_plan* p) {
         t.type = kPieceQKda;
         t.pool_off = L.q_off + j * L.d_v;
         t.scale_off = p->int8_scale_base + L.s_off + j * 4;
-        p->pack_q.push_back(t);
         p->unpack_q.push_back(t);
+        if (L.d_k == 128 && L.d_v == 128) {
+          // pack: 32-channel column blocks with a retained channel (16 KiB
+          // each) instead of the whole head
+          Piece u = t;
+          u.type = kPieceQKdaBlock;
+          for (uint32_t cb = 0; cb < 4; ++cb) {
+            u.bytes = cb;
+            if (t.mask[cb] != 0) p->pack_q.push_back(u);
+          }
+        } else {
+          p->pack_q.push_back(t);
+        }
       }
       j += r;
     }
   }
   push_range(p->pack_q, I.temporal_dense_bytes, p->int8_conv_base, I.conv_bytes, kPieceCopy);
+  p->int8_pack_blocks_only = std::all_of(p->pack_q.begin(), p->pack_q.end(), [](const Piece& t) {
+    return t.type == kPieceCopy || t.type == kPieceQKdaBlock;
+  });
   push_range(p->unpack_q, I.temporal_dense_bytes, p->int8_conv_base, I.conv_bytes, kPieceCopy);
 
   // TP storage-balancing lists: the fp32 lists with the pool side remapped.
@@ -913,6 +928,7 @@ int run_move(const dasc_plan* p, bool pack, const void* src_base, int64_t src_st
   m.n_pieces = static_cast<uint32_t>(pieces.size());
   m.kda_r_max = p->kda_r_max;
   m.kda_128 = p->kda_128;
+  m.q_blocks = int8 && pack && p->int8_pack_blocks_only;
   m.src_idx = src_idx;
   m.dst_idx = dst_idx;
   m.src_base = static_cast<const uint8_t*>(src_base);

@@ -27,6 +27,10 @@ constexpr uint32_t kPieceQKda = 4;  // a KDA head with >= 1 retained channel
 // kKdaRows rb .. and channels 32 cb .. (cb in the piece's `bytes` field),
 // 4 KiB of the dense state, for a block with >= 1 retained channel
 constexpr uint32_t kPieceKdaBlock = 5;
+// INT8 pack of a d_k = d_v = 128 KDA head: the 32 channels from 32 cb on (cb
+// in the piece's `bytes` field), all rows (16 KiB), for a block with >= 1
+// retained channel; a column's scale spans the rows, so the block is whole
+constexpr uint32_t kPieceQKdaBlock = 6;
 
 // Largest byte range one copy / zero piece covers: 256 lanes x 16 B.  Small
 // pieces stream HBM markedly faster on MI355X than 64 KiB pieces do.
@@ -124,6 +128,7 @@ struct MoveArgs {
   uint32_t n_pieces;
   int32_t kda_r_max;  // most unit segments a KDA piece stages (sizes the LDS); 0 if none
   bool kda_128;       // every KDA piece has d_k = d_v = 128
+  bool q_blocks;      // INT8 pack list of copy pieces and KDA column blocks only
   const int32_t* src_idx;
   const int32_t* dst_idx;
   const uint8_t* src_base;

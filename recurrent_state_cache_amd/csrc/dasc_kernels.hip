@@ -480,6 +480,76 @@ __device__ __forceinline__ void qpack_kda_head(const Piece& t, const uint8_t* sr
   }
 }
 
+// INT8 pack of a 32-channel column block of a d = 128 KDA head (all 128
+// rows, 16 KiB): lane (v8, cg), v8 = tid / 8, cg = tid % 8, holds rows
+// 4 v8 .. 4 v8 + 3 of channels 32 cb + 4 cg .. + 3 (one 16-byte load per
+// row; 8 lanes cover a 128-byte row segment).  The column maxima are
+// combined over the 8 row lanes of a wave by lane exchanges and over the 4
+// waves in LDS; each retained column's 4 bytes of the lane's rows go to its
+// unit row in LDS, and the block's units leave as 16-byte pieces.  Segment
+// j of the block is unit (retained channels below 32 cb) + j of the head.
+__device__ __forceinline__ void qpack_kda_block(const Piece& t, const uint8_t* src, uint8_t* dst,
+                                                float (&red)[8][128], uint8_t* qbuf) {
+  constexpr int D = 128;
+  const int cb = static_cast<int>(t.bytes);
+  const int tid = threadIdx.x, v8 = tid >> 3, cg = tid & 7, wave = tid >> 6;
+  uint32_t bits4 = 0, below = 0;
+  lane_ranks(t, 8 * cb + cg, bits4, below);
+  const int base = (cb > 0 ? __popc(t.mask[0]) : 0) + (cb > 1 ? __popc(t.mask[1]) : 0) +
+                   (cb > 2 ? __popc(t.mask[2]) : 0);
+  const uint32_t mc = cb == 0 ? t.mask[0] : cb == 1 ? t.mask[1] : cb == 2 ? t.mask[2] : t.mask[3];
+  const int rc = __popc(mc);
+  const float* S = reinterpret_cast<const float*>(src + t.dense_off) + 32 * cb + 4 * cg;
+  f32x4 x[4];
+  f32x4 mx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = ld_stream(reinterpret_cast<const f32x4*>(S + (4 * v8 + i) * D));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float m = fabsf(x[i][c]);
+      mx[c] = m > mx[c] ? m : mx[c];  // NaN entries never win
+    }
+  }
+#pragma unroll
+  for (int sh = 8; sh < 64; sh <<= 1) {  // the wave's 8 row lanes of this cg
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float o = __shfl_xor(mx[c], sh);
+      mx[c] = o > mx[c] ? o : mx[c];
+    }
+  }
+  if ((tid & 63) < 8) *reinterpret_cast<f32x4*>(&red[wave][4 * cg]) = mx;
+  __syncthreads();
+  f32x4 sc, inv;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float m = 0.f;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) m = red[w][4 * cg + c] > m ? red[w][4 * cg + c] : m;
+    sc[c] = (m > kScaleFloor ? m : kScaleFloor) / 127.f;  // correctly rounded fp32 division
+    inv[c] = 1.f / sc[c];
+  }
+  const uint32_t w[4] = {quant4(x[0], sc, inv), quant4(x[1], sc, inv), quant4(x[2], sc, inv),
+                         quant4(x[3], sc, inv)};
+  uint32_t b[4];
+  transpose4(w, b);  // b[c]: column c, rows 4 v8 .. 4 v8 + 3
+  uint32_t rk = below - base;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if ((bits4 >> c) & 1u) {
+      *reinterpret_cast<uint32_t*>(&qbuf[rk * kQStride + 4 * v8]) = b[c];
+      if (v8 == 0) reinterpret_cast<float*>(dst + t.scale_off)[base + rk] = sc[c];
+      ++rk;
+    }
+  }
+  __syncthreads();
+  const int j = tid >> 3, g = tid & 7;  // unit j of the block, 16-byte piece g
+  if (j < rc)
+    st_stream(*reinterpret_cast<const u32x4*>(&qbuf[j * kQStride + 16 * g]),
+              reinterpret_cast<u32x4*>(dst + t.pool_off + (base + j) * D + 16 * g));
+}
+
 // Unpack of kQGdnRows rows of a GDN head: lane (vl, kg) writes columns
 // 4 kg .. 4 kg + 3 of row kQGdnRows rb + vl.
 __device__ __forceinline__ void qunpack_gdn_rows(const Piece& t, const uint8_t* src, uint8_t* dst) {
@@ -554,16 +624,22 @@ __device__ __forceinline__ void qunpack_kda_head(const Piece& t, const uint8_t* 
   }
 }
 
-template <bool kPack>
+// kBlocks (pack lists of copy pieces and KDA column blocks only): an
+// instantiation without the whole-head code, whose 64 VGPRs of rows would
+// otherwise hold every workgroup of the launch to four per CU.
+template <bool kPack, bool kBlocks = false>
 __global__ void __launch_bounds__(kThreads) qmove_kernel(MoveArgs a) {
+  static_assert(kPack || !kBlocks, "block lists are pack lists");
   __shared__ __attribute__((aligned(16))) float red[kPack ? 8 : 1][128];  // column maxima per row lane
-  __shared__ __attribute__((aligned(16))) uint8_t qbuf[128 * kQStride];   // KDA units, int8
+  __shared__ __attribute__((aligned(16))) uint8_t qbuf[(kBlocks ? 32 : 128) * kQStride];  // KDA units
   __shared__ float qs[kPack ? 1 : 128];                                   // KDA scales (unpack)
   const Piece t = a.pieces[blockIdx.x];
   const int64_t si = a.src_idx[blockIdx.y];
   const int64_t di = a.dst_idx[blockIdx.y];
   const bool bad_idx = !in_range(si, a.n_src) || !in_range(di, a.n_dst);
-  if (bad_idx | (t.type > kPieceQKda)) {
+  const bool valid = kBlocks ? (t.type == kPieceCopy || t.type == kPieceQKdaBlock)
+                             : (t.type <= kPieceQKda || (kPack && t.type == kPieceQKdaBlock));
+  if (bad_idx | !valid) {
     if (bad_idx && blockIdx.x == 0 && threadIdx.x == 0) flag(a.status, DASC_STATUS_BAD_INDEX);
     return;
   }
@@ -573,8 +649,12 @@ __global__ void __launch_bounds__(kThreads) qmove_kernel(MoveArgs a) {
     copy_piece<kPack>(t, src, dst);
     return;
   }
-  if constexpr (kPack) {
-    if (t.type == kPieceQKda)
+  if constexpr (kBlocks) {
+    qpack_kda_block(t, src, dst, red, qbuf);
+  } else if constexpr (kPack) {
+    if (t.type == kPieceQKdaBlock)
+      qpack_kda_block(t, src, dst, red, qbuf);
+    else if (t.type == kPieceQKda)
       qpack_kda_head(t, src, dst, red, qbuf);
     else
       qpack_gdn_head(t, src, dst, red);
@@ -1442,7 +1522,8 @@ int launch_qmove(bool pack, const MoveArgs& args, void* stream) {
   if (args.n_pieces > 0x7FFFFFFFu) return static_cast<int>(hipErrorInvalidValue);
   dim3 grid(args.n_pieces, static_cast<uint32_t>(args.n));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (pack) qmove_kernel<true><<<grid, kThreads, 0, s>>>(args);
+  if (pack && args.q_blocks) qmove_kernel<true, true><<<grid, kThreads, 0, s>>>(args);
+  else if (pack) qmove_kernel<true><<<grid, kThreads, 0, s>>>(args);
   else qmove_kernel<false><<<grid, kThreads, 0, s>>>(args);
   return static_cast<int>(hipGetLastError());
 }

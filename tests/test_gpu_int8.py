@@ -180,3 +180,19 @@ def test_int8_rejects_unsupported_widths():
     with pytest.raises(R.DascError) as e:
         R.ckpt_pack_int8(P, dense, idx, pool, idx)
     assert e.value.code == -5
+
+
+def test_int8_kda_column_blocks_full_empty_and_edges():
+    # d = 128 KDA heads pack as 32-channel column blocks (the INT8 pack list
+    # then holds only blocks and copies); full, empty, sparse and edge blocks
+    from test_gpu_ckpt import _block_pattern_layers
+    cfg = W.Config("blocks", _block_pattern_layers(), w_max=64)
+    P, O = _plans(cfg)
+    n = 3
+    dense = W.dense_states(cfg, n, device="cuda", seed=23)
+    _run(P, O, dense, n, list(range(n)), seed=23)
+    # raw random bits: NaN, infinite and denormal entries inside the blocks
+    g = torch.Generator(device="cuda")
+    g.manual_seed(29)
+    dense = torch.randint(0, 256, (n, O.dense_bytes), dtype=torch.uint8, device="cuda", generator=g)
+    _run(P, O, dense, n, list(range(n)), seed=29)
