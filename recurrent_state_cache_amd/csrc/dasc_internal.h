@@ -43,9 +43,10 @@ constexpr int kKdaRows = 32;
 constexpr int kKdaLdsRow = kKdaRows + 4;
 // Channels of one KDA block piece (d = 128 heads): 32 rows x 32 channels.
 constexpr int kKdaBlockCols = 32;
-// Rows of a GDN head one INT8 unpack piece writes: 8 rows of 128 fp32 are
-// 4 KiB, one 16-byte store per lane, like the copy pieces.
-constexpr int kQGdnRows = 8;
+// Rows of a GDN head one INT8 unpack piece writes: 32 rows of 128 fp32 are
+// 16 KiB, four 16-byte stores per lane (unpack pieces of 16 KiB streamed
+// HBM best in the fp32 movers).
+constexpr int kQGdnRows = 32;
 
 // One workgroup's work for one (checkpoint, slot) pair.  For a KDA piece the
 // head's r retained columns (r = popcount of mask) are the units

@@ -551,18 +551,29 @@ __device__ __forceinline__ void qpack_kda_block(const Piece& t, const uint8_t* s
 }
 
 // Unpack of kQGdnRows rows of a GDN head: lane (vl, kg) writes columns
-// 4 kg .. 4 kg + 3 of row kQGdnRows rb + vl.
+// 4 kg .. 4 kg + 3 of rows kQGdnRows rb + 8 i + vl (every store instruction
+// of the workgroup covers 8 consecutive rows); the int8 words are all loaded
+// before the first store.
 __device__ __forceinline__ void qunpack_gdn_rows(const Piece& t, const uint8_t* src, uint8_t* dst) {
+  constexpr int kPer = kQGdnRows / 8;  // rows per lane
   const int dk = t.d_k, dv = t.d_v, KG = dk / 4;
   const int tid = threadIdx.x, kg = tid % 32, vl = tid / 32;
-  const int v = kQGdnRows * t.rb + vl;
-  if (kg >= KG || vl >= kQGdnRows || v >= dv) return;
+  if (kg >= KG) return;
   float* S = reinterpret_cast<float*>(dst + t.dense_off);
   const uint8_t* Sc = src + t.scale_off;
   const f32x4 sc = {load_scale(Sc + 16 * kg), load_scale(Sc + 16 * kg + 4),
                     load_scale(Sc + 16 * kg + 8), load_scale(Sc + 16 * kg + 12)};
-  const uint32_t w = *reinterpret_cast<const uint32_t*>(src + t.pool_off + v * dk + 4 * kg);
-  st_stream(dequant4(w, sc), reinterpret_cast<f32x4*>(S + v * dk + 4 * kg));
+  uint32_t w[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int v = kQGdnRows * t.rb + 8 * i + vl;
+    w[i] = v < dv ? *reinterpret_cast<const uint32_t*>(src + t.pool_off + v * dk + 4 * kg) : 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int v = kQGdnRows * t.rb + 8 * i + vl;
+    if (v < dv) st_stream(dequant4(w[i], sc), reinterpret_cast<f32x4*>(S + v * dk + 4 * kg));
+  }
 }
 
 // Unpack of a KDA head, whole: units and scales into LDS, then every element.
