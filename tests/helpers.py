@@ -1,10 +1,12 @@
-"""Test-side helpers shared by the GPU parity tests (comparison only; no
-step of the method lives here)."""
+"""Test-side helpers shared by the tests (comparison and input layouts only;
+no step of the method lives here)."""
 from __future__ import annotations
 
 import sys
 
 import numpy as np
+
+import workloads as W
 
 
 def log(msg: str) -> None:
@@ -52,3 +54,20 @@ def refresh_error(gpu: np.ndarray, ref64: np.ndarray, local: np.ndarray) -> floa
     if not local.any():
         return 0.0
     return float(np.max(np.abs(gpu[local].astype(np.float64) - ref64[local]))) / nrm
+
+
+def block_pattern_layers():
+    """d = 128 KDA heads whose 32-channel blocks are full, empty, sparse or
+    retained at a single edge channel (A_log -4 is retained at W_max = 64,
+    A_log 1 is not: H_s = ln(eps) / g is about 680 and 4.6 tokens)."""
+    f = np.float32
+    keep = np.zeros((4, 128), bool)
+    keep[0, :32] = True
+    keep[0, 64:96:2] = True
+    keep[0, 127] = True
+    keep[1, [0, 96]] = True
+    keep[2, :] = True
+    keep[2, [31, 32]] = False
+    a = np.where(keep, -4.0, 1.0).reshape(-1).astype(f)
+    z = np.zeros(512, f)
+    return [W.Layer(W.KDA, 4, 128, 128, a, z, 64), W.Layer(W.KDA, 4, 128, 128, a[::-1].copy(), z, 0)]

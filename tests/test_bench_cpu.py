@@ -46,3 +46,41 @@ def test_windowed_work_and_bytes_recounted_from_the_oracle(name):
     assert bench._windowed_work(P, Wn) == (flops, ht)
     assert bench._windowed_bytes(P, Wn) == nbytes
     assert ht > 0
+
+
+def test_mover_bytes_recounted_from_the_oracle():
+    """pack reads every retained GDN head and, of a d = 128 KDA head, each
+    32-channel block with a retained channel (whole heads at other widths),
+    writes the ragged payload and copies conv; unpack reads the payload and
+    conv and writes the dense checkpoint; INT8 pack reads KDA heads whole."""
+    from helpers import block_pattern_layers
+    rng = np.random.default_rng(5)
+    f = np.float32
+    layers = block_pattern_layers() + [
+        W.Layer(W.KDA, 3, 32, 32, rng.normal(-1, 2, 96).astype(f), np.zeros(96, f), 32),
+        W.Layer(W.GDN, 5, 16, 16, rng.uniform(-3, 2, 5).astype(f), np.zeros(5, f), 16)]
+    cfg = W.Config("movers", layers, w_max=64)
+    P = R.Plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max)
+    O = oracle.build_plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max)
+    read = read_q = 0
+    for L in O.layers:
+        if L.kind == oracle.GDN:
+            read += int(L.retained.sum()) * L.d_v * L.d_k * 4
+            read_q += int(L.retained.sum()) * L.d_v * L.d_k * 4
+            continue
+        heads = L.retained.reshape(L.n_heads, L.d_k)
+        read_q += int(heads.any(axis=1).sum()) * L.d_v * L.d_k * 4
+        if L.d_k == 128 and L.d_v == 128:
+            for h in range(L.n_heads):
+                for b in range(4):
+                    read += 128 * 32 * 4 if heads[h, 32 * b:32 * (b + 1)].any() else 0
+        else:
+            read += int(heads.any(axis=1).sum()) * L.d_v * L.d_k * 4
+    assert read < read_q  # the pattern has empty blocks in heads that are read
+    q = sum(int(L.retained.sum()) * (L.d_v * L.d_k if L.kind == oracle.GDN else L.d_v) for L in O.layers)
+    q += sum(int(L.retained.sum()) * (L.d_k if L.kind == oracle.GDN else 1) * 4 for L in O.layers)
+    pack, unpack, pack_q, unpack_q = bench._algorithmic_bytes(P)
+    assert pack == read + O.B_temp_rag + 2 * O.B_conv
+    assert unpack == O.B_temp_rag + O.B_temp_dense + 2 * O.B_conv
+    assert pack_q == read_q + q + 2 * O.B_conv
+    assert unpack_q == q + O.B_temp_dense + 2 * O.B_conv

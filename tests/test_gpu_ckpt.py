@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import workloads as W
-from helpers import log, mask_words
+from helpers import block_pattern_layers, log, mask_words
 
 pytestmark = pytest.mark.gpu
 
@@ -167,25 +167,8 @@ def test_host_validation_on_device_buffers():
         R.ckpt_pack(P, dense, idx.long(), pool, idx)
 
 
-def _block_pattern_layers():
-    """d = 128 KDA heads whose 32-channel blocks are full, empty, sparse or
-    retained at a single edge channel (A_log -4 is retained at W_max = 64,
-    A_log 1 is not: H_s = ln(eps) / g is about 680 and 4.6 tokens)."""
-    f = np.float32
-    keep = np.zeros((4, 128), bool)
-    keep[0, :32] = True
-    keep[0, 64:96:2] = True
-    keep[0, 127] = True
-    keep[1, [0, 96]] = True
-    keep[2, :] = True
-    keep[2, [31, 32]] = False
-    a = np.where(keep, -4.0, 1.0).reshape(-1).astype(f)
-    z = np.zeros(512, f)
-    return [W.Layer(W.KDA, 4, 128, 128, a, z, 64), W.Layer(W.KDA, 4, 128, 128, a[::-1].copy(), z, 0)]
-
-
 def test_kda_column_blocks_full_empty_and_edges():
-    cfg = W.Config("blocks", _block_pattern_layers(), w_max=64)
+    cfg = W.Config("blocks", block_pattern_layers(), w_max=64)
     P, O = _plans(cfg)
     kept = O.layers[0].retained.reshape(4, 128)
     assert kept[0, :32].all() and not kept[0, 32:64].any() and kept[0, 127]

@@ -185,8 +185,8 @@ def test_int8_rejects_unsupported_widths():
 def test_int8_kda_column_blocks_full_empty_and_edges():
     # d = 128 KDA heads pack as 32-channel column blocks (the INT8 pack list
     # then holds only blocks and copies); full, empty, sparse and edge blocks
-    from test_gpu_ckpt import _block_pattern_layers
-    cfg = W.Config("blocks", _block_pattern_layers(), w_max=64)
+    from helpers import block_pattern_layers
+    cfg = W.Config("blocks", block_pattern_layers(), w_max=64)
     P, O = _plans(cfg)
     n = 3
     dense = W.dense_states(cfg, n, device="cuda", seed=23)
