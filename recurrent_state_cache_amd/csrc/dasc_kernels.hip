@@ -8,9 +8,10 @@
 // Pack and unpack are pure data movement: every workgroup takes one piece of
 // the plan's task lists for one (checkpoint, slot) pair and moves raw bits
 // with 16-byte accesses.  KDA units are strided columns of a row-major state,
-// so a KDA piece (32 rows of a head) goes through a 4x4-block register
-// transpose and LDS.  The refresh keeps one head's fp32 state resident in
-// MFMA accumulator registers and replays Eq. 1 in exact chunks of 16 tokens.
+// so a KDA piece (32 rows of a head; for the pack of d = 128 heads a 32 x 32
+// column block) goes through registers and LDS.  The refresh keeps one
+// head's fp32 state resident in MFMA accumulator registers and replays
+// Eq. 1 in exact chunks of 16 tokens.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -64,7 +65,10 @@ __device__ __forceinline__ void st_stream(T v, T* p) {
 // holds only the head's r retained columns, as 32-row segments U[j][..] in
 // pool order (j = rank of the channel among the retained ones, a popcount
 // of the piece's mask), written and read as 16-byte vectors; each segment
-// is one 128-byte line of its unit.
+// is one 128-byte line of its unit.  The pack of d = 128 heads uses 32 x 32
+// column blocks instead (kda_block_pack below): 4 KiB of reads per
+// workgroup, which streams HBM better; the unpack keeps the 32-row pieces,
+// whose 16 KiB of contiguous writes measured faster than 8 or 32 KiB.
 // ---------------------------------------------------------------------------
 
 // Retained bits of channels 4 kg .. 4 kg + 3 (low 4 bits) and the number of
@@ -266,22 +270,24 @@ __global__ void __launch_bounds__(kThreads) move_kernel(MoveArgs a) {
 // rounded division; unpack writes q s (fp32 product).  Maxima are taken with
 // `>` so that NaN entries are skipped; a NaN quotient stores 0.
 //
-// Pack pieces are whole heads (a column's scale spans all d_v rows): lane
-// (vl, kg), kg = tid % 32, vl = tid / 32, holds columns 4 kg .. 4 kg + 3 of
-// the 16 consecutive rows 16 vl .. 16 vl + 15 in registers; the column
-// maxima are combined over the 8 row lanes in LDS.  A GDN head writes its
-// int8 rows directly (32 lanes cover a row) and its d_k scales.  A KDA head
-// transposes each lane's 16 x 4 int8 block in registers, so that a retained
-// column's 16 bytes are one 16-byte LDS store into its unit; the units then
-// leave LDS as 16-byte pieces of contiguous pool bytes.  (Pieces of 32
-// channels x all rows, 16 KiB like the fp32 pieces, read 128-byte segments
-// at the row stride and streamed HBM far worse than whole heads.)  Unpack
-// pieces are GDN heads by blocks of 8 rows (lane: 4 columns of one row, a
-// 4 KiB piece like the copy pieces) and KDA heads whole: the units and scales come into LDS as 16-byte pieces,
-// each lane reads the 16 bytes of its rows for each of its retained columns
-// and writes its 16 rows x 4 columns (+0.0 in omitted columns).  LDS unit
-// rows are padded to 144 bytes so that lanes reading or writing different
-// units at the same row offset fall on different banks.
+// A column's scale spans all d_v rows, so a pack piece holds whole columns.
+// d = 128 KDA heads are packed as 32-channel column blocks of all rows
+// (qpack_kda_block below, 16 KiB per workgroup, in an instantiation of
+// their own when the list holds nothing else).  Other heads are whole
+// pieces: lane (vl, kg), kg = tid % 32, vl = tid / 32, holds columns
+// 4 kg .. 4 kg + 3 of the 16 consecutive rows 16 vl .. 16 vl + 15 in
+// registers; the column maxima are combined over the 8 row lanes in LDS.  A
+// GDN head writes its int8 rows directly (32 lanes cover a row) and its d_k
+// scales.  A KDA head transposes each lane's 16 x 4 int8 block in
+// registers, so that a retained column's 16 bytes are one 16-byte LDS store
+// into its unit; the units then leave LDS as 16-byte pieces of contiguous
+// pool bytes.  Unpack pieces are GDN heads by blocks of 32 rows (lane: 4
+// columns of 4 rows, 16 KiB of dense writes per workgroup) and KDA heads
+// whole: the units and scales come into LDS as 16-byte pieces, each lane
+// reads the 16 bytes of its rows for each of its retained columns and
+// writes its 16 rows x 4 columns (+0.0 in omitted columns).  LDS unit rows
+// are padded to 144 bytes so that lanes reading or writing different units
+// at the same row offset fall on different banks.
 // ---------------------------------------------------------------------------
 constexpr float kScaleFloor = 1e-8f;
 constexpr int kQRows = 16;     // consecutive rows a lane holds (d_v <= 128, 8 row lanes)
