@@ -838,12 +838,6 @@ __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, true));
 }
 
-// Rows 1 and 3 of each wave get lane 15 of rows 0 and 2 (DPP row_bcast:15);
-// rows 0 and 2 get 0.
-__device__ __forceinline__ float row_bcast15_upper(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xA, 0xF, false));
-}
-
 // Sum over the G consecutive lanes of a 16-lane row (G in {1, 2, 4, 8, 16});
 // every lane of the group gets the sum.
 template <int G>
@@ -853,6 +847,20 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (G >= 8) x += dpp<0x141>(x);  // row_half_mirror
   if constexpr (G >= 16) x += dpp<0x140>(x); // row_mirror
   return x;
+}
+
+// One step of a reduce-scatter over the 16 lanes of a row: the lane and its
+// DPP partner (kCtrl) hold the same 2N entries in v[0 .. 2N); the lane keeps
+// the half its `upper` flag names, sends the other half, and adds what the
+// partner sends, so that v[0 .. N) holds its half summed over both lanes.
+template <int N, int kCtrl>
+__device__ __forceinline__ void reduce_scatter_step(float (&v)[16], bool upper) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float keep = upper ? v[i + N] : v[i];
+    const float send = upper ? v[i] : v[i + N];
+    v[i] = keep + dpp<kCtrl>(send);
+  }
 }
 
 __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
@@ -990,10 +998,10 @@ refresh_kernel(RefreshArgs a) {
     static_assert(PW < 0 || (NB4 == 32 && kAllStage), "wave-uniform rows need d = 128");
     if (kAllStage || tid < 2 * D) {
       // L, rows p and 15 - p (15 entries in all), 4 channels per lane,
-      // summed over the NB4 lanes of the row pair: within a 16-lane row by
-      // DPP, and for NB4 = 32 across the row pair by a row broadcast, which
-      // leaves the full sum in the upper row.  The last lane of the group
-      // stores the entries after the loop, so the loop has no branch.
+      // summed over the NB4 lanes of the row pair after the loop (so the
+      // loop has no branch): for NB4 = 32 by a reduce-scatter that leaves
+      // one entry per lane, otherwise by DPP sums within a row whose last
+      // lane stores every entry.
       const bool h = PW >= 0 && (tid & 32) != 0;  // upper half-wave
       const int p = PW >= 0 ? 2 * PW + (h ? 1 : 0) : tid / NB4, c4 = 4 * (tid % NB4);
       // entry i is in row p (i < p), and row 15 - p starts at i = p
@@ -1034,15 +1042,32 @@ refresh_kernel(RefreshArgs a) {
           pk[e] *= al[e];
           part = fmaf(pk[e], ks[e], part);
         }
-        part = group_sum<(NB4 < 16 ? NB4 : 16)>(part);
-        if constexpr (NB4 == 32) part += row_bcast15_upper(part);
+        if constexpr (NB4 != 32) part = group_sum<(NB4 < 16 ? NB4 : 16)>(part);
         lv[i] = part;
       }
-      if (tid % NB4 == NB4 - 1) {
-        // L[p][p - 1 - i] and L[15 - p][14 - i], stored transposed: two
-        // bases, constant steps
-        float* const lP = &sh.LT[0][0] + (p - 1) * (kC + 4) + p;
-        float* const lQ = &sh.LT[0][0] + (kC - 2) * (kC + 4) + (kC - 1 - p);
+      // L[p][p - 1 - i] and L[15 - p][14 - i], stored transposed: two
+      // bases, constant steps
+      float* const lP = &sh.LT[0][0] + (p - 1) * (kC + 4) + p;
+      float* const lQ = &sh.LT[0][0] + (kC - 2) * (kC + 4) + (kC - 1 - p);
+      if constexpr (NB4 == 32) {
+        // The 15 entries' partial sums (4 channels each) are summed over the
+        // row pair's 32 lanes by a reduce-scatter: four DPP exchanges within
+        // each 16-lane row leave lane r16 with entry r16's row sum, and one
+        // lane exchange across the two rows completes it; lanes 0 .. 14 of
+        // the lower row then store one entry each.
+        const int r16 = lane & 15;
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < kC - 1; ++i) v[i] = lv[i];
+        v[15] = 0.f;
+        reduce_scatter_step<8, 0x140>(v, (r16 & 8) != 0);  // row_mirror: l <-> 15 - l
+        reduce_scatter_step<4, 0x141>(v, (r16 & 4) != 0);  // row_half_mirror
+        reduce_scatter_step<2, 0x4E>(v, (r16 & 2) != 0);   // quad_perm [2,3,0,1]
+        reduce_scatter_step<1, 0xB1>(v, (r16 & 1) != 0);   // quad_perm [1,0,3,2]
+        const float sum = v[0] + __shfl_xor(v[0], 16);
+        if ((lane & 16) == 0 && r16 < kC - 1)
+          *((in_row_p(r16) ? lP : lQ) - r16 * (kC + 4)) = sum;
+      } else if (tid % NB4 == NB4 - 1) {
 #pragma unroll
         for (int i = 0; i < kC - 1; ++i) *((in_row_p(i) ? lP : lQ) - i * (kC + 4)) = lv[i];
       }
