@@ -700,7 +700,7 @@ def main():
             "frac_of_unpacked_peak": round(flops / t_rec / 1e12 / FP32_VALU_UNPACKED_TF, 4),
             "chunked_speedup": round(t_rec / t_ref.mean(), 3),
             "note": "same suffixes, output and tolerance as the chunked refresh; the vector "
-                    "units' fp32 rate without packed FMA (not emitted by this build) is half "
+                    "units' fp32 rate without packed FMA (the library is compiled without packed fp32 instructions) is half "
                     "the 157.3 TF/s datasheet figure",
         },
         "refresh_eq7_windows": {
