@@ -1,8 +1,10 @@
 """Oracle: bounded-suffix refresh, dasc-wr (test infrastructure only).
 
-[dasc] §4.2: on a compressed hit, dasc-wr replays a bounded suffix from a
-zero-initialised scratch recurrent state and copies only the refreshed local
-units into the active state; the stored checkpoint is unchanged.
+[dasc] §4.2 (load policies): the dasc-wr load rebuilds the omitted (local)
+units of a compressed hit by running the recurrence over the last few
+tokens, starting from an all-zero state of its own, and then overwrites
+only those local units in the restored state; the pool slot is not
+modified.
 
 The recurrence is [dasc] §3.1 Eq. 1, with S in R^{d_v x d_k}:
 
@@ -17,15 +19,20 @@ so S_t = A + beta_t (v_t - A k_t) k_t^T with A = S_{t-1} Diag(alpha_t).
 For GDN the decay is one scalar per head and token, Diag(alpha_t) =
 alpha_t I ([dasc] §3.1: GDN gates per head, KDA per channel).
 
-The decay of each token comes from the model's gate, [dasc] §3.3 Eq. 2 with
-the token's own logit a_t in place of the static a_s: alpha_t = exp(g_t),
-g_t = -exp(A_log) softplus(a_t + dt_bias).
+The decays alpha_t enter in one of two ways:
 
-Inputs (token-major rows over the concatenated tokens of all requests; the
-layer blocks follow one another in layer order, heads in order inside):
-k [T, sum_l H d_k] and v [T, sum_l H d_v] as raw bf16 bits, gate logits
-a [T, sum_l (H d_k for KDA, H for GDN)] as raw bf16 bits, beta [T, sum_l H]
-float32, token offsets [n+1].  Everything is upcast exactly to float64.
+* given directly, as Eq. 1 is written: fp32 alpha [T, sum_l (H d_k for
+  KDA, H for GDN)], upcast exactly to float64;
+* from the model's gate, [dasc] §3.3 Eq. 2 with the token's own logit a_t
+  in place of the static a_s: alpha_t = exp(g_t), g_t = -exp(A_log)
+  softplus(a_t + dt_bias), with a_t given as raw bf16 bits in a row of the
+  same width.
+
+Other inputs (token-major rows over the concatenated tokens of all
+requests; the layer blocks follow one another in layer order, heads in
+order inside): k [T, sum_l H d_k] and v [T, sum_l H d_v] as raw bf16 bits,
+beta [T, sum_l H] float32, token offsets [n+1].  Everything is upcast
+exactly to float64.
 """
 from __future__ import annotations
 
@@ -91,7 +98,7 @@ def _row_offsets(plan: OraclePlan):
 
 
 def refresh_expected(plan: OraclePlan, k_bits, v_bits, a_bits, beta, tok_off,
-                     requests=None, layers=None, heads=None, head_windows=False):
+                     requests=None, layers=None, heads=None, head_windows=False, alpha=None):
     """Scratch states of the bounded-suffix refresh, float64.
 
     For each request r (all, or the given subset), each layer (all, or the
@@ -102,11 +109,17 @@ def refresh_expected(plan: OraclePlan, k_bits, v_bits, a_bits, beta, tok_off,
     head's own Eq. 7 window ([dasc-sum] "Methodology" Eq. 7, taken per head
     rather than as one W_replay for the whole model).
 
+    alpha: None to take each token's decays from its gate logits a_bits
+    (Eq. 2), or fp32 decays [T, gate row] given directly (Eq. 1 as
+    written; a_bits is then not read and may be None).
+
     Returns {(r, layer, head): S [d_v, d_k] float64}.  Only the local units
     of each S are written into the active state by the refresh.
     """
     ko, vo, go, bo = _row_offsets(plan)
     beta = np.asarray(beta, dtype=np.float32)
+    if alpha is not None:
+        alpha = np.asarray(alpha, dtype=np.float32)
     tok_off = np.asarray(tok_off, dtype=np.int64)
     n = len(tok_off) - 1
     out = {}
@@ -125,19 +138,26 @@ def refresh_expected(plan: OraclePlan, k_bits, v_bits, a_bits, beta, tok_off,
                 starts = np.maximum(starts, t1 - w)
             for t0 in np.unique(starts):
                 out.update(_replay_heads(plan, li, hs_all[starts == t0], int(t0), t1, r,
-                                         k_bits, v_bits, a_bits, beta, ko, vo, go, bo))
+                                         k_bits, v_bits, a_bits, beta, ko, vo, go, bo, alpha))
     return out
 
 
-def _replay_heads(plan, li, hs, t0, t1, r, k_bits, v_bits, a_bits, beta, ko, vo, go, bo):
-    """Eq. 1 from S = 0 over tokens t0 .. t1-1 for heads hs of layer li."""
+def _replay_heads(plan, li, hs, t0, t1, r, k_bits, v_bits, a_bits, beta, ko, vo, go, bo,
+                  alpha=None):
+    """Eq. 1 from S = 0 over tokens t0 .. t1-1 for heads hs of layer li; the
+    decays are read from alpha when given, else made from a_bits by Eq. 2."""
     out = {}
     lay = plan.layers[li]
     H, dk, dv = lay.n_heads, lay.d_k, lay.d_v
     ks = bf16_bits_to_f64(k_bits[t0:t1, ko[li]:ko[li] + H * dk]).reshape(-1, H, dk)[:, hs]
     vs = bf16_bits_to_f64(v_bits[t0:t1, vo[li]:vo[li] + H * dv]).reshape(-1, H, dv)[:, hs]
     bs = beta[t0:t1, bo[li]:bo[li] + H].astype(np.float64)[:, hs]
-    if lay.kind == GDN:
+    if alpha is not None and lay.kind == GDN:
+        al = alpha[t0:t1, go[li]:go[li] + H].astype(np.float64)[:, hs]   # [W, nh]
+        al = np.repeat(al[:, :, None], dk, axis=2)                       # alpha_t I
+    elif alpha is not None:
+        al = alpha[t0:t1, go[li]:go[li] + H * dk].astype(np.float64).reshape(-1, H, dk)[:, hs]
+    elif lay.kind == GDN:
         a = bf16_bits_to_f64(a_bits[t0:t1, go[li]:go[li] + H])[:, hs]
         g = gate_log_decay(lay.A_log[hs], lay.dt_bias[hs], a)      # [W, nh]
         al = np.repeat(np.exp(g)[:, :, None], dk, axis=2)          # alpha_t I

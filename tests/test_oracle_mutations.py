@@ -78,7 +78,10 @@ REFRESH_PINS = [T_ref.test_rank1_matches_printed_matrix_form, T_ref.test_beta_on
                 T_ref.test_contraction_bound, lambda: T_ref.test_refresh_expected_wiring_gate_and_rows(8, 8),
                 lambda: T_ref.test_refresh_expected_wiring_gate_and_rows(8, 4),
                 T_ref.test_refresh_expected_respects_windows, T_ref.test_gdn_scalar_decay_equals_broadcast,
-                T_ref.test_head_windows_replay_each_heads_last_tokens]
+                T_ref.test_head_windows_replay_each_heads_last_tokens,
+                lambda: T_ref.test_refresh_expected_alpha_rows(8, 8),
+                lambda: T_ref.test_refresh_expected_alpha_rows(4, 12),
+                T_ref.test_refresh_expected_alpha_matches_gate_when_alpha_is_the_gate]
 
 INT8_PINS = [T_int8.test_pages_8p11_capacity_and_3p88_quantization_only,
              T_int8.test_scale_is_column_max_over_127_and_rounding_is_half_even,
@@ -121,6 +124,11 @@ MUTATIONS = [
     ("refresh", "g += lay.n_heads * lay.d_k if lay.kind != GDN else lay.n_heads", "g += lay.n_heads * lay.d_k", REFRESH_PINS),
     ("refresh", "vs = bf16_bits_to_f64(v_bits[t0:t1, vo[li]", "vs = bf16_bits_to_f64(v_bits[t0:t1, ko[li]", REFRESH_PINS),
     ("refresh", "starts = np.maximum(starts, t1 - w)", "starts = np.maximum(starts, t1 - w + 1)", REFRESH_PINS),
+    # decays given directly
+    ("refresh", "al = alpha[t0:t1, go[li]:go[li] + H].astype(np.float64)[:, hs]", "al = alpha[t0:t1, go[li]:go[li] + H * dk:dk].astype(np.float64)[:, hs]", REFRESH_PINS),
+    ("refresh", "al = alpha[t0:t1, go[li]:go[li] + H * dk].astype(np.float64).reshape(-1, H, dk)[:, hs]", "al = alpha[t0:t1, go[li]:go[li] + H * dk].astype(np.float64).reshape(-1, dk, H).transpose(0, 2, 1)[:, hs]", REFRESH_PINS),
+    ("refresh", "al = alpha[t0:t1, go[li]:go[li] + H * dk].astype(np.float64).reshape(-1, H, dk)[:, hs]", "al = alpha[t0:t1, ko[li]:ko[li] + H * dk].astype(np.float64).reshape(-1, H, dk)[:, hs]", REFRESH_PINS),
+    ("refresh", "al = np.repeat(al[:, :, None], dk, axis=2)                       # alpha_t I", "al = np.repeat(al[:, :1, None], len(hs), axis=1).repeat(dk, axis=2)", REFRESH_PINS),
     ("plan", "return int(lay.W_u[sel].max()) if sel.any() else 0", "return int(lay.W_u[sel].min()) if sel.any() else 0", PLAN_PINS),
     ("plan", "sel = (lay.local_idx // lay.d_k) == h", "sel = (lay.local_idx % lay.d_k) == h", PLAN_PINS),
     # INT8 (Eq. 10)

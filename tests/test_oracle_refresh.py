@@ -239,3 +239,66 @@ def test_head_windows_replay_each_heads_last_tokens():
             assert not np.array_equal(S, full[(r, li, h)])
         if lens[r] == 0:
             assert not np.any(S)
+
+
+@pytest.mark.parametrize("dk,dv", [(8, 8), (8, 4), (4, 12)])
+def test_refresh_expected_alpha_rows(dk, dv):
+    # Decays given directly (Eq. 1 as written), one per head for GDN and one
+    # per channel for KDA, read from their own columns of the alpha row: a
+    # one-hot write phase (beta = 1, k = e_j at token j) then beta = 0, so
+    # column j of every head's state is v_j times the product of the decays
+    # that column sees after token j.  Every head and channel gets its own
+    # decay sequence, so a wrong row offset, a GDN decay read per channel or
+    # a KDA decay taken per head would change the result.
+    gdn = Layer(GDN, 2, dk, dv, np.zeros(2, np.float32), np.full(2, 0.25, np.float32))
+    A = np.zeros(2 * dk, np.float32)
+    A[:3] = -9.0                               # KDA head 0: channels 0..2 retained
+    kda = Layer(KDA, 2, dk, dv, A, np.full(2 * dk, 0.25, np.float32))
+    plan = oracle.build_plan([gdn, kda], a_s=-0.3, w_max=64)
+    W = 2 * dk + 3
+    rng = np.random.default_rng(31)
+    kw, vw, gw, bw = 4 * dk, 4 * dv, 2 + 2 * dk, 4
+    k = np.zeros((W, kw), np.float32)
+    v = rng.integers(-8, 8, (W, vw)).astype(np.float32)
+    alpha = rng.uniform(0.5, 1.0, (W, gw)).astype(np.float32)
+    beta = np.zeros((W, bw), np.float32)
+    for t in range(dk):
+        for h in range(4):
+            k[t, h * dk + t] = 1.0
+        beta[t, :] = 1.0
+    out = oracle.refresh_expected(plan, _bf16_bits(k), _bf16_bits(v), None, beta,
+                                  np.array([0, W]), alpha=alpha)
+    for li in (0, 1):
+        for h in (0, 1):
+            S = out[(0, li, h)]
+            c0 = (2 * li + h) * dv
+            vv = v[:, c0:c0 + dv].astype(np.float64)
+            for j in range(dk):
+                col = h if li == 0 else 2 + h * dk + j       # the unit's alpha column
+                f = np.prod(alpha[j + 1:, col].astype(np.float64))
+                np.testing.assert_allclose(S[:, j], vv[j] * f, rtol=1e-12)
+
+
+def test_refresh_expected_alpha_matches_gate_when_alpha_is_the_gate():
+    # The two ways of giving the decays agree when the alpha row holds the
+    # gate's decays exactly: a_t = -1/4, dt_bias = 1/4, A_log = 0 makes every
+    # decay exactly 1/2 by Eq. 2, and an alpha row of 1/2 gives the same
+    # states bit for bit.
+    d = 8
+    kda = Layer(KDA, 2, d, d, np.zeros(2 * d, np.float32), np.full(2 * d, 0.25, np.float32))
+    gdn = Layer(GDN, 2, d, d, np.zeros(2, np.float32), np.full(2, 0.25, np.float32))
+    plan = oracle.build_plan([kda, gdn], a_s=-0.3, w_max=64)
+    rng = np.random.default_rng(32)
+    T = 13
+    trunc = lambda x: (x.astype(np.float32).view(np.uint32) & 0xFFFF0000).view(np.float32)
+    k = _bf16_bits(trunc(rng.normal(0, 0.4, (T, 4 * d))))
+    v = _bf16_bits(trunc(rng.normal(0, 1, (T, 4 * d))))
+    a = _bf16_bits(np.full((T, 2 * d + 2), -0.25, np.float32))
+    beta = rng.uniform(0, 1, (T, 4)).astype(np.float32)
+    tok = np.array([0, 5, T])
+    via_gate = oracle.refresh_expected(plan, k, v, a, beta, tok)
+    direct = oracle.refresh_expected(plan, k, v, None, beta, tok,
+                                     alpha=np.full((T, 2 * d + 2), 0.5, np.float32))
+    assert via_gate.keys() == direct.keys()
+    for key in via_gate:
+        np.testing.assert_array_equal(via_gate[key], direct[key])
