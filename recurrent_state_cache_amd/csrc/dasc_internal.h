@@ -36,6 +36,17 @@ constexpr uint32_t kPieceQKdaBlock = 6;
 // pieces stream HBM markedly faster on MI355X than 64 KiB pieces do.
 constexpr uint32_t kCopyChunk = 4096;
 
+// Pairs one mover launch covers: a call over n (checkpoint, slot) pairs is
+// issued as launches of at most this many pairs.  Within one launch the
+// rate per checkpoint falls as the launch grows (mixed 27-layer model,
+// unpack: 5.76 TB/s as eight back-to-back launches of 64 pairs against 5.55
+// TB/s as one launch of 512, the same bytes and the same span of time, so
+// not a clock or power effect; 5.94-5.96 TB/s at 8-16 pairs); 16 is the
+// measured best for the fp32 movers and the INT8 unpack, while the INT8
+// pack, whose whole-head pieces are few and large, prefers 64.
+constexpr int kMovePairs = 16;
+constexpr int kQPackPairs = 64;
+
 // Rows of a KDA head one piece moves: 32 rows make every unit segment a
 // whole 128-byte line (32 fp32).
 constexpr int kKdaRows = 32;

@@ -1530,15 +1530,12 @@ bool kda_shape_supported(int d_k, int d_v) {
   return d_k >= 4 && d_v >= 4 && d_k <= 128 && d_v <= 128 && d_k % 4 == 0 && d_v % 4 == 0;
 }
 
-int launch_move(bool pack, const MoveArgs& args, void* stream) {
-  if (args.n == 0 || args.n_pieces == 0) return hipSuccess;
-  if (args.n_pieces > 0x7FFFFFFFu || args.kda_r_max < 0 || args.kda_r_max > 128)
-    return static_cast<int>(hipErrorInvalidValue);
-  const size_t lds = static_cast<size_t>(args.kda_r_max) * kKdaLdsRow * sizeof(float);  // <= 18 KiB
+namespace {
+
+// One launch of a mover over the pairs of `args`.
+void launch_move_part(bool pack, const MoveArgs& args, hipStream_t s, size_t lds) {
   dim3 grid(args.n_pieces, static_cast<uint32_t>(args.n));
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const bool alt = args.tp;
-  if (args.alt_base && !args.alt_idx) return static_cast<int>(hipErrorInvalidValue);
   if (pack) {
     if (alt) {
       if (args.kda_128) move_kernel<true, 128, 128, true><<<grid, kThreads, lds, s>>>(args);
@@ -1556,18 +1553,51 @@ int launch_move(bool pack, const MoveArgs& args, void* stream) {
       else move_kernel<false, 0, 0, false><<<grid, kThreads, lds, s>>>(args);
     }
   }
-  return static_cast<int>(hipGetLastError());
+}
+
+void launch_qmove_part(bool pack, const MoveArgs& args, hipStream_t s) {
+  dim3 grid(args.n_pieces, static_cast<uint32_t>(args.n));
+  if (pack && args.q_blocks) qmove_kernel<true, true><<<grid, kThreads, 0, s>>>(args);
+  else if (pack) qmove_kernel<true><<<grid, kThreads, 0, s>>>(args);
+  else qmove_kernel<false><<<grid, kThreads, 0, s>>>(args);
+}
+
+// The pairs of a call, `per` at a time: the index arrays advance, every
+// other argument stays.
+template <typename F>
+int by_pairs(const MoveArgs& args, int per, F&& launch) {
+  MoveArgs part = args;
+  for (int32_t i = 0; i < args.n; i += per) {
+    part.n = args.n - i < per ? args.n - i : per;
+    part.src_idx = args.src_idx + i;
+    part.dst_idx = args.dst_idx + i;
+    if (args.alt_idx) part.alt_idx = args.alt_idx + i;
+    launch(part);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return static_cast<int>(e);
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+int launch_move(bool pack, const MoveArgs& args, void* stream) {
+  if (args.n == 0 || args.n_pieces == 0) return hipSuccess;
+  if (args.n < 0 || args.n_pieces > 0x7FFFFFFFu || args.kda_r_max < 0 || args.kda_r_max > 128)
+    return static_cast<int>(hipErrorInvalidValue);
+  if (args.alt_base && !args.alt_idx) return static_cast<int>(hipErrorInvalidValue);
+  const size_t lds = static_cast<size_t>(args.kda_r_max) * kKdaLdsRow * sizeof(float);  // <= 18 KiB
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return by_pairs(args, kMovePairs,
+                  [&](const MoveArgs& part) { launch_move_part(pack, part, s, lds); });
 }
 
 int launch_qmove(bool pack, const MoveArgs& args, void* stream) {
   if (args.n == 0 || args.n_pieces == 0) return hipSuccess;
-  if (args.n_pieces > 0x7FFFFFFFu) return static_cast<int>(hipErrorInvalidValue);
-  dim3 grid(args.n_pieces, static_cast<uint32_t>(args.n));
+  if (args.n < 0 || args.n_pieces > 0x7FFFFFFFu) return static_cast<int>(hipErrorInvalidValue);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (pack && args.q_blocks) qmove_kernel<true, true><<<grid, kThreads, 0, s>>>(args);
-  else if (pack) qmove_kernel<true><<<grid, kThreads, 0, s>>>(args);
-  else qmove_kernel<false><<<grid, kThreads, 0, s>>>(args);
-  return static_cast<int>(hipGetLastError());
+  return by_pairs(args, pack ? kQPackPairs : kMovePairs,
+                  [&](const MoveArgs& part) { launch_qmove_part(pack, part, s); });
 }
 
 bool refresh_shape_supported(int d_k, int d_v) {
