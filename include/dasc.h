@@ -294,6 +294,48 @@ int dasc_ckpt_refresh_suffix(dasc_plan_t plan, const uint16_t* k, const uint16_t
                              const int32_t* dst_idx, int32_t n, void* stream);
 
 /*
+ * Bounded-suffix refresh, dasc-wr ([dasc] §4.2), with the decays given
+ * directly, as Eq. 1 is written ([dasc] §3.1: alpha_t in (0, 1)^{d_k} for
+ * KDA, one scalar alpha_t per head for GDN): for each request r in [0, n),
+ * each layer l and each head h the plan replays, start from a zero fp32
+ * scratch state S [d_v, d_k] and apply, for every token t of the request,
+ *   S <- S Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ * then write only the local units of S into dense[dst_idx[r]] (retained
+ * units, the conv bytes and the pool are left untouched).  The same call
+ * as dasc_ckpt_refresh_suffix except for where the decays come from: the
+ * caller's decays, whatever produced them, instead of the plan's gate
+ * parameters applied to logits.
+ *   alpha [T, sum_l (H_l d_k for KDA, H_l for GDN)] fp32, token-major, the
+ *         same row layout as the gate logits of dasc_ckpt_refresh_suffix
+ *         (dasc_layer_info.gate_row_offset): KDA head h's decays of token t
+ *         at alpha[t][off_l + h d_k + k], a GDN head's at alpha[t][off_l + h].
+ *         16-byte aligned.  Values are applied as given (fp32).
+ * k, v, beta, tok_offsets, dst_idx, the alignment rules, the arithmetic
+ * (fp32 state, bf16 inputs widened exactly) and the errors are those of
+ * dasc_ckpt_refresh_suffix.
+ */
+int dasc_ckpt_refresh_suffix_alpha(dasc_plan_t plan, const uint16_t* k, const uint16_t* v,
+                                   const float* alpha, const float* beta,
+                                   const int64_t* tok_offsets, int64_t n_tokens,
+                                   void* dense_base, int64_t dense_stride, int64_t n_dense,
+                                   const int32_t* dst_idx, int32_t n, void* stream);
+
+/*
+ * dasc_ckpt_refresh_suffix_alpha with per-head Eq. 7 windows ([dasc-sum]
+ * "Methodology" Eq. 7, [dasc] §4.2): head (l, h) of request r replays only
+ * the last min(W_lh, n_r) of the request's n_r tokens, W_lh being the
+ * largest Eq. 7 window over the head's local units, as in
+ * dasc_ckpt_refresh_suffix_windowed.  Same arguments, rules and errors as
+ * dasc_ckpt_refresh_suffix_alpha.
+ */
+int dasc_ckpt_refresh_suffix_alpha_windowed(dasc_plan_t plan, const uint16_t* k,
+                                            const uint16_t* v, const float* alpha,
+                                            const float* beta, const int64_t* tok_offsets,
+                                            int64_t n_tokens, void* dense_base,
+                                            int64_t dense_stride, int64_t n_dense,
+                                            const int32_t* dst_idx, int32_t n, void* stream);
+
+/*
  * The same operation as dasc_ckpt_refresh_suffix ([dasc] §3.1 Eq. 1,
  * §4.2), computed in the recurrence's own form: token by token on the
  * vector units (u = S (alpha o k), c = beta (v - u), S <- S Diag(alpha)

@@ -22,6 +22,7 @@ import torch  # noqa: F401
 
 __all__ = ["Plan", "DascError", "ckpt_pack", "ckpt_unpack_zero_fill",
            "ckpt_refresh_suffix", "ckpt_refresh_suffix_windowed",
+           "ckpt_refresh_suffix_alpha", "ckpt_refresh_suffix_alpha_windowed",
            "ckpt_refresh_suffix_recurrent", "ckpt_pack_int8",
            "ckpt_unpack_int8_zero_fill", "ckpt_pack_tp", "ckpt_unpack_tp_zero_fill",
            "ckpt_unpack_refresh",
@@ -110,6 +111,11 @@ def _load():
                                                        _c_p, _c_i64, _c_i64, _c_p, _c_i32, _c_p]),
         "dasc_ckpt_refresh_suffix_recurrent": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
                                                         _c_p, _c_i64, _c_i64, _c_p, _c_i32, _c_p]),
+        "dasc_ckpt_refresh_suffix_alpha": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i64,
+                                                    _c_p, _c_i64, _c_i64, _c_p, _c_i32, _c_p]),
+        "dasc_ckpt_refresh_suffix_alpha_windowed": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                                             _c_i64, _c_p, _c_i64, _c_i64, _c_p,
+                                                             _c_i32, _c_p]),
         "dasc_ckpt_unpack_refresh": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p,
                                               _c_p, _c_p, _c_i64, _c_p, _c_i64, _c_i64, _c_p,
                                               _c_i32, _c_i32, _c_p]),
@@ -380,22 +386,42 @@ def ckpt_unpack_tp_zero_fill(plan: Plan, pool, src_slot, recv, recv_idx, dense, 
            "ckpt_unpack_tp_zero_fill")
 
 
-def _refresh(fn, name, plan, k, v, a, beta, tok_off, dense, dst_idx, stream):
+def _refresh(fn, name, plan, k, v, a, beta, tok_off, dense, dst_idx, stream, alpha=False):
+    """Marshal a refresh call; `a` holds bf16 gate logits, or fp32 decays
+    when alpha is True (same row width)."""
     import torch
     n = dst_idx.numel()
     if tok_off.numel() != n + 1:
         raise ValueError("tok_off must have n+1 entries")
     T = k.shape[0]
     info = plan.info()
+    an = "alpha" if alpha else "a"
     for nm, t, w in (("k", k, info["k_row"]), ("v", v, info["v_row"]),
-                     ("a", a, info["gate_row"]), ("beta", beta, info["beta_row"])):
+                     (an, a, info["gate_row"]), ("beta", beta, info["beta_row"])):
         if t.dim() != 2 or t.shape[0] != T or t.shape[1] != w:
             raise ValueError(f"{nm} must be [{T}, {w}], got {tuple(t.shape)}")
     dp, ds, dn = _rows(dense, "dense")
     _check(fn(plan._h, _dev_ptr(k, "k", torch.bfloat16), _dev_ptr(v, "v", torch.bfloat16),
-              _dev_ptr(a, "a", torch.bfloat16), _dev_ptr(beta, "beta", torch.float32),
+              _dev_ptr(a, an, torch.float32 if alpha else torch.bfloat16),
+              _dev_ptr(beta, "beta", torch.float32),
               _dev_ptr(tok_off, "tok_off", torch.int64), T, dp, ds, dn,
               _dev_ptr(dst_idx, "dst_idx", torch.int32), n, _stream_handle(stream)), name)
+
+
+def ckpt_refresh_suffix_alpha(plan: Plan, k, v, alpha, beta, tok_off, dense, dst_idx,
+                              stream=None) -> None:
+    """Bounded-suffix refresh with the decays given directly (Eq. 1 as
+    written): alpha is fp32 [T, gate row] (one per channel for KDA layers,
+    one per head for GDN layers); other arguments as ckpt_refresh_suffix."""
+    _refresh(lib.dasc_ckpt_refresh_suffix_alpha, "ckpt_refresh_suffix_alpha", plan, k, v,
+             alpha, beta, tok_off, dense, dst_idx, stream, alpha=True)
+
+
+def ckpt_refresh_suffix_alpha_windowed(plan: Plan, k, v, alpha, beta, tok_off, dense, dst_idx,
+                                       stream=None) -> None:
+    """ckpt_refresh_suffix_alpha with per-head Eq. 7 windows."""
+    _refresh(lib.dasc_ckpt_refresh_suffix_alpha_windowed, "ckpt_refresh_suffix_alpha_windowed",
+             plan, k, v, alpha, beta, tok_off, dense, dst_idx, stream, alpha=True)
 
 
 def ckpt_refresh_suffix(plan: Plan, k, v, a, beta, tok_off, dense, dst_idx, stream=None) -> None:

@@ -384,7 +384,7 @@ void build_tables(dasc_plan* p) {
     int64_t kept = 0;  // retained units of the layer before head h
     for (int h = 0; h < L.n_heads; ++h) {
       RefreshTask t{};
-      t.pool_off = static_cast<uint32_t>(L.pool_off + kept * L.unit_bytes);
+      t.pool_off = static_cast<uint64_t>(L.pool_off + kept * L.unit_bytes);
       if (L.kind == kGDN) {
         kept += L.retained[h];
       } else {
@@ -598,7 +598,9 @@ static int plan_build_impl(const dasc_layer_desc* layers, int32_t n_layers, doub
       b_row += L.n_heads;
       p->layers.push_back(std::move(L));
     }
-    if (k_row > std::numeric_limits<uint32_t>::max() || unit_base > std::numeric_limits<uint32_t>::max()) {
+    // Refresh tasks keep row offsets and gate-parameter indices in 32 bits.
+    constexpr int64_t kU32 = std::numeric_limits<uint32_t>::max();
+    if (k_row > kU32 || v_row > kU32 || g_row > kU32 || b_row > kU32 || unit_base > kU32) {
       delete p;
       return fail(DASC_EINVAL, "plan_build: model too wide for 32-bit row offsets");
     }
@@ -1077,13 +1079,16 @@ int dasc_ckpt_unpack_tp_zero_fill(dasc_plan_t p, const void* pool_base, int64_t 
                      n_recv, recv_idx, n, stream);
 }
 
+// The refresh in all its forms: `a` (bf16 gate logits) or `alpha` (fp32
+// decays) gives the decays, whichever is non-null when the other is null.
 static int run_refresh(const char* w, bool head_windows, dasc_plan_t p, const uint16_t* k,
                        const uint16_t* v, const uint16_t* a, const float* beta,
                        const int64_t* tok_offsets, int64_t n_tokens, void* dense_base,
                        int64_t dense_stride, int64_t n_dense, const int32_t* dst_idx, int32_t n,
                        void* stream, const void* pool_base = nullptr, int64_t pool_stride = 0,
                        int64_t n_slots = 0, const int32_t* src_slot = nullptr,
-                       bool recurrent = false) {
+                       bool recurrent = false, const float* alpha = nullptr,
+                       bool use_alpha = false) {
   if (!p) return fail(DASC_EINVAL, std::string(w) + ": null plan");
   if (!p->device) return fail(DASC_ENOTUPLOADED, std::string(w) + ": plan tables not uploaded");
   if (n < 0 || n > 65535) return fail(DASC_EINVAL, std::string(w) + ": n must be in [0, 65535]");
@@ -1093,13 +1098,15 @@ static int run_refresh(const char* w, bool head_windows, dasc_plan_t p, const ui
   if (n == 0 || p->refresh.empty()) return DASC_OK;
   if (!tok_offsets || !dense_base || !dst_idx) return fail(DASC_EINVAL, std::string(w) + ": null pointer");
   if (n_tokens < 0) return fail(DASC_EINVAL, std::string(w) + ": n_tokens must be >= 0");
-  if (n_tokens > 0 && (!k || !v || !a || !beta))
+  const void* decays = use_alpha ? static_cast<const void*>(alpha) : static_cast<const void*>(a);
+  if (n_tokens > 0 && (!k || !v || !decays || !beta))
     return fail(DASC_EINVAL, std::string(w) + ": null input pointer");
   if (p->k_row % 8 || p->v_row % 8)
     return fail(DASC_EUNSUPPORTED, std::string(w) + ": k and v rows must be multiples of 8 elements");
-  if (n_tokens > 0 && (!aligned16(k) || !aligned16(v) || !aligned16(a) ||
+  if (n_tokens > 0 && (!aligned16(k) || !aligned16(v) || !aligned16(decays) ||
                        reinterpret_cast<uintptr_t>(beta) % 4))
-    return fail(DASC_EINVAL, std::string(w) + ": k, v and a must be 16-byte aligned");
+    return fail(DASC_EINVAL, std::string(w) + (use_alpha ? ": k, v and alpha" : ": k, v and a") +
+                                 " must be 16-byte aligned");
   if (!aligned16(dense_base) || dense_stride < p->info.dense_bytes || dense_stride % 16)
     return fail(DASC_EINVAL, std::string(w) + ": dense base/stride misaligned or too small");
   if (n_dense <= 0) return fail(DASC_EINVAL, std::string(w) + ": n_dense must be > 0");
@@ -1108,7 +1115,8 @@ static int run_refresh(const char* w, bool head_windows, dasc_plan_t p, const ui
   args.gate_dt = p->dev.gate_dt;
   args.k = k;
   args.v = v;
-  args.a = a;
+  args.a = use_alpha ? nullptr : a;
+  args.alpha = use_alpha ? alpha : nullptr;
   args.beta = beta;
   args.k_row = p->k_row;
   args.v_row = p->v_row;
@@ -1145,6 +1153,27 @@ int dasc_ckpt_refresh_suffix(dasc_plan_t p, const uint16_t* k, const uint16_t* v
                              int64_t n_dense, const int32_t* dst_idx, int32_t n, void* stream) {
   return run_refresh("ckpt_refresh_suffix", false, p, k, v, a, beta, tok_offsets, n_tokens,
                      dense_base, dense_stride, n_dense, dst_idx, n, stream);
+}
+
+int dasc_ckpt_refresh_suffix_alpha(dasc_plan_t p, const uint16_t* k, const uint16_t* v,
+                                   const float* alpha, const float* beta,
+                                   const int64_t* tok_offsets, int64_t n_tokens,
+                                   void* dense_base, int64_t dense_stride, int64_t n_dense,
+                                   const int32_t* dst_idx, int32_t n, void* stream) {
+  return run_refresh("ckpt_refresh_suffix_alpha", false, p, k, v, nullptr, beta, tok_offsets,
+                     n_tokens, dense_base, dense_stride, n_dense, dst_idx, n, stream, nullptr, 0,
+                     0, nullptr, false, alpha, true);
+}
+
+int dasc_ckpt_refresh_suffix_alpha_windowed(dasc_plan_t p, const uint16_t* k, const uint16_t* v,
+                                            const float* alpha, const float* beta,
+                                            const int64_t* tok_offsets, int64_t n_tokens,
+                                            void* dense_base, int64_t dense_stride,
+                                            int64_t n_dense, const int32_t* dst_idx, int32_t n,
+                                            void* stream) {
+  return run_refresh("ckpt_refresh_suffix_alpha_windowed", true, p, k, v, nullptr, beta,
+                     tok_offsets, n_tokens, dense_base, dense_stride, n_dense, dst_idx, n, stream,
+                     nullptr, 0, 0, nullptr, false, alpha, true);
 }
 
 int dasc_ckpt_refresh_suffix_recurrent(dasc_plan_t p, const uint16_t* k, const uint16_t* v,

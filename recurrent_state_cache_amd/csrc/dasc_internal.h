@@ -93,8 +93,8 @@ struct alignas(64) RefreshTask {
   uint32_t kind;       // kGDN: one gate per head; kKDA: one per channel
   uint32_t local[4];   // bit k set: column k is local and gets written
   uint32_t window;     // Eq. 7 window of the head: max W_u over its local units
-  uint32_t pool_off;   // fused load: byte offset of the head's first retained unit in a slot
-  uint32_t pad[2];
+  uint32_t pad;
+  uint64_t pool_off;   // fused load: byte offset of the head's first retained unit in a slot
 };
 
 static_assert(sizeof(Piece) == 64, "Piece layout");
@@ -115,10 +115,16 @@ struct DeviceTables {
   uint32_t* status;        // DASC_STATUS_* bits
 };
 
-// How a refresh task reads its gate logits `a`.
+// How a refresh task reads its decays: gate logits `a` (bf16, turned into
+// decays by Eq. 2 in the kernel) or the decays themselves (fp32 alpha).
 constexpr int kGateHead = 0;       // one logit per head (GDN)
 constexpr int kGateChan = 1;       // one per channel, 16-byte aligned rows of 8 (KDA)
 constexpr int kGateChanSplit = 2;  // one per channel, read element by element (KDA)
+constexpr int kGateAlphaHead = 3;       // one fp32 decay per head (GDN)
+constexpr int kGateAlphaChan = 4;       // one per channel, 16-byte aligned rows of 8 (KDA)
+constexpr int kGateAlphaChanSplit = 5;  // one per channel, read element by element (KDA)
+// The decay mode that reads fp32 alpha in place of a logit mode.
+constexpr int alpha_gate(int gate) { return gate + kGateAlphaHead; }
 
 constexpr int kRefreshChunk = 16;  // tokens per refresh chunk (the MFMA tile edge)
 
@@ -173,7 +179,8 @@ struct RefreshArgs {
   const float* gate_dt;
   const uint16_t* k;
   const uint16_t* v;
-  const uint16_t* a;
+  const uint16_t* a;      // gate logits (bf16), or
+  const float* alpha;     // the decays (fp32), same row layout; non-null selects them
   const float* beta;
   int64_t k_row, v_row, g_row, b_row;
   const int64_t* tok_off;

@@ -886,7 +886,8 @@ refresh_kernel(RefreshArgs a) {
   static_assert(!ONE || WINDOWED, "the one-chunk kernel serves windowed replays");
   using Sh = RefreshShape<D>;
   constexpr int KT = Sh::kKT, VTW = Sh::kVTW, JB = Sh::kJB, NB4 = Sh::kNB4;
-  constexpr bool kChan = GATE != kGateHead;
+  constexpr bool kAlpha = GATE >= kGateAlphaHead;  // decays given as fp32
+  constexpr bool kChan = GATE != kGateHead && GATE != kGateAlphaHead;
   constexpr bool kAllStage = Sh::kNT == 2 * D;  // every lane stages an item
   __shared__ RefreshLds<D, ONE ? 1 : 2> sh;
 
@@ -919,10 +920,11 @@ refresh_kernel(RefreshArgs a) {
   const int it_t = (tid / JB) % kC, it_jb = tid % JB, j0 = 8 * it_jb;
 
   // Inputs of one token for this lane (8 bf16 of k, v and the gate logits,
-  // packed, and beta), fetched one chunk ahead of their staging.  The row is
-  // clamped into the request, so every load is in bounds; past the end the
-  // values are replaced by the no-op token when staged.
-  u32x4 rk, rv, ra;
+  // packed, or 8 fp32 decays in ra and ra2, and beta), fetched one chunk
+  // ahead of their staging.  The row is clamped into the request, so every
+  // load is in bounds; past the end the values are replaced by the no-op
+  // token when staged.
+  u32x4 rk, rv, ra, ra2;
   float rb;
   bool r_real;
   auto fetch = [&](int64_t n) {
@@ -931,23 +933,40 @@ refresh_kernel(RefreshArgs a) {
     const int64_t tc = r_real ? tok : t1 - 1;
     rk = *reinterpret_cast<const u32x4*>(a.k + tc * a.k_row + task.k_off + j0);
     rv = *reinterpret_cast<const u32x4*>(a.v + tc * a.v_row + task.v_off + j0);
-    const uint16_t* ap = a.a + tc * a.g_row + task.g_off;
-    if constexpr (GATE == kGateChan) {
-      ra = *reinterpret_cast<const u32x4*>(ap + j0);
-    } else if constexpr (GATE == kGateChanSplit) {
+    if constexpr (kAlpha) {
+      const float* pp = a.alpha + tc * a.g_row + task.g_off;
+      if constexpr (GATE == kGateAlphaChan) {
+        ra = *reinterpret_cast<const u32x4*>(pp + j0);
+        ra2 = *reinterpret_cast<const u32x4*>(pp + j0 + 4);
+      } else if constexpr (GATE == kGateAlphaChanSplit) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        ra[q] = static_cast<uint32_t>(ap[j0 + 2 * q]) |
-                (static_cast<uint32_t>(ap[j0 + 2 * q + 1]) << 16);
+        for (int q = 0; q < 4; ++q) {
+          ra[q] = __float_as_uint(pp[j0 + q]);
+          ra2[q] = __float_as_uint(pp[j0 + 4 + q]);
+        }
+      } else {
+        ra = u32x4{__float_as_uint(pp[0]), 0u, 0u, 0u};
+      }
     } else {
-      ra = u32x4{static_cast<uint32_t>(ap[0]), 0u, 0u, 0u};
+      const uint16_t* ap = a.a + tc * a.g_row + task.g_off;
+      if constexpr (GATE == kGateChan) {
+        ra = *reinterpret_cast<const u32x4*>(ap + j0);
+      } else if constexpr (GATE == kGateChanSplit) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          ra[q] = static_cast<uint32_t>(ap[j0 + 2 * q]) |
+                  (static_cast<uint32_t>(ap[j0 + 2 * q + 1]) << 16);
+      } else {
+        ra = u32x4{static_cast<uint32_t>(ap[0]), 0u, 0u, 0u};
+      }
     }
     rb = a.beta[tc * a.b_row + task.b_off];
   };
 
-  // Stage the fetched token into LDS buffer vb: decays (Eq. 2), k, v, beta.
-  // A token past the end becomes the no-op token: k = v = 0 words, beta = 0,
-  // and a zero gate scale, which makes the decay exp2(-0) = 1 exactly.  (The
+  // Stage the fetched token into LDS buffer vb: decays (given, or by Eq. 2),
+  // k, v, beta.  A token past the end becomes the no-op token: k = v = 0
+  // words, beta = 0, and a decay of exactly 1 (given decays are replaced by
+  // 1; for logits a zero gate scale makes the decay exp2(-0) = 1).  (The
   // padding is applied to inputs, not by selecting results, so the code has
   // no branch.)
   auto stage1 = [&](int vb) {
@@ -959,7 +978,17 @@ refresh_kernel(RefreshArgs a) {
       kf[2 * q] = bf16_lo(wk[q]);
       kf[2 * q + 1] = bf16_hi(wk[q]);
     }
-    if constexpr (kChan) {
+    if constexpr (kAlpha && kChan) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        al[q] = r_real ? __uint_as_float(ra[q]) : 1.f;
+        al[q + 4] = r_real ? __uint_as_float(ra2[q]) : 1.f;
+      }
+    } else if constexpr (kAlpha) {
+      const float x = r_real ? __uint_as_float(ra[0]) : 1.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) al[c] = x;
+    } else if constexpr (kChan) {
       const v4f e0 = *reinterpret_cast<const v4f*>(&sh.PA[j0]);
       const v4f e1 = *reinterpret_cast<const v4f*>(&sh.PA[j0 + 4]);
       const v4f d0 = *reinterpret_cast<const v4f*>(&sh.PD[j0]);
@@ -1178,7 +1207,7 @@ refresh_kernel(RefreshArgs a) {
   if (nchunks > 0) {
     // The head's gate parameters into LDS (read by every staging), while
     // the first chunk's inputs are in flight.
-    if (tid < (kChan ? D : 1)) {
+    if (!kAlpha && tid < (kChan ? D : 1)) {
       sh.PA[tid] = a.gate_expA[task.param_off + tid];
       sh.PD[tid] = a.gate_dt[task.param_off + tid];
     }
@@ -1618,9 +1647,37 @@ void launch_refresh_f(const RefreshArgs& args, dim3 grid, hipStream_t s) {
   else refresh_kernel<D, GATE, W, false, false><<<grid, kNT, 0, s>>>(args);
 }
 
+// Decays given as fp32 (no fused-load form).
+template <int D, int GATE, bool W>
+void launch_refresh_alpha_f(const RefreshArgs& args, dim3 grid, hipStream_t s) {
+  constexpr int kNT = RefreshShape<D>::kNT;
+  if (W && args.one_chunk) refresh_kernel<D, GATE, true, false, true><<<grid, kNT, 0, s>>>(args);
+  else refresh_kernel<D, GATE, W, false, false><<<grid, kNT, 0, s>>>(args);
+}
+
 template <int D>
 int launch_refresh_d(int gate, const RefreshArgs& args, dim3 grid, hipStream_t s) {
   const bool w = args.head_windows != 0;
+  if (args.alpha) {
+    if (args.pool) return static_cast<int>(hipErrorInvalidValue);
+    switch (alpha_gate(gate)) {
+      case kGateAlphaHead:
+        if (w) launch_refresh_alpha_f<D, kGateAlphaHead, true>(args, grid, s);
+        else launch_refresh_alpha_f<D, kGateAlphaHead, false>(args, grid, s);
+        break;
+      case kGateAlphaChan:
+        if (w) launch_refresh_alpha_f<D, kGateAlphaChan, true>(args, grid, s);
+        else launch_refresh_alpha_f<D, kGateAlphaChan, false>(args, grid, s);
+        break;
+      case kGateAlphaChanSplit:
+        if (w) launch_refresh_alpha_f<D, kGateAlphaChanSplit, true>(args, grid, s);
+        else launch_refresh_alpha_f<D, kGateAlphaChanSplit, false>(args, grid, s);
+        break;
+      default:
+        return static_cast<int>(hipErrorInvalidValue);
+    }
+    return static_cast<int>(hipGetLastError());
+  }
   switch (gate) {
     case kGateHead:
       if (w) launch_refresh_f<D, kGateHead, true>(args, grid, s);
@@ -1653,6 +1710,7 @@ int launch_recurrent_d(int gate, const RefreshArgs& args, dim3 grid, hipStream_t
 
 int launch_recurrent(int d, int gate, const RefreshArgs& args, void* stream) {
   if (args.n_tasks == 0 || args.n == 0) return hipSuccess;
+  if (args.alpha) return static_cast<int>(hipErrorInvalidValue);  // gate logits only
   dim3 grid(args.n_tasks, static_cast<uint32_t>(args.n));
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (d) {

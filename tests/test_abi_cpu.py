@@ -25,7 +25,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 23
+    assert len(names) == 25
     out = subprocess.run(["nm", "-D", "--defined-only", R.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\b[TW]\s+(dasc_[a-z0-9_]+)\b", out))
@@ -127,6 +127,8 @@ def _desc(kind=0, H=2, dk=8, dv=8, A=None, D=None, conv=0):
     (dict(conv=8), {}),
     (dict(conv=-16), {}),
     (dict(A=np.array([np.nan, 0], np.float32)), {}),
+    # refresh row offsets are 32-bit: a v row of 4 x 2^30 elements is too wide
+    (dict(H=4, dk=4, dv=1 << 30, A=np.zeros(4, np.float32), D=np.zeros(4, np.float32)), {}),
     (dict(D=np.array([0, np.inf], np.float32)), {}),
     ({}, dict(eps=0.0)),
     ({}, dict(eps=1.0)),
@@ -253,6 +255,10 @@ def test_every_data_call_needs_uploaded_tables():
         "refresh_recurrent": lambda h: L.dasc_ckpt_refresh_suffix_recurrent(h, f, f, f, f, f, 1,
                                                                             f, 4096, 1, f, 1,
                                                                             None),
+        "refresh_alpha": lambda h: L.dasc_ckpt_refresh_suffix_alpha(h, f, f, f, f, f, 1, f,
+                                                                    4096, 1, f, 1, None),
+        "refresh_alpha_windowed": lambda h: L.dasc_ckpt_refresh_suffix_alpha_windowed(
+            h, f, f, f, f, f, 1, f, 4096, 1, f, 1, None),
         "pack_tp": lambda h: L.dasc_ckpt_pack_tp(h, f, 4096, 1, f, f, 4096, 1, f, f, 4096, 1, f,
                                                  1, None),
         "unpack_tp": lambda h: L.dasc_ckpt_unpack_tp_zero_fill(h, f, 4096, 1, f, f, 4096, 1, f,

@@ -271,3 +271,26 @@ def refresh_inputs(cfg: Config, W: np.ndarray, device="cpu",
     tok = torch.zeros(len(W) + 1, dtype=torch.int64)
     tok[1:] = torch.from_numpy(np.cumsum(W).astype(np.int64))
     return RefreshInputs(k, v, a, beta.contiguous(), tok.to(device))
+
+
+def refresh_decays(cfg: Config, T: int, device="cpu", seed: int | None = None) -> torch.Tensor:
+    """fp32 decays [T, sum gate_width] for the refresh that takes the decays
+    directly: each unit (a KDA channel, or a GDN head) gets a floor
+    f_u = x^3 with x ~ U(0, 1), drawn once, and each token the decay
+    f_u + (1 - f_u) w with w ~ U(0, 1).  The median decay is near 0.67 (the
+    pages' median one-step KDA decay is 0.47); the few units with a floor
+    near 1 decay slowly over every token (long memories, which stress the
+    accumulation over long windows), the many with a low floor see decays
+    over most of (0, 1).  A plain random draw: these decays do not come
+    from the model's gate."""
+    seed = cfg.seed if seed is None else seed
+    g = torch.Generator(device=device)
+    g.manual_seed(seed + 29)
+    gw = sum(l.gate_width for l in cfg.layers)
+    floor = torch.rand((1, gw), generator=g, device=device) ** 3
+    out = torch.empty((T, gw), dtype=torch.float32, device=device)
+    step = 4096
+    for t0 in range(0, T, step):
+        w = torch.rand((min(step, T - t0), gw), generator=g, device=device)
+        out[t0:t0 + w.shape[0]] = floor + (1.0 - floor) * w
+    return out
