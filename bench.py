@@ -2,20 +2,29 @@
 
 One step = one pass of the whole path over one batch of synthetic input:
 pack n checkpoints into pool slots, unpack them with zero-fill, and refresh
-n_req requests over their suffix windows (the static plan is built once,
-before timing, as the pages build it offline; its host time is reported).
+n_req requests over their suffix windows with the decays given directly
+(Eq. 1 as written).  The static plan is built once, before timing, as the
+pages build it offline; its host time is reported.
 
-Default workload "kda": Kimi-Linear-shaped KDA layers (20 x 32 heads,
-d = 128, fp32 state, bf16 conv 4 x (3*32*128) per layer), 64 checkpoints
-packed and unpacked, 64 requests x 256 tokens refreshed.  Other workloads:
-"gdn" (36 x 32 GDN heads, 64 checkpoints; refresh 64 x 256 tokens over the
-omitted heads) and "mixed" (27 alternating layers, 512 checkpoints, 64
-requests with windows U{64..1024}).
+Headline workload, the largest configuration: "mixed", 27 layers
+alternating GDN and KDA (32 heads, d = 128, per-layer retention 20-80%,
+W_max = 64), 512 checkpoints in a random slot order, 64 requests with
+suffixes of U{64..1024} tokens.  The same JSON line carries two
+sub-objects with the same measurements: "gdn" (36 GDN layers x 32 heads,
+64 checkpoints, 64 x 256 tokens over the omitted heads) and "kda" (20 KDA
+layers x 32 heads with conv state, 64 checkpoints, 64 x 256 tokens).
+`--workload mixed|gdn|kda` runs one of them alone (the profiling runs).
 
-Prints ONE JSON line.  value = pack+unpack GB/s (algorithmic bytes / time);
-refresh request-tokens/s and the per-kernel rooflines ride along, and an
-"int8" object times INT8 checkpoint pack and unpack (Eq. 10) of the same
-checkpoints on their own, after the timed steps.
+Prints ONE JSON line.  value = pack+unpack GB/s of the headline workload
+(algorithmic bytes / time); its refresh request-tokens/s and every
+kernel's roofline ride along.  Timed after the steps, on their own: INT8
+checkpoint pack and unpack (Eq. 10), the refresh from bf16 gate logits
+(the fused gate, Eq. 2 in the kernel), per-head Eq. 7 windows for both,
+the dasc-wr load (unpack then refresh against the fused load), TP8
+storage balancing (gdn, kda) and the token-by-token vector form of the
+refresh (kda).  A cpu_baseline times the fp64 oracle on a bounded sample
+of the headline workload: pack and unpack in one process, the refresh
+over a pool of one worker per host core.
 """
 from __future__ import annotations
 
@@ -38,29 +47,39 @@ FP32_VALU_UNPACKED_TF = 78.6   # fp32 vector FMA rate without packed (2-wide) FM
 KERNEL_SOURCES = ["recurrent_state_cache_amd/csrc/dasc_kernels.hip",
                   "recurrent_state_cache_amd/csrc/dasc_internal.h",
                   "recurrent_state_cache_amd/csrc/dasc_host.cpp"]
-# kernel name pattern -> role (the TP movers and the windowed refresh are
-# instantiations of their own)
 # rounds of the rocprofv3 kernel-statistics run (--warmup, --steps)
 PROFILE_WARMUP, PROFILE_STEPS = 3, 10
 
+# kernel name pattern -> role.  refresh_kernel<D, gate mode, windowed, fused,
+# one chunk>: gate modes 0-2 read bf16 gate logits, 3-5 fp32 decays.
 KERNEL_ROLES = {r"qmove_kernel<true(, (true|false))?>": "pack_int8",
                 r"qmove_kernel<false(, false)?>": "unpack_int8",
                 r"(?<!q)move_kernel<true, \d+, \d+, false>": "pack",
                 r"(?<!q)move_kernel<false, \d+, \d+, false>": "unpack",
                 r"(?<!q)move_kernel<true, \d+, \d+, true>": "pack_tp",
                 r"(?<!q)move_kernel<false, \d+, \d+, true>": "unpack_tp",
-                r"refresh_kernel<\d+, \d+, false, false, false>": "refresh",
-                r"refresh_kernel<\d+, \d+, true, false, (true|false)>": "refresh_windowed",
+                r"refresh_kernel<\d+, [345], false, false, false>": "refresh",
+                r"refresh_kernel<\d+, [012], false, false, false>": "refresh_gate",
+                r"refresh_kernel<\d+, [345], true, false, (true|false)>": "refresh_windowed",
+                r"refresh_kernel<\d+, [012], true, false, (true|false)>": "refresh_windowed_gate",
                 r"refresh_kernel<\d+, \d+, (true|false), true, (true|false)>": "refresh_fused",
                 r"recurrent_kernel<": "refresh_recurrent"}
+ROLE_ORDER = ("pack", "unpack", "refresh", "refresh_gate", "pack_int8", "unpack_int8", "pack_tp",
+              "unpack_tp", "refresh_windowed", "refresh_windowed_gate", "refresh_fused",
+              "refresh_recurrent")
+WORKLOADS = ("mixed", "gdn", "kda")
 
 
 def _args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=300,
+                    help="timed steps of every workload's pack + unpack + refresh")
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["kda", "gdn", "mixed"], default="kda")
+    ap.add_argument("--side-steps", type=int, default=10,
+                    help="timed rounds of each section after the steps (INT8, windows, ...)")
+    ap.add_argument("--workload", choices=("all",) + WORKLOADS, default="all",
+                    help="all: the mixed headline with gdn and kda sub-objects")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-wr-load", action="store_true",
                     help="skip the dasc-wr load section (its unpack launches would share the "
@@ -89,7 +108,8 @@ def _workload(name):
         desc = "GDN 36x32 heads d=128: pack+unpack 64 ckpts, refresh 64 req x 256 tok"
     else:
         cfg = W.mixed(n_ckpt=512, n_req=64)
-        desc = "mixed 27 layers GDN/KDA d=128: pack+unpack 512 ckpts, refresh 64 req x U{64..1024}"
+        desc = ("mixed 27 layers GDN/KDA 32 heads d=128: pack+unpack 512 ckpts, "
+                "refresh 64 req x U{64..1024} tok")
     return cfg, desc
 
 
@@ -170,25 +190,189 @@ def _windowed_work(P, Wn):
     return flops, head_tokens
 
 
-def _windowed_bytes(P, Wn):
+def _windowed_bytes(P, Wn, decay_bytes=2):
     """Algorithmic HBM bytes of the refresh with per-head Eq. 7 windows: the
-    token inputs each replayed head reads (k, v, gate logits bf16, beta
-    fp32 for min(W_lh, n_r) tokens) and the local columns it writes."""
+    token inputs each replayed head reads for min(W_lh, n_r) tokens (k and
+    v bf16, the decays as bf16 gate logits (decay_bytes = 2) or fp32
+    (decay_bytes = 4), beta fp32), and the write-back of the local columns,
+    counted by the whole 32-channel row segments (128-byte lines at d_k =
+    128) that hold a local channel: a column is strided in the row-major
+    state, and a line it touches is written whole.  Every request writes
+    every replayed head."""
     import numpy as np
     total = 0
     for l in range(P.info()["n_layers"]):
         L = P.layer(l)
         ret, _, win = P.units(l)
         kda = L["kind"] != 0
-        per = L["d_k"] if kda else 1
+        dk, dv = L["d_k"], L["d_v"]
+        per = dk if kda else 1
         local = ~ret.reshape(L["n_heads"], per).astype(bool)
         heads = local.any(axis=1)
         w = np.where(local, win.reshape(L["n_heads"], per), 0).max(axis=1)[heads]
         ht = int(np.minimum(w[:, None], np.asarray(Wn)[None, :]).sum())
-        per_token = 2 * L["d_k"] + 2 * L["d_v"] + (2 * L["d_k"] if kda else 2) + 4
-        cols = local.sum(axis=1)[heads] if kda else np.full(int(heads.sum()), L["d_k"])
-        total += ht * per_token + int(cols.sum()) * L["d_v"] * 4 * len(Wn)
+        per_token = 2 * dk + 2 * dv + (dk if kda else 1) * decay_bytes + 4
+        nseg = (dk + 31) // 32
+        seg_w = np.minimum(32, dk - 32 * np.arange(nseg))       # channels per segment
+        if kda:
+            lc = np.zeros((int(heads.sum()), nseg * 32), bool)
+            lc[:, :dk] = local[heads]
+            cols = int((lc.reshape(-1, nseg, 32).any(axis=2) * seg_w).sum())
+        else:
+            cols = int(heads.sum()) * dk
+        total += ht * per_token + cols * dv * 4 * len(Wn)
     return total
+
+
+def _calibrate_copy(steps):
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_per_dispatch_read": n,
+                      "bytes_per_dispatch_write": n, "dispatches": steps}), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a bounded sample of the workload.
+# ---------------------------------------------------------------------------
+
+def _cpu_worker_init():
+    os.environ["OMP_NUM_THREADS"] = "1"
+    os.environ["OPENBLAS_NUM_THREADS"] = "1"
+    os.environ["MKL_NUM_THREADS"] = "1"
+
+
+def _cpu_warm(i):
+    time.sleep(0.25)   # long enough that every worker takes one
+    return os.getpid()
+
+
+def _cpu_refresh_task(task):
+    """One request's refresh over a few layers with the oracle, in a worker:
+    the layers' own plan (a unit's retention depends on its own parameters
+    only, so their heads are the ones the full plan replays) and their
+    slices of the token rows.  Returns (head-token replays, flops, seconds)."""
+    from threadpoolctl import threadpool_limits
+    import numpy as np
+    import oracle
+    layers, a_s, eps, w_max, k, v, alpha, beta, head_windows = task
+    with threadpool_limits(limits=1):
+        t = time.perf_counter()
+        O = oracle.build_plan(layers, a_s, eps, w_max)
+        n = k.shape[0]
+        out = oracle.refresh_expected(O, k, v, None, beta, np.array([0, n]), alpha=alpha,
+                                      head_windows=head_windows)
+        secs = time.perf_counter() - t
+    ht = flops = 0
+    for (_, li, h) in out:
+        L = O.layers[li]
+        w = min(O.head_window(li, h), n) if head_windows else n
+        ht += w
+        flops += 5 * L.d_v * L.d_k * w
+    return ht, flops, secs, os.getpid()
+
+
+def _cpu_pool():
+    """One worker process per host core, started before the GPU is touched
+    (spawned interpreters that import nothing of the GPU path)."""
+    import multiprocessing
+    from concurrent.futures import ProcessPoolExecutor
+    n = os.cpu_count() or 1
+    ex = ProcessPoolExecutor(max_workers=n, mp_context=multiprocessing.get_context("spawn"),
+                             initializer=_cpu_worker_init)
+    list(ex.map(_cpu_warm, range(n)))   # every submission spawns a worker until n exist
+    return ex, n
+
+
+def _cpu_baseline(cfg, P, ex, n_workers, dense_cpu, pack_bytes_per_ckpt, unpack_bytes_per_ckpt,
+                  rows, Wn, int8_bytes_per_ckpt):
+    """The fp64 NumPy oracle on a bounded sample of the workload, on this
+    host's cores: pack and unpack of a few checkpoints in one process
+    (memory-bound, single-threaded); the refresh with the decays given
+    directly, one task per (request, pair of layers), over the pool of
+    n_workers processes (one per core); the same with per-head Eq. 7
+    windows; INT8 pack and unpack of a few checkpoints in one process."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    with threadpool_limits(limits=1):
+        O = oracle.build_plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max)
+        n = dense_cpu.shape[0]
+        pool = np.zeros((n, O.slot_bytes), np.uint8)
+        out = np.zeros((n, O.dense_bytes), np.uint8)
+        t = time.perf_counter()
+        oracle.pack(O, dense_cpu, list(range(n)), pool, list(range(n)))
+        oracle.unpack_zero_fill(O, pool, list(range(n)), out, list(range(n)))
+        t_move = time.perf_counter() - t
+        m = min(4, n)
+        lo = oracle.Int8Layout(O)
+        pool_q = np.zeros((m, lo.slot_bytes), np.uint8)
+        out_q = np.zeros((m, O.dense_bytes), np.uint8)
+        t = time.perf_counter()
+        oracle.pack_int8(O, dense_cpu[:m], list(range(m)), pool_q, list(range(m)))
+        oracle.unpack_int8_zero_fill(O, pool_q, list(range(m)), out_q, list(range(m)))
+        t_q = time.perf_counter() - t
+
+    # refresh tasks: request r_i = i mod n_req over layers (2j, 2j + 1), j = i mod
+    # (L / 2), so the sample covers every layer and many window lengths
+    k_all, v_all, alpha_all, beta_all, tok = rows
+    ko = vo = go = bo = 0
+    offs = []
+    for L in cfg.layers:
+        offs.append((ko, vo, go, bo))
+        ko += L.n_heads * L.d_k
+        vo += L.n_heads * L.d_v
+        go += L.gate_width
+        bo += L.n_heads
+    pairs = [(2 * j, 2 * j + 1) for j in range(len(cfg.layers) // 2)] or [(0,)]
+    n_tasks = 4 * n_workers
+
+    def task(i, head_windows):
+        r = i % cfg.n_req
+        ls = pairs[i % len(pairs)]
+        t0, t1 = int(tok[r]), int(tok[r + 1])
+        sl = lambda a, o, w: np.concatenate([a[t0:t1, offs[l][o]:offs[l][o] + w(cfg.layers[l])]
+                                             for l in ls], axis=1)
+        return ([cfg.layers[l] for l in ls], cfg.a_s, cfg.eps, cfg.w_max,
+                sl(k_all, 0, lambda L: L.n_heads * L.d_k), sl(v_all, 1, lambda L: L.n_heads * L.d_v),
+                sl(alpha_all, 2, lambda L: L.gate_width), sl(beta_all, 3, lambda L: L.n_heads),
+                head_windows)
+
+    def run(head_windows):
+        tasks = [task(i, head_windows) for i in range(n_tasks)]
+        t = time.perf_counter()
+        res = list(ex.map(_cpu_refresh_task, tasks))
+        wall = time.perf_counter() - t
+        return (sum(r[0] for r in res), sum(r[1] for r in res), wall, len(tasks),
+                len({r[3] for r in res}))
+
+    ht, fl, t_ref, nt, used = run(False)
+    ht_w, fl_w, t_win, _, _ = run(True)
+    heads_all = sum(len(O.refreshed_heads(l)) for l in range(len(O.layers)))
+    gbs = n * (pack_bytes_per_ckpt + unpack_bytes_per_ckpt) / t_move / 1e9
+    return {
+        "value": round(gbs, 4), "unit": "GB/s pack+unpack",
+        "cores": used, "kind": "oracle",
+        "refresh_request_tokens_per_s": round(ht / t_ref / heads_all, 3),
+        "refresh_gflops": round(fl / t_ref / 1e9, 3),
+        "refresh_eq7_windows_head_tokens_per_s": round(ht_w / t_win, 1),
+        "int8_pack_unpack_gbs": round(m * int8_bytes_per_ckpt / t_q / 1e9, 4),
+        "sample": (f"pack+unpack of {n} checkpoints in one process ({t_move:.2f} s); refresh "
+                   f"with the decays given: {nt} tasks (request i mod {cfg.n_req}, a pair of "
+                   f"layers) over {n_workers} worker processes ({used} of them took tasks), "
+                   f"one thread each, {ht} head-token replays "
+                   f"({t_ref:.2f} s wall), converted to request-tokens at {heads_all} replayed "
+                   f"heads per token; the same with per-head Eq. 7 windows ({ht_w} head-token "
+                   f"replays, {t_win:.2f} s); INT8 pack+unpack of {m} checkpoints in one "
+                   f"process ({t_q:.2f} s)"),
+        "host_cpus": os.cpu_count(),
+    }
 
 
 def _bench_tp(cfg, args, stream):
@@ -214,9 +398,10 @@ def _bench_tp(cfg, args, stream):
             for i in infos]
     out = [torch.empty_like(d) for d in dense]
     idx = torch.arange(n, dtype=torch.int32, device="cuda")
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for i in range(args.warmup + args.steps):
-        e = ev[i - args.warmup] if i >= args.warmup else None
+    rounds, warm = max(1, min(args.steps, args.side_steps)), min(args.warmup, 2)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(rounds)]
+    for i in range(warm + rounds):
+        e = ev[i - warm] if i >= warm else None
         if e: e[0].record(stream)
         for r, p in enumerate(plans):
             R.ckpt_pack_tp(p, dense[r], idx, pools[r], idx, rows[r], idx, stream)
@@ -250,96 +435,6 @@ def _bench_tp(cfg, args, stream):
         "frac_of_hbm_peak": round(moved / (t_pack + t_unpack) / 1e9 / HBM_PEAK_GBS, 4),
         "kernel": "move_kernel<*, kAlt> (8 launches per direction)",
         "rank0_pack_unpack_bytes_per_checkpoint": int(sum(_algorithmic_bytes(plans[0])[:2])),
-    }
-
-
-def _calibrate_copy(steps):
-    import torch
-    n = 1 << 30
-    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-    b = torch.empty_like(a)
-    torch.cuda.synchronize()
-    for _ in range(steps):
-        b.copy_(a)
-    torch.cuda.synchronize()
-    print(json.dumps({"calibration": "device copy", "bytes_per_dispatch_read": n,
-                      "bytes_per_dispatch_write": n, "dispatches": steps}), flush=True)
-
-
-def _cpu_baseline(cfg, P, dense_cpu, pack_bytes_per_ckpt, unpack_bytes_per_ckpt, inp_rows,
-                  tokens_per_req, int8_bytes_per_ckpt=None, tp_bytes_per_ckpt=None):
-    """The fp64 NumPy oracle, single-threaded, on a bounded sample: pack and
-    unpack of a few checkpoints, refresh of one request over 8 layers (full
-    suffix and per-head Eq. 7 windows), INT8 pack and unpack of a few
-    checkpoints, and rank 0's TP8 pack / partition and gather / unpack."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
-
-    import oracle
-    with threadpool_limits(limits=1):
-        O = oracle.build_plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max)
-        n = dense_cpu.shape[0]
-        pool = np.zeros((n, O.slot_bytes), np.uint8)
-        out = np.zeros((n, O.dense_bytes), np.uint8)
-        t = time.perf_counter()
-        oracle.pack(O, dense_cpu, list(range(n)), pool, list(range(n)))
-        oracle.unpack_zero_fill(O, pool, list(range(n)), out, list(range(n)))
-        t_move = time.perf_counter() - t
-        k, v, a, b = inp_rows
-        layers = [l for l in range(len(O.layers)) if len(O.refreshed_heads(l))][:20]
-        t = time.perf_counter()
-        oracle.refresh_expected(O, k, v, a, b, np.array([0, tokens_per_req]), layers=layers)
-        t_ref = time.perf_counter() - t
-        t = time.perf_counter()
-        oracle.refresh_expected(O, k, v, a, b, np.array([0, tokens_per_req]), layers=layers,
-                                head_windows=True)
-        t_win = time.perf_counter() - t
-        win_head_tokens = sum(min(O.head_window(l, int(h)), tokens_per_req)
-                              for l in layers for h in O.refreshed_heads(l))
-        extra = {}
-        if int8_bytes_per_ckpt is not None:
-            m = min(16, n)
-            lo = oracle.Int8Layout(O)
-            pool_q = np.zeros((m, lo.slot_bytes), np.uint8)
-            out_q = np.zeros((m, O.dense_bytes), np.uint8)
-            t = time.perf_counter()
-            oracle.pack_int8(O, dense_cpu[:m], list(range(m)), pool_q, list(range(m)))
-            oracle.unpack_int8_zero_fill(O, pool_q, list(range(m)), out_q, list(range(m)))
-            t_q = time.perf_counter() - t
-            extra["int8_pack_unpack_gbs"] = round(m * int8_bytes_per_ckpt / t_q / 1e9, 4)
-            extra["int8_sample"] = f"INT8 pack+unpack of {m} checkpoints ({t_q:.2f} s)"
-        if tp_bytes_per_ckpt is not None:
-            m = min(32, n)
-            orac = oracle.rank_plans(cfg.layers, 8, cfg.a_s, cfg.eps, cfg.w_max)
-            bal = oracle.plans_balance(orac)
-            O0 = orac[0]
-            d0 = np.random.default_rng(0).integers(0, 256, (m, O0.dense_bytes), dtype=np.uint8)
-            pool0 = np.zeros((m, oracle.slot_bytes_tp(O0, bal)), np.uint8)
-            send0 = np.zeros((m, max(16, oracle.send_bytes_tp(O0, bal, 0))), np.uint8)
-            out0 = np.zeros_like(d0)
-            ix = list(range(m))
-            t = time.perf_counter()
-            oracle.pack_tp(O0, bal, 0, d0, ix, pool0, ix, send0, ix)
-            oracle.unpack_tp(O0, bal, 0, pool0, ix, send0, ix, out0, ix)
-            t_tp = time.perf_counter() - t
-            extra["tp8_rank0_pack_unpack_gbs"] = round(m * tp_bytes_per_ckpt / t_tp / 1e9, 4)
-            extra["tp_sample"] = f"rank 0 of TP8, pack_tp+unpack_tp of {m} checkpoints ({t_tp:.2f} s)"
-    heads_sampled = sum(len(O.refreshed_heads(l)) for l in layers)
-    heads_all = sum(len(O.refreshed_heads(l)) for l in range(len(O.layers)))
-    # one request-token = one token through every refreshed head of every layer
-    sec_per_req_token = t_ref / tokens_per_req * heads_all / heads_sampled
-    gbs = n * (pack_bytes_per_ckpt + unpack_bytes_per_ckpt) / t_move / 1e9
-    return {
-        "value": round(gbs, 4), "unit": "GB/s pack+unpack",
-        "refresh_request_tokens_per_s": round(1.0 / sec_per_req_token, 3),
-        "cores": 1, "kind": "oracle",
-        "refresh_eq7_windows_head_tokens_per_s": round(win_head_tokens / t_win, 3),
-        "sample": (f"pack+unpack of {n} checkpoints ({t_move:.2f} s); refresh of 1 request x "
-                   f"{tokens_per_req} tokens over {len(layers)} layers / {heads_sampled} heads "
-                   f"({t_ref:.2f} s), scaled to all {heads_all} refreshed heads; the same with "
-                   f"per-head windows ({win_head_tokens} head-token replays, {t_win:.2f} s)"),
-        **extra,
-        "host_cpus": os.cpu_count(),
     }
 
 
@@ -438,8 +533,7 @@ def _summarize(dirs, workload):
     lines = [f"| kernel | calls | average (us) | timed launches: average (us) | min (us) | "
              f"max (us) | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM bytes per launch (calibrated) |",
              "|---|---|---|---|---|---|---|---|---|"]
-    order = ("pack", "unpack", "refresh", "pack_int8", "unpack_int8", "pack_tp", "unpack_tp",
-             "refresh_windowed", "refresh_fused", "refresh_recurrent")
+    order = ROLE_ORDER
     for k in sorted(stats, key=lambda k: (order.index(k.split(" ")[0]), k)):
         c, avg, mn, mx = stats[k]
         lines.append(f"| {k} | {c} | {avg / 1e3:.1f} | {timed.get(k, float('nan')) / 1e3:.1f} | "
@@ -454,6 +548,13 @@ def _summarize(dirs, workload):
     out += f"    workload: {workload}\n"
     out += f"    kernel_sources_sha256: {_sources_sha256()}\n"
     machine = {k: v for k, v in traffic.items() if k in order}
+    # A role served by several instantiations, each launched once per call
+    # (the refresh of a model with GDN and KDA layers): its bytes per call.
+    for role, kernels in names.items():
+        keys = [key(nm) for nm in kernels]
+        if len(keys) > 1 and all(k in traffic for k in keys) and \
+                len({stats[k][0] for k in keys if k in stats}) == 1:
+            machine[role] = sum(traffic[k] for k in keys)
     out += f"    traffic_bytes: {json.dumps(machine, sort_keys=True)}\n"
     return out
 
@@ -466,8 +567,7 @@ def _counter_table(dirs):
             if role:
                 table.setdefault(r["Counter_Name"], {}).setdefault(role, []).append(
                     float(r["Counter_Value"]))
-    roles = ("pack", "unpack", "refresh", "pack_int8", "unpack_int8", "pack_tp", "unpack_tp",
-             "refresh_windowed", "refresh_recurrent")
+    roles = [r for r in ROLE_ORDER if any(r in v for v in table.values())]
     lines = ["| counter | " + " | ".join(roles) + " |", "|" + "---|" * (len(roles) + 1)]
     for c in sorted(table):
         vals = [table[c].get(r) for r in roles]
@@ -494,29 +594,37 @@ def _recorded_traffic(workload):
     return json.loads(rec.get("traffic_bytes", "{}"))
 
 
-def main():
-    args = _args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the library has no "
-              f"multi-GPU path", file=sys.stderr)
-        sys.exit(2)
+def _timed(stream, rounds, warmup, *fns):
+    """Mean seconds of each of fns over `rounds` timed rounds (after warm-up
+    rounds), with HIP events recorded on `stream` around every call."""
     import numpy as np
     import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+          for _ in range(rounds)]
+    for i in range(warmup + rounds):
+        e = ev[i - warmup] if i >= warmup else None
+        if e: e[0].record(stream)
+        for j, fn in enumerate(fns):
+            fn()
+            if e: e[j + 1].record(stream)
+    torch.cuda.synchronize()
+    return [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev])) * 1e-3
+            for j in range(len(fns))]
 
-    if args.calibrate_copy:
-        _calibrate_copy(args.steps)
-        return
-    if args.summarize:
-        print(_summarize(args.summarize, args.workload))
-        return
-    if args.counters:
-        print(_counter_table(args.counters))
-        return
+
+def _launches(n, per):
+    return (n + per - 1) // per
+
+
+def _run_workload(name, args, stream, ex=None, n_workers=0):
+    """Every measurement of one workload; the cpu_baseline when ex is given."""
+    import numpy as np
+    import torch
 
     import recurrent_state_cache_amd as R
     import workloads as W
 
-    cfg, desc = _workload(args.workload)
+    cfg, desc = _workload(name)
     t = time.perf_counter()
     P = R.Plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max)
     plan_ms = (time.perf_counter() - t) * 1e3
@@ -530,16 +638,18 @@ def main():
     src = torch.arange(n, dtype=torch.int32, device="cuda")
     slot = torch.from_numpy(perm).cuda()
     Wn = W.windows(cfg)
+    T = int(Wn.sum())
     inp = W.refresh_inputs(cfg, Wn, device="cuda")
+    alpha = W.refresh_decays(cfg, T, device="cuda")
     dst = torch.arange(cfg.n_req, dtype=torch.int32, device="cuda") % n
-    total_tokens = int(Wn.sum())
     pack_b, unpack_b, pack_qb, unpack_qb = _algorithmic_bytes(P)
     # Eq. 1 per token and replayed head: decay (1), readout (2), rank-1 write (2) flops per element
-    flops = total_tokens * sum(5 * P.layer(l)["d_v"] * P.layer(l)["d_k"] * P.layer(l)["n_refresh_heads"]
-                               for l in range(info["n_layers"]))
+    flops = T * sum(5 * P.layer(l)["d_v"] * P.layer(l)["d_k"] * P.layer(l)["n_refresh_heads"]
+                    for l in range(info["n_layers"]))
+    n_groups = len({(P.layer(l)["kind"], P.layer(l)["d_k"]) for l in range(info["n_layers"])
+                    if P.layer(l)["n_refresh_heads"]})
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
 
     def step(e=None):
@@ -548,7 +658,8 @@ def main():
         if e: e[1].record(stream)
         R.ckpt_unpack_zero_fill(P, pool, slot, out, src, stream)
         if e: e[2].record(stream)
-        R.ckpt_refresh_suffix(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, out, dst, stream)
+        R.ckpt_refresh_suffix_alpha(P, inp.k, inp.v, alpha, inp.beta, inp.tok_off, out, dst,
+                                    stream)
         if e: e[3].record(stream)
 
     for _ in range(args.warmup):
@@ -561,178 +672,223 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     assert P.status() == 0
+    t_pack = np.array([e[0].elapsed_time(e[1]) for e in ev]).mean() * 1e-3
+    t_unpack = np.array([e[1].elapsed_time(e[2]) for e in ev]).mean() * 1e-3
+    t_ref = np.array([e[2].elapsed_time(e[3]) for e in ev]).mean() * 1e-3
 
-    # INT8 checkpoints (Eq. 10), timed on their own after the step: pack and
-    # unpack of the same checkpoints through an INT8 pool.
+    rounds, warm = max(1, min(args.steps, args.side_steps)), min(args.warmup, 2)
+    # INT8 checkpoints (Eq. 10): pack and unpack of the same checkpoints.
     pool_q = torch.empty((n, info["int8_slot_bytes"]), dtype=torch.uint8, device="cuda")
-    evq = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for i in range(args.warmup + args.steps):
-        e = evq[i - args.warmup] if i >= args.warmup else None
-        if e: e[0].record(stream)
-        R.ckpt_pack_int8(P, dense, src, pool_q, slot, stream)
-        if e: e[1].record(stream)
-        R.ckpt_unpack_int8_zero_fill(P, pool_q, slot, out, src, stream)
-        if e: e[2].record(stream)
-    torch.cuda.synchronize()
+    t_pack_q, t_unpack_q = _timed(
+        stream, rounds, warm,
+        lambda: R.ckpt_pack_int8(P, dense, src, pool_q, slot, stream),
+        lambda: R.ckpt_unpack_int8_zero_fill(P, pool_q, slot, out, src, stream))
+    del pool_q
+    # The same suffixes with the decays made in the kernel from bf16 gate
+    # logits (Eq. 2), and both forms with per-head Eq. 7 windows.
+    t_gate, = _timed(stream, rounds, warm,
+                     lambda: R.ckpt_refresh_suffix(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off,
+                                                   out, dst, stream))
+    t_win, t_win_gate = _timed(
+        stream, rounds, warm,
+        lambda: R.ckpt_refresh_suffix_alpha_windowed(P, inp.k, inp.v, alpha, inp.beta,
+                                                     inp.tok_off, out, dst, stream),
+        lambda: R.ckpt_refresh_suffix_windowed(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off,
+                                               out, dst, stream))
     assert P.status() == 0
-    t_pack_q = np.array([e[0].elapsed_time(e[1]) for e in evq]) * 1e-3
-    t_unpack_q = np.array([e[1].elapsed_time(e[2]) for e in evq]) * 1e-3
-
-    # Refresh with per-head Eq. 7 windows on the same suffixes, timed on its own.
-    evw = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    for i in range(args.warmup + args.steps):
-        e = evw[i - args.warmup] if i >= args.warmup else None
-        if e: e[0].record(stream)
-        R.ckpt_refresh_suffix_windowed(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, out, dst,
-                                       stream)
-        if e: e[1].record(stream)
-    torch.cuda.synchronize()
-    assert P.status() == 0
-    t_win = np.array([e[0].elapsed_time(e[1]) for e in evw]) * 1e-3
     win_flops, win_head_tokens = _windowed_work(P, Wn)
-    win_bytes = _windowed_bytes(P, Wn)
+    win_bytes = _windowed_bytes(P, Wn, decay_bytes=4)
+    win_bytes_gate = _windowed_bytes(P, Wn, decay_bytes=2)
 
     # dasc-wr load of the refreshed requests: unpack then refresh, against
-    # the fused load, with the full suffixes and with per-head windows.
-    src_slot = slot[:cfg.n_req].contiguous()
-    req_out = torch.arange(cfg.n_req, dtype=torch.int32, device="cuda")
-
-    def timed(fn):
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-        for i in range(args.warmup + args.steps):
-            e = evs[i - args.warmup] if i >= args.warmup else None
-            if e: e[0].record(stream)
-            fn()
-            if e: e[1].record(stream)
-        torch.cuda.synchronize()
-        assert P.status() == 0
-        return float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-
-    # The recurrence's own form (token by token on the vector units) on the
-    # same suffixes: the reference point for the chunked kernel.
-    t_rec = timed(lambda: R.ckpt_refresh_suffix_recurrent(P, inp.k, inp.v, inp.a, inp.beta,
-                                                          inp.tok_off, out, dst, stream)) * 1e-3
-
+    # the fused load (gate logits), with the full suffixes and with windows.
     wr = {}
-    for hw, name in (() if args.skip_wr_load else ((False, "full_suffix"), (True, "eq7_windows"))):
-        refresh = R.ckpt_refresh_suffix_windowed if hw else R.ckpt_refresh_suffix
+    if not args.skip_wr_load:
+        src_slot = slot[:cfg.n_req].contiguous()
+        req_out = torch.arange(cfg.n_req, dtype=torch.int32, device="cuda")
+        for hw, key in ((False, "full_suffix"), (True, "eq7_windows")):
+            refresh = R.ckpt_refresh_suffix_windowed if hw else R.ckpt_refresh_suffix
 
-        def two_step():
-            R.ckpt_unpack_zero_fill(P, pool, src_slot, out, req_out, stream)
-            refresh(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, out, req_out, stream)
+            def two_step():
+                R.ckpt_unpack_zero_fill(P, pool, src_slot, out, req_out, stream)
+                refresh(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, out, req_out, stream)
 
-        def fused():
-            R.ckpt_unpack_refresh(P, pool, src_slot, inp.k, inp.v, inp.a, inp.beta, inp.tok_off,
-                                  out, req_out, head_windows=hw, stream=stream)
-        t2, t1 = timed(two_step), timed(fused)
-        wr[name] = {"unpack_then_refresh_ms": round(t2, 4), "fused_ms": round(t1, 4),
-                    "speedup": round(t2 / t1, 3)}
+            def fused():
+                R.ckpt_unpack_refresh(P, pool, src_slot, inp.k, inp.v, inp.a, inp.beta,
+                                      inp.tok_off, out, req_out, head_windows=hw, stream=stream)
+            t2, = _timed(stream, rounds, warm, two_step)
+            t1, = _timed(stream, rounds, warm, fused)
+            wr[key] = {"unpack_then_refresh_ms": round(t2 * 1e3, 4), "fused_ms": round(t1 * 1e3, 4),
+                       "speedup": round(t2 / t1, 3)}
+        assert P.status() == 0
 
-    tp8 = _bench_tp(cfg, args, stream) if args.workload in ("kda", "gdn") else None
+    # The recurrence's own form (token by token on the vector units): the
+    # reference point for the chunked kernel, on the KDA workload.
+    t_rec = None
+    if name == "kda":
+        t_rec, = _timed(stream, rounds, warm,
+                        lambda: R.ckpt_refresh_suffix_recurrent(P, inp.k, inp.v, inp.a, inp.beta,
+                                                                inp.tok_off, out, dst, stream))
+        assert P.status() == 0
 
-    t_pack = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
-    t_unpack = np.array([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
-    t_ref = np.array([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
-    pack_total = n * pack_b
-    unpack_total = n * unpack_b
-    mover_gbs = (pack_total + unpack_total) * args.steps / (t_pack.sum() + t_unpack.sum()) / 1e9
-    ref_tf = flops / t_ref.mean() / 1e12
+    tp8 = _bench_tp(cfg, args, stream) if name in ("kda", "gdn") else None
 
-    traffic = _recorded_traffic(args.workload)
+    traffic = _recorded_traffic(name)
+    mm_bf16, mm_f32 = _refresh_mfma_flops(P, Wn)
 
-    def hbm(role, bytes_, secs):
+    def hbm(role, bytes_, secs, launches, kernel):
         a = bytes_ / secs / 1e9
         return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic.get(role),
-                "kernel": f"move_kernel<{'true' if role == 'pack' else 'false'}>",
-                "ms": round(secs * 1e3, 4), "bytes": int(bytes_)}
+                "kernel": kernel, "ms": round(secs * 1e3, 4), "bytes": int(bytes_),
+                "launches": launches, "bytes_per_launch": int(bytes_ // launches)}
 
-    mm_bf16, mm_f32 = _refresh_mfma_flops(P, Wn)
-    roof_ref = {"bound": "mfma", "achieved": round(ref_tf, 3), "peak": FP32_MFMA_PEAK_TF,
-                "unit": "TFLOP/s", "frac": round(ref_tf / FP32_MFMA_PEAK_TF, 4),
-                "traffic": traffic.get("refresh"), "kernel": "refresh_kernel<128, gate, false, false, false>",
-                "ms": round(t_ref.mean() * 1e3, 4), "flops": int(flops),
-                "note": "algorithmic fp32 flops (5 d^2 per token-head) against the fp32 matrix "
-                        "peak; the big products run as bf16 hi/lo splits on the bf16 matrix "
-                        "cores, whose issued rate is below",
-                "bf16_mfma_issued_tflops": round(mm_bf16 / t_ref.mean() / 1e12, 2),
-                "bf16_mfma_peak": BF16_MFMA_PEAK_TF,
-                "fp32_mfma_issued_tflops": round(mm_f32 / t_ref.mean() / 1e12, 2)}
+    def mfma(role, fl, secs, kernel, extra=None):
+        a = fl / secs / 1e12
+        return {"bound": "mfma", "achieved": round(a, 3), "peak": FP32_MFMA_PEAK_TF,
+                "unit": "TFLOP/s", "frac": round(a / FP32_MFMA_PEAK_TF, 4),
+                "traffic": traffic.get(role), "kernel": kernel, "ms": round(secs * 1e3, 4),
+                "flops": int(fl), "launches": n_groups, **(extra or {})}
+
+    mover_gbs = (pack_b + unpack_b) * n / (t_pack + t_unpack) / 1e9
+    res = {
+        "workload": desc,
+        "checkpoints": n, "requests": cfg.n_req, "refresh_tokens": T, "w_max": cfg.w_max,
+        "dense_bytes": info["dense_bytes"], "slot_bytes": info["slot_bytes"],
+        "c_ckpt": round(info["c_ckpt"], 4),
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "pack_unpack_gbs": round(mover_gbs, 2),
+        "pack_unpack_frac_of_hbm_peak": round(mover_gbs / HBM_PEAK_GBS, 4),
+        "refresh_request_tokens_per_s": round(T / t_ref, 1),
+        "plan_build_ms": round(plan_ms, 3),
+        "roofline": mfma("refresh", flops, t_ref,
+                         "refresh_kernel<128, fp32 decays, false, false, false>",
+                         {"note": "algorithmic fp32 flops (5 d^2 per token-head) against the fp32 "
+                                  "matrix peak; the big products run as bf16 hi/lo splits on the "
+                                  "bf16 matrix cores, whose issued rate is below",
+                          "bf16_mfma_issued_tflops": round(mm_bf16 / t_ref / 1e12, 2),
+                          "bf16_mfma_peak": BF16_MFMA_PEAK_TF,
+                          "fp32_mfma_issued_tflops": round(mm_f32 / t_ref / 1e12, 2)}),
+        "roofline_pack": hbm("pack", pack_b * n, t_pack, _launches(n, 16),
+                             "move_kernel<true> (16 pairs per launch)"),
+        "roofline_unpack": hbm("unpack", unpack_b * n, t_unpack, _launches(n, 16),
+                               "move_kernel<false> (16 pairs per launch)"),
+        "int8": {
+            "c_ckpt_int8": round(info["c_ckpt_int8"], 4),
+            "pack_unpack_gbs": round(n * (pack_qb + unpack_qb) / (t_pack_q + t_unpack_q) / 1e9, 2),
+            "pack": hbm("pack_int8", n * pack_qb, t_pack_q, _launches(n, 64),
+                        "qmove_kernel<true, *> (64 pairs per launch)"),
+            "unpack": hbm("unpack_int8", n * unpack_qb, t_unpack_q, _launches(n, 16),
+                          "qmove_kernel<false> (16 pairs per launch)"),
+        },
+        "refresh_fused_gate": mfma("refresh_gate", flops, t_gate,
+                                   "refresh_kernel<128, gate logits, false, false, false>",
+                                   {"note": "the same suffixes with the decays made in the kernel "
+                                            "from bf16 gate logits by Eq. 2"}),
+        "refresh_eq7_windows": {
+            "kernel": "refresh_kernel<128, fp32 decays, true, false, one_chunk> (per-head "
+                      "windows; the one-chunk kernel when every window is at most 16 tokens)",
+            "ms": round(t_win * 1e3, 4),
+            "head_tokens": int(win_head_tokens),
+            "head_tokens_per_s": round(win_head_tokens / t_win, 1),
+            "speedup_vs_full_suffix": round(t_ref / t_win, 3),
+            "roofline": {**mfma("refresh_windowed", win_flops, t_win, "refresh_kernel<.., true, ..>"),
+                         "hbm_bytes": int(win_bytes),
+                         "hbm_achieved_gbs": round(win_bytes / t_win / 1e9, 1),
+                         "hbm_frac": round(win_bytes / t_win / 1e9 / HBM_PEAK_GBS, 4)},
+            "fused_gate_ms": round(t_win_gate * 1e3, 4),
+            "fused_gate_hbm_frac": round(win_bytes_gate / t_win_gate / 1e9 / HBM_PEAK_GBS, 4),
+            "fused_gate_traffic": traffic.get("refresh_windowed_gate"),
+        },
+    }
+    if wr:
+        res["dasc_wr_load"] = dict(wr, requests=cfg.n_req)
+    if tp8:
+        res["tp8_storage_balancing"] = tp8
+    if t_rec is not None:
+        res["refresh_recurrent_form"] = {
+            "kernel": "recurrent_kernel<128, gate> (token by token, fp32 vector units)",
+            "ms": round(t_rec * 1e3, 4),
+            "achieved_tflops": round(flops / t_rec / 1e12, 3),
+            "fp32_vector_peak_unpacked": FP32_VALU_UNPACKED_TF,
+            "frac_of_unpacked_peak": round(flops / t_rec / 1e12 / FP32_VALU_UNPACKED_TF, 4),
+            "chunked_fused_gate_speedup": round(t_rec / t_gate, 3),
+            "note": "same suffixes, output and tolerance as the chunked refresh from gate logits; "
+                    "the vector units' fp32 rate without packed FMA (the library is compiled "
+                    "without packed fp32 instructions) is half the 157.3 TF/s datasheet figure",
+        }
+    if ex is not None:
+        m = min(32, n)
+        dense_cpu = dense[:m].cpu().numpy()
+        bits = lambda x: x.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+        rows = (bits(inp.k), bits(inp.v), alpha.cpu().numpy(), inp.beta.cpu().numpy(),
+                inp.tok_off.cpu().numpy())
+        res["cpu_baseline"] = _cpu_baseline(cfg, P, ex, n_workers, dense_cpu, pack_b, unpack_b,
+                                            rows, Wn, pack_qb + unpack_qb)
+    del dense, pool, out, inp, alpha
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the library has no "
+              f"multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    if args.summarize:
+        print(_summarize(args.summarize, args.workload))
+        return
+    if args.counters:
+        print(_counter_table(args.counters))
+        return
+    # The oracle's worker pool starts before anything touches the GPU.
+    ex = n_workers = None
+    if not args.no_cpu_baseline and not args.calibrate_copy:
+        ex, n_workers = _cpu_pool()
+    import torch
+    if args.calibrate_copy:
+        _calibrate_copy(args.steps)
+        return
+    stream = torch.cuda.current_stream()
+    names = WORKLOADS if args.workload == "all" else (args.workload,)
+    results = {}
+    for i, name in enumerate(names):
+        results[name] = _run_workload(name, args, stream, ex if i == 0 else None, n_workers)
+    if ex is not None:
+        ex.shutdown()
+    head = results[names[0]]
+    cpu = head.pop("cpu_baseline", None)
     line = {
         "metric": "checkpoint pack+unpack GB/s (% HBM peak); suffix-refresh tokens/s, 1 MI355X",
-        "value": round(mover_gbs, 2),
+        "value": head["pack_unpack_gbs"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "u32 copy (pack/unpack), f32 (refresh: fp32 state and accumulation, "
                  "products on bf16 hi/lo splits)",
         "data": "synthetic",
-        "config": {"workload": desc, "checkpoints": n, "requests": cfg.n_req,
-                   "refresh_tokens": total_tokens, "w_max": cfg.w_max,
-                   "dense_bytes": info["dense_bytes"], "slot_bytes": info["slot_bytes"],
-                   "c_ckpt": round(info["c_ckpt"], 4)},
-        "pack_unpack_frac_of_hbm_peak": round(mover_gbs / HBM_PEAK_GBS, 4),
-        "refresh_request_tokens_per_s": round(total_tokens / t_ref.mean(), 1),
-        "plan_build_ms": round(plan_ms, 3),
-        "roofline": roof_ref,
-        "roofline_pack": hbm("pack", pack_total, t_pack.mean()),
-        "roofline_unpack": hbm("unpack", unpack_total, t_unpack.mean()),
-        "int8": {
-            "c_ckpt_int8": round(info["c_ckpt_int8"], 4),
-            "pack_unpack_gbs": round(n * (pack_qb + unpack_qb) / (t_pack_q.mean() + t_unpack_q.mean()) / 1e9, 2),
-            "pack": {k: v for k, v in hbm("pack_int8", n * pack_qb, t_pack_q.mean()).items() if k != "kernel"}
-                    | {"kernel": "qmove_kernel<true, *> (column blocks when the list has no whole head)"},
-            "unpack": {k: v for k, v in hbm("unpack_int8", n * unpack_qb, t_unpack_q.mean()).items() if k != "kernel"}
-                      | {"kernel": "qmove_kernel<false>"},
-        },
-        **({"tp8_storage_balancing": tp8} if tp8 else {}),
-        **({"dasc_wr_load": dict(wr, requests=cfg.n_req)} if wr else {}),
-        "refresh_recurrent_form": {
-            "kernel": "recurrent_kernel<128, gate> (token by token, fp32 vector units)",
-            "ms": round(t_rec * 1e3, 4),
-            "achieved_tflops": round(flops / t_rec / 1e12, 3),
-            "fp32_vector_peak_unpacked": FP32_VALU_UNPACKED_TF,
-            "frac_of_unpacked_peak": round(flops / t_rec / 1e12 / FP32_VALU_UNPACKED_TF, 4),
-            "chunked_speedup": round(t_rec / t_ref.mean(), 3),
-            "note": "same suffixes, output and tolerance as the chunked refresh; the vector "
-                    "units' fp32 rate without packed FMA (the library is compiled without packed fp32 instructions) is half "
-                    "the 157.3 TF/s datasheet figure",
-        },
-        "refresh_eq7_windows": {
-            "kernel": "refresh_kernel<128, gate, true, false, one_chunk> (per-head windows; the one-chunk kernel when every window is at most 16 tokens)",
-            "ms": round(t_win.mean() * 1e3, 4),
-            "head_tokens": int(win_head_tokens),
-            "head_tokens_per_s": round(win_head_tokens / t_win.mean(), 1),
-            "flops": int(win_flops),
-            "achieved_tflops": round(win_flops / t_win.mean() / 1e12, 3),
-            "speedup_vs_full_suffix": round(t_ref.mean() / t_win.mean(), 3),
-            "roofline": {"bound": "mfma", "achieved": round(win_flops / t_win.mean() / 1e12, 3),
-                         "peak": FP32_MFMA_PEAK_TF, "unit": "TFLOP/s",
-                         "frac": round(win_flops / t_win.mean() / 1e12 / FP32_MFMA_PEAK_TF, 4),
-                         "traffic": traffic.get("refresh_windowed"),
-                         "hbm_bytes": int(win_bytes),
-                         "hbm_achieved_gbs": round(win_bytes / t_win.mean() / 1e9, 1),
-                         "hbm_frac": round(win_bytes / t_win.mean() / 1e9 / HBM_PEAK_GBS, 4),
-                         "note": "one 16-token chunk per head: neither roof is reached; the "
-                                 "time is each head's serial chain and the partial-line "
-                                 "write-back of the local columns"},
-        },
+        "config": {k: head[k] for k in ("workload", "checkpoints", "requests", "refresh_tokens",
+                                        "w_max", "dense_bytes", "slot_bytes", "c_ckpt")},
+        "pack_unpack_frac_of_hbm_peak": head["pack_unpack_frac_of_hbm_peak"],
+        "refresh_request_tokens_per_s": head["refresh_request_tokens_per_s"],
+        "roofline": head["roofline"],
+        "roofline_pack": head["roofline_pack"],
+        "roofline_unpack": head["roofline_unpack"],
+        **{k: v for k, v in head.items()
+           if k not in ("workload", "checkpoints", "requests", "refresh_tokens", "w_max",
+                        "dense_bytes", "slot_bytes", "c_ckpt", "ms_per_step", "pack_unpack_gbs",
+                        "pack_unpack_frac_of_hbm_peak", "refresh_request_tokens_per_s",
+                        "roofline", "roofline_pack", "roofline_unpack")},
+        **{name: results[name] for name in names[1:]},
     }
-    if not args.no_cpu_baseline:
-        m = min(32, n)
-        dense_cpu = dense[:m].cpu().numpy()
-        T0, T1 = int(inp.tok_off[0]), int(inp.tok_off[1])
-        bits = lambda x: x[T0:T1].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
-        rows = (bits(inp.k), bits(inp.v), bits(inp.a), inp.beta[T0:T1].cpu().numpy())
-        tp_b = tp8["rank0_pack_unpack_bytes_per_checkpoint"] if tp8 else None
-        line["cpu_baseline"] = _cpu_baseline(cfg, P, dense_cpu, pack_b, unpack_b, rows, T1 - T0,
-                                             int8_bytes_per_ckpt=pack_qb + unpack_qb,
-                                             tp_bytes_per_ckpt=tp_b)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 

@@ -43,9 +43,12 @@ constexpr uint32_t kCopyChunk = 4096;
 // TB/s as one launch of 512, the same bytes and the same span of time, so
 // not a clock or power effect; 5.94-5.96 TB/s at 8-16 pairs); 16 is the
 // measured best for the fp32 movers and the INT8 unpack, while the INT8
-// pack, whose whole-head pieces are few and large, prefers 64.
+// pack, whose whole-head pieces are few and large, prefers 64.  A launch
+// also keeps at least kMinLaunchGroups workgroups (a TP rank's share of a
+// checkpoint has few pieces; short launches pay their start and drain).
 constexpr int kMovePairs = 16;
 constexpr int kQPackPairs = 64;
+constexpr int64_t kMinLaunchGroups = 32768;
 
 // Rows of a KDA head one piece moves: 32 rows make every unit segment a
 // whole 128-byte line (32 fp32).

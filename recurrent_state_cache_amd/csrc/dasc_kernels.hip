@@ -1591,10 +1591,13 @@ void launch_qmove_part(bool pack, const MoveArgs& args, hipStream_t s) {
   else qmove_kernel<false><<<grid, kThreads, 0, s>>>(args);
 }
 
-// The pairs of a call, `per` at a time: the index arrays advance, every
-// other argument stays.
+// The pairs of a call, `per` at a time (more when a launch of `per` pairs
+// would hold fewer than kMinLaunchGroups workgroups): the index arrays
+// advance, every other argument stays.
 template <typename F>
 int by_pairs(const MoveArgs& args, int per, F&& launch) {
+  const int64_t need = (kMinLaunchGroups + args.n_pieces - 1) / args.n_pieces;
+  if (need > per) per = need > args.n ? args.n : static_cast<int>(need);
   MoveArgs part = args;
   for (int32_t i = 0; i < args.n; i += per) {
     part.n = args.n - i < per ? args.n - i : per;

@@ -1,8 +1,9 @@
 """The benchmark's work accounting for the refresh with per-head Eq. 7
 windows, recounted from the oracle plan: head-token replays (each replayed
 head (l, h) of request r replays min(W_lh, n_r) tokens), flops (5 d_v d_k
-per replay) and algorithmic HBM bytes (the replayed tokens' k, v, gate
-logits and beta, plus the local columns written)."""
+per replay) and algorithmic HBM bytes (the replayed tokens' k, v, decays
+and beta, plus the write-back of every 32-channel row segment that holds a
+local column); and the CPU baseline's layer-pair sample."""
 import os
 import sys
 
@@ -31,21 +32,28 @@ def test_windowed_work_and_bytes_recounted_from_the_oracle(name):
     P = R.Plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max)
     O = oracle.build_plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max)
     Wn = np.array([0, 3, 9, 40])
-    ht = flops = nbytes = 0
-    for li, L in enumerate(O.layers):
-        kda = L.kind == oracle.KDA
-        for h in O.refreshed_heads(li):
-            w = O.head_window(li, int(h))
-            cols = int((~L.retained.reshape(L.n_heads, L.d_k)[h]).sum()) if kda else L.d_k
-            for n_r in Wn:
-                t = min(w, int(n_r))
-                ht += t
-                flops += 5 * L.d_v * L.d_k * t
-                nbytes += t * (2 * L.d_k + 2 * L.d_v + (2 * L.d_k if kda else 2) + 4)
-                nbytes += cols * L.d_v * 4
-    assert bench._windowed_work(P, Wn) == (flops, ht)
-    assert bench._windowed_bytes(P, Wn) == nbytes
-    assert ht > 0
+    for decay_bytes in (2, 4):
+        ht = flops = nbytes = 0
+        for li, L in enumerate(O.layers):
+            kda = L.kind == oracle.KDA
+            for h in O.refreshed_heads(li):
+                w = O.head_window(li, int(h))
+                if kda:
+                    loc = ~L.retained.reshape(L.n_heads, L.d_k)[h]
+                    # channels of the 32-channel row segments holding a local column
+                    cols = sum(min(32, L.d_k - c0) for c0 in range(0, L.d_k, 32)
+                               if loc[c0:c0 + 32].any())
+                else:
+                    cols = L.d_k
+                for n_r in Wn:
+                    t = min(w, int(n_r))
+                    ht += t
+                    flops += 5 * L.d_v * L.d_k * t
+                    nbytes += t * (2 * L.d_k + 2 * L.d_v + (L.d_k if kda else 1) * decay_bytes + 4)
+                    nbytes += cols * L.d_v * 4
+        assert bench._windowed_work(P, Wn) == (flops, ht)
+        assert bench._windowed_bytes(P, Wn, decay_bytes=decay_bytes) == nbytes
+        assert ht > 0
 
 
 def test_mover_bytes_recounted_from_the_oracle():
@@ -84,3 +92,18 @@ def test_mover_bytes_recounted_from_the_oracle():
     assert unpack == O.B_temp_rag + O.B_temp_dense + 2 * O.B_conv
     assert pack_q == read_q + q + 2 * O.B_conv
     assert unpack_q == q + O.B_temp_dense + 2 * O.B_conv
+
+
+def test_cpu_sample_layer_pairs_replay_the_full_plans_heads():
+    # The CPU baseline replays a pair of layers with a plan of those layers
+    # only: a unit's retention depends on its own parameters, so the pair
+    # plan replays exactly the heads (and windows) the full plan does.
+    cfg = W.mixed(n_ckpt=2, n_req=2)
+    O = oracle.build_plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max)
+    for j in (0, 5, 12):
+        sub = oracle.build_plan(cfg.layers[2 * j:2 * j + 2], cfg.a_s, cfg.eps, cfg.w_max)
+        for i in range(2):
+            heads = O.refreshed_heads(2 * j + i)
+            assert np.array_equal(sub.refreshed_heads(i), heads)
+            assert [sub.head_window(i, int(h)) for h in heads] == \
+                [O.head_window(2 * j + i, int(h)) for h in heads]
