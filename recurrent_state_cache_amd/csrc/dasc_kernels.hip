@@ -1195,6 +1195,36 @@ refresh_kernel(RefreshArgs a) {
       }
     }
   };
+  // The same with the next row of L^T loaded while the current one is
+  // applied (the chain no longer waits for LDS at every row); the compiler
+  // fence keeps it from hoisting every load, which would spill.  Used where
+  // registers allow (the chunk-loop kernels).
+  auto invert_prefetch = [&]() {
+    const int sc = lane & 15;
+    float run[kC];
+#pragma unroll
+    for (int t = 0; t < kC; ++t) run[t] = 0.f;
+    v4f rowv[2][kC / 4];
+#pragma unroll
+    for (int q = 0; q < kC / 4; ++q) rowv[0][q] = *reinterpret_cast<const v4f*>(&sh.LT[0][4 * q]);
+#pragma unroll
+    for (int u = 0; u < kC; ++u) {
+      if (u + 1 < kC - 1) {
+#pragma unroll
+        for (int q = (u + 2) / 4; q < kC / 4; ++q)
+          rowv[(u + 1) & 1][q] = *reinterpret_cast<const v4f*>(&sh.LT[u + 1][4 * q]);
+      }
+      const float tu = (u == sc ? 1.f : 0.f) - run[u];
+#pragma unroll
+      for (int q = (u + 1) / 4; q < kC / 4; ++q) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * q + e > u) run[4 * q + e] = fmaf(rowv[u & 1][q][e], tu, run[4 * q + e]);
+      }
+      sh.T[u][sc] = tu;
+      __asm__ volatile("" ::: "memory");
+    }
+  };
 
   v4f acc[KT][VTW];
 #pragma unroll
@@ -1225,7 +1255,10 @@ refresh_kernel(RefreshArgs a) {
     for (int64_t n = 0; n < nchunks; ++n) {
       const int cb = ONE ? 0 : static_cast<int>(n & 1), nb = cb ^ 1;
       // ---- phase 1: T(n), U0 = S Q(n)  ||  stage chunk n + 1, fetch n + 2
-      if (wave == static_cast<int>(n % Sh::kNW)) invert();  // one wave, rotating
+      if (wave == static_cast<int>(n % Sh::kNW)) {  // one wave, rotating
+        if constexpr (ONE) invert();
+        else invert_prefetch();
+      }
       v4f U[VTW];
 #pragma unroll
       for (int vv = 0; vv < VTW; ++vv) U[vv] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -1390,26 +1423,42 @@ refresh_kernel(RefreshArgs a) {
             y[kt][vv];
     return;
   }
+  // The local columns are strided in the row-major state.  Each wave stages
+  // one 16-row tile at a time in LDS (the staging buffers are dead by now)
+  // and writes it row by row, lane c taking channel c (and c + 64): one
+  // store instruction covers 64 consecutive channels of a row (two 128-byte
+  // lines) with the local columns as its lane mask, where the tile layout
+  // would spread a masked store over 16 rows.
+  constexpr int RS = D + 4;  // padded LDS row
+  static_assert(sizeof(sh) >= sizeof(float) * Sh::kNW * 16 * RS, "write-back staging");
+  float* const stage = reinterpret_cast<float*>(&sh) + wave * 16 * RS;
+  bool mine[(D + 63) / 64];
 #pragma unroll
-  for (int kt = 0; kt < KT; ++kt) {
-    const int k0 = 16 * kt + 4 * g;
-    const uint32_t lw = k0 < 32 ? task.local[0] : k0 < 64 ? task.local[1]
-                      : k0 < 96 ? task.local[2] : task.local[3];
-    const uint32_t m4 = (lw >> (k0 & 31)) & 0xFu;
-#pragma unroll
-    for (int vv = 0; vv < VTW; ++vv) {
-      const int v = 16 * (wave * VTW + vv) + m;
-      float* row = out + v * D + k0;
-      const v4f x = acc[kt][vv];
-      if (m4 == 0xFu) {
-        *reinterpret_cast<v4f*>(row) = x;
-      } else if (m4) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if ((m4 >> r) & 1u) row[r] = x[r];
-      }
-    }
+  for (int hc = 0; hc < (D + 63) / 64; ++hc) {
+    const int c = 64 * hc + lane;
+    const int w = c >> 5;  // selects, not an index: task stays in registers
+    const uint32_t lw = w == 0 ? task.local[0] : w == 1 ? task.local[1]
+                      : w == 2 ? task.local[2] : task.local[3];
+    mine[hc] = c < D && ((lw >> (c & 31)) & 1u);
   }
+  auto write_tile = [&](auto vv_c) __attribute__((always_inline)) {
+    constexpr int vv = decltype(vv_c)::value;  // a constant: acc stays in registers
+    __syncthreads();  // the previous tile's rows (or the last chunk's operands) are read
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+      *reinterpret_cast<v4f*>(&stage[m * RS + 16 * kt + 4 * g]) = acc[kt][vv];
+    __syncthreads();
+    float* const rows = out + 16 * (wave * VTW + vv) * D;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+#pragma unroll
+      for (int hc = 0; hc < (D + 63) / 64; ++hc)
+        if (mine[hc]) rows[r * D + 64 * hc + lane] = stage[r * RS + 64 * hc + lane];
+    }
+  };
+  write_tile(IntC<0>{});
+  if constexpr (VTW > 1) write_tile(IntC<1>{});
+  static_assert(VTW <= 2, "v tiles per wave");
 }
 
 // ---------------------------------------------------------------------------
