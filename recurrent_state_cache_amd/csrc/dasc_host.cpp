@@ -264,8 +264,43 @@ void build_tables(dasc_plan* p) {
   push_range(p->unpack, I.temporal_dense_bytes, I.temporal_rag_bytes, I.conv_bytes, kPieceCopy);
 
   // INT8 pieces ([dasc] Appendix E.1 Eq. 10): pack quantizes each head with a
-  // retained unit whole; unpack dequantizes GDN heads by row blocks and KDA
-  // heads whole, and clears omitted heads as above.
+  // retained unit, d = 128 heads as 32-column blocks (a column's scale spans
+  // its rows, so a block holds whole columns) and other heads whole; unpack
+  // dequantizes GDN heads by row blocks and KDA heads whole, and clears
+  // omitted heads as above.
+  // Heads of d = 128 packed as 32-column blocks, in groups of 8 heads: a
+  // group takes 32 list positions starting at a multiple of 8, head h's
+  // block cb at position 8 cb + h, so that, workgroups being dealt to the 8
+  // XCDs in turn, a head's four blocks run on one XCD and its L2 merges the
+  // blocks' parts of shared 128-byte lines into whole lines (a GDN head's
+  // int8 rows, a KDA head's run of scales).  Nop pieces fill the alignment,
+  // the missing heads of a last group and KDA blocks without a retained
+  // channel.  Measured INT8 pack: GDN workload 4.9 TB/s with whole heads,
+  // 3.8 TB/s with blocks in head order, 5.4-5.7 TB/s grouped; mixed 4.8
+  // TB/s whole GDN heads, 5.3-5.7 TB/s grouped.
+  std::vector<Piece> block_heads;
+  auto flush_blocks = [&]() {
+    Piece nop{};
+    nop.type = kPieceNop;
+    for (size_t g0 = 0; g0 < block_heads.size(); g0 += 8) {
+      while (p->pack_q.size() % 8) p->pack_q.push_back(nop);
+      const size_t nh = std::min<size_t>(8, block_heads.size() - g0);
+      for (uint32_t cb = 0; cb < 4; ++cb) {
+        for (size_t h = 0; h < 8; ++h) {
+          Piece u = h < nh ? block_heads[g0 + h] : nop;
+          const bool live = h < nh && (u.type == kPieceQGdn || u.mask[cb] != 0);
+          if (!live) {
+            p->pack_q.push_back(nop);
+            continue;
+          }
+          u.type = u.type == kPieceQGdn ? kPieceQGdnBlock : kPieceQKdaBlock;
+          u.bytes = cb;
+          p->pack_q.push_back(u);
+        }
+      }
+    }
+    block_heads.clear();
+  };
   for (const auto& L : p->layers) {
     const int64_t head_bytes = int64_t(L.d_v) * L.d_k * 4;
     const int row_blocks = (L.d_v + kQGdnRows - 1) / kQGdnRows;
@@ -296,7 +331,8 @@ void build_tables(dasc_plan* p) {
         t.type = kPieceQGdn;
         t.pool_off = L.q_off + j * L.d_v * L.d_k;
         t.scale_off = p->int8_scale_base + L.s_off + j * L.d_k * 4;
-        p->pack_q.push_back(t);
+        if (L.d_k == 128 && L.d_v == 128) block_heads.push_back(t);
+        else p->pack_q.push_back(t);
         for (int rb = 0; rb < row_blocks; ++rb) {
           t.rb = static_cast<uint16_t>(rb);
           p->unpack_q.push_back(t);
@@ -309,12 +345,7 @@ void build_tables(dasc_plan* p) {
         if (L.d_k == 128 && L.d_v == 128) {
           // pack: 32-channel column blocks with a retained channel (16 KiB
           // each) instead of the whole head
-          Piece u = t;
-          u.type = kPieceQKdaBlock;
-          for (uint32_t cb = 0; cb < 4; ++cb) {
-            u.bytes = cb;
-            if (t.mask[cb] != 0) p->pack_q.push_back(u);
-          }
+          block_heads.push_back(t);
         } else {
           p->pack_q.push_back(t);
         }
@@ -322,9 +353,16 @@ void build_tables(dasc_plan* p) {
       j += r;
     }
   }
+  flush_blocks();
   push_range(p->pack_q, I.temporal_dense_bytes, p->int8_conv_base, I.conv_bytes, kPieceCopy);
+  {
+    Piece nop{};
+    nop.type = kPieceNop;
+    while (p->pack_q.size() % 8) p->pack_q.push_back(nop);  // every pair starts on XCD 0
+  }
   p->int8_pack_blocks_only = std::all_of(p->pack_q.begin(), p->pack_q.end(), [](const Piece& t) {
-    return t.type == kPieceCopy || t.type == kPieceQKdaBlock;
+    return t.type == kPieceCopy || t.type == kPieceQKdaBlock || t.type == kPieceQGdnBlock ||
+           t.type == kPieceNop;
   });
   push_range(p->unpack_q, I.temporal_dense_bytes, p->int8_conv_base, I.conv_bytes, kPieceCopy);
 

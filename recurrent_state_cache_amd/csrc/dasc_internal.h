@@ -31,6 +31,13 @@ constexpr uint32_t kPieceKdaBlock = 5;
 // in the piece's `bytes` field), all rows (16 KiB), for a block with >= 1
 // retained channel; a column's scale spans the rows, so the block is whole
 constexpr uint32_t kPieceQKdaBlock = 6;
+// INT8 pack of a d_k = d_v = 128 GDN head: the 32 columns from 32 cb on (cb
+// in the piece's `bytes` field), all rows (16 KiB); the head's four blocks
+// run on one XCD (the INT8 pack list places them so), whose L2 merges their
+// quarters of each 128-byte int8 row into whole lines
+constexpr uint32_t kPieceQGdnBlock = 7;
+// A piece that moves nothing (keeps the XCD order of an INT8 pack list)
+constexpr uint32_t kPieceNop = 8;
 
 // Largest byte range one copy / zero piece covers: 256 lanes x 16 B.  Small
 // pieces stream HBM markedly faster on MI355X than 64 KiB pieces do.

@@ -556,6 +556,58 @@ __device__ __forceinline__ void qpack_kda_block(const Piece& t, const uint8_t* s
               reinterpret_cast<u32x4*>(dst + t.pool_off + (base + j) * D + 16 * g));
 }
 
+// INT8 pack of a 32-column block of a d = 128 GDN head (all 128 rows, 16
+// KiB): lanes, loads and the column maxima as in qpack_kda_block.  The
+// unit is the head's int8 rows [d_v][d_k], so lane (v8, cg) writes the
+// codes of its 4 rows x 4 columns as four 4-byte words (8 lanes cover the
+// block's 32 bytes of a row) and, for v8 = 0, the scales of its columns.
+__device__ __forceinline__ void qpack_gdn_block(const Piece& t, const uint8_t* src, uint8_t* dst,
+                                                float (&red)[8][128]) {
+  constexpr int D = 128;
+  const int cb = static_cast<int>(t.bytes);
+  const int tid = threadIdx.x, v8 = tid >> 3, cg = tid & 7, wave = tid >> 6;
+  const float* S = reinterpret_cast<const float*>(src + t.dense_off) + 32 * cb + 4 * cg;
+  f32x4 x[4];
+  f32x4 mx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = ld_stream(reinterpret_cast<const f32x4*>(S + (4 * v8 + i) * D));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float m = fabsf(x[i][c]);
+      mx[c] = m > mx[c] ? m : mx[c];  // NaN entries never win
+    }
+  }
+#pragma unroll
+  for (int sh = 8; sh < 64; sh <<= 1) {  // the wave's 8 row lanes of this cg
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float o = __shfl_xor(mx[c], sh);
+      mx[c] = o > mx[c] ? o : mx[c];
+    }
+  }
+  if ((tid & 63) < 8) *reinterpret_cast<f32x4*>(&red[wave][4 * cg]) = mx;
+  __syncthreads();
+  f32x4 sc, inv;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float m = 0.f;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) m = red[w][4 * cg + c] > m ? red[w][4 * cg + c] : m;
+    sc[c] = (m > kScaleFloor ? m : kScaleFloor) / 127.f;  // correctly rounded fp32 division
+    inv[c] = 1.f / sc[c];
+  }
+  uint8_t* Q = dst + t.pool_off + 32 * cb + 4 * cg;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<uint32_t*>(Q + (4 * v8 + i) * D) = quant4(x[i], sc, inv);
+  if (v8 == 0) {
+    float* Sc = reinterpret_cast<float*>(dst + t.scale_off) + 32 * cb + 4 * cg;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) Sc[c] = sc[c];
+  }
+}
+
 // Unpack of kQGdnRows rows of a GDN head: lane (vl, kg) writes columns
 // 4 kg .. 4 kg + 3 of rows kQGdnRows rb + 8 i + vl (every store instruction
 // of the workgroup covers 8 consecutive rows); the int8 words are all loaded
@@ -654,8 +706,8 @@ __global__ void __launch_bounds__(kThreads) qmove_kernel(MoveArgs a) {
   const int64_t si = a.src_idx[blockIdx.y];
   const int64_t di = a.dst_idx[blockIdx.y];
   const bool bad_idx = !in_range(si, a.n_src) || !in_range(di, a.n_dst);
-  const bool valid = kBlocks ? (t.type == kPieceCopy || t.type == kPieceQKdaBlock)
-                             : (t.type <= kPieceQKda || (kPack && t.type == kPieceQKdaBlock));
+  const bool block = kPack && (t.type == kPieceQKdaBlock || t.type == kPieceQGdnBlock);
+  const bool valid = kBlocks ? (t.type == kPieceCopy || block) : (t.type <= kPieceQKda || block);
   if (bad_idx | !valid) {
     if (bad_idx && blockIdx.x == 0 && threadIdx.x == 0) flag(a.status, DASC_STATUS_BAD_INDEX);
     return;
@@ -667,9 +719,12 @@ __global__ void __launch_bounds__(kThreads) qmove_kernel(MoveArgs a) {
     return;
   }
   if constexpr (kBlocks) {
-    qpack_kda_block(t, src, dst, red, qbuf);
+    if (t.type == kPieceQGdnBlock) qpack_gdn_block(t, src, dst, red);
+    else qpack_kda_block(t, src, dst, red, qbuf);
   } else if constexpr (kPack) {
-    if (t.type == kPieceQKdaBlock)
+    if (t.type == kPieceQGdnBlock)
+      qpack_gdn_block(t, src, dst, red);
+    else if (t.type == kPieceQKdaBlock)
       qpack_kda_block(t, src, dst, red, qbuf);
     else if (t.type == kPieceQKda)
       qpack_kda_head(t, src, dst, red, qbuf);

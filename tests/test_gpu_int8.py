@@ -196,3 +196,28 @@ def test_int8_kda_column_blocks_full_empty_and_edges():
     g.manual_seed(29)
     dense = torch.randint(0, 256, (n, O.dense_bytes), dtype=torch.uint8, device="cuda", generator=g)
     _run(P, O, dense, n, list(range(n)), seed=29)
+
+
+def test_int8_grouped_column_blocks_partial_groups():
+    # d = 128 heads are packed as 32-column blocks in groups of 8 heads with
+    # nop fillers: GDN layers of 5 and 11 heads with a few retained (partial
+    # groups), a KDA layer whose blocks are full, empty or sparse, a d = 64
+    # GDN layer packed whole in between, and conv bytes; bit-exact.
+    f = np.float32
+    z = lambda n: np.zeros(n, f)
+    g5 = np.array([-4.0, 1.0, -4.0, -4.0, 1.0], f)        # heads 0, 2, 3 retained at W_max 64
+    g11 = np.where(np.arange(11) % 3 == 0, -4.0, 1.0).astype(f)
+    keep = np.zeros((3, 128), bool)
+    keep[0, :40] = True
+    keep[1, [5, 127]] = True
+    kd = np.where(keep, -4.0, 1.0).reshape(-1).astype(f)
+    layers = [W.Layer(W.GDN, 5, 128, 128, g5, z(5), 32),
+              W.Layer(W.KDA, 3, 128, 128, kd, z(384), 0),
+              W.Layer(W.GDN, 4, 64, 64, np.array([-4.0, -4.0, 1.0, -4.0], f), z(4), 16),
+              W.Layer(W.GDN, 11, 128, 128, g11, z(11), 48)]
+    cfg = W.Config("grouped", layers, w_max=64, seed=77)
+    P, O = _plans(cfg)
+    assert [int(L.retained.sum()) for L in O.layers] == [3, 42, 3, 4]
+    n = 5
+    dense = W.dense_states(cfg, n, device="cuda")
+    _run(P, O, dense, n, list(range(n)), seed=21)
