@@ -398,7 +398,7 @@ def _bench_tp(cfg, args, stream):
             for i in infos]
     out = [torch.empty_like(d) for d in dense]
     idx = torch.arange(n, dtype=torch.int32, device="cuda")
-    rounds, warm = max(1, min(args.steps, args.side_steps)), min(args.warmup, 2)
+    rounds, warm = max(1, min(args.steps, args.side_steps)), args.warmup
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(rounds)]
     for i in range(warm + rounds):
         e = ev[i - warm] if i >= warm else None
@@ -676,7 +676,7 @@ def _run_workload(name, args, stream, ex=None, n_workers=0):
     t_unpack = np.array([e[1].elapsed_time(e[2]) for e in ev]).mean() * 1e-3
     t_ref = np.array([e[2].elapsed_time(e[3]) for e in ev]).mean() * 1e-3
 
-    rounds, warm = max(1, min(args.steps, args.side_steps)), min(args.warmup, 2)
+    rounds, warm = max(1, min(args.steps, args.side_steps)), args.warmup
     # INT8 checkpoints (Eq. 10): pack and unpack of the same checkpoints.
     pool_q = torch.empty((n, info["int8_slot_bytes"]), dtype=torch.uint8, device="cuda")
     t_pack_q, t_unpack_q = _timed(
