@@ -1534,9 +1534,12 @@ recurrent_kernel(RefreshArgs a) {
   constexpr int B = D / 16;
   constexpr int JB = D / 8;
   constexpr bool kChan = GATE != kGateHead;
-  __shared__ __attribute__((aligned(16))) float sK[kC][D];
-  __shared__ __attribute__((aligned(16))) float sA[kC][D];
-  __shared__ __attribute__((aligned(16))) float sV[kC][D];
+  // k, decays and v of a batch of tokens; the write-back stages rows of the
+  // state in the same memory
+  __shared__ __attribute__((aligned(16))) float sKAV[3][kC][D];
+  float(*const sK)[D] = sKAV[0];
+  float(*const sA)[D] = sKAV[1];
+  float(*const sV)[D] = sKAV[2];
   __shared__ float sB[kC];
   __shared__ float sPA[D], sPD[D];
 
@@ -1628,28 +1631,34 @@ recurrent_kernel(RefreshArgs a) {
     }
   }
 
-  // the local columns of the head ([dasc] §4.2): 16-byte stores where four
-  // consecutive columns are all local
+  // The local columns of the head ([dasc] §4.2), as in the chunked kernel:
+  // RP rows at a time staged in LDS, then stored row by row, lane t taking
+  // channel t % D, so that one store instruction covers consecutive
+  // channels of a row with the local columns as its lane mask.
   float* out = reinterpret_cast<float*>(a.dense + dst * a.dense_stride + task.dense_off);
+  constexpr int RS = D + 4, RP = D < 32 ? D : 32;
+  static_assert(RP * RS <= 3 * kC * D && kThreads % D == 0, "write-back staging");
+  float* const stage = &sKAV[0][0][0];
+  const int ch = tid % D;
+  const int w = ch >> 5;  // selects, not an index: task stays in registers
+  const uint32_t lw = w == 0 ? task.local[0] : w == 1 ? task.local[1]
+                    : w == 2 ? task.local[2] : task.local[3];
+  const bool mine = (lw >> (ch & 31)) & 1u;
 #pragma unroll
-  for (int c4 = 0; c4 < B; c4 += 4) {
-    constexpr int G = B < 4 ? B : 4;  // columns per group
-    const int k0 = c0 + c4;
-    const uint32_t lw = k0 < 32 ? task.local[0] : k0 < 64 ? task.local[1]
-                      : k0 < 96 ? task.local[2] : task.local[3];
-    const uint32_t m = (lw >> (k0 & 31)) & ((1u << G) - 1u);
-    if (G == 4 && m == 0xFu) {
+  for (int p0 = 0; p0 < D; p0 += RP) {
+    __syncthreads();  // the last batch's reads, or the previous rows' stores
+    if (r0 >= p0 && r0 < p0 + RP) {
 #pragma unroll
       for (int r = 0; r < B; ++r)
-        *reinterpret_cast<v4f*>(out + (r0 + r) * D + k0) =
-            v4f{S[r][c4], S[r][c4 + G / 4], S[r][c4 + 2 * (G / 4)], S[r][c4 + 3 * (G / 4)]};
-    } else if (m) {
 #pragma unroll
-      for (int c = 0; c < G; ++c)
-        if ((m >> c) & 1u) {
+        for (int c = 0; c < B; ++c) stage[(r0 - p0 + r) * RS + c0 + c] = S[r][c];
+    }
+    __syncthreads();
+    static_assert((RP * D) % kThreads == 0, "whole store rounds");
 #pragma unroll
-          for (int r = 0; r < B; ++r) out[(r0 + r) * D + k0 + c] = S[r][c4 + c];
-        }
+    for (int j = 0; j < RP * D / kThreads; ++j) {
+      const int row = (tid + j * kThreads) / D;
+      if (mine) out[(p0 + row) * D + ch] = stage[row * RS + ch];
     }
   }
 }

@@ -349,28 +349,44 @@ def test_fused_load_equals_unpack_then_refresh(head_windows):
         _fused_vs_two_step(cfg, P, len(windows), windows, seed, head_windows)
 
 
-def test_fused_load_against_the_oracle():
-    cfg = W.tiny_kda()
+@pytest.mark.parametrize("name,head_windows", [("tiny_kda", False), ("kda", False),
+                                               ("kda", True), ("mixed", True)])
+def test_fused_load_against_the_oracle(name, head_windows):
+    # The fused dasc-wr load against the oracle itself (zero-fill unpack of
+    # the slot, then the refresh over the request's tokens): retained units
+    # and conv bytes bit-exact, the refreshed local units within the
+    # tolerance; d = 128 KDA and GDN heads on the full-size layers, layers
+    # sampled.
+    if name == "tiny_kda":
+        cfg, windows, layers = W.tiny_kda(), [8, 5], None
+    elif name == "kda":
+        cfg, windows, layers = W.kda_refresh(n_req=2), [256, 37], [0, 13]
+    else:
+        cfg, windows, layers = W.mixed(n_ckpt=4, n_req=2), [300, 64], [0, 1, 26]
     P, O = _plans(cfg)
-    inp, pool, src_slot, dst, out = _fused_vs_two_step(cfg, P, 2, [8, 5], 7, False)
+    inp, pool, src_slot, dst, out = _fused_vs_two_step(cfg, P, 2, windows, 7, head_windows)
     tok = inp.tok_off.cpu().numpy()
-    host_pool = pool.cpu().numpy()
+    mask = mask_words(O)
+    worst = 0.0
     for r in range(2):
         d, sl = int(dst[r]), int(src_slot[r])
         exp = np.full((1, O.dense_bytes), 0xEE, np.uint8)
-        oracle.unpack_zero_fill(O, host_pool, [sl], exp, [0])
+        oracle.unpack_zero_fill(O, pool[sl:sl + 1].cpu().numpy(), [0], exp, [0])
         got = out[d].cpu().numpy()
-        mask = mask_words(O)
         assert np.array_equal(got.view(np.uint32) & mask, exp[0].view(np.uint32) & mask)
         t0, t1 = int(tok[r]), int(tok[r + 1])
         ref = oracle.refresh_expected(O, _bits16(_host_rows(inp.k, (t0, t1))),
                                       _bits16(_host_rows(inp.v, (t0, t1))),
                                       _bits16(_host_rows(inp.a, (t0, t1))),
                                       _host_rows(inp.beta, (t0, t1)).numpy(),
-                                      np.array([0, t1 - t0]))
+                                      np.array([0, t1 - t0]), layers=layers,
+                                      head_windows=head_windows)
         for (_, li, h), S64 in ref.items():
             local = local_mask_of_head(O, li, h)
-            assert refresh_error(head_state(got, O, li, h), S64, local) <= TOL
+            err = refresh_error(head_state(got, O, li, h), S64, local)
+            worst = max(worst, err)
+            assert err <= TOL, f"{name} req {r} layer {li} head {h}: {err:.3e}"
+    log(f"[fused] {name} against the oracle: worst error {worst:.3e}")
 
 
 def test_fused_load_bad_slot_is_flagged():
