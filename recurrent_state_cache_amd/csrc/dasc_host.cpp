@@ -285,10 +285,12 @@ void build_tables(dasc_plan* p) {
     for (size_t g0 = 0; g0 < block_heads.size(); g0 += 8) {
       while (p->pack_q.size() % 8) p->pack_q.push_back(nop);
       const size_t nh = std::min<size_t>(8, block_heads.size() - g0);
-      for (uint32_t cb = 0; cb < 4; ++cb) {
+      for (uint32_t cb = 0; cb < 4; cb += kQPackBlocks) {
         for (size_t h = 0; h < 8; ++h) {
           Piece u = h < nh ? block_heads[g0 + h] : nop;
-          const bool live = h < nh && (u.type == kPieceQGdn || u.mask[cb] != 0);
+          bool any = false;
+          for (uint32_t b = cb; b < cb + kQPackBlocks; ++b) any = any || u.mask[b] != 0;
+          const bool live = h < nh && (u.type == kPieceQGdn || any);
           if (!live) {
             p->pack_q.push_back(nop);
             continue;

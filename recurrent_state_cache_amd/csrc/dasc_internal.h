@@ -38,6 +38,9 @@ constexpr uint32_t kPieceQKdaBlock = 6;
 constexpr uint32_t kPieceQGdnBlock = 7;
 // A piece that moves nothing (keeps the XCD order of an INT8 pack list)
 constexpr uint32_t kPieceNop = 8;
+// 32-column blocks one INT8 pack piece covers, their loads issued together
+// (1, 2 and 4 measured: 2 and 4 gave no gain, 4 held occupancy to half)
+constexpr int kQPackBlocks = 1;
 
 // Largest byte range one copy / zero piece covers: 256 lanes x 16 B.  Small
 // pieces stream HBM markedly faster on MI355X than 64 KiB pieces do.

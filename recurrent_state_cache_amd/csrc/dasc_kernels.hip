@@ -486,37 +486,35 @@ __device__ __forceinline__ void qpack_kda_head(const Piece& t, const uint8_t* sr
   }
 }
 
-// INT8 pack of a 32-channel column block of a d = 128 KDA head (all 128
-// rows, 16 KiB): lane (v8, cg), v8 = tid / 8, cg = tid % 8, holds rows
-// 4 v8 .. 4 v8 + 3 of channels 32 cb + 4 cg .. + 3 (one 16-byte load per
-// row; 8 lanes cover a 128-byte row segment).  The column maxima are
-// combined over the 8 row lanes of a wave by lane exchanges and over the 4
-// waves in LDS; each retained column's 4 bytes of the lane's rows go to its
-// unit row in LDS, and the block's units leave as 16-byte pieces.  Segment
-// j of the block is unit (retained channels below 32 cb) + j of the head.
-__device__ __forceinline__ void qpack_kda_block(const Piece& t, const uint8_t* src, uint8_t* dst,
-                                                float (&red)[8][128], uint8_t* qbuf) {
-  constexpr int D = 128;
-  const int cb = static_cast<int>(t.bytes);
-  const int tid = threadIdx.x, v8 = tid >> 3, cg = tid & 7, wave = tid >> 6;
-  uint32_t bits4 = 0, below = 0;
-  lane_ranks(t, 8 * cb + cg, bits4, below);
-  const int base = (cb > 0 ? __popc(t.mask[0]) : 0) + (cb > 1 ? __popc(t.mask[1]) : 0) +
-                   (cb > 2 ? __popc(t.mask[2]) : 0);
-  const uint32_t mc = cb == 0 ? t.mask[0] : cb == 1 ? t.mask[1] : cb == 2 ? t.mask[2] : t.mask[3];
-  const int rc = __popc(mc);
+// INT8 pack of 32-column blocks of d = 128 heads (all 128 rows, 16 KiB a
+// block): lane (v8, cg), v8 = tid / 8, cg = tid % 8, holds rows 4 v8 ..
+// 4 v8 + 3 of channels 32 cb + 4 cg .. + 3 (one 16-byte load per row; 8
+// lanes cover a 128-byte row segment).  The column maxima are combined over
+// the 8 row lanes of a wave by lane exchanges and over the 4 waves in LDS.
+// A piece covers kQPackBlocks consecutive blocks of one head; every
+// block's loads are issued before the first block is processed.
+constexpr int kQBlocks = kQPackBlocks;
+
+__device__ __forceinline__ void qblock_load(const Piece& t, const uint8_t* src, int cb,
+                                            f32x4 (&x)[4]) {
+  const int tid = threadIdx.x, v8 = tid >> 3, cg = tid & 7;
   const float* S = reinterpret_cast<const float*>(src + t.dense_off) + 32 * cb + 4 * cg;
-  f32x4 x[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = ld_stream(reinterpret_cast<const f32x4*>(S + (4 * v8 + i) * 128));
+}
+
+// Scales of the lane's four columns: s = max(a, 1e-8) / 127 and 1 / s.
+__device__ __forceinline__ void qblock_scales(const f32x4 (&x)[4], float (&red)[8][128], f32x4& sc,
+                                              f32x4& inv) {
+  const int tid = threadIdx.x, cg = tid & 7, wave = tid >> 6;
   f32x4 mx = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[i] = ld_stream(reinterpret_cast<const f32x4*>(S + (4 * v8 + i) * D));
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const float m = fabsf(x[i][c]);
       mx[c] = m > mx[c] ? m : mx[c];  // NaN entries never win
     }
-  }
 #pragma unroll
   for (int sh = 8; sh < 64; sh <<= 1) {  // the wave's 8 row lanes of this cg
 #pragma unroll
@@ -527,7 +525,6 @@ __device__ __forceinline__ void qpack_kda_block(const Piece& t, const uint8_t* s
   }
   if ((tid & 63) < 8) *reinterpret_cast<f32x4*>(&red[wave][4 * cg]) = mx;
   __syncthreads();
-  f32x4 sc, inv;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     float m = 0.f;
@@ -536,6 +533,25 @@ __device__ __forceinline__ void qpack_kda_block(const Piece& t, const uint8_t* s
     sc[c] = (m > kScaleFloor ? m : kScaleFloor) / 127.f;  // correctly rounded fp32 division
     inv[c] = 1.f / sc[c];
   }
+}
+
+// A KDA head's block: each retained column's 4 bytes of the lane's rows go
+// to its unit row in LDS, and the block's units leave as 16-byte pieces.
+// Segment j of the block is unit (retained channels below 32 cb) + j of the
+// head.
+__device__ __forceinline__ void qpack_kda_block(const Piece& t, uint8_t* dst, int cb,
+                                                const f32x4 (&x)[4], float (&red)[8][128],
+                                                uint8_t* qbuf) {
+  constexpr int D = 128;
+  const int tid = threadIdx.x, v8 = tid >> 3, cg = tid & 7;
+  uint32_t bits4 = 0, below = 0;
+  lane_ranks(t, 8 * cb + cg, bits4, below);
+  const int base = (cb > 0 ? __popc(t.mask[0]) : 0) + (cb > 1 ? __popc(t.mask[1]) : 0) +
+                   (cb > 2 ? __popc(t.mask[2]) : 0);
+  const uint32_t mc = cb == 0 ? t.mask[0] : cb == 1 ? t.mask[1] : cb == 2 ? t.mask[2] : t.mask[3];
+  const int rc = __popc(mc);
+  f32x4 sc, inv;
+  qblock_scales(x, red, sc, inv);
   const uint32_t w[4] = {quant4(x[0], sc, inv), quant4(x[1], sc, inv), quant4(x[2], sc, inv),
                          quant4(x[3], sc, inv)};
   uint32_t b[4];
@@ -556,47 +572,16 @@ __device__ __forceinline__ void qpack_kda_block(const Piece& t, const uint8_t* s
               reinterpret_cast<u32x4*>(dst + t.pool_off + (base + j) * D + 16 * g));
 }
 
-// INT8 pack of a 32-column block of a d = 128 GDN head (all 128 rows, 16
-// KiB): lanes, loads and the column maxima as in qpack_kda_block.  The
-// unit is the head's int8 rows [d_v][d_k], so lane (v8, cg) writes the
-// codes of its 4 rows x 4 columns as four 4-byte words (8 lanes cover the
-// block's 32 bytes of a row) and, for v8 = 0, the scales of its columns.
-__device__ __forceinline__ void qpack_gdn_block(const Piece& t, const uint8_t* src, uint8_t* dst,
-                                                float (&red)[8][128]) {
+// A GDN head's block.  The unit is the head's int8 rows [d_v][d_k], so lane
+// (v8, cg) writes the codes of its 4 rows x 4 columns as four 4-byte words
+// (8 lanes cover the block's 32 bytes of a row) and, for v8 = 0, the scales
+// of its columns.
+__device__ __forceinline__ void qpack_gdn_block(const Piece& t, uint8_t* dst, int cb,
+                                                const f32x4 (&x)[4], float (&red)[8][128]) {
   constexpr int D = 128;
-  const int cb = static_cast<int>(t.bytes);
-  const int tid = threadIdx.x, v8 = tid >> 3, cg = tid & 7, wave = tid >> 6;
-  const float* S = reinterpret_cast<const float*>(src + t.dense_off) + 32 * cb + 4 * cg;
-  f32x4 x[4];
-  f32x4 mx = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[i] = ld_stream(reinterpret_cast<const f32x4*>(S + (4 * v8 + i) * D));
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float m = fabsf(x[i][c]);
-      mx[c] = m > mx[c] ? m : mx[c];  // NaN entries never win
-    }
-  }
-#pragma unroll
-  for (int sh = 8; sh < 64; sh <<= 1) {  // the wave's 8 row lanes of this cg
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float o = __shfl_xor(mx[c], sh);
-      mx[c] = o > mx[c] ? o : mx[c];
-    }
-  }
-  if ((tid & 63) < 8) *reinterpret_cast<f32x4*>(&red[wave][4 * cg]) = mx;
-  __syncthreads();
+  const int tid = threadIdx.x, v8 = tid >> 3, cg = tid & 7;
   f32x4 sc, inv;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    float m = 0.f;
-#pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) m = red[w][4 * cg + c] > m ? red[w][4 * cg + c] : m;
-    sc[c] = (m > kScaleFloor ? m : kScaleFloor) / 127.f;  // correctly rounded fp32 division
-    inv[c] = 1.f / sc[c];
-  }
+  qblock_scales(x, red, sc, inv);
   uint8_t* Q = dst + t.pool_off + 32 * cb + 4 * cg;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -605,6 +590,29 @@ __device__ __forceinline__ void qpack_gdn_block(const Piece& t, const uint8_t* s
     float* Sc = reinterpret_cast<float*>(dst + t.scale_off) + 32 * cb + 4 * cg;
 #pragma unroll
     for (int c = 0; c < 4; ++c) Sc[c] = sc[c];
+  }
+}
+
+// The kQBlocks blocks cb0 .. of a piece (cb0 in the piece's `bytes`); a KDA
+// block without a retained channel is skipped (uniform per workgroup).
+__device__ __forceinline__ void qpack_blocks(const Piece& t, const uint8_t* src, uint8_t* dst,
+                                             float (&red)[8][128], uint8_t* qbuf) {
+  const int cb0 = static_cast<int>(t.bytes);
+  const bool gdn = t.type == kPieceQGdnBlock;
+  auto live = [&](int cb) {
+    const uint32_t mc = cb == 0 ? t.mask[0] : cb == 1 ? t.mask[1] : cb == 2 ? t.mask[2] : t.mask[3];
+    return gdn || mc != 0;
+  };
+  f32x4 x[kQBlocks][4];
+#pragma unroll
+  for (int b = 0; b < kQBlocks; ++b)
+    if (live(cb0 + b)) qblock_load(t, src, cb0 + b, x[b]);
+#pragma unroll
+  for (int b = 0; b < kQBlocks; ++b) {
+    if (!live(cb0 + b)) continue;
+    if (b > 0) __syncthreads();  // the previous block's reads of red and qbuf are done
+    if (gdn) qpack_gdn_block(t, dst, cb0 + b, x[b], red);
+    else qpack_kda_block(t, dst, cb0 + b, x[b], red, qbuf);
   }
 }
 
@@ -719,13 +727,10 @@ __global__ void __launch_bounds__(kThreads) qmove_kernel(MoveArgs a) {
     return;
   }
   if constexpr (kBlocks) {
-    if (t.type == kPieceQGdnBlock) qpack_gdn_block(t, src, dst, red);
-    else qpack_kda_block(t, src, dst, red, qbuf);
+    qpack_blocks(t, src, dst, red, qbuf);
   } else if constexpr (kPack) {
-    if (t.type == kPieceQGdnBlock)
-      qpack_gdn_block(t, src, dst, red);
-    else if (t.type == kPieceQKdaBlock)
-      qpack_kda_block(t, src, dst, red, qbuf);
+    if (t.type == kPieceQGdnBlock || t.type == kPieceQKdaBlock)
+      qpack_blocks(t, src, dst, red, qbuf);
     else if (t.type == kPieceQKda)
       qpack_kda_head(t, src, dst, red, qbuf);
     else
@@ -943,6 +948,7 @@ refresh_kernel(RefreshArgs a) {
   constexpr int KT = Sh::kKT, VTW = Sh::kVTW, JB = Sh::kJB, NB4 = Sh::kNB4;
   constexpr bool kAlpha = GATE >= kGateAlphaHead;  // decays given as fp32
   constexpr bool kChan = GATE != kGateHead && GATE != kGateAlphaHead;
+  constexpr bool kGram = !kChan && Sh::kSplit;  // GDN heads, d >= 64: L from the Gram matrix
   constexpr bool kAllStage = Sh::kNT == 2 * D;  // every lane stages an item
   __shared__ RefreshLds<D, ONE ? 1 : 2> sh;
 
@@ -1077,10 +1083,47 @@ refresh_kernel(RefreshArgs a) {
   // direction of the Q / W lanes are known to the compiler and the only
   // per-lane selects left are at the two entries where the half-waves'
   // rows differ; PW = -1: the same work with p and the direction per lane.
+  // L of a chunk of a GDN head (d >= 64), on wave 0: with one decay per
+  // head and token, L_{t,s} = beta_t D_{t,s} (k_t . k_s) with the scalar
+  // D_{t,s} = alpha_{s+1} ... alpha_t, and the keys are bf16 values, so the
+  // Gram matrix G = K K^T comes exact in its products from bf16 MFMA (fp32
+  // sums; one operand serves as A and B).  Lane (g, m) gets G[4 g + r][m]
+  // and makes L[t][s] for t = 4 g + r, s = m: the running product of the
+  // decays after s is captured at each of its rows t; entries with t <= s
+  // are stored as zeros (the inverse never reads them).
+  auto gram_L = [&](int vb) __attribute__((always_inline)) {
+    if (wave != 0) return;  // uniform
+    v4f G = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      const v4f a0 = *reinterpret_cast<const v4f*>(&sh.K[m][32 * kk + 8 * g]);
+      const v4f a1 = *reinterpret_cast<const v4f*>(&sh.K[m][32 * kk + 8 * g + 4]);
+      const u32x4 ka = {pack_bf16(__float_as_uint(a0[0]), __float_as_uint(a0[1])),
+                        pack_bf16(__float_as_uint(a0[2]), __float_as_uint(a0[3])),
+                        pack_bf16(__float_as_uint(a1[0]), __float_as_uint(a1[1])),
+                        pack_bf16(__float_as_uint(a1[2]), __float_as_uint(a1[3]))};
+      G = mfma_bf16(ka, ka, G);
+    }
+    float run = 1.f;
+    v4f dr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 1; u < kC; ++u) {
+      run *= u > m ? sh.A[u][0] : 1.f;  // D_{u,m} once u > m
+      if ((u >> 2) == g) dr[u & 3] = run;
+    }
+    const v4f b4 = *reinterpret_cast<const v4f*>(&sh.B[vb][4 * g]);
+    v4f l4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) l4[r] = 4 * g + r > m ? b4[r] * dr[r] * G[r] : 0.f;
+    *reinterpret_cast<v4f*>(&sh.LT[m][4 * g]) = l4;
+  };
+
   auto stage2_body = [&](int vb, auto pw_c) __attribute__((always_inline)) {
     constexpr int PW = decltype(pw_c)::value;
     static_assert(PW < 0 || (NB4 == 32 && kAllStage), "wave-uniform rows need d = 128");
+    if constexpr (kGram) gram_L(vb);
     if (kAllStage || tid < 2 * D) {
+     if constexpr (!kGram) {
       // L, rows p and 15 - p (15 entries in all), 4 channels per lane,
       // summed over the NB4 lanes of the row pair after the loop (so the
       // loop has no branch): for NB4 = 32 by a reduce-scatter that leaves
@@ -1155,6 +1198,7 @@ refresh_kernel(RefreshArgs a) {
 #pragma unroll
         for (int i = 0; i < kC - 1; ++i) *((in_row_p(i) ? lP : lQ) - i * (kC + 4)) = lv[i];
       }
+     }
       // gamma_t and Q (forward lanes, tid < D) or W (backward lanes)
       const int j = tid % D;
       const bool fwd = PW >= 0 ? PW < 2 : tid < D;
@@ -1711,6 +1755,9 @@ template <typename F>
 int by_pairs(const MoveArgs& args, int per, F&& launch) {
   const int64_t need = (kMinLaunchGroups + args.n_pieces - 1) / args.n_pieces;
   if (need > per) per = need > args.n ? args.n : static_cast<int>(need);
+  // launches of equal size (e.g. 64 pairs as 22 + 21 + 21, not 30 + 30 + 4)
+  const int launches = (args.n + per - 1) / per;
+  per = (args.n + launches - 1) / launches;
   MoveArgs part = args;
   for (int32_t i = 0; i < args.n; i += per) {
     part.n = args.n - i < per ? args.n - i : per;
