@@ -224,3 +224,37 @@ def test_alpha_rejects_misaligned_and_null_decays():
         R.ckpt_refresh_suffix_alpha(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, dense, dst)
     torch.cuda.synchronize()
     assert torch.equal(dense, before)
+
+
+@pytest.mark.parametrize("kind", [W.KDA, W.GDN])
+def test_alpha_recall_invariant(kind):
+    # beta = 1 and keys of exactly unit norm in bf16 (+-1/4 on 16 of 128
+    # coordinates): whatever the decays, the final state recalls the last
+    # value, S_W k_W = v_W ([dasc] §3.1 Eq. 1), independently of the oracle.
+    d, H, T = 128, 4, 40
+    n = H * d if kind == W.KDA else H
+    lay = W.Layer(kind, H, d, d, np.full(n, 2.0, np.float32), np.zeros(n, np.float32), 0)
+    cfg = W.Config("recall", [lay], w_max=64, seed=41)
+    P, O = _plans(cfg)
+    assert len(O.refreshed_heads(0)) == H
+    rng = np.random.default_rng(9)
+    k = np.zeros((T, H, d), np.float32)
+    for t in range(T):
+        for h in range(H):
+            idx = rng.choice(d, 16, replace=False)
+            k[t, h, idx] = rng.choice([-0.25, 0.25], 16)
+    kt = torch.from_numpy(k.reshape(T, H * d)).to(torch.bfloat16).cuda()
+    vt = torch.randn(T, H * d).to(torch.bfloat16).cuda()
+    alpha = W.refresh_decays(cfg, T, device="cuda")
+    bt = torch.ones(T, H, dtype=torch.float32, device="cuda")
+    dense = torch.zeros((1, O.dense_bytes), dtype=torch.uint8, device="cuda")
+    R.ckpt_refresh_suffix_alpha(P, kt, vt, alpha, bt, torch.tensor([0, T], device="cuda"),
+                                dense, torch.zeros(1, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert P.status() == 0
+    row = dense[0].cpu().numpy()
+    for h in range(H):
+        S = head_state(row, O, 0, h).astype(np.float64)
+        vlast = vt[-1, h * d:(h + 1) * d].float().cpu().numpy()
+        recall = S @ k[-1, h].astype(np.float64)
+        assert np.max(np.abs(recall - vlast)) <= 1e-5 * max(1.0, np.linalg.norm(vlast))
