@@ -326,6 +326,40 @@ __device__ __forceinline__ uint32_t quant4(f32x4 x, f32x4 s, f32x4 inv) {
   return lo | hi;
 }
 
+// quant4 for the 16 entries of a lane's 4 rows x 4 columns, with one
+// branch for the whole set: the products are rounded first, and only if
+// any of them lies within the guard of a half-integer are those entries
+// redone by division (the same codes as quant4).
+__device__ __forceinline__ void quant16(const f32x4 (&x)[4], f32x4 s, f32x4 inv, uint32_t (&w)[4]) {
+  float r[4][4];
+  bool near = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float y = x[i][c] * inv[c];
+      r[i][c] = rintf(y);
+      near |= fabsf(y - r[i][c]) > kHalfGuard;
+    }
+  if (__builtin_expect(near, 0)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (fabsf(x[i][c] * inv[c] - r[i][c]) > kHalfGuard) r[i][c] = rintf(x[i][c] / s[c]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t q[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      q[c] = r[i][c] != r[i][c] ? 0u : static_cast<uint32_t>(static_cast<int32_t>(r[i][c]));
+    const uint32_t lo = __builtin_amdgcn_perm(q[1], q[0], 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(q[3], q[2], 0x04000c0cu);
+    w[i] = lo | hi;
+  }
+}
+
 __device__ __forceinline__ f32x4 dequant4(uint32_t w, f32x4 s) {
   f32x4 x;
 #pragma unroll
@@ -525,14 +559,21 @@ __device__ __forceinline__ void qblock_scales(const f32x4 (&x)[4], float (&red)[
   }
   if ((tid & 63) < 8) *reinterpret_cast<f32x4*>(&red[wave][4 * cg]) = mx;
   __syncthreads();
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  // One lane per column (lanes 0 .. 31 of wave 0) combines the 4 waves'
+  // maxima and divides once; every lane reads its columns' scale and
+  // reciprocal back (the divisions are most of the block's arithmetic
+  // when every lane repeats them).
+  if (tid < 32) {
     float m = 0.f;
 #pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) m = red[w][4 * cg + c] > m ? red[w][4 * cg + c] : m;
-    sc[c] = (m > kScaleFloor ? m : kScaleFloor) / 127.f;  // correctly rounded fp32 division
-    inv[c] = 1.f / sc[c];
+    for (int w = 0; w < kThreads / 64; ++w) m = red[w][tid] > m ? red[w][tid] : m;
+    const float s = (m > kScaleFloor ? m : kScaleFloor) / 127.f;  // correctly rounded fp32 division
+    red[4][tid] = s;
+    red[5][tid] = 1.f / s;
   }
+  __syncthreads();
+  sc = *reinterpret_cast<const f32x4*>(&red[4][4 * cg]);
+  inv = *reinterpret_cast<const f32x4*>(&red[5][4 * cg]);
 }
 
 // A KDA head's block: each retained column's 4 bytes of the lane's rows go
@@ -552,8 +593,8 @@ __device__ __forceinline__ void qpack_kda_block(const Piece& t, uint8_t* dst, in
   const int rc = __popc(mc);
   f32x4 sc, inv;
   qblock_scales(x, red, sc, inv);
-  const uint32_t w[4] = {quant4(x[0], sc, inv), quant4(x[1], sc, inv), quant4(x[2], sc, inv),
-                         quant4(x[3], sc, inv)};
+  uint32_t w[4];
+  quant16(x, sc, inv, w);
   uint32_t b[4];
   transpose4(w, b);  // b[c]: column c, rows 4 v8 .. 4 v8 + 3
   uint32_t rk = below - base;
@@ -583,9 +624,10 @@ __device__ __forceinline__ void qpack_gdn_block(const Piece& t, uint8_t* dst, in
   f32x4 sc, inv;
   qblock_scales(x, red, sc, inv);
   uint8_t* Q = dst + t.pool_off + 32 * cb + 4 * cg;
+  uint32_t w[4];
+  quant16(x, sc, inv, w);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *reinterpret_cast<uint32_t*>(Q + (4 * v8 + i) * D) = quant4(x[i], sc, inv);
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(Q + (4 * v8 + i) * D) = w[i];
   if (v8 == 0) {
     float* Sc = reinterpret_cast<float*>(dst + t.scale_off) + 32 * cb + 4 * cg;
 #pragma unroll
