@@ -268,41 +268,14 @@ void build_tables(dasc_plan* p) {
   // its rows, so a block holds whole columns) and other heads whole; unpack
   // dequantizes GDN heads by row blocks and KDA heads whole, and clears
   // omitted heads as above.
-  // Heads of d = 128 packed as 32-column blocks, in groups of 8 heads: a
-  // group takes 32 list positions starting at a multiple of 8, head h's
-  // block cb at position 8 cb + h, so that, workgroups being dealt to the 8
-  // XCDs in turn, a head's four blocks run on one XCD and its L2 merges the
-  // blocks' parts of shared 128-byte lines into whole lines (a GDN head's
-  // int8 rows, a KDA head's run of scales).  Nop pieces fill the alignment,
-  // the missing heads of a last group and KDA blocks without a retained
-  // channel.  Measured INT8 pack: GDN workload 4.9 TB/s with whole heads,
-  // 3.8 TB/s with blocks in head order, 5.4-5.7 TB/s grouped; mixed 4.8
-  // TB/s whole GDN heads, 5.3-5.7 TB/s grouped.
-  std::vector<Piece> block_heads;
-  auto flush_blocks = [&]() {
-    Piece nop{};
-    nop.type = kPieceNop;
-    for (size_t g0 = 0; g0 < block_heads.size(); g0 += 8) {
-      while (p->pack_q.size() % 8) p->pack_q.push_back(nop);
-      const size_t nh = std::min<size_t>(8, block_heads.size() - g0);
-      for (uint32_t cb = 0; cb < 4; cb += kQPackBlocks) {
-        for (size_t h = 0; h < 8; ++h) {
-          Piece u = h < nh ? block_heads[g0 + h] : nop;
-          bool any = false;
-          for (uint32_t b = cb; b < cb + kQPackBlocks; ++b) any = any || u.mask[b] != 0;
-          const bool live = h < nh && (u.type == kPieceQGdn || any);
-          if (!live) {
-            p->pack_q.push_back(nop);
-            continue;
-          }
-          u.type = u.type == kPieceQGdn ? kPieceQGdnBlock : kPieceQKdaBlock;
-          u.bytes = cb;
-          p->pack_q.push_back(u);
-        }
-      }
-    }
-    block_heads.clear();
-  };
+  // Heads of d = 128 are packed as four 32-column blocks (16 KiB each) that
+  // one workgroup loads together and quantizes in turn (kPieceQGdnBlock,
+  // kPieceQKdaBlock), writing the head's codes as whole lines.  Measured
+  // INT8 pack, GDN workload: 0.61 of the HBM peak as whole heads held in
+  // registers (126 VGPRs) with direct stores, 0.48 as one block a workgroup
+  // in head order (a head's int8 rows written from four XCDs), 0.63-0.70 as
+  // one block a workgroup with a head's four blocks placed on one XCD, 0.71
+  // as four blocks a workgroup staged through LDS.
   for (const auto& L : p->layers) {
     const int64_t head_bytes = int64_t(L.d_v) * L.d_k * 4;
     const int row_blocks = (L.d_v + kQGdnRows - 1) / kQGdnRows;
@@ -333,8 +306,9 @@ void build_tables(dasc_plan* p) {
         t.type = kPieceQGdn;
         t.pool_off = L.q_off + j * L.d_v * L.d_k;
         t.scale_off = p->int8_scale_base + L.s_off + j * L.d_k * 4;
-        if (L.d_k == 128 && L.d_v == 128) block_heads.push_back(t);
-        else p->pack_q.push_back(t);
+        Piece b = t;
+        if (L.d_k == 128 && L.d_v == 128) b.type = kPieceQGdnBlock;
+        p->pack_q.push_back(b);
         for (int rb = 0; rb < row_blocks; ++rb) {
           t.rb = static_cast<uint16_t>(rb);
           p->unpack_q.push_back(t);
@@ -344,27 +318,16 @@ void build_tables(dasc_plan* p) {
         t.pool_off = L.q_off + j * L.d_v;
         t.scale_off = p->int8_scale_base + L.s_off + j * 4;
         p->unpack_q.push_back(t);
-        if (L.d_k == 128 && L.d_v == 128) {
-          // pack: 32-channel column blocks with a retained channel (16 KiB
-          // each) instead of the whole head
-          block_heads.push_back(t);
-        } else {
-          p->pack_q.push_back(t);
-        }
+        Piece b = t;
+        if (L.d_k == 128 && L.d_v == 128) b.type = kPieceQKdaBlock;
+        p->pack_q.push_back(b);
       }
       j += r;
     }
   }
-  flush_blocks();
   push_range(p->pack_q, I.temporal_dense_bytes, p->int8_conv_base, I.conv_bytes, kPieceCopy);
-  {
-    Piece nop{};
-    nop.type = kPieceNop;
-    while (p->pack_q.size() % 8) p->pack_q.push_back(nop);  // every pair starts on XCD 0
-  }
   p->int8_pack_blocks_only = std::all_of(p->pack_q.begin(), p->pack_q.end(), [](const Piece& t) {
-    return t.type == kPieceCopy || t.type == kPieceQKdaBlock || t.type == kPieceQGdnBlock ||
-           t.type == kPieceNop;
+    return t.type == kPieceCopy || t.type == kPieceQKdaBlock || t.type == kPieceQGdnBlock;
   });
   push_range(p->unpack_q, I.temporal_dense_bytes, p->int8_conv_base, I.conv_bytes, kPieceCopy);
 

@@ -27,20 +27,15 @@ constexpr uint32_t kPieceQKda = 4;  // a KDA head with >= 1 retained channel
 // kKdaRows rb .. and channels 32 cb .. (cb in the piece's `bytes` field),
 // 4 KiB of the dense state, for a block with >= 1 retained channel
 constexpr uint32_t kPieceKdaBlock = 5;
-// INT8 pack of a d_k = d_v = 128 KDA head: the 32 channels from 32 cb on (cb
-// in the piece's `bytes` field), all rows (16 KiB), for a block with >= 1
-// retained channel; a column's scale spans the rows, so the block is whole
+// INT8 pack of a d_k = d_v = 128 KDA head with >= 1 retained channel, as
+// four 32-channel column blocks of all 128 rows (16 KiB each; a column's
+// scale spans the rows, so a block is whole), loaded together and quantized
+// in turn by one workgroup; blocks without a retained channel are skipped
 constexpr uint32_t kPieceQKdaBlock = 6;
-// INT8 pack of a d_k = d_v = 128 GDN head: the 32 columns from 32 cb on (cb
-// in the piece's `bytes` field), all rows (16 KiB); the head's four blocks
-// run on one XCD (the INT8 pack list places them so), whose L2 merges their
-// quarters of each 128-byte int8 row into whole lines
+// INT8 pack of a retained d_k = d_v = 128 GDN head, as four 32-column blocks
+// loaded together and quantized in turn by one workgroup, which writes the
+// head's int8 rows as whole lines
 constexpr uint32_t kPieceQGdnBlock = 7;
-// A piece that moves nothing (keeps the XCD order of an INT8 pack list)
-constexpr uint32_t kPieceNop = 8;
-// 32-column blocks one INT8 pack piece covers, their loads issued together
-// (1, 2 and 4 measured: 2 and 4 gave no gain, 4 held occupancy to half)
-constexpr int kQPackBlocks = 1;
 
 // Largest byte range one copy / zero piece covers: 256 lanes x 16 B.  Small
 // pieces stream HBM markedly faster on MI355X than 64 KiB pieces do.
@@ -159,7 +154,7 @@ struct MoveArgs {
   uint32_t n_pieces;
   int32_t kda_r_max;  // most unit segments a KDA piece stages (sizes the LDS); 0 if none
   bool kda_128;       // every KDA piece has d_k = d_v = 128
-  bool q_blocks;      // INT8 pack list of copy pieces and KDA column blocks only
+  bool q_blocks;      // INT8 pack list of copy pieces and d = 128 block heads only
   const int32_t* src_idx;
   const int32_t* dst_idx;
   const uint8_t* src_base;

@@ -73,6 +73,28 @@ __device__ __forceinline__ void st_stream(T v, T* p) {
 
 // Retained bits of channels 4 kg .. 4 kg + 3 (low 4 bits) and the number of
 // retained channels below 4 kg, from a head's 128-bit mask.
+// Piece i of a list, read through the constant address space: nothing in a
+// launch writes the list, so the words come in as scalar loads (a plain
+// load is otherwise made a vector load where the compiler cannot rule out
+// the launch's own stores).
+__device__ __forceinline__ Piece load_piece(const Piece* list, uint32_t i) {
+  using CWords = const __attribute__((address_space(4))) u32x4;
+  static_assert(sizeof(Piece) == 4 * sizeof(u32x4), "a piece is four 16-byte words");
+  CWords* w = (CWords*)(uintptr_t)list + 4 * static_cast<uint64_t>(i);
+  const u32x4 words[4] = {w[0], w[1], w[2], w[3]};
+  Piece t;
+  __builtin_memcpy(&t, words, sizeof(Piece));
+  return t;
+}
+
+// Word w (0..3) of a piece's channel mask, selected arithmetically: a chain
+// of selects over the four words is otherwise turned into an indexed load,
+// which puts a piece held in registers on the stack.
+__device__ __forceinline__ uint32_t mask_word(const Piece& t, int w) {
+  return (t.mask[0] & (0u - (w == 0))) | (t.mask[1] & (0u - (w == 1))) |
+         (t.mask[2] & (0u - (w == 2))) | (t.mask[3] & (0u - (w == 3)));
+}
+
 __device__ __forceinline__ void lane_ranks(const Piece& t, int kg, uint32_t& bits4,
                                            uint32_t& below) {
   const int k0 = 4 * kg, w = k0 >> 5, sh = k0 & 31;
@@ -525,16 +547,19 @@ __device__ __forceinline__ void qpack_kda_head(const Piece& t, const uint8_t* sr
 // 4 v8 + 3 of channels 32 cb + 4 cg .. + 3 (one 16-byte load per row; 8
 // lanes cover a 128-byte row segment).  The column maxima are combined over
 // the 8 row lanes of a wave by lane exchanges and over the 4 waves in LDS.
-// A piece covers kQPackBlocks consecutive blocks of one head; every
-// block's loads are issued before the first block is processed.
-constexpr int kQBlocks = kQPackBlocks;
-
-__device__ __forceinline__ void qblock_load(const Piece& t, const uint8_t* src, int cb,
-                                            f32x4 (&x)[4]) {
+//
+// The loads are buffer loads over the head's 64 KiB; a block that is not
+// packed (a KDA block without a retained channel) is given range 0, whose
+// loads return zeros without touching memory, so that every block issues
+// the same loads and the waits before a block's first use stay partial.
+__device__ __forceinline__ void qblock_load(const uint8_t* head, bool live, int cb, f32x4 (&x)[4]) {
   const int tid = threadIdx.x, v8 = tid >> 3, cg = tid & 7;
-  const float* S = reinterpret_cast<const float*>(src + t.dense_off) + 32 * cb + 4 * cg;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(head), 0, live ? 128 * 128 * 4 : 0, 0x00020000);
+  const int off = 128 * cb + 16 * cg + 4 * v8 * 512;  // row 4 v8, channel 32 cb + 4 cg
 #pragma unroll
-  for (int i = 0; i < 4; ++i) x[i] = ld_stream(reinterpret_cast<const f32x4*>(S + (4 * v8 + i) * 128));
+  for (int i = 0; i < 4; ++i)
+    x[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 512 * i, 0, 2));  // slc
 }
 
 // Scales of the lane's four columns: s = max(a, 1e-8) / 127 and 1 / s.
@@ -577,85 +602,88 @@ __device__ __forceinline__ void qblock_scales(const f32x4 (&x)[4], float (&red)[
 }
 
 // A KDA head's block: each retained column's 4 bytes of the lane's rows go
-// to its unit row in LDS, and the block's units leave as 16-byte pieces.
-// Segment j of the block is unit (retained channels below 32 cb) + j of the
-// head.
-__device__ __forceinline__ void qpack_kda_block(const Piece& t, uint8_t* dst, int cb,
-                                                const f32x4 (&x)[4], float (&red)[8][128],
-                                                uint8_t* qbuf) {
-  constexpr int D = 128;
+// to its unit row in LDS (qbuf) and its scale to qs.  Segment j of the block
+// is unit (retained channels below 32 cb) + j of the head.
+__device__ __forceinline__ void qpack_kda_block(const Piece& t, int cb, const f32x4 (&x)[4],
+                                                float (&red)[8][128], uint8_t* qbuf, float* qs) {
   const int tid = threadIdx.x, v8 = tid >> 3, cg = tid & 7;
   uint32_t bits4 = 0, below = 0;
   lane_ranks(t, 8 * cb + cg, bits4, below);
-  const int base = (cb > 0 ? __popc(t.mask[0]) : 0) + (cb > 1 ? __popc(t.mask[1]) : 0) +
-                   (cb > 2 ? __popc(t.mask[2]) : 0);
-  const uint32_t mc = cb == 0 ? t.mask[0] : cb == 1 ? t.mask[1] : cb == 2 ? t.mask[2] : t.mask[3];
-  const int rc = __popc(mc);
   f32x4 sc, inv;
   qblock_scales(x, red, sc, inv);
   uint32_t w[4];
   quant16(x, sc, inv, w);
   uint32_t b[4];
   transpose4(w, b);  // b[c]: column c, rows 4 v8 .. 4 v8 + 3
-  uint32_t rk = below - base;
+  uint32_t rk = below;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     if ((bits4 >> c) & 1u) {
       *reinterpret_cast<uint32_t*>(&qbuf[rk * kQStride + 4 * v8]) = b[c];
-      if (v8 == 0) reinterpret_cast<float*>(dst + t.scale_off)[base + rk] = sc[c];
+      if (v8 == 0) qs[rk] = sc[c];
       ++rk;
     }
   }
-  __syncthreads();
-  const int j = tid >> 3, g = tid & 7;  // unit j of the block, 16-byte piece g
-  if (j < rc)
-    st_stream(*reinterpret_cast<const u32x4*>(&qbuf[j * kQStride + 16 * g]),
-              reinterpret_cast<u32x4*>(dst + t.pool_off + (base + j) * D + 16 * g));
 }
 
-// A GDN head's block.  The unit is the head's int8 rows [d_v][d_k], so lane
-// (v8, cg) writes the codes of its 4 rows x 4 columns as four 4-byte words
-// (8 lanes cover the block's 32 bytes of a row) and, for v8 = 0, the scales
-// of its columns.
-__device__ __forceinline__ void qpack_gdn_block(const Piece& t, uint8_t* dst, int cb,
-                                                const f32x4 (&x)[4], float (&red)[8][128]) {
-  constexpr int D = 128;
+// A GDN head's block: the codes of the lane's 4 rows x 4 columns go to the
+// head's int8 rows in LDS (qbuf, row v at v kQStride), the scales of its
+// columns to qs.
+__device__ __forceinline__ void qpack_gdn_block(int cb, const f32x4 (&x)[4], float (&red)[8][128],
+                                                uint8_t* qbuf, float* qs) {
   const int tid = threadIdx.x, v8 = tid >> 3, cg = tid & 7;
   f32x4 sc, inv;
   qblock_scales(x, red, sc, inv);
-  uint8_t* Q = dst + t.pool_off + 32 * cb + 4 * cg;
   uint32_t w[4];
   quant16(x, sc, inv, w);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(Q + (4 * v8 + i) * D) = w[i];
-  if (v8 == 0) {
-    float* Sc = reinterpret_cast<float*>(dst + t.scale_off) + 32 * cb + 4 * cg;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) Sc[c] = sc[c];
-  }
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<uint32_t*>(&qbuf[(4 * v8 + i) * kQStride + 32 * cb + 4 * cg]) = w[i];
+  if (v8 == 0) *reinterpret_cast<f32x4*>(&qs[32 * cb + 4 * cg]) = sc;
 }
 
-// The kQBlocks blocks cb0 .. of a piece (cb0 in the piece's `bytes`); a KDA
-// block without a retained channel is skipped (uniform per workgroup).
-__device__ __forceinline__ void qpack_blocks(const Piece& t, const uint8_t* src, uint8_t* dst,
-                                             float (&red)[8][128], uint8_t* qbuf) {
-  const int cb0 = static_cast<int>(t.bytes);
+// A d = 128 head's four 32-column blocks: the loads of all four (the head's
+// 64 KiB) are issued first, then the blocks are reduced, scaled and
+// quantized one after the other (a barrier waits only for LDS traffic, so
+// the later blocks' loads stay in flight across the earlier blocks'
+// barriers).  The codes and scales collect in LDS and leave after the last
+// block as whole 128-byte lines: a store issued between the loads would
+// hold the next block's first use until the store completes (one counter
+// tracks loads and stores, in order), and one workgroup writing all of a
+// head's int8 rows needs no partial-line writes.  Measured INT8 pack rates
+// (GDN / mixed / KDA workloads, one box): 0.71 / 0.72 / 0.71 of the HBM peak
+// with all four blocks in flight (100 VGPRs, 4 workgroups a CU), 0.71 /
+// 0.70 / 0.67 with two blocks ahead of the one in hand, 0.70 / 0.67 / 0.66
+// with one, 0.63 / 0.65 / 0.67 as one block a workgroup (a head's blocks
+// placed on one XCD, stores after each block).  A KDA block without a
+// retained channel loads nothing and is skipped (uniform per workgroup).
+__device__ __forceinline__ void qpack_head_blocks(const Piece& t, const uint8_t* src, uint8_t* dst,
+                                                  float (&red)[8][128], uint8_t* qbuf, float* qs) {
+  constexpr int D = 128;
+  const int tid = threadIdx.x;
   const bool gdn = t.type == kPieceQGdnBlock;
-  auto live = [&](int cb) {
-    const uint32_t mc = cb == 0 ? t.mask[0] : cb == 1 ? t.mask[1] : cb == 2 ? t.mask[2] : t.mask[3];
-    return gdn || mc != 0;
-  };
-  f32x4 x[kQBlocks][4];
+  const uint8_t* head = src + t.dense_off;
+  f32x4 x[4][4];
 #pragma unroll
-  for (int b = 0; b < kQBlocks; ++b)
-    if (live(cb0 + b)) qblock_load(t, src, cb0 + b, x[b]);
+  for (int cb = 0; cb < 4; ++cb) qblock_load(head, gdn || mask_word(t, cb) != 0, cb, x[cb]);
 #pragma unroll
-  for (int b = 0; b < kQBlocks; ++b) {
-    if (!live(cb0 + b)) continue;
-    if (b > 0) __syncthreads();  // the previous block's reads of red and qbuf are done
-    if (gdn) qpack_gdn_block(t, dst, cb0 + b, x[b], red);
-    else qpack_kda_block(t, dst, cb0 + b, x[b], red, qbuf);
+  for (int cb = 0; cb < 4; ++cb) {
+    if (gdn) qpack_gdn_block(cb, x[cb], red, qbuf, qs);
+    else if (mask_word(t, cb) != 0) qpack_kda_block(t, cb, x[cb], red, qbuf, qs);
   }
+  __syncthreads();
+  // GDN: the head's d_v int8 rows; KDA: its r units.  Both are rows of 128
+  // bytes, 8 lanes to a row.
+  const int rows = gdn ? D : t.r;
+  uint8_t* U = dst + t.pool_off;
+#pragma unroll
+  for (int k = 0; k < D * 8 / kThreads; ++k) {
+    const int q = tid + k * kThreads, row = q >> 3, g = q & 7;
+    if (row < rows)
+      st_stream(*reinterpret_cast<const u32x4*>(&qbuf[row * kQStride + 16 * g]),
+                reinterpret_cast<u32x4*>(U + row * D + 16 * g));
+  }
+  if (tid < rows) reinterpret_cast<float*>(dst + t.scale_off)[tid] = qs[tid];  // GDN: 128 columns
 }
 
 // Unpack of kQGdnRows rows of a GDN head: lane (vl, kg) writes columns
@@ -750,9 +778,9 @@ template <bool kPack, bool kBlocks = false>
 __global__ void __launch_bounds__(kThreads) qmove_kernel(MoveArgs a) {
   static_assert(kPack || !kBlocks, "block lists are pack lists");
   __shared__ __attribute__((aligned(16))) float red[kPack ? 8 : 1][128];  // column maxima per row lane
-  __shared__ __attribute__((aligned(16))) uint8_t qbuf[(kBlocks ? 32 : 128) * kQStride];  // KDA units
-  __shared__ float qs[kPack ? 1 : 128];                                   // KDA scales (unpack)
-  const Piece t = a.pieces[blockIdx.x];
+  __shared__ __attribute__((aligned(16))) uint8_t qbuf[128 * kQStride];  // int8 rows / units
+  __shared__ __attribute__((aligned(16))) float qs[128];                 // scales
+  const Piece t = load_piece(a.pieces, blockIdx.x);
   const int64_t si = a.src_idx[blockIdx.y];
   const int64_t di = a.dst_idx[blockIdx.y];
   const bool bad_idx = !in_range(si, a.n_src) || !in_range(di, a.n_dst);
@@ -769,10 +797,10 @@ __global__ void __launch_bounds__(kThreads) qmove_kernel(MoveArgs a) {
     return;
   }
   if constexpr (kBlocks) {
-    qpack_blocks(t, src, dst, red, qbuf);
+    qpack_head_blocks(t, src, dst, red, qbuf, qs);
   } else if constexpr (kPack) {
     if (t.type == kPieceQGdnBlock || t.type == kPieceQKdaBlock)
-      qpack_blocks(t, src, dst, red, qbuf);
+      qpack_head_blocks(t, src, dst, red, qbuf, qs);
     else if (t.type == kPieceQKda)
       qpack_kda_head(t, src, dst, red, qbuf);
     else

@@ -183,8 +183,9 @@ def test_int8_rejects_unsupported_widths():
 
 
 def test_int8_kda_column_blocks_full_empty_and_edges():
-    # d = 128 KDA heads pack as 32-channel column blocks (the INT8 pack list
-    # then holds only blocks and copies); full, empty, sparse and edge blocks
+    # d = 128 KDA heads pack as four 32-channel column blocks in one
+    # workgroup (the INT8 pack list then holds only such heads and copies);
+    # full, empty, sparse and edge blocks
     from helpers import block_pattern_layers
     cfg = W.Config("blocks", block_pattern_layers(), w_max=64)
     P, O = _plans(cfg)
@@ -198,11 +199,12 @@ def test_int8_kda_column_blocks_full_empty_and_edges():
     _run(P, O, dense, n, list(range(n)), seed=29)
 
 
-def test_int8_grouped_column_blocks_partial_groups():
-    # d = 128 heads are packed as 32-column blocks in groups of 8 heads with
-    # nop fillers: GDN layers of 5 and 11 heads with a few retained (partial
-    # groups), a KDA layer whose blocks are full, empty or sparse, a d = 64
-    # GDN layer packed whole in between, and conv bytes; bit-exact.
+def test_int8_block_heads_beside_whole_heads():
+    # d = 128 heads pack as four 32-column blocks in one workgroup, other
+    # heads whole: GDN layers of 5 and 11 heads with a few retained, a KDA
+    # layer whose blocks are full, empty or sparse, a d = 64 GDN layer in
+    # between (so one list holds both kinds of piece), and conv bytes;
+    # bit-exact.
     f = np.float32
     z = lambda n: np.zeros(n, f)
     g5 = np.array([-4.0, 1.0, -4.0, -4.0, 1.0], f)        # heads 0, 2, 3 retained at W_max 64
@@ -215,7 +217,7 @@ def test_int8_grouped_column_blocks_partial_groups():
               W.Layer(W.KDA, 3, 128, 128, kd, z(384), 0),
               W.Layer(W.GDN, 4, 64, 64, np.array([-4.0, -4.0, 1.0, -4.0], f), z(4), 16),
               W.Layer(W.GDN, 11, 128, 128, g11, z(11), 48)]
-    cfg = W.Config("grouped", layers, w_max=64, seed=77)
+    cfg = W.Config("block_and_whole", layers, w_max=64, seed=77)
     P, O = _plans(cfg)
     assert [int(L.retained.sum()) for L in O.layers] == [3, 42, 3, 4]
     n = 5
