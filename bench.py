@@ -224,6 +224,32 @@ def _windowed_bytes(P, Wn, decay_bytes=2):
     return total
 
 
+def _windowed_sector_reads(P, Wn):
+    """HBM bytes the windowed refresh's write-back must also read: a store
+    that covers part of a 32-byte sector (8 fp32 channels of a row) costs
+    the memory a read of the sector, so every sector of a replayed head
+    that holds both local and retained channels is read once per row and
+    request (all-local heads, such as GDN heads, have none)."""
+    import numpy as np
+    total = 0
+    for l in range(P.info()["n_layers"]):
+        L = P.layer(l)
+        if L["kind"] == 0:
+            continue
+        ret, _, _ = P.units(l)
+        dk, dv = L["d_k"], L["d_v"]
+        local = ~ret.reshape(L["n_heads"], dk).astype(bool)
+        heads = local.any(axis=1)
+        nsec = (dk + 7) // 8
+        lc = np.zeros((int(heads.sum()), nsec * 8), bool)
+        rc = np.zeros_like(lc)
+        lc[:, :dk] = local[heads]
+        rc[:, :dk] = ~local[heads]
+        mixed = int((lc.reshape(-1, nsec, 8).any(axis=2) & rc.reshape(-1, nsec, 8).any(axis=2)).sum())
+        total += mixed * 32 * dv * len(Wn)
+    return total
+
+
 def _calibrate_copy(steps):
     import torch
     n = 1 << 30
@@ -699,6 +725,7 @@ def _run_workload(name, args, stream, ex=None, n_workers=0):
     win_flops, win_head_tokens = _windowed_work(P, Wn)
     win_bytes = _windowed_bytes(P, Wn, decay_bytes=4)
     win_bytes_gate = _windowed_bytes(P, Wn, decay_bytes=2)
+    win_sector_reads = _windowed_sector_reads(P, Wn)
 
     # dasc-wr load of the refreshed requests: unpack then refresh, against
     # the fused load (gate logits), with the full suffixes and with windows.
@@ -795,7 +822,10 @@ def _run_workload(name, args, stream, ex=None, n_workers=0):
             "roofline": {**mfma("refresh_windowed", win_flops, t_win, "refresh_kernel<.., true, ..>"),
                          "hbm_bytes": int(win_bytes),
                          "hbm_achieved_gbs": round(win_bytes / t_win / 1e9, 1),
-                         "hbm_frac": round(win_bytes / t_win / 1e9 / HBM_PEAK_GBS, 4)},
+                         "hbm_frac": round(win_bytes / t_win / 1e9 / HBM_PEAK_GBS, 4),
+                         "sector_read_bytes": int(win_sector_reads),
+                         "hbm_frac_with_sector_reads":
+                             round((win_bytes + win_sector_reads) / t_win / 1e9 / HBM_PEAK_GBS, 4)},
             "fused_gate_ms": round(t_win_gate * 1e3, 4),
             "fused_gate_hbm_frac": round(win_bytes_gate / t_win_gate / 1e9 / HBM_PEAK_GBS, 4),
             "fused_gate_traffic": traffic.get("refresh_windowed_gate"),

@@ -32,6 +32,18 @@ def test_windowed_work_and_bytes_recounted_from_the_oracle(name):
     P = R.Plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max)
     O = oracle.build_plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max)
     Wn = np.array([0, 3, 9, 40])
+    # sectors (8 channels of a row) of a replayed KDA head holding both a
+    # local and a retained channel, read once per row and request
+    reads = 0
+    for li, L in enumerate(O.layers):
+        if L.kind != oracle.KDA:
+            continue
+        for h in O.refreshed_heads(li):
+            loc = ~L.retained.reshape(L.n_heads, L.d_k)[h]
+            mixed = sum(1 for c0 in range(0, L.d_k, 8)
+                        if loc[c0:c0 + 8].any() and not loc[c0:c0 + 8].all())
+            reads += mixed * 32 * L.d_v * len(Wn)
+    assert bench._windowed_sector_reads(P, Wn) == reads
     for decay_bytes in (2, 4):
         ht = flops = nbytes = 0
         for li, L in enumerate(O.layers):
