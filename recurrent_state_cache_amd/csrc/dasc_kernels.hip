@@ -293,10 +293,10 @@ __global__ void __launch_bounds__(kThreads) move_kernel(MoveArgs a) {
 // `>` so that NaN entries are skipped; a NaN quotient stores 0.
 //
 // A column's scale spans all d_v rows, so a pack piece holds whole columns.
-// d = 128 KDA heads are packed as 32-channel column blocks of all rows
-// (qpack_kda_block below, 16 KiB per workgroup, in an instantiation of
-// their own when the list holds nothing else).  Other heads are whole
-// pieces: lane (vl, kg), kg = tid % 32, vl = tid / 32, holds columns
+// d = 128 heads are packed as four 32-column blocks of all rows that one
+// workgroup loads together and quantizes in turn (qpack_head_blocks below,
+// in an instantiation of its own when the list holds nothing else).  Other
+// heads are whole pieces: lane (vl, kg), kg = tid % 32, vl = tid / 32, holds columns
 // 4 kg .. 4 kg + 3 of the 16 consecutive rows 16 vl .. 16 vl + 15 in
 // registers; the column maxima are combined over the 8 row lanes in LDS.  A
 // GDN head writes its int8 rows directly (32 lanes cover a row) and its d_k
