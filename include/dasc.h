@@ -324,9 +324,10 @@ int dasc_ckpt_refresh_suffix_alpha(dasc_plan_t plan, const uint16_t* k, const ui
  * dasc_ckpt_refresh_suffix_alpha with per-head Eq. 7 windows ([dasc-sum]
  * "Methodology" Eq. 7, [dasc] §4.2): head (l, h) of request r replays only
  * the last min(W_lh, n_r) of the request's n_r tokens, W_lh being the
- * largest Eq. 7 window over the head's local units, as in
- * dasc_ckpt_refresh_suffix_windowed.  Same arguments, rules and errors as
- * dasc_ckpt_refresh_suffix_alpha.
+ * largest Eq. 7 window over the head's local units, and writes a head that
+ * also holds retained channels as whole rows, as
+ * dasc_ckpt_refresh_suffix_windowed does.  Same arguments, rules and errors
+ * as dasc_ckpt_refresh_suffix_alpha.
  */
 int dasc_ckpt_refresh_suffix_alpha_windowed(dasc_plan_t plan, const uint16_t* k,
                                             const uint16_t* v, const float* alpha,
@@ -361,7 +362,12 @@ int dasc_ckpt_refresh_suffix_recurrent(dasc_plan_t plan, const uint16_t* k, cons
  * couples its columns).  The caller passes the suffix for the model-wide
  * window (dasc_plan_info.w_replay, or any longer one); heads whose local
  * units have short horizons then skip the tokens they do not need.  Same
- * arguments, rules and errors as dasc_ckpt_refresh_suffix.
+ * arguments, rules and errors as dasc_ckpt_refresh_suffix, with one
+ * difference in how the result is written: a replayed KDA head that also
+ * holds retained channels is written as whole rows, its retained values read
+ * and written back unchanged (a partial write of a 32-byte sector costs the
+ * memory a read and a write anyway), so its retained bytes keep their
+ * values but no other work may write that head while the call runs.
  */
 int dasc_ckpt_refresh_suffix_windowed(dasc_plan_t plan, const uint16_t* k, const uint16_t* v,
                                       const uint16_t* a, const float* beta,
