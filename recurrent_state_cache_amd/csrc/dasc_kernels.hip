@@ -673,15 +673,27 @@ __device__ __forceinline__ void qpack_head_blocks(const Piece& t, const uint8_t*
   }
   __syncthreads();
   // GDN: the head's d_v int8 rows; KDA: its r units.  Both are rows of 128
-  // bytes, 8 lanes to a row.
+  // bytes, 8 lanes to a row in 16-byte pieces, or 32 lanes in 4-byte words
+  // where the payload offset is not 16-byte aligned (a layer before this one
+  // with d_v not a multiple of 16 leaves the INT8 payload 4-byte aligned).
   const int rows = gdn ? D : t.r;
   uint8_t* U = dst + t.pool_off;
+  if ((t.pool_off & 15u) == 0) {  // uniform
 #pragma unroll
-  for (int k = 0; k < D * 8 / kThreads; ++k) {
-    const int q = tid + k * kThreads, row = q >> 3, g = q & 7;
-    if (row < rows)
-      st_stream(*reinterpret_cast<const u32x4*>(&qbuf[row * kQStride + 16 * g]),
-                reinterpret_cast<u32x4*>(U + row * D + 16 * g));
+    for (int k = 0; k < D * 8 / kThreads; ++k) {
+      const int q = tid + k * kThreads, row = q >> 3, g = q & 7;
+      if (row < rows)
+        st_stream(*reinterpret_cast<const u32x4*>(&qbuf[row * kQStride + 16 * g]),
+                  reinterpret_cast<u32x4*>(U + row * D + 16 * g));
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < D * 32 / kThreads; ++k) {
+      const int q = tid + k * kThreads, row = q >> 5, w = q & 31;
+      if (row < rows)
+        *reinterpret_cast<uint32_t*>(U + row * D + 4 * w) =
+            *reinterpret_cast<const uint32_t*>(&qbuf[row * kQStride + 4 * w]);
+    }
   }
   if (tid < rows) reinterpret_cast<float*>(dst + t.scale_off)[tid] = qs[tid];  // GDN: 128 columns
 }

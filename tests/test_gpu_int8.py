@@ -199,12 +199,15 @@ def test_int8_kda_column_blocks_full_empty_and_edges():
     _run(P, O, dense, n, list(range(n)), seed=29)
 
 
-def test_int8_block_heads_beside_whole_heads():
+@pytest.mark.parametrize("unaligned", [False, True])
+def test_int8_block_heads_beside_whole_heads(unaligned):
     # d = 128 heads pack as four 32-column blocks in one workgroup, other
     # heads whole: GDN layers of 5 and 11 heads with a few retained, a KDA
     # layer whose blocks are full, empty or sparse, a d = 64 GDN layer in
     # between (so one list holds both kinds of piece), and conv bytes;
-    # bit-exact.
+    # bit-exact.  unaligned: a KDA layer of d_v = 4 with 3 retained channels
+    # in front leaves every later INT8 payload offset at 12 mod 16 (the
+    # block heads then store 4-byte words).
     f = np.float32
     z = lambda n: np.zeros(n, f)
     g5 = np.array([-4.0, 1.0, -4.0, -4.0, 1.0], f)        # heads 0, 2, 3 retained at W_max 64
@@ -217,9 +220,15 @@ def test_int8_block_heads_beside_whole_heads():
               W.Layer(W.KDA, 3, 128, 128, kd, z(384), 0),
               W.Layer(W.GDN, 4, 64, 64, np.array([-4.0, -4.0, 1.0, -4.0], f), z(4), 16),
               W.Layer(W.GDN, 11, 128, 128, g11, z(11), 48)]
+    if unaligned:
+        k8 = np.array([-4.0, -4.0, -4.0, 1.0, 1.0, 1.0, 1.0, 1.0], f)
+        layers = [W.Layer(W.KDA, 1, 8, 4, k8, z(8), 16)] + layers
     cfg = W.Config("block_and_whole", layers, w_max=64, seed=77)
     P, O = _plans(cfg)
-    assert [int(L.retained.sum()) for L in O.layers] == [3, 42, 3, 4]
+    kept = [int(L.retained.sum()) for L in O.layers]
+    assert kept == ([3] if unaligned else []) + [3, 42, 3, 4]
+    offs = [P.layer(l)["int8_pool_offset"] % 16 for l in range(len(layers))]
+    assert offs == ([0, 12, 12, 12, 12] if unaligned else [0, 0, 0, 0])
     n = 5
     dense = W.dense_states(cfg, n, device="cuda")
     _run(P, O, dense, n, list(range(n)), seed=21)
