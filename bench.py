@@ -119,8 +119,10 @@ def _algorithmic_bytes(P):
     (d = 128; the whole head for other widths) with a retained channel (a
     strided column forces whole 128-byte row segments), writes the ragged
     payload, and copies the conv bytes; unpack reads the payload and the conv
-    bytes and writes the whole dense checkpoint.  INT8 pack reads every KDA
-    head with a retained channel whole (a column's scale spans the head)."""
+    bytes and writes the whole dense checkpoint.  INT8 pack reads the same
+    (a column's scale spans the rows of its block, and a d = 128 head's
+    block without a retained channel is not read) and writes the int8
+    payload, the scales and the conv bytes."""
     info = P.info()
     read_pack = read_pack_q = 0
     for l in range(info["n_layers"]):
@@ -131,13 +133,14 @@ def _algorithmic_bytes(P):
             read_pack_q += int(ret.sum()) * L["unit_bytes"]
         else:
             per_head = ret.reshape(L["n_heads"], L["d_k"]).any(axis=1)
-            read_pack_q += int(per_head.sum()) * L["d_v"] * L["d_k"] * 4
             if L["d_k"] == 128 and L["d_v"] == 128:
-                # the fp32 pack reads 32-channel column blocks with a retained channel
+                # both packs read the 32-channel column blocks with a retained channel
                 per_block = ret.reshape(L["n_heads"], 4, 32).any(axis=2)
                 read_pack += int(per_block.sum()) * L["d_v"] * 32 * 4
+                read_pack_q += int(per_block.sum()) * L["d_v"] * 32 * 4
             else:
                 read_pack += int(per_head.sum()) * L["d_v"] * L["d_k"] * 4
+                read_pack_q += int(per_head.sum()) * L["d_v"] * L["d_k"] * 4
     pack = read_pack + info["temporal_rag_bytes"] + 2 * info["conv_bytes"]
     unpack = info["temporal_rag_bytes"] + info["temporal_dense_bytes"] + 2 * info["conv_bytes"]
     q = info["int8_payload_bytes"] + info["int8_scale_bytes"]

@@ -72,7 +72,7 @@ def test_mover_bytes_recounted_from_the_oracle():
     """pack reads every retained GDN head and, of a d = 128 KDA head, each
     32-channel block with a retained channel (whole heads at other widths),
     writes the ragged payload and copies conv; unpack reads the payload and
-    conv and writes the dense checkpoint; INT8 pack reads KDA heads whole."""
+    conv and writes the dense checkpoint; INT8 pack reads as pack does."""
     from helpers import block_pattern_layers
     rng = np.random.default_rng(5)
     f = np.float32
@@ -89,14 +89,16 @@ def test_mover_bytes_recounted_from_the_oracle():
             read_q += int(L.retained.sum()) * L.d_v * L.d_k * 4
             continue
         heads = L.retained.reshape(L.n_heads, L.d_k)
-        read_q += int(heads.any(axis=1).sum()) * L.d_v * L.d_k * 4
         if L.d_k == 128 and L.d_v == 128:
             for h in range(L.n_heads):
                 for b in range(4):
                     read += 128 * 32 * 4 if heads[h, 32 * b:32 * (b + 1)].any() else 0
         else:
             read += int(heads.any(axis=1).sum()) * L.d_v * L.d_k * 4
-    assert read < read_q  # the pattern has empty blocks in heads that are read
+    read_q = read
+    # the pattern has empty blocks in heads that are read
+    assert read < sum(int(L.retained.reshape(L.n_heads, -1).any(axis=1).sum()) * L.d_v * L.d_k * 4
+                      for L in O.layers)
     q = sum(int(L.retained.sum()) * (L.d_v * L.d_k if L.kind == oracle.GDN else L.d_v) for L in O.layers)
     q += sum(int(L.retained.sum()) * (L.d_k if L.kind == oracle.GDN else 1) * 4 for L in O.layers)
     pack, unpack, pack_q, unpack_q = bench._algorithmic_bytes(P)
