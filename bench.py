@@ -806,8 +806,8 @@ def _run_workload(name, args, stream, ex=None, n_workers=0):
         "int8": {
             "c_ckpt_int8": round(info["c_ckpt_int8"], 4),
             "pack_unpack_gbs": round(n * (pack_qb + unpack_qb) / (t_pack_q + t_unpack_q) / 1e9, 2),
-            "pack": hbm("pack_int8", n * pack_qb, t_pack_q, _launches(n, 64),
-                        "qmove_kernel<true, *> (64 pairs per launch)"),
+            "pack": hbm("pack_int8", n * pack_qb, t_pack_q, _launches(n, 32),
+                        "qmove_kernel<true, *> (32 pairs per launch)"),
             "unpack": hbm("unpack_int8", n * unpack_qb, t_unpack_q, _launches(n, 16),
                           "qmove_kernel<false> (16 pairs per launch)"),
         },

@@ -47,13 +47,16 @@ constexpr uint32_t kCopyChunk = 4096;
 // unpack: 5.76 TB/s as eight back-to-back launches of 64 pairs against 5.55
 // TB/s as one launch of 512, the same bytes and the same span of time, so
 // not a clock or power effect; 5.94-5.96 TB/s at 8-16 pairs); 16 is the
-// measured best for the fp32 movers and the INT8 unpack, while the INT8
-// pack, whose whole-head pieces are few and large, prefers 64.  A launch
-// also keeps at least kMinLaunchGroups workgroups (a TP rank's share of a
+// measured best for the fp32 movers and the INT8 unpack.  A launch also
+// keeps at least kMinLaunchGroups workgroups (a TP rank's share of a
 // checkpoint has few pieces; short launches pay their start and drain).
+// The INT8 pack, one workgroup per 64 KiB head, takes launches of 32 pairs
+// and at least kQPackMinGroups workgroups (0.5-1% ahead of 64 pairs and
+// 32768 workgroups, and of 16 pairs).
 constexpr int kMovePairs = 16;
-constexpr int kQPackPairs = 64;
+constexpr int kQPackPairs = 32;
 constexpr int64_t kMinLaunchGroups = 32768;
+constexpr int64_t kQPackMinGroups = 8192;
 
 // Rows of a KDA head one piece moves: 32 rows make every unit segment a
 // whole 128-byte line (32 fp32).

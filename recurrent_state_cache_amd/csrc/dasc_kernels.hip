@@ -1877,11 +1877,11 @@ void launch_qmove_part(bool pack, const MoveArgs& args, hipStream_t s) {
 }
 
 // The pairs of a call, `per` at a time (more when a launch of `per` pairs
-// would hold fewer than kMinLaunchGroups workgroups): the index arrays
-// advance, every other argument stays.
+// would hold fewer than min_groups workgroups): the index arrays advance,
+// every other argument stays.
 template <typename F>
-int by_pairs(const MoveArgs& args, int per, F&& launch) {
-  const int64_t need = (kMinLaunchGroups + args.n_pieces - 1) / args.n_pieces;
+int by_pairs(const MoveArgs& args, int per, F&& launch, int64_t min_groups = kMinLaunchGroups) {
+  const int64_t need = (min_groups + args.n_pieces - 1) / args.n_pieces;
   if (need > per) per = need > args.n ? args.n : static_cast<int>(need);
   // launches of equal size (e.g. 64 pairs as 22 + 21 + 21, not 30 + 30 + 4)
   const int launches = (args.n + per - 1) / per;
@@ -1916,8 +1916,10 @@ int launch_qmove(bool pack, const MoveArgs& args, void* stream) {
   if (args.n == 0 || args.n_pieces == 0) return hipSuccess;
   if (args.n < 0 || args.n_pieces > 0x7FFFFFFFu) return static_cast<int>(hipErrorInvalidValue);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return by_pairs(args, pack ? kQPackPairs : kMovePairs,
-                  [&](const MoveArgs& part) { launch_qmove_part(pack, part, s); });
+  return by_pairs(
+      args, pack ? kQPackPairs : kMovePairs,
+      [&](const MoveArgs& part) { launch_qmove_part(pack, part, s); },
+      pack ? kQPackMinGroups : kMinLaunchGroups);
 }
 
 bool refresh_shape_supported(int d_k, int d_v) {
