@@ -286,6 +286,37 @@ def test_windowed_refresh_kda_and_mixed_sampled():
                         label=f"windowed {cfg.name}", head_windows=True)
 
 
+def test_windowed_refresh_keeps_retained_bits():
+    # The windowed refresh writes heads that also hold retained channels as
+    # whole rows (their retained values read and written back): retained
+    # words holding any bit pattern (NaN payloads, infinities, -0.0,
+    # denormals, raw random bits) must come back unchanged, and the local
+    # entries must still match the oracle.
+    cfg = W.kda_refresh(n_req=4)
+    P, O = _plans(cfg)
+    Wn = W.windows(cfg)
+    inp = W.refresh_inputs(cfg, Wn, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(41)
+    dense = torch.randint(0, 256, (cfg.n_req, O.dense_bytes), dtype=torch.uint8, device="cuda",
+                          generator=g)
+    words = dense[:, :O.B_temp_dense].view(torch.int32)
+    special = torch.from_numpy(W.special_values_f32().view(np.int32)).cuda()
+    pick = torch.randint(0, words.shape[1], (4096,), generator=g, device="cuda")
+    words[:, pick] = special[torch.arange(4096, device="cuda") % special.numel()]
+    before = dense.clone()
+    dst = torch.arange(cfg.n_req, dtype=torch.int32, device="cuda")
+    R.ckpt_refresh_suffix_windowed(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, dense, dst)
+    torch.cuda.synchronize()
+    assert P.status() == 0
+    _check_requests(P, O, inp, before, dense, dst.cpu().numpy(), [0, 3], layers=[0, 19],
+                    label="windowed kda, raw bits", head_windows=True)
+    keep = torch.from_numpy(mask_words(O).view(np.int32)).cuda()
+    for j in range(cfg.n_req):
+        a, b = dense[j].view(torch.int32), before[j].view(torch.int32)
+        assert torch.equal(a & keep, b & keep), f"retained words of checkpoint {j}"
+
+
 @pytest.mark.parametrize("w_max", [16, 64])
 def test_windowed_equals_full_when_requests_fit_the_windows(w_max):
     # every head window is >= 4, so requests of at most 4 tokens replay the
