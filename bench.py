@@ -76,7 +76,7 @@ def _args():
     ap.add_argument("--steps", type=int, default=300,
                     help="timed steps of every workload's pack + unpack + refresh")
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--side-steps", type=int, default=10,
+    ap.add_argument("--side-steps", type=int, default=20,
                     help="timed rounds of each section after the steps (INT8, windows, ...)")
     ap.add_argument("--workload", choices=("all",) + WORKLOADS, default="all",
                     help="all: the mixed headline with gdn and kda sub-objects")
@@ -387,7 +387,7 @@ def _cpu_baseline(cfg, P, ex, n_workers, dense_cpu, pack_bytes_per_ckpt, unpack_
     gbs = n * (pack_bytes_per_ckpt + unpack_bytes_per_ckpt) / t_move / 1e9
     return {
         "value": round(gbs, 4), "unit": "GB/s pack+unpack",
-        "cores": used, "kind": "oracle",
+        "cores": used, "kind": "oracle", "blas_threads_per_worker": 1,
         "refresh_request_tokens_per_s": round(ht / t_ref / heads_all, 3),
         "refresh_gflops": round(fl / t_ref / 1e9, 3),
         "refresh_eq7_windows_head_tokens_per_s": round(ht_w / t_win, 1),
@@ -440,8 +440,8 @@ def _bench_tp(cfg, args, stream):
         if e: e[2].record(stream)
     torch.cuda.synchronize()
     assert all(p.status() == 0 for p in plans)
-    t_pack = np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
-    t_unpack = np.mean([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
+    t_pack = np.median([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
+    t_unpack = np.median([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
     moved = 0
     for p in plans:
         pk, upk, _, _ = _algorithmic_bytes(p)
@@ -462,7 +462,9 @@ def _bench_tp(cfg, args, stream):
         "unpack_tp_ms": round(t_unpack * 1e3, 4),
         "pack_unpack_gbs": round(moved / (t_pack + t_unpack) / 1e9, 2),
         "frac_of_hbm_peak": round(moved / (t_pack + t_unpack) / 1e9 / HBM_PEAK_GBS, 4),
-        "kernel": "move_kernel<*, kAlt> (8 launches per direction)",
+        "kernel": (f"move_kernel<*, kAlt> ({sum(p.launches('pack_tp', n)[0] for p in plans)} "
+                   f"pack and {sum(p.launches('unpack_tp', n)[0] for p in plans)} unpack "
+                   f"launches over the {len(plans)} ranks)"),
         "rank0_pack_unpack_bytes_per_checkpoint": int(sum(_algorithmic_bytes(plans[0])[:2])),
     }
 
@@ -624,8 +626,8 @@ def _recorded_traffic(workload):
 
 
 def _timed(stream, rounds, warmup, *fns):
-    """Mean seconds of each of fns over `rounds` timed rounds (after warm-up
-    rounds), with HIP events recorded on `stream` around every call."""
+    """Median seconds of each of fns over `rounds` timed rounds (after
+    warm-up rounds), with HIP events recorded on `stream` around every call."""
     import numpy as np
     import torch
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
@@ -637,12 +639,8 @@ def _timed(stream, rounds, warmup, *fns):
             fn()
             if e: e[j + 1].record(stream)
     torch.cuda.synchronize()
-    return [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev])) * 1e-3
+    return [float(np.median([e[j].elapsed_time(e[j + 1]) for e in ev])) * 1e-3
             for j in range(len(fns))]
-
-
-def _launches(n, per):
-    return (n + per - 1) // per
 
 
 def _run_workload(name, args, stream, ex=None, n_workers=0):
@@ -675,6 +673,7 @@ def _run_workload(name, args, stream, ex=None, n_workers=0):
     # Eq. 1 per token and replayed head: decay (1), readout (2), rank-1 write (2) flops per element
     flops = T * sum(5 * P.layer(l)["d_v"] * P.layer(l)["d_k"] * P.layer(l)["n_refresh_heads"]
                     for l in range(info["n_layers"]))
+    head_steps = T * sum(P.layer(l)["n_refresh_heads"] for l in range(info["n_layers"]))
     n_groups = len({(P.layer(l)["kind"], P.layer(l)["d_k"]) for l in range(info["n_layers"])
                     if P.layer(l)["n_refresh_heads"]})
     torch.cuda.synchronize()
@@ -701,9 +700,10 @@ def _run_workload(name, args, stream, ex=None, n_workers=0):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     assert P.status() == 0
-    t_pack = np.array([e[0].elapsed_time(e[1]) for e in ev]).mean() * 1e-3
-    t_unpack = np.array([e[1].elapsed_time(e[2]) for e in ev]).mean() * 1e-3
-    t_ref = np.array([e[2].elapsed_time(e[3]) for e in ev]).mean() * 1e-3
+    # per section: the median over the timed steps (HIP events on the stream)
+    t_pack = float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+    t_unpack = float(np.median([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    t_ref = float(np.median([e[2].elapsed_time(e[3]) for e in ev])) * 1e-3
 
     rounds, warm = max(1, min(args.steps, args.side_steps)), args.warmup
     # INT8 checkpoints (Eq. 10): pack and unpack of the same checkpoints.
@@ -768,10 +768,14 @@ def _run_workload(name, args, stream, ex=None, n_workers=0):
 
     def hbm(role, bytes_, secs, launches, kernel):
         a = bytes_ / secs / 1e9
+        per_launch = int(bytes_ // launches)
+        tr = traffic.get(role)
         return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic.get(role),
+                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": tr,
+                # measured HBM bytes over the algorithmic bytes (a guard: <= 1.05)
+                "traffic_over_algorithmic": round(tr / per_launch, 4) if tr else None,
                 "kernel": kernel, "ms": round(secs * 1e3, 4), "bytes": int(bytes_),
-                "launches": launches, "bytes_per_launch": int(bytes_ // launches)}
+                "launches": launches, "bytes_per_launch": per_launch}
 
     def mfma(role, fl, secs, kernel, extra=None):
         a = fl / secs / 1e12
@@ -796,20 +800,24 @@ def _run_workload(name, args, stream, ex=None, n_workers=0):
                          {"note": "algorithmic fp32 flops (5 d^2 per token-head) against the fp32 "
                                   "matrix peak; the big products run as bf16 hi/lo splits on the "
                                   "bf16 matrix cores, whose issued rate is below",
+                          "token_head_steps_per_s": round(head_steps / t_ref, 1),
                           "bf16_mfma_issued_tflops": round(mm_bf16 / t_ref / 1e12, 2),
                           "bf16_mfma_peak": BF16_MFMA_PEAK_TF,
                           "fp32_mfma_issued_tflops": round(mm_f32 / t_ref / 1e12, 2)}),
-        "roofline_pack": hbm("pack", pack_b * n, t_pack, _launches(n, 16),
-                             "move_kernel<true> (16 pairs per launch)"),
-        "roofline_unpack": hbm("unpack", unpack_b * n, t_unpack, _launches(n, 16),
-                               "move_kernel<false> (16 pairs per launch)"),
+        "roofline_pack": hbm("pack", pack_b * n, t_pack, P.launches("pack", n)[0],
+                             f"move_kernel<true> ({P.launches('pack', n)[1]} pairs per launch)"),
+        "roofline_unpack": hbm("unpack", unpack_b * n, t_unpack, P.launches("unpack", n)[0],
+                               f"move_kernel<false> ({P.launches('unpack', n)[1]} pairs per "
+                               "launch)"),
         "int8": {
             "c_ckpt_int8": round(info["c_ckpt_int8"], 4),
             "pack_unpack_gbs": round(n * (pack_qb + unpack_qb) / (t_pack_q + t_unpack_q) / 1e9, 2),
-            "pack": hbm("pack_int8", n * pack_qb, t_pack_q, _launches(n, 32),
-                        "qmove_kernel<true, *> (32 pairs per launch)"),
-            "unpack": hbm("unpack_int8", n * unpack_qb, t_unpack_q, _launches(n, 16),
-                          "qmove_kernel<false> (16 pairs per launch)"),
+            "pack": hbm("pack_int8", n * pack_qb, t_pack_q, P.launches("pack_int8", n)[0],
+                        f"qmove_kernel<true, *> ({P.launches('pack_int8', n)[1]} pairs per "
+                        "launch)"),
+            "unpack": hbm("unpack_int8", n * unpack_qb, t_unpack_q, P.launches("unpack_int8", n)[0],
+                          f"qmove_kernel<false> ({P.launches('unpack_int8', n)[1]} pairs per "
+                          "launch)"),
         },
         "refresh_fused_gate": mfma("refresh_gate", flops, t_gate,
                                    "refresh_kernel<128, gate logits, false, false, false>",

@@ -230,6 +230,27 @@ int dasc_plan_upload(dasc_plan_t plan, void* device_buffer, int64_t bytes, void*
  * `stream`. */
 int dasc_plan_status(dasc_plan_t plan, uint32_t* status, int32_t clear, void* stream);
 
+/* Mover calls, for dasc_plan_launches. */
+enum {
+  DASC_MOVER_PACK = 0,        /* dasc_ckpt_pack */
+  DASC_MOVER_UNPACK = 1,      /* dasc_ckpt_unpack_zero_fill */
+  DASC_MOVER_PACK_INT8 = 2,   /* dasc_ckpt_pack_int8 */
+  DASC_MOVER_UNPACK_INT8 = 3, /* dasc_ckpt_unpack_int8_zero_fill */
+  DASC_MOVER_PACK_TP = 4,     /* dasc_ckpt_pack_tp */
+  DASC_MOVER_UNPACK_TP = 5    /* dasc_ckpt_unpack_tp_zero_fill */
+};
+
+/* How the given mover call over n (checkpoint, slot) pairs is issued: as
+ * *launches kernel launches of *pairs_per_launch pairs each (the last may
+ * hold fewer).  A call takes launches of a bounded number of pairs, raised
+ * where a launch would hold too few workgroups and then evened out; this
+ * query lets a caller relate per-launch measurements (profiler traces) to
+ * the bytes of its pairs.  Host only; DASC_EINVAL for an unknown mover, a
+ * TP mover on a plan that has no TP lists (dasc_plan_tp_info.one_store ==
+ * 0), or n < 0. */
+int dasc_plan_launches(dasc_plan_t plan, int32_t mover, int32_t n, int32_t* launches,
+                       int32_t* pairs_per_launch);
+
 int dasc_plan_destroy(dasc_plan_t plan);
 
 /*

@@ -100,6 +100,8 @@ def _load():
         "dasc_plan_slots": (_c_i64, [_c_p, _c_i64, _c_i32]),
         "dasc_plan_upload": (_c_i32, [_c_p, _c_p, _c_i64, _c_p]),
         "dasc_plan_status": (_c_i32, [_c_p, ctypes.POINTER(ctypes.c_uint32), _c_i32, _c_p]),
+        "dasc_plan_launches": (_c_i32, [_c_p, _c_i32, _c_i32, ctypes.POINTER(_c_i32),
+                                        ctypes.POINTER(_c_i32)]),
         "dasc_plan_destroy": (_c_i32, [_c_p]),
         "dasc_ckpt_pack": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_i64, _c_i64, _c_p,
                                     _c_i32, _c_p]),
@@ -268,6 +270,16 @@ class Plan:
         _check(lib.dasc_plan_status(self._h, ctypes.byref(s), 1 if clear else 0,
                                     _stream_handle(stream)), "plan_status")
         return int(s.value)
+
+    MOVERS = {"pack": 0, "unpack": 1, "pack_int8": 2, "unpack_int8": 3, "pack_tp": 4,
+              "unpack_tp": 5}
+
+    def launches(self, mover: str, n: int) -> tuple:
+        """(launches, pairs per launch) of a mover call over n pairs."""
+        nl, per = _c_i32(0), _c_i32(0)
+        _check(lib.dasc_plan_launches(self._h, self.MOVERS[mover], int(n), ctypes.byref(nl),
+                                      ctypes.byref(per)), "plan_launches")
+        return int(nl.value), int(per.value)
 
     def close(self):
         h = getattr(self, "_h", None)

@@ -881,6 +881,41 @@ int dasc_plan_status(dasc_plan_t p, uint32_t* status, int32_t clear, void* strea
   return DASC_OK;
 }
 
+int dasc_plan_launches(dasc_plan_t p, int32_t mover, int32_t n, int32_t* launches,
+                       int32_t* pairs_per_launch) {
+  if (!p || !launches || !pairs_per_launch) return fail(DASC_EINVAL, "plan_launches: null argument");
+  if (n < 0) return fail(DASC_EINVAL, "plan_launches: n < 0");
+  const std::vector<Piece>* list = nullptr;
+  int per = kMovePairs;
+  int64_t min_groups = kMinLaunchGroups;
+  switch (mover) {
+    case DASC_MOVER_PACK: list = &p->pack; break;
+    case DASC_MOVER_UNPACK: list = &p->unpack; break;
+    case DASC_MOVER_PACK_INT8:
+      list = &p->pack_q;
+      per = kQPackPairs;
+      min_groups = kQPackMinGroups;
+      break;
+    case DASC_MOVER_UNPACK_INT8: list = &p->unpack_q; break;
+    case DASC_MOVER_PACK_TP:
+    case DASC_MOVER_UNPACK_TP:
+      if (!p->tp.one_store) return fail(DASC_EINVAL, "plan_launches: plan has no TP storage balancing");
+      list = mover == DASC_MOVER_PACK_TP ? &p->pack_tp : &p->unpack_tp;
+      break;
+    default: return fail(DASC_EINVAL, "plan_launches: unknown mover");
+  }
+  const uint32_t np = static_cast<uint32_t>(list->size());
+  if (n == 0 || np == 0) {
+    *launches = 0;
+    *pairs_per_launch = 0;
+    return DASC_OK;
+  }
+  const int32_t pl = mover_pairs_per_launch(n, np, per, min_groups);
+  *pairs_per_launch = pl;
+  *launches = (n + pl - 1) / pl;
+  return DASC_OK;
+}
+
 int dasc_plan_destroy(dasc_plan_t p) {
   delete p;
   return DASC_OK;

@@ -58,6 +58,19 @@ constexpr int kQPackPairs = 32;
 constexpr int64_t kMinLaunchGroups = 32768;
 constexpr int64_t kQPackMinGroups = 8192;
 
+// Pairs per launch of a mover call over n pairs of a list of n_pieces
+// pieces: at most `per`, raised until a launch holds at least min_groups
+// workgroups, then evened out over the launches (64 pairs in launches of 30
+// become 22 + 21 + 21, not 30 + 30 + 4).  The number of launches is
+// ceil(n / result).  Shared by the launcher and the plan's launch query.
+inline int32_t mover_pairs_per_launch(int32_t n, uint32_t n_pieces, int per, int64_t min_groups) {
+  if (n <= 0 || n_pieces == 0) return 1;
+  const int64_t need = (min_groups + n_pieces - 1) / n_pieces;
+  if (need > per) per = need > n ? n : static_cast<int>(need);
+  const int32_t launches = (n + per - 1) / per;
+  return (n + launches - 1) / launches;
+}
+
 // Rows of a KDA head one piece moves: 32 rows make every unit segment a
 // whole 128-byte line (32 fp32).
 constexpr int kKdaRows = 32;

@@ -1881,11 +1881,7 @@ void launch_qmove_part(bool pack, const MoveArgs& args, hipStream_t s) {
 // every other argument stays.
 template <typename F>
 int by_pairs(const MoveArgs& args, int per, F&& launch, int64_t min_groups = kMinLaunchGroups) {
-  const int64_t need = (min_groups + args.n_pieces - 1) / args.n_pieces;
-  if (need > per) per = need > args.n ? args.n : static_cast<int>(need);
-  // launches of equal size (e.g. 64 pairs as 22 + 21 + 21, not 30 + 30 + 4)
-  const int launches = (args.n + per - 1) / per;
-  per = (args.n + launches - 1) / launches;
+  per = mover_pairs_per_launch(args.n, args.n_pieces, per, min_groups);
   MoveArgs part = args;
   for (int32_t i = 0; i < args.n; i += per) {
     part.n = args.n - i < per ? args.n - i : per;

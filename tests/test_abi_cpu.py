@@ -25,7 +25,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 25
+    assert len(names) == 26
     out = subprocess.run(["nm", "-D", "--defined-only", R.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\b[TW]\s+(dasc_[a-z0-9_]+)\b", out))
@@ -279,3 +279,28 @@ def test_tp_calls_reject_a_mixed_store_plan():
     f = ctypes.c_void_p(16)
     assert R.lib.dasc_ckpt_pack_tp(P._h, f, 4096, 1, f, f, 4096, 1, f, f, 4096, 1, f, 1,
                                    None) == -5
+
+
+def test_plan_launches():
+    # dasc_plan_launches: launches of at most 16 pairs (INT8 pack: 32),
+    # raised where a launch would hold too few workgroups, evened out
+    cfg = W.kda(n_ckpt=64, n_req=2, window=8)
+    P = R.Plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max)
+    for mover in ("pack", "unpack", "pack_int8", "unpack_int8"):
+        for n in (1, 5, 16, 17, 64, 100, 512):
+            nl, per = P.launches(mover, n)
+            assert nl >= 1 and per >= 1 and (nl - 1) * per < n <= nl * per, (mover, n, nl, per)
+            base = 32 if mover == "pack_int8" else 16
+            assert nl <= -(-n // base)  # the workgroup minimum only merges launches
+        assert P.launches(mover, 0) == (0, 0)
+    assert P.launches("pack", 64) == (4, 16)
+    # the INT8 unpack list holds few pieces here: launches of 22 + 21 + 21
+    assert P.launches("unpack_int8", 64) == (3, 22)
+    assert P.launches("pack_tp", 64)[0] >= 1  # TP = 1: the plain slot
+    with pytest.raises(R.DascError):
+        P.launches("unpack", -1)
+    h = ctypes.c_int32(0)
+    assert R.lib.dasc_plan_launches(P._h, 9, 4, ctypes.byref(h), ctypes.byref(h)) != 0
+    Pt = R.Plan(cfg.layers, cfg.a_s, cfg.eps, cfg.w_max, tp=8, rank=3)
+    nl, per = Pt.launches("unpack_tp", 64)
+    assert nl * per >= 64
