@@ -1211,8 +1211,15 @@ refresh_kernel(RefreshArgs a) {
       // loop has no branch): for NB4 = 32 by a reduce-scatter that leaves
       // one entry per lane, otherwise by DPP sums within a row whose last
       // lane stores every entry.
-      const bool h = PW >= 0 && (tid & 32) != 0;  // upper half-wave
-      const int p = PW >= 0 ? 2 * PW + (h ? 1 : 0) : tid / NB4, c4 = 4 * (tid % NB4);
+      // PW >= 0: lanes with bit 3 clear serve row pair 2 PW, the others
+      // 2 PW + 1, so that both pairs span all four 16-lane rows and the
+      // sums over a pair's lanes can cross rows with lane swaps (below).
+      // Channel block ci of a lane: bits 0-2 from the lane, bits 3-4 from
+      // its row, flipped for the second pair so that the two pairs of a
+      // 16-lane row read different LDS banks.
+      const bool h = PW >= 0 && (lane & 8) != 0;
+      const int ci = PW >= 0 ? (lane & 7) | (((lane >> 4) ^ (h ? 1 : 0)) << 3) : tid % NB4;
+      const int p = PW >= 0 ? 2 * PW + (h ? 1 : 0) : tid / NB4, c4 = 4 * ci;
       // entry i is in row p (i < p), and row 15 - p starts at i = p
       auto in_row_p = [&](int i) {
         return PW >= 0 ? (i < 2 * PW || (i == 2 * PW && h)) : i < p;
@@ -1258,12 +1265,43 @@ refresh_kernel(RefreshArgs a) {
       // bases, constant steps
       float* const lP = &sh.LT[0][0] + (p - 1) * (kC + 4) + p;
       float* const lQ = &sh.LT[0][0] + (kC - 2) * (kC + 4) + (kC - 1 - p);
-      if constexpr (NB4 == 32) {
+      if constexpr (PW >= 0) {
         // The 15 entries' partial sums (4 channels each) are summed over the
-        // row pair's 32 lanes by a reduce-scatter: four DPP exchanges within
-        // each 16-lane row leave lane r16 with entry r16's row sum, and one
-        // lane exchange across the two rows completes it; lanes 0 .. 14 of
-        // the lower row then store one entry each.
+        // row pair's 32 lanes by a reduce-scatter.  Across rows, a lane swap
+        // between two registers (v_permlane32_swap / v_permlane16_swap: the
+        // upper half of the first register trades places with the lower
+        // half of the second) gives each lane its kept entry from both
+        // partners with one add and no select: the lanes 32 apart, then 16
+        // apart.  Within the 8 lanes of a pair in a row, two DPP exchanges
+        // halve the rest, and one more adds the last partner's sum.  The
+        // lane keeps entry e = 8 b5 + 4 b4 + 2 b2 + b1 (b = its lane bits);
+        // lanes with b0 = 0 store it.
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < kC - 1; ++i) v[i] = lv[i];
+        v[15] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]),
+                                                          __float_as_uint(v[i + 8]), false, false);
+          v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]),
+                                                          __float_as_uint(v[i + 4]), false, false);
+          v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        }
+        reduce_scatter_step<2, 0x141>(v, (lane & 4) != 0);  // row_half_mirror: l <-> 7 - l
+        reduce_scatter_step<1, 0x4E>(v, (lane & 2) != 0);   // quad_perm [2,3,0,1]
+        const float sum = v[0] + dpp<0xB1>(v[0]);           // quad_perm [1,0,3,2]
+        const int e = ((lane >> 2) & 8) | ((lane >> 2) & 4) | ((lane >> 1) & 2) | ((lane >> 1) & 1);
+        if ((lane & 1) == 0 && e < kC - 1) *((in_row_p(e) ? lP : lQ) - e * (kC + 4)) = sum;
+      } else if constexpr (NB4 == 32) {
+        // The same sums for a lane layout known only at run time: four DPP
+        // exchanges within each 16-lane row leave lane r16 with entry r16's
+        // row sum, and one lane exchange across the two rows completes it;
+        // lanes 0 .. 14 of the lower row then store one entry each.
         const int r16 = lane & 15;
         float v[16];
 #pragma unroll
