@@ -931,6 +931,7 @@ struct alignas(16) RefreshLds {
   float PA[D], PD[D];         // exp(A_log) and dt_bias per channel (GDN: [0])
   float LT[kC][kC + 4];       // L transposed: LT[s][t] = beta_t M_{t,s}, s < t
   float T[kC][kC + 4];        // (I + L)^-1
+  float Xt[8][8 + 4];         // the inverse's L21 T11, transposed
 };
 
 // Split of an fp32 value into bf16 hi + lo (hi = x truncated to bf16, lo =
@@ -1387,62 +1388,69 @@ refresh_kernel(RefreshArgs a) {
     }
   };
 
-  // T = (I + L)^-1 by columns: lane s = lane % 16 owns column s,
-  // T[t][s] = delta_{ts} - sum_{u<t} L[t][u] T[u][s].  For t <= s the sum
-  // only meets T[u][s] = 0 (u < s), so one formula serves every row and the
-  // code has no branch.  The sums are built right-looking: as soon as
-  // T[u][s] is known it is added into the running sums of every later row,
-  // so the dependent chain is one multiply-add per row, not one per term.
-  // One wave per chunk computes it (its four lane groups hold the same
-  // column, so their stores write identical values); the others read T
-  // after the barrier that ends the phase.
+  // T = (I + L)^-1 in 8 x 8 blocks: with L = [[L11, 0], [L21, L22]] the
+  // inverse is [[T11, 0], [T21, T22]] with T11 = (I + L11)^-1,
+  // T22 = (I + L22)^-1 and T21 = -T22 L21 T11.  One wave per chunk computes
+  // it (its four 16-lane rows do the same work; their stores write the same
+  // values); the others read T after the barrier that ends the phase.
+  //  1. Lane sc = lane % 16 < 8 computes column sc of T11, lanes 8 .. 15
+  //     column sc of T22 (block offset o), T[u][s] = delta_{us} -
+  //     sum_{v<u} L[u][v] T[v][s] right-looking: as soon as T[u][s] is
+  //     known it is added into the running sums of the later rows, so the
+  //     dependent chain is one multiply-add per row (8 rows, not 16).  For
+  //     u < s the sums only meet zeros, so one formula serves every row.
+  //     Row u + 1 of L^T is loaded while row u is applied (the compiler
+  //     fence keeps it from hoisting every load).
+  //  2. Every lane takes column lane % 8 of T11 (DPP within its row), and
+  //     lane (t, s) = (8 + lane / 8, lane % 8) forms X = L21 T11 at (t, s),
+  //     stored transposed, then T21[t][s] = -sum_u T22[t][u] X[u][s].
+  // T12 stays zero (cleared once before the chunk loop).
   auto invert = [&]() {
-    const int sc = lane & 15;
-    float run[kC];
+    const int sc = lane & 15, o = sc & 8;
+    float run[8], tc[8];
 #pragma unroll
-    for (int t = 0; t < kC; ++t) run[t] = 0.f;
+    for (int t = 0; t < 8; ++t) run[t] = 0.f;
+    v4f rowv[2][2];
+    rowv[0][0] = *reinterpret_cast<const v4f*>(&sh.LT[o][o]);
+    rowv[0][1] = *reinterpret_cast<const v4f*>(&sh.LT[o][o + 4]);
 #pragma unroll
-    for (int u = 0; u < kC; ++u) {
-      const float tu = (u == sc ? 1.f : 0.f) - run[u];
-      sh.T[u][sc] = tu;
+    for (int u = 0; u < 8; ++u) {
+      if (u + 1 < 7) {
 #pragma unroll
-      for (int q = (u + 1) / 4; q < kC / 4; ++q) {  // row u of L^T, 4 at a time
-        const v4f lt = *reinterpret_cast<const v4f*>(&sh.LT[u][4 * q]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (4 * q + e > u) run[4 * q + e] = fmaf(lt[e], tu, run[4 * q + e]);
+        for (int q = (u + 2) / 4; q < 2; ++q)
+          rowv[(u + 1) & 1][q] = *reinterpret_cast<const v4f*>(&sh.LT[o + u + 1][o + 4 * q]);
       }
-    }
-  };
-  // The same with the next row of L^T loaded while the current one is
-  // applied (the chain no longer waits for LDS at every row); the compiler
-  // fence keeps it from hoisting every load, which would spill.  Used where
-  // registers allow (the chunk-loop kernels).
-  auto invert_prefetch = [&]() {
-    const int sc = lane & 15;
-    float run[kC];
+      const float tu = (o + u == sc ? 1.f : 0.f) - run[u];
+      tc[u] = tu;
 #pragma unroll
-    for (int t = 0; t < kC; ++t) run[t] = 0.f;
-    v4f rowv[2][kC / 4];
-#pragma unroll
-    for (int q = 0; q < kC / 4; ++q) rowv[0][q] = *reinterpret_cast<const v4f*>(&sh.LT[0][4 * q]);
-#pragma unroll
-    for (int u = 0; u < kC; ++u) {
-      if (u + 1 < kC - 1) {
-#pragma unroll
-        for (int q = (u + 2) / 4; q < kC / 4; ++q)
-          rowv[(u + 1) & 1][q] = *reinterpret_cast<const v4f*>(&sh.LT[u + 1][4 * q]);
-      }
-      const float tu = (u == sc ? 1.f : 0.f) - run[u];
-#pragma unroll
-      for (int q = (u + 1) / 4; q < kC / 4; ++q) {
+      for (int q = (u + 1) / 4; q < 2; ++q) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (4 * q + e > u) run[4 * q + e] = fmaf(rowv[u & 1][q][e], tu, run[4 * q + e]);
       }
-      sh.T[u][sc] = tu;
+      sh.T[o + u][sc] = tu;
       __asm__ volatile("" ::: "memory");
     }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)  // row_ror:8 into lanes 8 .. 15 of each row (banks 2, 3)
+      tc[u] = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(tc[u]),
+                                                         __float_as_int(tc[u]), 0x128, 0xF, 0xC, false));
+    const int t = 8 + (lane >> 3), s = lane & 7;
+    float x = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x = fmaf(sh.LT[u][t], tc[u], x);  // L[t][u] = LT[u][t]
+    sh.Xt[s][t - 8] = x;
+    const v4f a0 = *reinterpret_cast<const v4f*>(&sh.T[t][8]);
+    const v4f a1 = *reinterpret_cast<const v4f*>(&sh.T[t][12]);
+    const v4f x0 = *reinterpret_cast<const v4f*>(&sh.Xt[s][0]);
+    const v4f x1 = *reinterpret_cast<const v4f*>(&sh.Xt[s][4]);
+    float y = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y = fmaf(a0[e], x0[e], y);
+      y = fmaf(a1[e], x1[e], y);
+    }
+    sh.T[t][s] = -y;
   };
 
   // Write-back of the windowed refresh (below): heads that also hold
@@ -1493,6 +1501,7 @@ refresh_kernel(RefreshArgs a) {
       sh.PA[tid] = a.gate_expA[task.param_off + tid];
       sh.PD[tid] = a.gate_dt[task.param_off + tid];
     }
+    if (tid < 64) sh.T[tid >> 3][8 + (tid & 7)] = 0.f;  // T12 of every chunk's inverse
     fetch(0);
     __syncthreads();
     stage1(0);
@@ -1507,10 +1516,7 @@ refresh_kernel(RefreshArgs a) {
     for (int64_t n = 0; n < nchunks; ++n) {
       const int cb = ONE ? 0 : static_cast<int>(n & 1), nb = cb ^ 1;
       // ---- phase 1: T(n), U0 = S Q(n)  ||  stage chunk n + 1, fetch n + 2
-      if (wave == static_cast<int>(n % Sh::kNW)) {  // one wave, rotating
-        if constexpr (ONE) invert();
-        else invert_prefetch();
-      }
+      if (wave == static_cast<int>(n % Sh::kNW)) invert();  // one wave, rotating
       v4f U[VTW];
 #pragma unroll
       for (int vv = 0; vv < VTW; ++vv) U[vv] = v4f{0.f, 0.f, 0.f, 0.f};
