@@ -887,7 +887,10 @@ struct RefreshShape {
   static constexpr int kKT = D / 16;                  // k tiles
   static constexpr bool kSplit = D >= 64;             // big products on split bf16 MFMA
   static constexpr int kWavesPerSimd = 2;  // occupancy target
-  static constexpr int kWavesPerSimdOne = D == 128 ? 2 : 4;  // ... of the one-chunk kernel
+  static constexpr int kWavesPerSimdOne = 4;  // ... of the one-chunk kernel
+  // ... of the one-chunk kernel over KDA heads of d = 128, which reads the
+  // old rows of its whole-row write-back before the replay
+  static constexpr int kWavesPerSimdOneEarly = D == 128 ? 2 : 4;
   static constexpr int kVTW = D >= 32 ? 2 : 1;        // v tiles per wave
   static constexpr int kNW = (D / 16) / kVTW;         // waves per head
   static constexpr int kNT = 64 * kNW;                // threads
@@ -1018,12 +1021,15 @@ __device__ __forceinline__ v4f mfma4(float a, float b, v4f c) {
 // ONE (with WINDOWED, chosen when every window of the launch is at most one
 // chunk, so that every head replays at most kC tokens): the pipeline's
 // staging of later chunks and the parity buffers are left out, which frees
-// LDS and registers for a third workgroup per CU; short replays are bound by
-// each head's serial chain (stage, L, T, products, write-back), which more
-// resident heads overlap.
+// LDS and registers for four workgroups per CU (two for KDA heads of d =
+// 128, whose registers go to reading the write-back's old rows early);
+// short replays are bound by each head's serial chain (stage, L, T,
+// products, write-back), which more resident heads overlap.
 template <int D, int GATE, bool WINDOWED, bool FUSED, bool ONE>
 __global__ void __launch_bounds__(RefreshShape<D>::kNT)
-    __attribute__((amdgpu_waves_per_eu(ONE ? RefreshShape<D>::kWavesPerSimdOne
+    __attribute__((amdgpu_waves_per_eu(ONE ? (GATE != kGateHead && GATE != kGateAlphaHead && !FUSED
+                                                  ? RefreshShape<D>::kWavesPerSimdOneEarly
+                                                  : RefreshShape<D>::kWavesPerSimdOne)
                                            : RefreshShape<D>::kWavesPerSimd)))
 refresh_kernel(RefreshArgs a) {
   static_assert(!ONE || WINDOWED, "the one-chunk kernel serves windowed replays");
@@ -1472,7 +1478,7 @@ refresh_kernel(RefreshArgs a) {
     }
     rmw = !all_local;
   }
-  constexpr bool kEarly = ONE && !FUSED;
+  constexpr bool kEarly = ONE && !FUSED && kChan;  // GDN heads are all local: no old rows
   v4f old[kEarly ? VTW : 1][NI];
   auto read_old = [&](auto vv_c) __attribute__((always_inline)) {
     constexpr int vv = decltype(vv_c)::value;
