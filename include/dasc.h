@@ -306,6 +306,8 @@ int dasc_ckpt_unpack_zero_fill(dasc_plan_t plan, const void* pool_base,
  *   tok_offsets [n+1] int64, device: request r owns tokens
  *     [tok_offsets[r], tok_offsets[r+1]); must be non-decreasing within
  *     [0, n_tokens] (a request that breaks this is skipped and flagged).
+ *   n_tokens (= T, the rows of k, v, a and beta) must be below 2^31
+ *     (DASC_EINVAL otherwise).
  *   dst_idx [n] int32, device; two entries must not name the same checkpoint.
  */
 int dasc_ckpt_refresh_suffix(dasc_plan_t plan, const uint16_t* k, const uint16_t* v,

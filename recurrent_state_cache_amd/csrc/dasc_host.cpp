@@ -1136,6 +1136,8 @@ static int run_refresh(const char* w, bool head_windows, dasc_plan_t p, const ui
   if (n == 0 || p->refresh.empty()) return DASC_OK;
   if (!tok_offsets || !dense_base || !dst_idx) return fail(DASC_EINVAL, std::string(w) + ": null pointer");
   if (n_tokens < 0) return fail(DASC_EINVAL, std::string(w) + ": n_tokens must be >= 0");
+  // the kernels index tokens in 32 bits
+  if (n_tokens > INT32_MAX) return fail(DASC_EINVAL, std::string(w) + ": n_tokens must be below 2^31");
   const void* decays = use_alpha ? static_cast<const void*>(alpha) : static_cast<const void*>(a);
   if (n_tokens > 0 && (!k || !v || !decays || !beta))
     return fail(DASC_EINVAL, std::string(w) + ": null input pointer");

@@ -1073,18 +1073,23 @@ refresh_kernel(RefreshArgs a) {
   // packed, or 8 fp32 decays in ra and ra2, and beta), fetched one chunk
   // ahead of their staging.  The row is clamped into the request, so every
   // load is in bounds; past the end the values are replaced by the no-op
-  // token when staged.
+  // token when staged.  Token indices are below 2^31 (the host checks
+  // n_tokens) and row widths below 2^32, so a row's offset is one 32 x 32
+  // -> 64-bit multiply-add.
+  const uint32_t t0u = static_cast<uint32_t>(t0), t1u = static_cast<uint32_t>(t1);
+  const uint32_t k_row = static_cast<uint32_t>(a.k_row), v_row = static_cast<uint32_t>(a.v_row);
+  const uint32_t g_row = static_cast<uint32_t>(a.g_row), b_row = static_cast<uint32_t>(a.b_row);
   u32x4 rk, rv, ra, ra2;
   float rb;
   bool r_real;
   auto fetch = [&](int64_t n) {
-    const int64_t tok = t0 + n * kC + it_t;
-    r_real = tok < t1;
-    const int64_t tc = r_real ? tok : t1 - 1;
-    rk = *reinterpret_cast<const u32x4*>(a.k + tc * a.k_row + task.k_off + j0);
-    rv = *reinterpret_cast<const u32x4*>(a.v + tc * a.v_row + task.v_off + j0);
+    const uint32_t tok = t0u + static_cast<uint32_t>(n) * kC + it_t;
+    r_real = tok < t1u;
+    const uint64_t tc = r_real ? tok : t1u - 1;
+    rk = *reinterpret_cast<const u32x4*>(a.k + tc * k_row + task.k_off + j0);
+    rv = *reinterpret_cast<const u32x4*>(a.v + tc * v_row + task.v_off + j0);
     if constexpr (kAlpha) {
-      const float* pp = a.alpha + tc * a.g_row + task.g_off;
+      const float* pp = a.alpha + tc * g_row + task.g_off;
       if constexpr (GATE == kGateAlphaChan) {
         ra = *reinterpret_cast<const u32x4*>(pp + j0);
         ra2 = *reinterpret_cast<const u32x4*>(pp + j0 + 4);
@@ -1098,7 +1103,7 @@ refresh_kernel(RefreshArgs a) {
         ra = u32x4{__float_as_uint(pp[0]), 0u, 0u, 0u};
       }
     } else {
-      const uint16_t* ap = a.a + tc * a.g_row + task.g_off;
+      const uint16_t* ap = a.a + tc * g_row + task.g_off;
       if constexpr (GATE == kGateChan) {
         ra = *reinterpret_cast<const u32x4*>(ap + j0);
       } else if constexpr (GATE == kGateChanSplit) {
@@ -1110,18 +1115,20 @@ refresh_kernel(RefreshArgs a) {
         ra = u32x4{static_cast<uint32_t>(ap[0]), 0u, 0u, 0u};
       }
     }
-    rb = a.beta[tc * a.b_row + task.b_off];
+    rb = a.beta[tc * b_row + task.b_off];
   };
 
   // Stage the fetched token into LDS buffer vb: decays (given, or by Eq. 2),
-  // k, v, beta.  A token past the end becomes the no-op token: k = v = 0
-  // words, beta = 0, and a decay of exactly 1 (given decays are replaced by
-  // 1; for logits a zero gate scale makes the decay exp2(-0) = 1).  (The
-  // padding is applied to inputs, not by selecting results, so the code has
-  // no branch.)
+  // k, v, beta.  A token past the end becomes a no-op: beta = 0 and a decay
+  // of exactly 1 (given decays are replaced by 1; for logits a zero gate
+  // scale makes the decay exp2(-0) = 1).  Its k and v (the last token's,
+  // finite) then meet only zero factors: its row of L is beta k = 0, so its
+  // row of T is the unit row and its entry of C = T R is R_t = beta (v -
+  // u) = 0, and no earlier token's entry reads it (T is lower triangular).
+  // (The padding is applied to inputs, not by selecting results, so the
+  // code has no branch.)
   auto stage1 = [&](int vb) {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    const u32x4 wk = r_real ? rk : zero, wv = r_real ? rv : zero;
+    const u32x4 wk = rk, wv = rv;
     float kf[8], al[8];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {

@@ -4,6 +4,8 @@ C ABI; plus the one-hot-write-then-decay closed form on the GPU path.  The
 error metric is the refresh's: max |S_gpu - S_fp64| over the written (local)
 entries, over the Frobenius norm of the fp64 scratch state, <= 1e-4; the
 bytes the refresh must not touch are compared bit for bit."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -224,6 +226,28 @@ def test_alpha_rejects_misaligned_and_null_decays():
         R.ckpt_refresh_suffix_alpha(P, inp.k, inp.v, inp.a, inp.beta, inp.tok_off, dense, dst)
     torch.cuda.synchronize()
     assert torch.equal(dense, before)
+
+
+def test_refresh_rejects_token_counts_from_2_31():
+    # The kernels index tokens in 32 bits: the host refuses n_tokens >= 2^31
+    # (DASC_EINVAL) before anything is launched.
+    cfg = W.tiny_kda()
+    P, O = _plans(cfg)
+    Wn = W.windows(cfg)
+    inp, alpha = _inputs(cfg, Wn, "cuda")
+    dense = W.dense_states(cfg, 2, device="cuda", seed=9)
+    before = dense.clone()
+    dst = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    args = (ptr(inp.k), ptr(inp.v), ptr(alpha), ptr(inp.beta), ptr(inp.tok_off))
+    tail = (ptr(dense), dense.stride(0), dense.shape[0], ptr(dst), 2, None)
+    for n_tokens in (2 ** 31, 2 ** 40):
+        assert R.lib.dasc_ckpt_refresh_suffix_alpha(P._h, *args, n_tokens, *tail) == -1
+        assert R.lib.dasc_ckpt_refresh_suffix_alpha_windowed(P._h, *args, n_tokens, *tail) == -1
+    assert R.lib.dasc_ckpt_refresh_suffix_alpha(P._h, *args, int(inp.k.shape[0]), *tail) == 0
+    torch.cuda.synchronize()
+    assert P.status() == 0
+    assert not torch.equal(dense, before)
 
 
 @pytest.mark.parametrize("kind", [W.KDA, W.GDN])
