@@ -228,6 +228,48 @@ def test_alpha_rejects_misaligned_and_null_decays():
     assert torch.equal(dense, before)
 
 
+@pytest.mark.parametrize("kind,d", [(W.KDA, 128), (W.GDN, 128), (W.KDA, 32), (W.GDN, 16)])
+def test_one_repeated_key_keeps_only_the_last_value(kind, d):
+    # Every token writes with the same unit key k (bf16-exact), beta = 1 and
+    # decay 1: each write replaces the whole state, S_t = v_t k^T ([dasc]
+    # §3.1 Eq. 1 with alpha = 1: S (I - k k^T) + v k^T and S = v' k^T gives
+    # v k^T).  Inside a chunk every entry of L is 1, the worst case of the
+    # inverse (its 8 x 8 blocks and their coupling block included); 40
+    # tokens span two full chunks and a partial one.  Independent of the
+    # oracle.
+    H, T = 4, 40
+    n = H * d if kind == W.KDA else H
+    lay = W.Layer(kind, H, d, d, np.full(n, 2.0, np.float32), np.zeros(n, np.float32), 0)
+    cfg = W.Config("repeat", [lay], w_max=64, seed=43)
+    P, O = _plans(cfg)
+    assert len(O.refreshed_heads(0)) == H and O.layers[0].r == 0
+    rng = np.random.default_rng(11)
+    key = np.zeros((H, d), np.float32)
+    for h in range(H):
+        idx = rng.choice(d, 16, replace=False)
+        key[h, idx] = rng.choice([-0.25, 0.25], 16)
+    kt = torch.from_numpy(np.broadcast_to(key.reshape(1, H * d), (T, H * d)).copy())
+    kt = kt.to(torch.bfloat16).cuda()
+    vt = torch.randn(T, H * d).to(torch.bfloat16).cuda()
+    alpha = torch.ones(T, n, dtype=torch.float32, device="cuda")
+    bt = torch.ones(T, H, dtype=torch.float32, device="cuda")
+    dense = torch.zeros((1, O.dense_bytes), dtype=torch.uint8, device="cuda")
+    R.ckpt_refresh_suffix_alpha(P, kt, vt, alpha, bt, torch.tensor([0, T], device="cuda"),
+                                dense, torch.zeros(1, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert P.status() == 0
+    row = dense[0].cpu().numpy()
+    worst = 0.0
+    for h in range(H):
+        S = head_state(row, O, 0, h).astype(np.float64)
+        vlast = vt[-1, h * d:(h + 1) * d].float().cpu().numpy().astype(np.float64)
+        ref = np.outer(vlast, key[h].astype(np.float64))
+        err = np.max(np.abs(S - ref)) / np.linalg.norm(ref)
+        worst = max(worst, err)
+        assert err <= TOL, f"head {h}: {err:.3e}"
+    log(f"[refresh alpha] repeated key, kind {kind} d {d}: worst error {worst:.3e}")
+
+
 def test_refresh_rejects_token_counts_from_2_31():
     # The kernels index tokens in 32 bits: the host refuses n_tokens >= 2^31
     # (DASC_EINVAL) before anything is launched.
