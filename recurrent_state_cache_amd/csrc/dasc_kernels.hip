@@ -1128,12 +1128,11 @@ refresh_kernel(RefreshArgs a) {
   // (The padding is applied to inputs, not by selecting results, so the
   // code has no branch.)
   auto stage1 = [&](int vb) {
-    const u32x4 wk = rk, wv = rv;
     float kf[8], al[8];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      kf[2 * q] = bf16_lo(wk[q]);
-      kf[2 * q + 1] = bf16_hi(wk[q]);
+      kf[2 * q] = bf16_lo(rk[q]);
+      kf[2 * q + 1] = bf16_hi(rk[q]);
     }
     if constexpr (kAlpha && kChan) {
 #pragma unroll
@@ -1168,7 +1167,7 @@ refresh_kernel(RefreshArgs a) {
       *reinterpret_cast<v4f*>(&sh.A[it_t][j0 + 4]) = v4f{al[4], al[5], al[6], al[7]};
       *reinterpret_cast<v4f*>(&sh.K[it_t][j0]) = v4f{kf[0], kf[1], kf[2], kf[3]};
       *reinterpret_cast<v4f*>(&sh.K[it_t][j0 + 4]) = v4f{kf[4], kf[5], kf[6], kf[7]};
-      *reinterpret_cast<u32x4*>(&sh.V[vb][it_t][j0]) = wv;
+      *reinterpret_cast<u32x4*>(&sh.V[vb][it_t][j0]) = rv;
       sh.B[vb][it_t] = bv;  // the JB lanes of a token store the same value
     }
   };
